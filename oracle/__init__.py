@@ -1,0 +1,232 @@
+"""CPU oracle for the routed-expert hot path -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, ``__graft_entry__.smoke()`` and the bench's ``cpu_baseline`` leg may
+import this package.  The product library (``mxfp4_routed_expert_k3x_amd``) never does; it
+has no CPU fallback.
+
+The arithmetic lives in ``k3x_oracle.c`` (plain C, built with ``-ffp-contract=off`` and
+compiled once with a float accumulator -- the verdict oracle -- and once with a double
+accumulator -- its self-check).  This module only loads it and marshals numpy arrays.
+Every function cites the passage of the kimi-k3-in-c README it follows in the C source.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "k3x_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-fPIC",
+           "-Wall", "-Wextra", "-Werror"]
+
+
+def build(force: bool = False) -> str:
+    """Compile liboracle.so with gcc (two objects: float and double accumulators)."""
+    if not force and os.path.exists(_LIB) and os.path.getmtime(_LIB) >= os.path.getmtime(_SRC):
+        return _LIB
+    objs = []
+    for acc, sfx, common in (("float", "f32", True), ("double", "f64", False)):
+        obj = os.path.join(_HERE, f"_oracle_{sfx}.o")
+        cmd = ["gcc", *_CFLAGS, f"-DORACLE_ACC={acc}", f"-DORACLE_SFX={sfx}", "-c", _SRC, "-o", obj]
+        if common:
+            cmd.insert(1, "-DORACLE_COMMON=1")
+        subprocess.run(cmd, check=True)
+        objs.append(obj)
+    tmp = _LIB + ".tmp"
+    subprocess.run(["gcc", "-shared", "-fopenmp", "-o", tmp, *objs, "-lm"], check=True)
+    os.replace(tmp, _LIB)
+    for o in objs:
+        os.remove(o)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+        L = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        i64 = ctypes.c_int64
+        ci = ctypes.c_int
+        L.oracle_e2m1.restype = ctypes.c_float
+        L.oracle_e2m1.argtypes = [ci]
+        L.oracle_e8m0.restype = ctypes.c_float
+        L.oracle_e8m0.argtypes = [ci]
+        L.oracle_bf16_to_f32.restype = ctypes.c_float
+        L.oracle_bf16_to_f32.argtypes = [ctypes.c_uint16]
+        L.oracle_f32_to_bf16.restype = ctypes.c_uint16
+        L.oracle_f32_to_bf16.argtypes = [ctypes.c_float]
+        L.oracle_sum64.restype = ctypes.c_double
+        L.oracle_sum64.argtypes = [P, P, i64]
+        L.oracle_route.restype = ci
+        L.oracle_route.argtypes = [P, ci, ci, P, P, ci, ci, ci, ctypes.c_float, P, P, P, P]
+        L.oracle_rmsnorm_bf16.restype = ci
+        L.oracle_rmsnorm_bf16.argtypes = [P, ci, ci, ctypes.c_float, P]
+        L.oracle_residual_add_bf16.restype = ci
+        L.oracle_residual_add_bf16.argtypes = [P, P, ci, ci]
+        for sfx in ("f32", "f64"):
+            f = getattr(L, f"oracle_mxfp4_matvec_{sfx}")
+            f.restype = None
+            f.argtypes = [P, P, P, i64, i64, P]
+            f = getattr(L, f"oracle_expert_forward_{sfx}")
+            f.restype = None
+            f.argtypes = [P, i64, i64, P, P, P, P, P, P, P, P, P, P]
+            f = getattr(L, f"oracle_combine_{sfx}")
+            f.restype = None
+            f.argtypes = [i64, i64, i64, P, P, P, P]
+            f = getattr(L, f"oracle_moe_forward_{sfx}")
+            f.restype = i64
+            f.argtypes = [i64, i64, i64, P, P, P, P, P, P, P, i64, P, P, P, i64, P]
+        _lib = L
+    return _lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def _sfx(acc):
+    assert acc in ("f32", "f64")
+    return acc
+
+
+# --------------------------------------------------------------------------------------
+# Thin wrappers
+# --------------------------------------------------------------------------------------
+def e2m1(code: int) -> float:
+    return float(lib().oracle_e2m1(int(code)))
+
+
+def e8m0(s: int) -> float:
+    return float(lib().oracle_e8m0(int(s)))
+
+
+def bf16_to_f32(bits: int) -> float:
+    return float(lib().oracle_bf16_to_f32(int(bits)))
+
+
+def f32_to_bf16(v: float) -> int:
+    return int(lib().oracle_f32_to_bf16(float(v)))
+
+
+def sum64(a, b) -> float:
+    a = _c(a, np.float64)
+    b = _c(b, np.float64)
+    assert a.shape == b.shape and a.size % 8 == 0
+    return float(lib().oracle_sum64(_p(a), _p(b), a.size))
+
+
+def mxfp4_matvec(x, packed, scales, acc="f32"):
+    """y = W.x for one MXFP4 matrix; x float32 [K], packed u8 [rows][K/2], scales u8 [rows][K/32]."""
+    x = _c(x, np.float32)
+    packed = _c(packed, np.uint8)
+    scales = _c(scales, np.uint8)
+    rows, half = packed.shape
+    K = 2 * half
+    assert x.shape == (K,) and scales.shape == (rows, K // 32)
+    y = np.empty(rows, dtype=np.float32)
+    getattr(lib(), f"oracle_mxfp4_matvec_{_sfx(acc)}")(_p(x), _p(packed), _p(scales), rows, K, _p(y))
+    return y
+
+
+def expert_forward(x_bf16, ex, acc="f32", want_hidden=False):
+    """One expert on one activation.  ex has w1_packed..w2_scale (numpy u8).  Returns d
+    (float32 [H]) or (h_bf16 [I], g [I], u [I], d [H])."""
+    x = _c(x_bf16, np.uint16)
+    H = x.shape[0]
+    I = ex.w1_packed.shape[0]
+    t = [_c(a, np.uint8) for a in ex.tensors()]
+    assert t[0].shape == (I, H // 2) and t[4].shape == (H, I // 2)
+    d = np.empty(H, dtype=np.float32)
+    h = np.empty(I, dtype=np.uint16) if want_hidden else None
+    g = np.empty(I, dtype=np.float32) if want_hidden else None
+    u = np.empty(I, dtype=np.float32) if want_hidden else None
+    getattr(lib(), f"oracle_expert_forward_{_sfx(acc)}")(
+        _p(x), H, I, *[_p(a) for a in t], _p(h), _p(g), _p(u), _p(d))
+    return (h, g, u, d) if want_hidden else d
+
+
+def combine(gates, d, valid=None, acc="f32"):
+    """y[t] = sum_j gates[t][j] * d[t][j] in slot order.  gates [T][k], d [T][k][H]."""
+    gates = _c(gates, np.float32)
+    d = _c(d, np.float32)
+    T, k, H = d.shape
+    assert gates.shape == (T, k)
+    v = None if valid is None else _c(valid, np.uint8)
+    y = np.empty((T, H), dtype=np.float32)
+    getattr(lib(), f"oracle_combine_{_sfx(acc)}")(T, k, H, _p(gates), _p(d), _p(v), _p(y))
+    return y
+
+
+def moe_forward(pool, x_bf16, idx, gates, acc="f32"):
+    """Whole forward over a host pool: pool = dict of six u8 arrays [E][rows][cols].
+    Returns (y float32 [T][H], drops)."""
+    x = _c(x_bf16, np.uint16)
+    T, H = x.shape
+    idx = _c(idx, np.int32)
+    gates = _c(gates, np.float32)
+    k = idx.shape[1]
+    names = ("w1_packed", "w1_scale", "w3_packed", "w3_scale", "w2_packed", "w2_scale")
+    t = [_c(pool[n], np.uint8) for n in names]
+    E, I = t[0].shape[0], t[0].shape[1]
+    assert t[0].shape == (E, I, H // 2) and t[4].shape == (E, H, I // 2)
+    y = np.empty((T, H), dtype=np.float32)
+    drops = getattr(lib(), f"oracle_moe_forward_{_sfx(acc)}")(
+        E, H, I, *[_p(a) for a in t], None, T, _p(x), _p(idx), _p(gates), k, _p(y))
+    return y, int(drops)
+
+
+def route(x_bf16, Wr_bf16, bias, topk, renorm=1, routed_scale=1.0, want_scores=False):
+    """Sigmoid + correction-bias top-k router.  Returns idx int32 [T][k], gates f32 [T][k]
+    (and logits, scores f32 [T][E] when asked)."""
+    x = _c(x_bf16, np.uint16)
+    T, H = x.shape
+    W = _c(Wr_bf16, np.uint16)
+    E = W.shape[0]
+    assert W.shape == (E, H)
+    b = None if bias is None else _c(bias, np.float32)
+    idx = np.empty((T, topk), dtype=np.int32)
+    gates = np.empty((T, topk), dtype=np.float32)
+    lg = np.empty((T, E), dtype=np.float32) if want_scores else None
+    sc = np.empty((T, E), dtype=np.float32) if want_scores else None
+    rc = lib().oracle_route(_p(x), T, H, _p(W), _p(b), E, topk, renorm, routed_scale,
+                            _p(idx), _p(gates), _p(lg), _p(sc))
+    if rc != 0:
+        raise ValueError("oracle_route: bad arguments")
+    return (idx, gates, lg, sc) if want_scores else (idx, gates)
+
+
+def rmsnorm_bf16(x_bf16, eps):
+    x = _c(x_bf16, np.uint16)
+    T, H = x.shape
+    out = np.empty_like(x)
+    if lib().oracle_rmsnorm_bf16(_p(x), T, H, eps, _p(out)) != 0:
+        raise ValueError("oracle_rmsnorm_bf16: bad arguments")
+    return out
+
+
+def residual_add_bf16(x_bf16, y):
+    x = _c(x_bf16, np.uint16).copy()
+    y = _c(y, np.float32)
+    T, H = x.shape
+    if lib().oracle_residual_add_bf16(_p(x), _p(y), T, H) != 0:
+        raise ValueError("oracle_residual_add_bf16: bad arguments")
+    return x
+
+
+def threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    n = os.environ.get("OMP_NUM_THREADS")
+    return int(n) if n and n.isdigit() else (os.cpu_count() or 1)

@@ -1,0 +1,308 @@
+/*
+ * k3x oracle -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, obviously ordered CPU implementation of the routed-expert hot path, used
+ * only by the test suite, the smoke check and the bench's CPU-baseline leg to judge the
+ * HIP kernels.  The product path never calls it and shares no code, header, table or
+ * constant with it.
+ *
+ * Sources (the pages describing the kimi-k3-in-c engine):
+ *  - kimi-k3-in-c README, Part II section 4 "Reduction one: the experts already ship at half
+ *    a byte": the E2M1 table, the E8M0 rule 2^(s-127) with byte 255 mapped to 0, low nibble =
+ *    even element, y = W.x taken straight from the nibbles with one scale per group of 32.
+ *  - same README, section 5 "Kernels with a floating point contract": RMSNorm with a double
+ *    sum of squares and eps inside the square root; widening bf16 to f32 is a 16-bit shift;
+ *    a fixed reduction order is part of the contract.
+ *  - same README, section 9 "Picking 16 experts of 896": router logits as double dot
+ *    products, sigmoid score, bias added for selection only, repeated strict-> argmax
+ *    (lowest index wins ties), gates from the unbiased scores, renormalised when the sum
+ *    is positive, times routed_scale; the slot-order weighted combine of expert outputs.
+ *  - Kimi K3 artifact audit, section 4.3: the six packed/scale tensors of one expert.
+ *
+ * Readings taken where the pages leave a step open (each also listed in the design notes):
+ *  - Activation: SwiGLU, h = silu(g) * u with silu(g) = g / (1 + expf(-g)) in fp32, and h
+ *    rounded to bf16 (round to nearest even) before W2.
+ *  - Expert dot products: each group of 32 is summed sequentially in ACC, multiplied by its
+ *    exact power-of-two scale, and the group partials are summed by a pairwise tree (zero
+ *    padded to a power of two).  ACC = float is the verdict oracle; ACC = double is its
+ *    self-check.  This file is compiled once per ACC.
+ *  - Router logits and the RMSNorm sum of squares: double, in a fixed 64-way order.  The
+ *    vector is cut into chunks of 8 elements; partial L (0..63) sums, in ascending order,
+ *    the chunks whose index is L mod 64; then partial[L] += partial[L + s] for
+ *    s = 32, 16, 8, 4, 2, 1.  Products of two bf16 values are exact in double, so only the
+ *    order of additions matters, and it is fixed here.
+ *  - Router sigmoid: computed in double from the float logit and rounded once to float.
+ *  - The combine y = sum_j gate_j * d_j runs in ACC in slot order and is rounded at the end.
+ *
+ * Build: cc -O2 -ffp-contract=off -fno-fast-math -fopenmp, once with
+ * -DORACLE_ACC=float -DORACLE_SFX=f32 -DORACLE_COMMON=1 and once with
+ * -DORACLE_ACC=double -DORACLE_SFX=f64.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifndef ORACLE_ACC
+#define ORACLE_ACC float
+#endif
+#ifndef ORACLE_SFX
+#define ORACLE_SFX f32
+#endif
+#define ORACLE_CAT2(a, b) a##_##b
+#define ORACLE_CAT(a, b) ORACLE_CAT2(a, b)
+#define ORC(name) ORACLE_CAT(name, ORACLE_SFX)
+
+typedef ORACLE_ACC acc_t;
+
+/* ----------------------------------------------------------------------------------------
+ * Tables and bit helpers (README section 4; section 5 for bf16 widening)
+ * -------------------------------------------------------------------------------------- */
+
+/* E2M1: sign, two exponent bits, one mantissa bit; the sixteen values as printed. */
+static const float ORACLE_E2M1_TABLE[16] = {
+    0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f,
+    -0.0f, -0.5f, -1.0f, -1.5f, -2.0f, -3.0f, -4.0f, -6.0f};
+
+static inline float e2m1_value(unsigned code) { return ORACLE_E2M1_TABLE[code & 15u]; }
+
+/* E8M0 scale byte -> 2^(s-127); byte 255 (NaN in the OCP format) is taken as 0. */
+static inline float e8m0_value(unsigned s) {
+  return s == 255u ? 0.0f : ldexpf(1.0f, (int)s - 127);
+}
+
+/* Nibble of logical element c in a packed row: low nibble holds the even element. */
+static inline unsigned nibble_at(const uint8_t *row, int64_t c) {
+  const uint8_t b = row[c >> 1];
+  return (c & 1) ? (unsigned)(b >> 4) : (unsigned)(b & 15u);
+}
+
+static inline float bf16_to_float(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return f;
+}
+
+/* float -> bf16, round to nearest even; NaN stays a quiet NaN. */
+static inline uint16_t float_to_bf16(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu) != 0) return (uint16_t)((u >> 16) | 0x40u);
+  const uint32_t lsb = (u >> 16) & 1u;
+  u += 0x7FFFu + lsb;
+  return (uint16_t)(u >> 16);
+}
+
+#ifdef ORACLE_COMMON
+/* Fixed 64-way double reduction of sum_i a[i]*b[i] over n elements (n % 8 == 0). */
+static double sum64_products(const double *a, const double *b, int64_t n) {
+  double part[64];
+  const int64_t chunks = n / 8;
+  for (int L = 0; L < 64; ++L) {
+    double p = 0.0;
+    for (int64_t c = L; c < chunks; c += 64)
+      for (int j = 0; j < 8; ++j) p += a[8 * c + j] * b[8 * c + j];
+    part[L] = p;
+  }
+  for (int s = 32; s >= 1; s >>= 1)
+    for (int L = 0; L < s; ++L) part[L] = part[L] + part[L + s];
+  return part[0];
+}
+
+float oracle_e2m1(int code) { return e2m1_value((unsigned)code); }
+float oracle_e8m0(int s) { return e8m0_value((unsigned)s); }
+float oracle_bf16_to_f32(uint16_t b) { return bf16_to_float(b); }
+uint16_t oracle_f32_to_bf16(float f) { return float_to_bf16(f); }
+
+double oracle_sum64(const double *a, const double *b, int64_t n) { return sum64_products(a, b, n); }
+
+/* --------------------------------------------------------------------------------------
+ * Router (README section 9).  x bf16 [T][H], Wr bf16 [E][H], bias fp32 [E] or NULL.
+ * Outputs idx [T][topk] in selection order and gates [T][topk]; optionally the float
+ * logits and unbiased scores [T][E].  Returns 0, or -1 on bad arguments.
+ * ------------------------------------------------------------------------------------ */
+int oracle_route(const uint16_t *x, int T, int H, const uint16_t *Wr, const float *bias, int E,
+                 int topk, int renorm, float routed_scale, int32_t *idx, float *gates,
+                 float *logits_out, float *scores_out) {
+  if (T < 0 || H <= 0 || H % 8 || E <= 0 || topk < 1 || topk > E) return -1;
+  double *xd = (double *)malloc(sizeof(double) * (size_t)H);
+  double *wd = (double *)malloc(sizeof(double) * (size_t)H);
+  float *sc = (float *)malloc(sizeof(float) * (size_t)E);
+  float *ch = (float *)malloc(sizeof(float) * (size_t)E);
+  char *taken = (char *)malloc((size_t)E);
+  for (int t = 0; t < T; ++t) {
+    for (int h = 0; h < H; ++h) xd[h] = (double)bf16_to_float(x[(size_t)t * H + h]);
+    for (int e = 0; e < E; ++e) {
+      for (int h = 0; h < H; ++h) wd[h] = (double)bf16_to_float(Wr[(size_t)e * H + h]);
+      const float l = (float)sum64_products(xd, wd, H);
+      sc[e] = (float)(1.0 / (1.0 + exp(-(double)l))); /* unbiased score */
+      ch[e] = sc[e] + (bias ? bias[e] : 0.0f);        /* selection score */
+      if (logits_out) logits_out[(size_t)t * E + e] = l;
+      if (scores_out) scores_out[(size_t)t * E + e] = sc[e];
+    }
+    memset(taken, 0, (size_t)E);
+    int32_t *it = idx + (size_t)t * topk;
+    float *wt = gates + (size_t)t * topk;
+    for (int j = 0; j < topk; ++j) {
+      int best = -1;
+      for (int e = 0; e < E; ++e)
+        if (!taken[e] && (best < 0 || ch[e] > ch[best])) best = e;
+      taken[best] = 1;
+      it[j] = best;
+      wt[j] = sc[best];
+    }
+    if (renorm) {
+      float s = 0.0f;
+      for (int j = 0; j < topk; ++j) s += wt[j];
+      if (s > 0.0f)
+        for (int j = 0; j < topk; ++j) wt[j] /= s;
+    }
+    for (int j = 0; j < topk; ++j) wt[j] *= routed_scale;
+  }
+  free(xd);
+  free(wd);
+  free(sc);
+  free(ch);
+  free(taken);
+  return 0;
+}
+
+/* RMSNorm with unit weight (README section 5): inv = (float)(1/sqrt(ss/H + (double)eps)),
+ * ss the double sum of squares in the fixed 64-way order; out = bf16(x * inv). */
+int oracle_rmsnorm_bf16(const uint16_t *x, int T, int H, float eps, uint16_t *out) {
+  if (T < 0 || H <= 0 || H % 8) return -1;
+  double *xd = (double *)malloc(sizeof(double) * (size_t)H);
+  for (int t = 0; t < T; ++t) {
+    for (int h = 0; h < H; ++h) xd[h] = (double)bf16_to_float(x[(size_t)t * H + h]);
+    const double ss = sum64_products(xd, xd, H);
+    const float inv = (float)(1.0 / sqrt(ss / (double)H + (double)eps));
+    for (int h = 0; h < H; ++h) {
+      const float v = bf16_to_float(x[(size_t)t * H + h]) * inv * 1.0f;
+      out[(size_t)t * H + h] = float_to_bf16(v);
+    }
+  }
+  free(xd);
+  return 0;
+}
+
+/* Residual update of the hidden state: x <- bf16(float(x) + y). */
+int oracle_residual_add_bf16(uint16_t *x, const float *y, int T, int H) {
+  if (T < 0 || H <= 0) return -1;
+  for (int64_t i = 0; i < (int64_t)T * H; ++i) x[i] = float_to_bf16(bf16_to_float(x[i]) + y[i]);
+  return 0;
+}
+#endif /* ORACLE_COMMON */
+
+/* ----------------------------------------------------------------------------------------
+ * MXFP4 matrix-vector product (README section 4), ACC-templated.
+ * y[r] = sum_g 2^(S[r][g]-127) * sum_{c in group g} x[c] * E2M1[nib(r, c)], r < rows.
+ * packed u8 [rows][K/2], scales u8 [rows][K/32], K % 32 == 0.
+ * -------------------------------------------------------------------------------------- */
+void ORC(oracle_mxfp4_matvec)(const float *x, const uint8_t *packed, const uint8_t *scales,
+                              int64_t rows, int64_t K, float *y) {
+  const int64_t ngroup = K / 32;
+  const int64_t rowbytes = K / 2;
+  int64_t npad = 1;
+  while (npad < ngroup) npad <<= 1;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r) {
+    acc_t *part = (acc_t *)calloc((size_t)npad, sizeof(acc_t));
+    const uint8_t *prow = packed + r * rowbytes;
+    const uint8_t *srow = scales + r * ngroup;
+    for (int64_t g = 0; g < ngroup; ++g) {
+      const unsigned s = srow[g];
+      if (s == 255u) {
+        part[g] = 0; /* a NaN scale zeroes the group */
+        continue;
+      }
+      acc_t p = 0;
+      for (int64_t c = 32 * g; c < 32 * g + 32; ++c)
+        p += (acc_t)x[c] * (acc_t)e2m1_value(nibble_at(prow, c));
+      part[g] = p * (acc_t)e8m0_value(s); /* exact power of two */
+    }
+    for (int64_t n = npad; n > 1; n >>= 1)
+      for (int64_t i = 0; i < n / 2; ++i) part[i] = part[2 * i] + part[2 * i + 1];
+    y[r] = (float)part[0];
+    free(part);
+  }
+}
+
+/* One routed expert on one activation: g = W1.x, u = W3.x, h = bf16(silu(g) * u), d = W2.h.
+ * x bf16 [H]; h_out bf16 [I] (may be NULL); g_out/u_out fp32 [I] (may be NULL);
+ * d_out fp32 [H]. */
+void ORC(oracle_expert_forward)(const uint16_t *x, int64_t H, int64_t I, const uint8_t *w1p,
+                                const uint8_t *w1s, const uint8_t *w3p, const uint8_t *w3s,
+                                const uint8_t *w2p, const uint8_t *w2s, uint16_t *h_out,
+                                float *g_out, float *u_out, float *d_out) {
+  float *xf = (float *)malloc(sizeof(float) * (size_t)H);
+  float *g = (float *)malloc(sizeof(float) * (size_t)I);
+  float *u = (float *)malloc(sizeof(float) * (size_t)I);
+  float *hf = (float *)malloc(sizeof(float) * (size_t)I);
+  for (int64_t c = 0; c < H; ++c) xf[c] = bf16_to_float(x[c]);
+  ORC(oracle_mxfp4_matvec)(xf, w1p, w1s, I, H, g);
+  ORC(oracle_mxfp4_matvec)(xf, w3p, w3s, I, H, u);
+  for (int64_t r = 0; r < I; ++r) {
+    const float silu = g[r] / (1.0f + expf(-g[r]));
+    const uint16_t hb = float_to_bf16(silu * u[r]);
+    if (h_out) h_out[r] = hb;
+    hf[r] = bf16_to_float(hb);
+  }
+  ORC(oracle_mxfp4_matvec)(hf, w2p, w2s, H, I, d_out);
+  if (g_out) memcpy(g_out, g, sizeof(float) * (size_t)I);
+  if (u_out) memcpy(u_out, u, sizeof(float) * (size_t)I);
+  free(xf);
+  free(g);
+  free(u);
+  free(hf);
+}
+
+/* Slot-order weighted combine: y[t][r] = sum_j gates[t][j] * d[t][j][r] in ACC, j ascending,
+ * rounded to float at the end; slots with valid[t][j] == 0 contribute nothing. */
+void ORC(oracle_combine)(int64_t T, int64_t topk, int64_t H, const float *gates, const float *d,
+                         const uint8_t *valid, float *y) {
+  for (int64_t t = 0; t < T; ++t)
+    for (int64_t r = 0; r < H; ++r) {
+      acc_t a = 0;
+      for (int64_t j = 0; j < topk; ++j) {
+        if (valid && !valid[t * topk + j]) continue;
+        a += (acc_t)gates[t * topk + j] * (acc_t)d[(t * topk + j) * H + r];
+      }
+      y[t * H + r] = (float)a;
+    }
+}
+
+/* Whole MoE forward over a pool held in host memory (small cases).  Pool tensors are
+ * [E][rows][cols] with the per-expert byte strides given (0 = dense).  An expert id outside
+ * [0, E) is a dropped slot: it contributes 0 and is counted.  Returns the drop count. */
+int64_t ORC(oracle_moe_forward)(int64_t E, int64_t H, int64_t I, const uint8_t *w1p,
+                                const uint8_t *w1s, const uint8_t *w3p, const uint8_t *w3s,
+                                const uint8_t *w2p, const uint8_t *w2s, const int64_t *strides,
+                                int64_t T, const uint16_t *x, const int32_t *idx,
+                                const float *gates, int64_t topk, float *y) {
+  const int64_t dflt[6] = {I * H / 2, I * H / 32, I * H / 2, I * H / 32, H * I / 2, H * I / 32};
+  int64_t st[6];
+  for (int i = 0; i < 6; ++i) st[i] = (strides && strides[i]) ? strides[i] : dflt[i];
+  float *d = (float *)malloc(sizeof(float) * (size_t)(T * topk * H));
+  uint8_t *valid = (uint8_t *)malloc((size_t)(T * topk));
+  int64_t drops = 0;
+  for (int64_t t = 0; t < T; ++t)
+    for (int64_t j = 0; j < topk; ++j) {
+      const int64_t e = idx[t * topk + j];
+      float *dj = d + (t * topk + j) * H;
+      if (e < 0 || e >= E) {
+        ++drops;
+        valid[t * topk + j] = 0;
+        memset(dj, 0, sizeof(float) * (size_t)H);
+        continue;
+      }
+      valid[t * topk + j] = 1;
+      ORC(oracle_expert_forward)(x + t * H, H, I, w1p + e * st[0], w1s + e * st[1],
+                                 w3p + e * st[2], w3s + e * st[3], w2p + e * st[4],
+                                 w2s + e * st[5], NULL, NULL, NULL, dj);
+    }
+  ORC(oracle_combine)(T, topk, H, gates, d, valid, y);
+  free(d);
+  free(valid);
+  return drops;
+}

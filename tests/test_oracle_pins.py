@@ -1,0 +1,485 @@
+"""Pins of the CPU oracle against facts fixed by the pages and by mathematics.
+
+Each test checks the oracle against something other than itself: a value printed on the
+pages (tests/golden/), a hand-worked example, a closed form, an invariant, or brute force
+through numpy's float64 dense algebra on tiny shapes.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import k3x_synth as S
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ------------------------------------------------------------------------------------------
+# independent decoders written in the test (closed forms from the bit layout)
+# ------------------------------------------------------------------------------------------
+def e2m1_closed(code):
+    """E2M1 from its bits: sign b3, exponent b2b1 (bias 1), mantissa b0; e = 0 is subnormal."""
+    sgn = -1.0 if (code >> 3) & 1 else 1.0
+    e = (code >> 1) & 3
+    m = code & 1
+    mag = m / 2.0 if e == 0 else 2.0 ** (e - 1) * (1.0 + m / 2.0)
+    return sgn * mag
+
+
+E2M1_NP = np.array([e2m1_closed(c) for c in range(16)], dtype=np.float64)
+
+
+def dequant64(packed, scales):
+    """Dense float64 matrix of an MXFP4 tensor: low nibble is the even column."""
+    rows, half = packed.shape
+    K = 2 * half
+    codes = np.empty((rows, K), dtype=np.uint8)
+    codes[:, 0::2] = packed & 15
+    codes[:, 1::2] = packed >> 4
+    w = E2M1_NP[codes]
+    sc = np.where(scales == 255, 0.0, np.ldexp(1.0, scales.astype(np.int64) - 127))
+    return w * np.repeat(sc, 32, axis=1)
+
+
+def bf16_rne_from64(v):
+    """Round float64 values to bf16 (RNE) exactly, returning float64 values."""
+    v = np.asarray(v, dtype=np.float64)
+    out = np.empty_like(v)
+    for i, a in enumerate(v.ravel()):
+        if a == 0.0:
+            out.ravel()[i] = a
+            continue
+        e = math.frexp(a)[1]  # a = m * 2^e, 0.5 <= |m| < 1
+        ulp = 2.0 ** (e - 8)  # bf16 keeps 8 significant bits
+        q = a / ulp
+        fl = math.floor(q)
+        rem = q - fl
+        if rem > 0.5 or (rem == 0.5 and fl % 2 == 1):
+            fl += 1
+        out.ravel()[i] = fl * ulp
+    return out
+
+
+def bits_to_f(b):
+    return S.bf16_bits_to_f32(b).astype(np.float64)
+
+
+# ------------------------------------------------------------------------------------------
+# tables
+# ------------------------------------------------------------------------------------------
+def test_e2m1_table_matches_page(orc):
+    g = _golden("e2m1_lut.json")
+    lut = g["e2m1_lut"]
+    assert len(lut) == 16
+    for code, v in enumerate(lut):
+        got = orc.e2m1(code)
+        assert got == v and math.copysign(1.0, got) == math.copysign(1.0, v), code
+
+
+def test_e2m1_closed_form(orc):
+    for code in range(16):
+        v = e2m1_closed(code)
+        got = orc.e2m1(code)
+        assert got == v and math.copysign(1.0, got) == math.copysign(1.0, v)
+
+
+def test_e8m0_powers_and_nan_byte(orc):
+    for s in range(255):
+        assert orc.e8m0(s) == math.ldexp(1.0, s - 127)
+    assert orc.e8m0(255) == 0.0
+
+
+def test_expert_layout_bytes():
+    g = _golden("expert_layout.json")
+    H, I = g["hidden"], g["inter"]
+    assert S.expert_bytes_per_expert(H, I) == g["bytes_per_expert"]
+    assert g["params_per_expert"] * 17 // 32 == g["bytes_per_expert"]  # 0.53125 B per weight
+    names = {S.W1_PACKED: "w1_packed", S.W1_SCALE: "w1_scale", S.W3_PACKED: "w3_packed",
+             S.W3_SCALE: "w3_scale", S.W2_PACKED: "w2_packed", S.W2_SCALE: "w2_scale"}
+    for t, n in names.items():
+        shp = S.tensor_shape(t, H, I)
+        assert list(shp) == g["tensors"][n]["shape"]
+        assert shp[0] * shp[1] == g["tensors"][n]["bytes"]
+
+
+def test_bf16_helpers(orc):
+    # widening is a 16-bit shift; rounding is RNE including ties to even
+    assert orc.bf16_to_f32(0x3F80) == 1.0
+    assert orc.bf16_to_f32(0xC0C0) == -6.0
+    assert orc.f32_to_bf16(1.0) == 0x3F80
+    tie_down = np.array([0x3F808000], dtype=np.uint32).view(np.float32)[0]  # 1 + 2^-8: tie, even is 1.0
+    tie_up = np.array([0x3F818000], dtype=np.uint32).view(np.float32)[0]    # tie, rounds up to even
+    assert orc.f32_to_bf16(float(tie_down)) == 0x3F80
+    assert orc.f32_to_bf16(float(tie_up)) == 0x3F82
+    rng = np.random.default_rng(0)
+    v = rng.standard_normal(2000).astype(np.float32) * 100
+    want = bf16_rne_from64(v.astype(np.float64))
+    got = np.array([orc.bf16_to_f32(orc.f32_to_bf16(float(a))) for a in v])
+    assert np.array_equal(got, want)
+
+
+# ------------------------------------------------------------------------------------------
+# hand-worked single groups and the tiny forward
+# ------------------------------------------------------------------------------------------
+def _group_case(case):
+    packed = np.zeros((1, 16), dtype=np.uint8)
+    b = int(case["bytes_hex"], 16)
+    if case["byte_fill"].startswith("all"):
+        packed[:] = b
+    else:
+        packed[0, 0] = b
+    scales = np.array([[case["scale"]]], dtype=np.uint8)
+    x = np.zeros(32, dtype=np.float32)
+    if case["x"].startswith("1.0 everywhere"):
+        x[:] = 1.0
+    elif case["x"] == "one-hot at c = 1":
+        x[1] = 1.0
+    elif case["x"] == "one-hot at c = 0":
+        x[0] = 1.0
+    else:
+        x[0] = x[1] = 1.0
+    return x, packed, scales
+
+
+@pytest.mark.parametrize("acc", ["f32", "f64"])
+def test_single_group_examples(orc, acc):
+    for case in _golden("hand_examples.json")["single_group"]:
+        x, p, s = _group_case(case)
+        y = orc.mxfp4_matvec(x, p, s, acc=acc)
+        assert y[0] == case["expected"], case["name"]
+
+
+@pytest.mark.parametrize("acc", ["f32", "f64"])
+def test_tiny_forward_s4(orc, acc):
+    c = _golden("hand_examples.json")["tiny_forward"]
+    H, I = c["H"], c["I"]
+    ex = S.ExpertBytes(
+        w1_packed=np.full((I, H // 2), int(c["w1_w3_byte"], 16), np.uint8),
+        w1_scale=np.full((I, H // 32), c["scale"], np.uint8),
+        w3_packed=np.full((I, H // 2), int(c["w1_w3_byte"], 16), np.uint8),
+        w3_scale=np.full((I, H // 32), c["scale"], np.uint8),
+        w2_packed=np.full((H, I // 2), int(c["w2_byte"], 16), np.uint8),
+        w2_scale=np.full((H, I // 32), c["scale"], np.uint8),
+    )
+    x = np.full(H, int(c["x_bf16_hex"], 16), np.uint16)
+    h, g, u, d = orc.expert_forward(x, ex, acc=acc, want_hidden=True)
+    assert np.all(g == 4.0) and np.all(u == 4.0)
+    assert np.all(h == int(c["h_bf16_hex"], 16))
+    assert np.all(d == c["d"])
+    pool = {n: np.stack([a, a]) for n, a in zip(S.TENSOR_NAMES, ex.tensors())}
+    y, drops = orc.moe_forward(pool, x[None, :], np.array([[0, 1]], np.int32),
+                               np.array([c["gates"]], np.float32), acc=acc)
+    assert drops == 0 and np.all(y == c["y"])
+
+
+# ------------------------------------------------------------------------------------------
+# brute force on tiny shapes
+# ------------------------------------------------------------------------------------------
+def _tiny_pool(seed, E, H, I, nan_scales=True):
+    exps = [S.expert_bytes(seed, 0, e, H, I) for e in range(E)]
+    pool = {n: np.stack([getattr(ex, n) for ex in exps]) for n in S.TENSOR_NAMES}
+    if nan_scales:
+        # a few NaN scale bytes (255) zero their groups
+        pool["w1_scale"][0, 0, 0] = 255
+        pool["w2_scale"][1, 2, 0] = 255
+        pool["w3_scale"][2, 1, -1] = 255
+    return pool
+
+
+def _brute_force_expert(pool, e, xf64, h_bits):
+    W1 = dequant64(pool["w1_packed"][e], pool["w1_scale"][e])
+    W3 = dequant64(pool["w3_packed"][e], pool["w3_scale"][e])
+    W2 = dequant64(pool["w2_packed"][e], pool["w2_scale"][e])
+    g = W1 @ xf64
+    u = W3 @ xf64
+    v = g / (1.0 + np.exp(-g)) * u
+    d = W2 @ bits_to_f(h_bits)
+    return g, u, v, d
+
+
+@pytest.mark.parametrize("H,I", [(32, 32), (64, 96), (96, 64)])
+@pytest.mark.parametrize("acc", ["f32", "f64"])
+def test_brute_force_tiny(orc, H, I, acc):
+    E, k, T = 8, 3, 5
+    pool = _tiny_pool(1000 + H + I, E, H, I)
+    x = S.normal_bf16(7, S.P_X, 0, (T, H))
+    idx, gates = S.uniform_routing(11, T, E, k)
+    y, drops = orc.moe_forward(pool, x, idx, gates, acc=acc)
+    assert drops == 0
+    y_ref = np.zeros((T, H))
+    for t in range(T):
+        xf = bits_to_f(x[t])
+        for j in range(k):
+            e = int(idx[t, j])
+            ex = S.ExpertBytes(*[pool[n][e] for n in S.TENSOR_NAMES])
+            h, g, u, d = orc.expert_forward(x[t], ex, acc=acc, want_hidden=True)
+            g64, u64, v64, d64 = _brute_force_expert(pool, e, xf, h)
+            scale_g = np.max(np.abs(g64)) + 1e-30
+            assert np.max(np.abs(g - g64)) <= 1e-6 * scale_g
+            assert np.max(np.abs(u - u64)) <= 1e-6 * (np.max(np.abs(u64)) + 1e-30)
+            # h = bf16(silu(g) * u): against the exact value built from the oracle's own g and u
+            # (g and u were pinned above), h may miss the exact rounding only next to a midpoint
+            g64o, u64o = g.astype(np.float64), u.astype(np.float64)
+            v = g64o / (1.0 + np.exp(-g64o)) * u64o
+            hf = bits_to_f(h)
+            want = bf16_rne_from64(v)
+            for r in np.nonzero(hf != want)[0]:
+                if abs(v[r]) < 2.0 ** -100:
+                    # for g < -88.7 expf(-g) overflows float32, so silu(g) is -0 there
+                    assert abs(hf[r] - v[r]) <= 2.0 ** -100
+                    continue
+                ulp = 2.0 ** (math.frexp(v[r])[1] - 8)
+                mid = math.floor(v[r] / ulp) * ulp + ulp / 2
+                assert abs(v[r] - mid) <= 1e-6 * abs(v[r]), (t, j, r)
+            assert np.max(np.abs(d - d64)) <= 1e-6 * (np.max(np.abs(d64)) + 1e-30)
+            y_ref[t] += float(gates[t, j]) * d64
+    rel = np.linalg.norm(y - y_ref) / np.linalg.norm(y_ref)
+    assert rel <= 1e-6
+
+
+def test_nan_scale_zeroes_only_its_group(orc):
+    rng = np.random.default_rng(3)
+    packed = rng.integers(0, 256, (4, 48), dtype=np.uint8)  # K = 96, 3 groups
+    scales = rng.integers(118, 131, (4, 3), dtype=np.uint8)
+    x = rng.standard_normal(96).astype(np.float32)
+    y0 = orc.mxfp4_matvec(x, packed, scales, acc="f64")
+    s2 = scales.copy()
+    s2[1, 1] = 255
+    y1 = orc.mxfp4_matvec(x, packed, s2, acc="f64")
+    W = dequant64(packed, scales)
+    contrib = W[1, 32:64] @ x[32:64].astype(np.float64)
+    assert np.array_equal(np.delete(y0, 1), np.delete(y1, 1))
+    assert abs(float(y1[1]) - (float(y0[1]) - contrib)) <= 1e-6 * (abs(float(y0[1])) + abs(contrib))
+
+
+# ------------------------------------------------------------------------------------------
+# invariants (exact)
+# ------------------------------------------------------------------------------------------
+def _small_case(seed=5, E=6, H=64, I=96, T=3, k=4):
+    pool = _tiny_pool(seed, E, H, I, nan_scales=False)
+    x = S.normal_bf16(seed, S.P_X, 0, (T, H))
+    idx, gates = S.uniform_routing(seed, T, E, k)
+    return pool, x, idx, gates
+
+
+@pytest.mark.parametrize("acc", ["f32", "f64"])
+@pytest.mark.parametrize("which", ["w2_scale", "w3_scale"])
+def test_scale_plus_one_doubles_y(orc, acc, which):
+    pool, x, idx, gates = _small_case()
+    y, _ = orc.moe_forward(pool, x, idx, gates, acc=acc)
+    p2 = dict(pool)
+    p2[which] = pool[which] + 1
+    y2, _ = orc.moe_forward(p2, x, idx, gates, acc=acc)
+    assert np.array_equal(y2, 2.0 * y)
+
+
+@pytest.mark.parametrize("acc", ["f32", "f64"])
+def test_zero_w1_gives_zero(orc, acc):
+    pool, x, idx, gates = _small_case()
+    pool["w1_packed"] = np.zeros_like(pool["w1_packed"])
+    y, _ = orc.moe_forward(pool, x, idx, gates, acc=acc)
+    assert np.all(y == 0.0)
+
+
+@pytest.mark.parametrize("acc", ["f32", "f64"])
+def test_zero_gate_contributes_nothing(orc, acc):
+    pool, x, idx, gates = _small_case(k=3)
+    g0 = gates.copy()
+    g0[:, 1] = 0.0
+    y, _ = orc.moe_forward(pool, x, idx, g0, acc=acc)
+    y2, _ = orc.moe_forward(pool, x, idx[:, [0, 2]], g0[:, [0, 2]], acc=acc)
+    assert np.array_equal(y, y2)
+
+
+@pytest.mark.parametrize("acc", ["f32", "f64"])
+def test_same_expert_everywhere_gives_d(orc, acc):
+    pool, x, _, _ = _small_case(T=1, k=16)
+    idx = np.full((1, 16), 2, np.int32)
+    _, gates = S.uniform_routing(9, 1, 16, 16)
+    y, _ = orc.moe_forward(pool, x, idx, gates, acc=acc)
+    ex = S.ExpertBytes(*[pool[n][2] for n in S.TENSOR_NAMES])
+    d = orc.expert_forward(x[0], ex, acc=acc)
+    # gates sum to 1 within float32 rounding of 16 terms
+    assert np.all(np.abs(y[0] - d) <= 2.0 ** -19 * np.abs(d))
+
+
+def test_permutation_invariance(orc):
+    pool, x, idx, gates = _small_case(T=4, k=6)
+    rng = np.random.default_rng(17)
+    y64, _ = orc.moe_forward(pool, x, idx, gates, acc="f64")
+    y32, _ = orc.moe_forward(pool, x, idx, gates, acc="f32")
+    for _ in range(4):
+        perm = rng.permutation(idx.shape[1])
+        p64, _ = orc.moe_forward(pool, x, idx[:, perm], gates[:, perm], acc="f64")
+        p32, _ = orc.moe_forward(pool, x, idx[:, perm], gates[:, perm], acc="f32")
+        assert np.count_nonzero(p64 != y64) == 0
+        assert np.linalg.norm(p32 - y32) <= 1e-6 * np.linalg.norm(y32)
+
+
+def test_dropped_slots_are_counted_and_contribute_nothing(orc):
+    pool, x, idx, gates = _small_case(E=6, T=3, k=4)
+    bad = idx.copy()
+    bad[0, 1] = -1
+    bad[2, 3] = 6
+    y, drops = orc.moe_forward(pool, x, bad, gates, acc="f32")
+    assert drops == 2
+    g2 = gates.copy()
+    g2[0, 1] = 0.0
+    g2[2, 3] = 0.0
+    y_ref, d0 = orc.moe_forward(pool, x, idx, g2, acc="f32")
+    assert d0 == 0 and np.array_equal(y, y_ref)
+
+
+def test_fp32_oracle_noise_floor_full_size(orc):
+    """The verdict (fp32) oracle against its fp64 self-check at the real expert shape."""
+    H, I, E, k = S.H_K3, S.I_K3, 4, 4
+    pool = {n: np.stack([getattr(S.expert_bytes(77, 0, e, H, I), n) for e in range(E)])
+            for n in S.TENSOR_NAMES}
+    x = S.normal_bf16(77, S.P_X, 0, (1, H))
+    idx = np.arange(k, dtype=np.int32)[None, :]
+    _, gates = S.uniform_routing(77, 1, k, k)
+    y32, _ = orc.moe_forward(pool, x, idx, gates, acc="f32")
+    y64, _ = orc.moe_forward(pool, x, idx, gates, acc="f64")
+    rel = np.linalg.norm(y32 - y64) / np.linalg.norm(y64)
+    assert rel <= 1e-6, rel
+
+
+# ------------------------------------------------------------------------------------------
+# fixed 64-way reduction
+# ------------------------------------------------------------------------------------------
+def test_sum64_exact_on_integers_and_bounded_otherwise(orc):
+    rng = np.random.default_rng(1)
+    a = rng.integers(-1000, 1000, 3584).astype(np.float64)
+    b = rng.integers(-1000, 1000, 3584).astype(np.float64)
+    assert orc.sum64(a, b) == float(np.sum(a.astype(np.int64) * b.astype(np.int64)))
+    a = rng.standard_normal(3584)
+    b = rng.standard_normal(3584)
+    prods = a * b
+    exact = math.fsum(prods)
+    bound = 3584 * 2.0 ** -53 * math.fsum(np.abs(prods))
+    assert abs(orc.sum64(a, b) - exact) <= bound
+
+
+# ------------------------------------------------------------------------------------------
+# router
+# ------------------------------------------------------------------------------------------
+def _router_case(T=6, E=128, H=512, seed=21, bias_std=0.01):
+    x = S.normal_bf16(seed, S.P_X, 0, (T, H))
+    W = S.normal_bf16(seed, S.P_WR, 0, (E, H), std=0.02 * math.sqrt(3584 / H))
+    b = S.normal_f32(seed, S.P_BIAS, 0, (E,), std=bias_std)
+    return x, W, b
+
+
+def test_router_logits_are_the_rounded_exact_dot(orc):
+    x, W, b = _router_case(T=4, E=896, H=3584)
+    _, _, lg, sc = orc.route(x, W, b, 16, want_scores=True)
+    xf, wf = bits_to_f(x), bits_to_f(W)
+    for t in range(4):
+        prods = xf[t][None, :] * wf  # exact in float64
+        exact = np.array([math.fsum(p) for p in prods], dtype=np.float64)
+        assert np.array_equal(lg[t], exact.astype(np.float32))
+        assert np.array_equal(sc[t], (1.0 / (1.0 + np.exp(-lg[t].astype(np.float64)))).astype(np.float32))
+
+
+def test_router_no_bias_is_stable_argsort_of_scores(orc):
+    x, W, _ = _router_case(T=16, E=256, H=512)
+    idx, gates, lg, sc = orc.route(x, W, None, 16, want_scores=True)
+    for t in range(16):
+        want = np.argsort(-sc[t], kind="stable")[:16]
+        assert np.array_equal(idx[t], want)
+        # sigmoid is monotone: the same set is the top-16 logits
+        assert set(idx[t]) == set(np.argsort(-lg[t], kind="stable")[:16]) or \
+            len(np.unique(sc[t])) < len(sc[t])
+
+
+def test_router_with_bias_is_stable_argsort_of_selection_scores(orc):
+    x, W, b = _router_case(T=16, E=256, H=512, bias_std=0.05)
+    idx, gates, lg, sc = orc.route(x, W, b, 16, want_scores=True)
+    for t in range(16):
+        c = (sc[t] + b).astype(np.float32)
+        assert np.array_equal(idx[t], np.argsort(-c, kind="stable")[:16])
+
+
+def test_router_full_permutation_when_k_equals_e(orc):
+    x, W, b = _router_case(T=3, E=64, H=256)
+    idx, gates = orc.route(x, W, b, 64)
+    for t in range(3):
+        assert sorted(idx[t].tolist()) == list(range(64))
+
+
+def test_router_exact_tie_goes_to_lower_index(orc):
+    x, W, b = _router_case(T=2, E=32, H=256)
+    W = W.copy()
+    W[9] = W[5]
+    b = b.copy()
+    b[5] = b[9] = 10.0
+    idx, _ = orc.route(x, W, b, 4)
+    assert idx[0, 0] == 5 and idx[0, 1] == 9 and idx[1, 0] == 5 and idx[1, 1] == 9
+
+
+def test_router_bias_steers_selection_only(orc):
+    """Combine weights come from the unbiased scores: changing the bias of experts that stay
+    unselected leaves idx and gates bit-identical (README section 9; invariant 5 of the
+    README's list of invariants)."""
+    x, W, b = _router_case(T=8, E=128, H=512)
+    idx, gates, _, sc = orc.route(x, W, b, 16, want_scores=True)
+    for t in range(8):
+        b2 = b.copy()
+        others = np.setdiff1d(np.arange(128), idx[t])
+        b2[others] -= 1.0
+        i2, g2 = orc.route(x[t:t + 1], W, b2, 16)
+        assert np.array_equal(i2[0], idx[t]) and np.array_equal(g2[0], gates[t])
+        # and the gates are the renormalised unbiased scores of the chosen experts
+        s = sc[t, idx[t]]
+        assert np.all(np.abs(gates[t] - s / s.sum(dtype=np.float64)) <= 4e-7)
+
+
+def test_router_renorm_and_scale(orc):
+    x, W, b = _router_case(T=4, E=64, H=256)
+    idx, g1, _, sc = orc.route(x, W, b, 8, renorm=1, routed_scale=1.0, want_scores=True)
+    assert np.all(np.abs(g1.sum(axis=1, dtype=np.float64) - 1.0) <= 8 * 2.0 ** -24)
+    i0, g0 = orc.route(x, W, b, 8, renorm=0, routed_scale=1.0)
+    assert np.array_equal(i0, idx)
+    assert np.array_equal(g0, np.take_along_axis(sc, idx, axis=1))
+    _, g25 = orc.route(x, W, b, 8, renorm=1, routed_scale=2.5)
+    assert np.array_equal(g25, (g1 * np.float32(2.5)).astype(np.float32))
+
+
+# ------------------------------------------------------------------------------------------
+# RMSNorm and residual
+# ------------------------------------------------------------------------------------------
+def test_rmsnorm_constant_vector_closed_form(orc):
+    eps = np.float32(1e-6)
+    for a_bits in (0x3F80, 0x4049, 0xBE00, 0x3A80, 0x4500):
+        a = float(S.bf16_bits_to_f32(np.uint16(a_bits)))
+        x = np.full((1, 3584), a_bits, np.uint16)
+        out = orc.rmsnorm_bf16(x, float(eps))
+        inv = np.float32(1.0 / math.sqrt(a * a + float(eps)))
+        want = S.f32_to_bf16_bits(np.float32(a) * inv)
+        assert np.all(out == want), hex(a_bits)
+
+
+def test_rmsnorm_random_against_fsum(orc):
+    x = S.normal_bf16(3, S.P_X, 0, (8, 3584))
+    out = orc.rmsnorm_bf16(x, 1e-6)
+    xf = bits_to_f(x)
+    for t in range(8):
+        ss = math.fsum(xf[t] * xf[t])
+        inv = np.float32(1.0 / math.sqrt(ss / 3584.0 + float(np.float32(1e-6))))
+        want = S.f32_to_bf16_bits((xf[t].astype(np.float32) * inv).astype(np.float32))
+        assert np.array_equal(out[t], want)
+
+
+def test_residual_add(orc):
+    x = S.normal_bf16(4, S.P_X, 0, (3, 64))
+    y = np.random.default_rng(4).standard_normal((3, 64)).astype(np.float32)
+    out = orc.residual_add_bf16(x, y)
+    want = S.f32_to_bf16_bits((S.bf16_bits_to_f32(x) + y).astype(np.float32))
+    assert np.array_equal(out, want)
