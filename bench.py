@@ -1,0 +1,265 @@
+"""Benchmark of the routed-expert hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one pass of the whole path over one batch: the router (when the workload has one)
+and the expert forward (sort, fused W1/W3 + SwiGLU, W2, combine).  The default workload is
+one decode token through one layer of 896 experts with the router (E = 896, H = 3584,
+I = 3072, top-16).  Inputs are synthetic and seeded (k3x_synth); pools are generated in
+device memory and resident before timing.  Successive steps rotate over 64 different
+tokens, so each step reads a different set of 16 experts and the 256 MB Infinity Cache
+cannot serve them from a previous step.
+
+Prints ONE JSON line.  Kernel durations come from HIP events the library records around
+each of its launches inside the timed region (k3x_profiler_*).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s + achieved HBM GB/s (decode), TFLOP/s (prefill)"
+PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0
+ROTATE = 64
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def expert_tensor_bytes(H, I):
+    w13 = 2 * (I * H // 2 + I * H // 32)
+    w2 = H * I // 2 + H * I // 32
+    return w13, w2
+
+
+def per_kernel_work(name, H, I, E, T, topk, U):
+    """Algorithmic (bytes, flops) of one launch: U distinct experts, T tokens, T*topk slots."""
+    w13, w2 = expert_tensor_bytes(H, I)
+    slots = T * topk
+    if name == "w13_decode" or name == "w13_prefill":
+        return U * w13 + T * H * 2 + slots * I * 2, slots * 4.0 * I * H
+    if name == "w2_decode" or name == "w2_prefill":
+        return U * w2 + slots * I * 2 + slots * H * 4, slots * 2.0 * H * I
+    if name == "route_scores":
+        return E * H * 2 + T * H * 2 + T * E * 4, 2.0 * T * E * H
+    if name == "route_select":
+        return T * E * 4 + E * 4 + T * topk * 8, 0.0
+    if name == "moe_combine":
+        return slots * H * 4 + T * H * 4 + slots * 8, 2.0 * slots * H
+    if name == "moe_sort":
+        return slots * 4 * 2, 0.0
+    if name == "rmsnorm_bf16":
+        return T * H * 4, 3.0 * T * H
+    if name == "residual_add_bf16":
+        return T * H * 8, 1.0 * T * H
+    return 0, 0.0
+
+
+def cpu_baseline(w, x, W, b, dev_idx, dev_gates, budget_s=12.0):
+    """The oracle as it stands, on this host's cores, over a bounded sample of the same
+    workload's tokens (expert bytes generated beforehand, outside the timing)."""
+    import k3x_synth as S
+    import oracle
+
+    tokens = []
+    t_used = 0.0
+    cache = {}
+    i = 0
+    while i < len(x) and (t_used < budget_s or not tokens):
+        xt = x[i:i + 1]
+        if w.router:
+            t0 = time.perf_counter()
+            idx, gates = oracle.route(xt, W, b, w.topk)
+            t_used += time.perf_counter() - t0
+        else:
+            idx, gates = dev_idx[i:i + 1], dev_gates[i:i + 1]
+        exps = []
+        for e in idx[0]:
+            key = int(e)
+            if key not in cache:
+                cache[key] = S.expert_bytes(w.seed, 0, key, w.H, w.I)
+            exps.append(cache[key])
+        t0 = time.perf_counter()
+        d = np.stack([oracle.expert_forward(xt[0], ex) for ex in exps])[None]
+        oracle.combine(gates, d)
+        t_used += time.perf_counter() - t0
+        tokens.append(i)
+        i += 1
+        if len(cache) > 256:
+            cache.clear()
+    return {
+        "value": len(tokens) / t_used,
+        "unit": "tokens/s",
+        "cores": oracle.threads(),
+        "kind": "oracle",
+        "sample": f"{len(tokens)} token(s) of the same workload ({'router + ' if w.router else ''}"
+                  f"{w.topk} experts each + combine), {t_used:.1f} s of oracle time, expert byte "
+                  f"generation excluded",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", default="decode_t1_e896_router")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path is "
+              f"built and measured for a single MI355X", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import k3x_synth as S
+    import mxfp4_routed_expert_k3x_amd as k3x
+
+    k3x.load_library()
+    wl = {w.name: w for w in S.WORKLOADS.values()}
+    if args.workload not in wl:
+        sys.exit(f"unknown workload {args.workload}; one of {sorted(wl)}")
+    w = wl[args.workload]
+    if w.layers != 1:
+        sys.exit("the chained workload is a parity case; bench one of the single-layer workloads")
+    prefill = w.T > 64
+    steps = args.steps if args.steps is not None else (20 if prefill else 200)
+    warmup = args.warmup if args.warmup is not None else (3 if prefill else 20)
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+
+    log(f"generating pool: E={w.E} H={w.H} I={w.I}")
+    pool = k3x.k3x_expert_pool_create(S.device_pool(w.seed, 0, w.E, w.H, w.I), hidden=w.H,
+                                      inter=w.I, n_experts=w.E)
+    R = 1 if prefill else ROTATE
+    x = S.normal_bf16(w.seed, S.P_X, 0, (R * w.T, w.H))
+    xs = [torch.from_numpy(x[r * w.T:(r + 1) * w.T].view(np.int16)).to(dev) for r in range(R)]
+    W = b = Wd = bd = None
+    if w.router:
+        W, b = S.router_inputs(w)
+        Wd = torch.from_numpy(W.view(np.int16)).to(dev)
+        bd = torch.from_numpy(b).to(dev)
+    routes, routes_np = [], []
+    if not w.router:
+        for r in range(R):
+            i_, g_ = S.uniform_routing(w.seed + r, w.T, w.E, w.topk)
+            routes_np.append((i_, g_))
+            routes.append((torch.from_numpy(i_).to(dev), torch.from_numpy(g_).to(dev)))
+    idx = torch.empty((w.T, w.topk), dtype=torch.int32, device=dev)
+    gates = torch.empty((w.T, w.topk), dtype=torch.float32, device=dev)
+    y = torch.empty((w.T, w.H), dtype=torch.float32, device=dev)
+    ws = k3x.alloc_workspace(k3x.k3x_moe_workspace_size(pool, w.T, w.topk), dev)
+    rdesc = k3x.router_desc(Wd, bd, w.topk) if w.router else None
+    rws = k3x.alloc_workspace(k3x.k3x_route_workspace_size(rdesc, w.T), dev) if w.router else None
+
+    def step(r):
+        if w.router:
+            k3x.k3x_route_topk(rdesc, xs[r], w.T, idx, gates, rws)
+            k3x.k3x_moe_forward(pool, xs[r], w.T, idx, gates, w.topk, y, ws)
+        else:
+            i_, g_ = routes[r]
+            k3x.k3x_moe_forward(pool, xs[r], w.T, i_, g_, w.topk, y, ws)
+
+    # distinct experts per rotated batch (from the GPU's own routing)
+    U = []
+    for r in range(R):
+        step(r)
+        torch.cuda.synchronize()
+        ids = (idx if w.router else routes[r][0]).cpu().numpy()
+        U.append(len(np.unique(ids)))
+    drops = k3x.k3x_fetch_drops(ws)
+    if drops:
+        sys.exit(f"run invalid: {drops} dropped slots")
+
+    for i in range(warmup):
+        step(i % R)
+    kernels_per_step = 6 if w.router else 4
+    prof = k3x.k3x_profiler_create(steps * kernels_per_step + 16)
+    torch.cuda.synchronize()
+    k3x.k3x_profiler_attach(prof)
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i % R)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    k3x.k3x_profiler_attach(None)
+    durs = k3x.profiler_durations(prof)
+    k3x.k3x_profiler_destroy(prof)
+
+    mean_U = float(np.mean([U[i % R] for i in range(steps)]))
+    kernels = {}
+    for name, ms in durs.items():
+        nbytes, flops = per_kernel_work(name, w.H, w.I, w.E, w.T, w.topk, mean_U)
+        avg_s = float(np.mean(ms)) * 1e-3
+        kernels[name] = {
+            "launches": len(ms),
+            "avg_us": round(avg_s * 1e6, 3),
+            "alg_bytes": int(nbytes),
+            "gbps": round(nbytes / avg_s / 1e9, 1),
+            "tflops": round(flops / avg_s / 1e12, 2),
+        }
+    dominant = max(kernels, key=lambda n: kernels[n]["avg_us"] * kernels[n]["launches"])
+    dk = kernels[dominant]
+    if prefill:
+        roof = {"bound": "mfma", "achieved": dk["tflops"], "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(dk["tflops"] / PEAK_BF16_TFLOPS, 4),
+                "traffic": None, "kernel": dominant}
+    else:
+        roof = {"bound": "hbm", "achieved": dk["gbps"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(dk["gbps"] / PEAK_HBM_GBS, 4), "traffic": None, "kernel": dominant}
+
+    w13, w2 = expert_tensor_bytes(w.H, w.I)
+    path_bytes = mean_U * (w13 + w2) + w.T * (w.H * 2 + w.H * 4)
+    if w.router:
+        path_bytes += w.E * w.H * 2 + w.E * 4
+    path_flops = w.T * w.topk * 6.0 * w.H * w.I
+    ksum = sum(k["avg_us"] * k["launches"] for k in kernels.values()) / steps * 1e-6
+    ms_per_step = wall / steps * 1e3
+    out = {
+        "metric": METRIC,
+        "value": round(w.T * steps / wall, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "tokens": w.T, "experts": w.E, "hidden": w.H,
+                   "inter": w.I, "topk": w.topk, "router": w.router, "zipf_bias": w.zipf,
+                   "weights": "mxfp4 (e2m1 + e8m0 per 32)", "rotated_batches": R,
+                   "distinct_experts_per_step": round(mean_U, 2)},
+        "roofline": roof,
+        "path": {"kernel_sum_us": round(ksum * 1e6, 3),
+                 "alg_bytes_per_step": int(path_bytes),
+                 "hbm_gbps_kernel_sum": round(path_bytes / ksum / 1e9, 1),
+                 "hbm_frac_kernel_sum": round(path_bytes / ksum / 1e9 / PEAK_HBM_GBS, 4),
+                 "tflops_kernel_sum": round(path_flops / ksum / 1e12, 2),
+                 "hbm_gbps_wall": round(path_bytes / (wall / steps) / 1e9, 1)},
+        "kernels": kernels,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the oracle on the host (bounded sample)")
+        di = np.concatenate([r_[0] for r_ in routes_np]) if routes_np else None
+        dg = np.concatenate([r_[1] for r_ in routes_np]) if routes_np else None
+        out["cpu_baseline"] = cpu_baseline(w, x, W, b, di, dg)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,192 @@
+/*
+ * k3x -- routed-expert SwiGLU over MXFP4-packed weights, with a sigmoid + correction-bias
+ * top-k router, for AMD Instinct MI355X (gfx950).  Plain C ABI.
+ *
+ * What is computed (sources: the kimi-k3-in-c README, Part II; the Kimi K3 artifact audit):
+ *
+ *   router (README section 9 "Picking 16 experts of 896"):
+ *     l[t][e] = x[t] . Wr[e]                        (double sum, rounded to float)
+ *     s[t][e] = sigmoid(l[t][e])                    (unbiased score)
+ *     c[t][e] = s[t][e] + bias[e]                   (selection score; bias steers selection only)
+ *     idx[t]  = the topk experts of largest c, picked one at a time; equal c -> lower e first
+ *     gates   = s of the chosen experts, divided by their float sum when renorm != 0 and the
+ *               sum is > 0, then times routed_scale
+ *
+ *   expert forward (README section 4 "Reduction one: the experts already ship at half a
+ *   byte", and the routed-expert loop of section 9), for every token t and slot j with
+ *   e = idx[t][j]:
+ *     g = W1_e . x[t],  u = W3_e . x[t]             (W1_e, W3_e: [I][H] MXFP4)
+ *     h = bf16_rne(silu(g) * u)                     (silu(g) = g / (1 + exp(-g)), fp32)
+ *     d = W2_e . h                                  (W2_e: [H][I] MXFP4)
+ *     y[t] = sum_j gates[t][j] * d                  (fp32, slot order)
+ *
+ *   MXFP4 weight (README section 4; audit section 4.3): element c of row r is
+ *   E2M1[nibble] * 2^(scale - 127); the nibble of even c is the low nibble of byte c/2 and
+ *   the nibble of odd c is its high nibble; one E8M0 scale byte per 32 consecutive elements
+ *   along K; scale byte 255 zeroes its group.  E2M1 = {0, .5, 1, 1.5, 2, 3, 4, 6} with a
+ *   sign bit (bit 3).
+ *
+ * Memory and threading conventions (all calls):
+ *  - Every tensor pointer is a DEVICE pointer unless stated; the library never allocates,
+ *    frees or copies caller memory, and never allocates device memory in a forward call.
+ *  - stream is a hipStream_t passed as void* (NULL = the null stream).  Device work is
+ *    enqueued asynchronously on it; host-detectable errors return at once and enqueue nothing.
+ *  - A pool is immutable after creation; concurrent calls on different streams are safe
+ *    when each has its own workspace and outputs.
+ *  - No exception crosses this ABI.  k3x_last_error() gives a thread-local message about the
+ *    latest failing call on the calling thread.
+ */
+#ifndef K3X_H
+#define K3X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum k3x_status {
+  K3X_OK = 0,
+  K3X_E_INVALID_ARG = -1, /* NULL pointer, negative size, topk out of range, ...          */
+  K3X_E_UNSUPPORTED = -2, /* a shape, group size or alignment this build does not support */
+  K3X_E_WORKSPACE = -3,   /* workspace missing, misaligned or smaller than required        */
+  K3X_E_HIP = -4,         /* a HIP launch or runtime error (message in k3x_last_error)    */
+  K3X_E_DROPS = -5        /* k3x_fetch_drops: at least one slot named an invalid expert    */
+} k3x_status;
+
+/* Static description of a status code. */
+const char *k3x_status_str(k3x_status s);
+
+/* Thread-local text of the latest error raised on this thread ("" if none). */
+const char *k3x_last_error(void);
+
+/* ------------------------------------------------------------------------------------------
+ * Expert pool: the borrowed device tensors of one MoE layer's routed experts.
+ * Layout per expert (audit section 4.3): w1_packed, w3_packed u8 [inter][hidden/2];
+ * w1_scale, w3_scale u8 [inter][hidden/32]; w2_packed u8 [hidden][inter/2];
+ * w2_scale u8 [hidden][inter/32]; all row-major.  Expert e of tensor k starts at
+ * base_k + e * stride_bytes[k]; stride 0 means dense (the tensor's own size).
+ * Tensor order in stride_bytes: w1_packed, w1_scale, w3_packed, w3_scale, w2_packed, w2_scale.
+ * ---------------------------------------------------------------------------------------- */
+typedef struct k3x_pool_desc {
+  int32_t n_experts; /* 1..8192                                                    */
+  int32_t hidden;    /* H: multiple of 128 (e.g. 3584)                              */
+  int32_t inter;     /* I: multiple of 128 (e.g. 3072)                              */
+  int32_t group;     /* must be 32                                                  */
+  const void *w1_packed, *w1_scale, *w3_packed, *w3_scale, *w2_packed, *w2_scale;
+  int64_t stride_bytes[6];
+} k3x_pool_desc;
+
+typedef struct k3x_pool k3x_pool;
+
+/* Validates d and creates a host-side handle in *out.  Refuses (K3X_E_UNSUPPORTED)
+ * group != 32, hidden or inter not a multiple of 128, packed pointers or strides not
+ * 16-byte aligned; refuses (K3X_E_INVALID_ARG) NULL pointers, n_experts out of range and
+ * strides smaller than the dense tensor size.  Allocates host memory only; the device
+ * tensors are borrowed and must outlive the pool.  Scale bytes are read as given: bytes
+ * 2..253 give normal weights; 255 zeroes a group; 0, 1 and 254 are outside the range this
+ * build promises to reproduce exactly. */
+k3x_status k3x_expert_pool_create(const k3x_pool_desc *d, k3x_pool **out);
+
+/* Frees the handle only (never the borrowed tensors).  NULL is a no-op. */
+void k3x_expert_pool_destroy(k3x_pool *p);
+
+/* ------------------------------------------------------------------------------------------
+ * Router (README section 9).
+ * ---------------------------------------------------------------------------------------- */
+typedef struct k3x_router_desc {
+  const void *weight; /* bf16 [n_experts][hidden], row-major, 16-byte aligned          */
+  const float *bias;  /* fp32 [n_experts] correction bias, or NULL for none             */
+  int32_t n_experts;  /* 1..4096                                                        */
+  int32_t hidden;     /* multiple of 8, <= 16384                                        */
+  int32_t topk;       /* 1..n_experts                                                   */
+  int32_t renorm;     /* nonzero: divide the gates by their sum when the sum is > 0     */
+  float routed_scale; /* gates are multiplied by this last                              */
+} k3x_router_desc;
+
+/* Bytes of device workspace k3x_route_topk needs for T tokens (0 if r is invalid). */
+size_t k3x_route_workspace_size(const k3x_router_desc *r, int32_t T);
+
+/* Routes T tokens.  x_bf16: bf16 [T][hidden] (16-byte aligned).  Outputs idx_out int32
+ * [T][topk] in selection order (descending selection score, equal scores -> lower expert
+ * first) and gates_out fp32 [T][topk].  ws: device workspace of at least
+ * k3x_route_workspace_size bytes, 256-byte aligned.  T = 0 enqueues nothing.
+ * The logits are summed in double in a fixed order and the sigmoid is evaluated in double
+ * and rounded once to float, so the selection is reproducible bit for bit. */
+k3x_status k3x_route_topk(const k3x_router_desc *r, const void *x_bf16, int32_t T,
+                          int32_t *idx_out, float *gates_out, void *ws, size_t ws_bytes,
+                          void *stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Expert forward (README sections 4 and 9).
+ * ---------------------------------------------------------------------------------------- */
+
+/* Bytes of device workspace k3x_moe_forward needs for T tokens with topk slots each
+ * (0 if the arguments are invalid).  It holds the drop counter, the expert-sorted slot
+ * list, h (bf16 [T*topk][inter]) and the per-slot expert outputs (fp32 [T*topk][hidden]). */
+size_t k3x_moe_workspace_size(const k3x_pool *p, int32_t T, int32_t topk);
+
+/* y[t] = sum_j gates[t][j] * W2_e(bf16(silu(W1_e x[t]) * (W3_e x[t]))), e = idx[t][j].
+ * x_bf16: bf16 [T][hidden], 16-byte aligned; idx int32 [T][topk]; gates fp32 [T][topk];
+ * y fp32 [T][hidden], overwritten (not accumulated).  topk in 1..64.  Duplicate experts
+ * within a token are allowed (slots are independent).  A slot whose expert id lies outside
+ * [0, n_experts) contributes 0 and is counted in the workspace's drop counter, which each
+ * call resets; read it with k3x_fetch_drops.  T = 0 only resets the counter. */
+k3x_status k3x_moe_forward(const k3x_pool *p, const void *x_bf16, int32_t T, const int32_t *idx,
+                           const float *gates, int32_t topk, float *y, void *ws,
+                           size_t ws_bytes, void *stream);
+
+/* Waits for stream, then stores in *n the number of dropped slots of the latest
+ * k3x_moe_forward that used ws.  Returns K3X_E_DROPS when *n > 0 (the run must be treated
+ * as invalid), K3X_OK when 0.  n is a host pointer. */
+k3x_status k3x_fetch_drops(const void *ws, int64_t *n, void *stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Hidden-state helpers for chaining layers (README section 5 "Kernels with a floating point
+ * contract"): RMSNorm with unit weight and a double sum of squares, eps inside the square
+ * root, and the residual update.
+ * ---------------------------------------------------------------------------------------- */
+
+/* out[t] = bf16_rne(x[t] * inv_t), inv_t = (float)(1 / sqrt(sum_h x[t][h]^2 / H + eps)),
+ * the sum taken in double in a fixed order.  x, out: bf16 [T][H] (16-byte aligned; may
+ * alias); H a multiple of 8, <= 16384. */
+k3x_status k3x_rmsnorm_bf16(const void *x, int32_t T, int32_t H, float eps, void *out,
+                            void *stream);
+
+/* x[t][h] <- bf16_rne(float(x[t][h]) + y[t][h]).  x bf16 [T][H], y fp32 [T][H]; H a
+ * multiple of 8. */
+k3x_status k3x_residual_add_bf16(void *x, const float *y, int32_t T, int32_t H, void *stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Kernel timing (instrumentation only; the work done is unchanged).  While a profiler is
+ * attached to the calling thread, every kernel the library enqueues from that thread is
+ * bracketed by two HIP events recorded on the same stream, up to the profiler's capacity.
+ * ---------------------------------------------------------------------------------------- */
+typedef struct k3x_profiler k3x_profiler;
+
+/* Creates a profiler able to record `capacity` (1..1<<20) kernel launches.  Creates 2 *
+ * capacity HIP events on the current device. */
+k3x_status k3x_profiler_create(int32_t capacity, k3x_profiler **out);
+
+/* Destroys the events and the handle (detaches it first if attached).  NULL is a no-op. */
+void k3x_profiler_destroy(k3x_profiler *p);
+
+/* Attaches p to the calling thread (NULL detaches).  One profiler per thread at a time. */
+k3x_status k3x_profiler_attach(k3x_profiler *p);
+
+/* Forgets the recorded launches (the events are reused). */
+k3x_status k3x_profiler_reset(k3x_profiler *p);
+
+/* Number of launches recorded since the last reset (at most the capacity). */
+int32_t k3x_profiler_count(const k3x_profiler *p);
+
+/* Waits for launch i's stop event, then returns its kernel name (a static string) and its
+ * duration in milliseconds.  name and ms are host pointers. */
+k3x_status k3x_profiler_read(k3x_profiler *p, int32_t i, const char **name, float *ms);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* K3X_H */

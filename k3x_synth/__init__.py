@@ -113,16 +113,62 @@ def tensor_shape(tensor: int, H: int, I: int):
 
 
 def expert_bytes(seed, layer, expert, H, I, lo=SCALE_LO, count=SCALE_COUNT) -> ExpertBytes:
+    """All six tensors of one expert (the C host twin when built, else numpy)."""
+    fast = _host_lib()
     out = []
     for t in range(6):
         shp = tensor_shape(t, H, I)
         n = shp[0] * shp[1]
-        if t % 2 == 0:
+        if fast is not None:
+            a = np.empty(n, dtype=np.uint8)
+            fast.k3x_synth_host_fill(a.ctypes.data, 0, n, seed & 0xFFFFFFFFFFFFFFFF, layer, expert,
+                                     t, t % 2, lo, count)
+        elif t % 2 == 0:
             a = packed_bytes(seed, layer, expert, t, n)
         else:
             a = scale_bytes(seed, layer, expert, t, n, lo=lo, count=count)
         out.append(a.reshape(shp))
     return ExpertBytes(*out)
+
+
+_HOST_SO = None
+
+
+def _host_lib():
+    """ctypes handle of libk3x_synth_host.so (built from csrc/synth_host.c), or None."""
+    global _HOST_SO
+    if _HOST_SO is None:
+        import ctypes
+        import os
+        here = os.path.dirname(os.path.abspath(__file__))
+        so = os.path.join(here, "libk3x_synth_host.so")
+        src = os.path.join(here, "csrc", "synth_host.c")
+        if not os.path.exists(so) or os.path.getmtime(so) < os.path.getmtime(src):
+            try:
+                build_host()
+            except Exception:
+                _HOST_SO = False
+                return None
+        L = ctypes.CDLL(so)
+        L.k3x_synth_host_fill.restype = None
+        L.k3x_synth_host_fill.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint64,
+                                          ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint32,
+                                          ctypes.c_uint32, ctypes.c_int, ctypes.c_uint32,
+                                          ctypes.c_uint32]
+        _HOST_SO = L
+    return _HOST_SO or None
+
+
+def build_host() -> str:
+    import os
+    import subprocess
+    here = os.path.dirname(os.path.abspath(__file__))
+    so = os.path.join(here, "libk3x_synth_host.so")
+    tmp = so + ".tmp"
+    subprocess.run(["gcc", "-O2", "-fPIC", "-shared", "-Wall", "-Werror",
+                    os.path.join(here, "csrc", "synth_host.c"), "-o", tmp], check=True)
+    os.replace(tmp, so)
+    return so
 
 
 # ---------------------------------------------------------------------------------------
@@ -255,3 +301,77 @@ def log_log_slope(counts, r_lo=20, r_hi=400) -> float:
     slope, _ = np.linalg.lstsq(A, np.log(c), rcond=None)[0]
     return float(slope)
 
+
+
+# ---------------------------------------------------------------------------------------
+# Device twin (csrc/synth_fill.hip): fills pools directly in GPU memory
+# ---------------------------------------------------------------------------------------
+import ctypes as _ct
+import os as _os
+
+_SYN_DIR = _os.path.dirname(_os.path.abspath(__file__))
+SYNTH_LIB = _os.path.join(_SYN_DIR, "libk3x_synth.so")
+_synth = None
+
+
+def build_device() -> str:
+    """Compile csrc/synth_fill.hip into libk3x_synth.so (gfx950)."""
+    import subprocess
+    src = _os.path.join(_SYN_DIR, "csrc", "synth_fill.hip")
+    tmp = SYNTH_LIB + ".tmp"
+    cmd = ["hipcc", "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+           "-mcode-object-version=5", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           src, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed:\n{r.stdout}{r.stderr}")
+    _os.replace(tmp, SYNTH_LIB)
+    return SYNTH_LIB
+
+
+def _synth_lib():
+    global _synth
+    if _synth is None:
+        import torch  # noqa: F401  (binds the HIP runtime first)
+        if not _os.path.exists(SYNTH_LIB):
+            raise ImportError(f"{SYNTH_LIB} missing: call k3x_synth.build_device()")
+        L = _ct.CDLL(SYNTH_LIB)
+        L.k3x_synth_fill.restype = _ct.c_int
+        L.k3x_synth_fill.argtypes = [_ct.c_void_p, _ct.c_uint64, _ct.c_uint32, _ct.c_uint32,
+                                     _ct.c_uint64, _ct.c_uint32, _ct.c_uint32, _ct.c_int,
+                                     _ct.c_uint32, _ct.c_uint32, _ct.c_void_p]
+        _synth = L
+    return _synth
+
+
+def device_fill(t, per_expert: int, e0: int, n_experts: int, seed: int, layer: int, tensor: int,
+                lo=SCALE_LO, count=SCALE_COUNT, stream=None):
+    """Fill the uint8 device tensor t ([n_experts][per_expert] bytes) with the stream bytes of
+    experts e0..e0+n_experts-1 of one tensor id (same bytes as packed_bytes / scale_bytes)."""
+    import torch
+    kind = 0 if tensor % 2 == 0 else 1
+    s = torch.cuda.current_stream().cuda_stream if stream is None else stream
+    rc = _synth_lib().k3x_synth_fill(t.data_ptr(), per_expert, e0, n_experts,
+                                     seed & 0xFFFFFFFFFFFFFFFF, layer, tensor, kind, lo, count, s)
+    if rc != 0:
+        raise RuntimeError(f"k3x_synth_fill failed ({rc})")
+
+
+def device_pool(seed, layer, E, H, I, device="cuda", lo=SCALE_LO, count=SCALE_COUNT):
+    """The six expert tensors of one layer, [E][rows][cols] uint8 on the device."""
+    import torch
+    out = {}
+    for t, name in enumerate(TENSOR_NAMES):
+        shp = tensor_shape(t, H, I)
+        buf = torch.empty((E, shp[0], shp[1]), dtype=torch.uint8, device=device)
+        device_fill(buf, shp[0] * shp[1], 0, E, seed, layer, t, lo=lo, count=count)
+        out[name] = buf
+    return out
+
+
+def host_pool(seed, layer, E, H, I, experts=None, lo=SCALE_LO, count=SCALE_COUNT):
+    """The same bytes on the host (numpy), for the listed experts (default all) stacked in
+    that order."""
+    ids = range(E) if experts is None else experts
+    exps = [expert_bytes(seed, layer, e, H, I, lo=lo, count=count) for e in ids]
+    return {n: np.stack([getattr(ex, n) for ex in exps]) for n in TENSOR_NAMES}

@@ -1,0 +1,329 @@
+"""Python binding of the k3x C ABI (include/k3x.h): argument marshalling only.
+
+Every step of the routed-expert path runs in the HIP kernels of libk3x.so.  There is no CPU
+or PyTorch fallback: importing this package without the built library raises.  PyTorch is
+used for device memory and streams only.
+
+The functions keep the C names (``k3x_expert_pool_create``, ``k3x_route_topk``,
+``k3x_moe_forward``, ...).  Tensors are passed as torch tensors on the GPU; the current torch
+stream is used unless a ``stream`` (an integer hipStream_t) is given.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # must be imported before libk3x.so so both bind the same HIP runtime
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libk3x.so")
+
+K3X_OK = 0
+K3X_E_INVALID_ARG = -1
+K3X_E_UNSUPPORTED = -2
+K3X_E_WORKSPACE = -3
+K3X_E_HIP = -4
+K3X_E_DROPS = -5
+
+
+class K3xError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"k3x status {status}: {message}")
+        self.status = status
+
+
+class k3x_pool_desc(ctypes.Structure):
+    _fields_ = [
+        ("n_experts", ctypes.c_int32),
+        ("hidden", ctypes.c_int32),
+        ("inter", ctypes.c_int32),
+        ("group", ctypes.c_int32),
+        ("w1_packed", ctypes.c_void_p),
+        ("w1_scale", ctypes.c_void_p),
+        ("w3_packed", ctypes.c_void_p),
+        ("w3_scale", ctypes.c_void_p),
+        ("w2_packed", ctypes.c_void_p),
+        ("w2_scale", ctypes.c_void_p),
+        ("stride_bytes", ctypes.c_int64 * 6),
+    ]
+
+
+class k3x_router_desc(ctypes.Structure):
+    _fields_ = [
+        ("weight", ctypes.c_void_p),
+        ("bias", ctypes.c_void_p),
+        ("n_experts", ctypes.c_int32),
+        ("hidden", ctypes.c_int32),
+        ("topk", ctypes.c_int32),
+        ("renorm", ctypes.c_int32),
+        ("routed_scale", ctypes.c_float),
+    ]
+
+
+EXPORTS = (
+    "k3x_status_str", "k3x_last_error", "k3x_expert_pool_create", "k3x_expert_pool_destroy",
+    "k3x_route_workspace_size", "k3x_route_topk", "k3x_moe_workspace_size", "k3x_moe_forward",
+    "k3x_fetch_drops", "k3x_rmsnorm_bf16", "k3x_residual_add_bf16",
+    "k3x_profiler_create", "k3x_profiler_destroy", "k3x_profiler_attach", "k3x_profiler_reset",
+    "k3x_profiler_count", "k3x_profiler_read",
+)
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libk3x.so (raises if it was not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with python -m mxfp4_routed_expert_k3x_amd.build")
+    L = ctypes.CDLL(path)
+    P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    L.k3x_status_str.restype = ctypes.c_char_p
+    L.k3x_status_str.argtypes = [ctypes.c_int]
+    L.k3x_last_error.restype = ctypes.c_char_p
+    L.k3x_last_error.argtypes = []
+    L.k3x_expert_pool_create.restype = ctypes.c_int
+    L.k3x_expert_pool_create.argtypes = [ctypes.POINTER(k3x_pool_desc), ctypes.POINTER(P)]
+    L.k3x_expert_pool_destroy.restype = None
+    L.k3x_expert_pool_destroy.argtypes = [P]
+    L.k3x_route_workspace_size.restype = SZ
+    L.k3x_route_workspace_size.argtypes = [ctypes.POINTER(k3x_router_desc), I32]
+    L.k3x_route_topk.restype = ctypes.c_int
+    L.k3x_route_topk.argtypes = [ctypes.POINTER(k3x_router_desc), P, I32, P, P, P, SZ, P]
+    L.k3x_moe_workspace_size.restype = SZ
+    L.k3x_moe_workspace_size.argtypes = [P, I32, I32]
+    L.k3x_moe_forward.restype = ctypes.c_int
+    L.k3x_moe_forward.argtypes = [P, P, I32, P, P, I32, P, P, SZ, P]
+    L.k3x_fetch_drops.restype = ctypes.c_int
+    L.k3x_fetch_drops.argtypes = [P, ctypes.POINTER(ctypes.c_int64), P]
+    L.k3x_rmsnorm_bf16.restype = ctypes.c_int
+    L.k3x_rmsnorm_bf16.argtypes = [P, I32, I32, ctypes.c_float, P, P]
+    L.k3x_residual_add_bf16.restype = ctypes.c_int
+    L.k3x_residual_add_bf16.argtypes = [P, P, I32, I32, P]
+    L.k3x_profiler_create.restype = ctypes.c_int
+    L.k3x_profiler_create.argtypes = [I32, ctypes.POINTER(P)]
+    L.k3x_profiler_destroy.restype = None
+    L.k3x_profiler_destroy.argtypes = [P]
+    L.k3x_profiler_attach.restype = ctypes.c_int
+    L.k3x_profiler_attach.argtypes = [P]
+    L.k3x_profiler_reset.restype = ctypes.c_int
+    L.k3x_profiler_reset.argtypes = [P]
+    L.k3x_profiler_count.restype = I32
+    L.k3x_profiler_count.argtypes = [P]
+    L.k3x_profiler_read.restype = ctypes.c_int
+    L.k3x_profiler_read.argtypes = [P, I32, ctypes.POINTER(ctypes.c_char_p),
+                                    ctypes.POINTER(ctypes.c_float)]
+    _lib = L
+    return L
+
+
+def lib():
+    return load_library()
+
+
+def _check(st: int):
+    if st != K3X_OK:
+        L = lib()
+        raise K3xError(st, f"{L.k3x_status_str(st).decode()}: {L.k3x_last_error().decode()}")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return int(stream)
+
+
+def k3x_status_str(status: int) -> str:
+    return lib().k3x_status_str(status).decode()
+
+
+def k3x_last_error() -> str:
+    return lib().k3x_last_error().decode()
+
+
+# ------------------------------------------------------------------------------------------
+# Expert pool
+# ------------------------------------------------------------------------------------------
+class Pool:
+    """Owns a k3x_pool handle and keeps the borrowed device tensors alive."""
+
+    def __init__(self, handle: int, tensors, E: int, H: int, I: int):
+        self.handle = handle
+        self.tensors = tensors
+        self.E, self.H, self.I = E, H, I
+
+    def close(self):
+        if self.handle:
+            lib().k3x_expert_pool_destroy(self.handle)
+            self.handle = 0
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+TENSOR_ORDER = ("w1_packed", "w1_scale", "w3_packed", "w3_scale", "w2_packed", "w2_scale")
+
+
+def k3x_expert_pool_create(tensors: dict, hidden: int, inter: int, n_experts: int,
+                           group: int = 32, strides=None) -> Pool:
+    """tensors: the six uint8 device tensors by name (each [E][rows][cols] or any layout that
+    matches the strides).  strides: per-expert byte strides (None / 0 = dense)."""
+    d = k3x_pool_desc()
+    d.n_experts, d.hidden, d.inter, d.group = n_experts, hidden, inter, group
+    for name in TENSOR_ORDER:
+        t = tensors.get(name)
+        setattr(d, name, None if t is None else _ptr(t))
+    for k in range(6):
+        d.stride_bytes[k] = 0 if strides is None else int(strides[k])
+    h = ctypes.c_void_p()
+    _check(lib().k3x_expert_pool_create(ctypes.byref(d), ctypes.byref(h)))
+    return Pool(h.value, dict(tensors), n_experts, hidden, inter)
+
+
+def k3x_expert_pool_destroy(pool: Pool):
+    pool.close()
+
+
+# ------------------------------------------------------------------------------------------
+# Router
+# ------------------------------------------------------------------------------------------
+def router_desc(weight, bias, topk, renorm=1, routed_scale=1.0) -> k3x_router_desc:
+    r = k3x_router_desc()
+    r.weight = _ptr(weight)
+    r.bias = _ptr(bias)
+    r.n_experts = int(weight.shape[0])
+    r.hidden = int(weight.shape[1])
+    r.topk, r.renorm, r.routed_scale = int(topk), int(renorm), float(routed_scale)
+    return r
+
+
+def k3x_route_workspace_size(r: k3x_router_desc, T: int) -> int:
+    return int(lib().k3x_route_workspace_size(ctypes.byref(r), int(T)))
+
+
+def k3x_route_topk(r: k3x_router_desc, x, T: int, idx_out, gates_out, ws, ws_bytes=None,
+                   stream=None):
+    nbytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    _check(lib().k3x_route_topk(ctypes.byref(r), _ptr(x), int(T), _ptr(idx_out),
+                                _ptr(gates_out), _ptr(ws), int(nbytes), _stream(stream)))
+
+
+# ------------------------------------------------------------------------------------------
+# Expert forward
+# ------------------------------------------------------------------------------------------
+def k3x_moe_workspace_size(pool: Pool, T: int, topk: int) -> int:
+    return int(lib().k3x_moe_workspace_size(pool.handle, int(T), int(topk)))
+
+
+def k3x_moe_forward(pool: Pool, x, T: int, idx, gates, topk: int, y, ws, ws_bytes=None,
+                    stream=None):
+    nbytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    _check(lib().k3x_moe_forward(pool.handle, _ptr(x), int(T), _ptr(idx), _ptr(gates),
+                                 int(topk), _ptr(y), _ptr(ws), int(nbytes), _stream(stream)))
+
+
+def k3x_fetch_drops(ws, stream=None) -> int:
+    n = ctypes.c_int64(0)
+    st = lib().k3x_fetch_drops(_ptr(ws), ctypes.byref(n), _stream(stream))
+    if st not in (K3X_OK, K3X_E_DROPS):
+        _check(st)
+    return int(n.value)
+
+
+def k3x_rmsnorm_bf16(x, T: int, H: int, eps: float, out, stream=None):
+    _check(lib().k3x_rmsnorm_bf16(_ptr(x), int(T), int(H), float(eps), _ptr(out), _stream(stream)))
+
+
+def k3x_residual_add_bf16(x, y, T: int, H: int, stream=None):
+    _check(lib().k3x_residual_add_bf16(_ptr(x), _ptr(y), int(T), int(H), _stream(stream)))
+
+
+# ------------------------------------------------------------------------------------------
+# Conveniences over the C calls (allocation of outputs and workspaces with torch)
+# ------------------------------------------------------------------------------------------
+def alloc_workspace(nbytes: int, device="cuda"):
+    """A 256-byte aligned uint8 device buffer (torch's caching allocator aligns to 512)."""
+    t = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+    assert t.data_ptr() % 256 == 0
+    return t
+
+
+def moe_forward(pool: Pool, x, idx, gates, y=None, ws=None, stream=None):
+    """y = k3x_moe_forward(...) with y and workspace allocated on demand.  x: bf16 [T][H]
+    (a torch.bfloat16 or int16/uint16 tensor of bf16 bits)."""
+    T, topk = int(idx.shape[0]), int(idx.shape[1])
+    if y is None:
+        y = torch.empty((T, pool.H), dtype=torch.float32, device=x.device)
+    if ws is None:
+        ws = alloc_workspace(k3x_moe_workspace_size(pool, T, topk), x.device)
+    k3x_moe_forward(pool, x, T, idx, gates, topk, y, ws, stream=stream)
+    return y, ws
+
+
+def route_topk(weight, bias, x, topk, renorm=1, routed_scale=1.0, idx=None, gates=None,
+               ws=None, stream=None):
+    T = int(x.shape[0])
+    r = router_desc(weight, bias, topk, renorm, routed_scale)
+    if idx is None:
+        idx = torch.empty((T, topk), dtype=torch.int32, device=x.device)
+    if gates is None:
+        gates = torch.empty((T, topk), dtype=torch.float32, device=x.device)
+    if ws is None:
+        ws = alloc_workspace(k3x_route_workspace_size(r, T), x.device)
+    k3x_route_topk(r, x, T, idx, gates, ws, stream=stream)
+    return idx, gates, ws
+
+
+# ------------------------------------------------------------------------------------------
+# Kernel timing (HIP events around every kernel the library launches from this thread)
+# ------------------------------------------------------------------------------------------
+def k3x_profiler_create(capacity: int) -> int:
+    h = ctypes.c_void_p()
+    _check(lib().k3x_profiler_create(int(capacity), ctypes.byref(h)))
+    return h.value
+
+
+def k3x_profiler_destroy(prof: int):
+    lib().k3x_profiler_destroy(prof)
+
+
+def k3x_profiler_attach(prof):
+    _check(lib().k3x_profiler_attach(prof))
+
+
+def k3x_profiler_reset(prof: int):
+    _check(lib().k3x_profiler_reset(prof))
+
+
+def k3x_profiler_count(prof: int) -> int:
+    return int(lib().k3x_profiler_count(prof))
+
+
+def k3x_profiler_read(prof: int, i: int):
+    """(kernel name, milliseconds) of recorded launch i."""
+    name = ctypes.c_char_p()
+    ms = ctypes.c_float()
+    _check(lib().k3x_profiler_read(prof, int(i), ctypes.byref(name), ctypes.byref(ms)))
+    return name.value.decode(), float(ms.value)
+
+
+def profiler_durations(prof: int):
+    """{kernel name: [ms, ...]} of everything recorded since the last reset."""
+    out = {}
+    for i in range(k3x_profiler_count(prof)):
+        n, ms = k3x_profiler_read(prof, i)
+        out.setdefault(n, []).append(ms)
+    return out

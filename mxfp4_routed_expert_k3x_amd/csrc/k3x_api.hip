@@ -1,0 +1,310 @@
+// C ABI of the k3x library: argument validation, workspace layout and dispatch.
+// The operations are defined in include/k3x.h (with their sources on the pages).
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <new>
+
+#include "k3x_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+k3x_status fail(k3x_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+k3x_status hip_fail(hipError_t e, const char* where) {
+  return fail(K3X_E_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+}  // namespace
+
+namespace k3x {
+
+int device_cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return 256;
+  return (n + kNumXcd - 1) / kNumXcd * kNumXcd;
+}
+
+}  // namespace k3x
+
+extern "C" {
+
+const char* k3x_status_str(k3x_status s) {
+  switch (s) {
+    case K3X_OK: return "ok";
+    case K3X_E_INVALID_ARG: return "invalid argument";
+    case K3X_E_UNSUPPORTED: return "unsupported shape, group size or alignment";
+    case K3X_E_WORKSPACE: return "workspace missing, misaligned or too small";
+    case K3X_E_HIP: return "HIP launch or runtime error";
+    case K3X_E_DROPS: return "slots with invalid expert ids were dropped";
+  }
+  return "unknown status";
+}
+
+const char* k3x_last_error(void) { return g_last_error; }
+
+k3x_status k3x_expert_pool_create(const k3x_pool_desc* d, k3x_pool** out) {
+  if (!d || !out) return fail(K3X_E_INVALID_ARG, "pool_create: NULL desc or out");
+  *out = nullptr;
+  if (d->n_experts < 1 || d->n_experts > 8192)
+    return fail(K3X_E_INVALID_ARG, "pool_create: n_experts %d not in 1..8192", d->n_experts);
+  if (d->group != 32) return fail(K3X_E_UNSUPPORTED, "pool_create: group %d != 32", d->group);
+  if (d->hidden <= 0 || d->inter <= 0)
+    return fail(K3X_E_INVALID_ARG, "pool_create: hidden %d / inter %d", d->hidden, d->inter);
+  if (d->hidden % 128 || d->inter % 128)
+    return fail(K3X_E_UNSUPPORTED, "pool_create: hidden %d and inter %d must be multiples of 128",
+                d->hidden, d->inter);
+  if (d->hidden > 65536 || d->inter > 65536)
+    return fail(K3X_E_UNSUPPORTED, "pool_create: hidden/inter above 65536");
+  const void* ptrs[6] = {d->w1_packed, d->w1_scale, d->w3_packed, d->w3_scale, d->w2_packed, d->w2_scale};
+  const int64_t H = d->hidden, I = d->inter;
+  const int64_t dense[6] = {I * H / 2, I * H / 32, I * H / 2, I * H / 32, H * I / 2, H * I / 32};
+  k3x_pool* p = new (std::nothrow) k3x_pool;
+  if (!p) return fail(K3X_E_INVALID_ARG, "pool_create: out of host memory");
+  p->E = d->n_experts;
+  p->H = d->hidden;
+  p->I = d->inter;
+  for (int k = 0; k < 6; ++k) {
+    if (!ptrs[k]) {
+      delete p;
+      return fail(K3X_E_INVALID_ARG, "pool_create: tensor %d is NULL", k);
+    }
+    const int64_t st = d->stride_bytes[k] ? d->stride_bytes[k] : dense[k];
+    if (st < dense[k]) {
+      delete p;
+      return fail(K3X_E_INVALID_ARG, "pool_create: stride of tensor %d (%lld) below its size %lld", k,
+                  (long long)st, (long long)dense[k]);
+    }
+    if (k % 2 == 0 && (!aligned(ptrs[k], 16) || st % 16)) {
+      delete p;
+      return fail(K3X_E_UNSUPPORTED, "pool_create: packed tensor %d not 16-byte aligned", k);
+    }
+    p->base[k] = static_cast<const uint8_t*>(ptrs[k]);
+    p->stride[k] = st;
+  }
+  *out = p;
+  g_last_error[0] = 0;
+  return K3X_OK;
+}
+
+void k3x_expert_pool_destroy(k3x_pool* p) { delete p; }
+
+static k3x_status check_router(const k3x_router_desc* r) {
+  if (!r) return fail(K3X_E_INVALID_ARG, "router: NULL desc");
+  if (!r->weight) return fail(K3X_E_INVALID_ARG, "router: NULL weight");
+  if (r->n_experts < 1 || r->n_experts > 4096)
+    return fail(K3X_E_INVALID_ARG, "router: n_experts %d not in 1..4096", r->n_experts);
+  if (r->hidden <= 0 || r->hidden % 8 || r->hidden > 16384)
+    return fail(K3X_E_UNSUPPORTED, "router: hidden %d must be a positive multiple of 8, <= 16384",
+                r->hidden);
+  if (r->topk < 1 || r->topk > r->n_experts)
+    return fail(K3X_E_INVALID_ARG, "router: topk %d not in 1..%d", r->topk, r->n_experts);
+  if (!aligned(r->weight, 16)) return fail(K3X_E_UNSUPPORTED, "router: weight not 16-byte aligned");
+  return K3X_OK;
+}
+
+size_t k3x_route_workspace_size(const k3x_router_desc* r, int32_t T) {
+  if (check_router(r) != K3X_OK || T < 0) return 0;
+  const size_t b = sizeof(float) * (size_t)T * (size_t)r->n_experts;
+  return b ? (b + 255) & ~(size_t)255 : 256;
+}
+
+k3x_status k3x_route_topk(const k3x_router_desc* r, const void* x_bf16, int32_t T,
+                          int32_t* idx_out, float* gates_out, void* ws, size_t ws_bytes,
+                          void* stream) {
+  k3x_status st = check_router(r);
+  if (st != K3X_OK) return st;
+  if (T < 0) return fail(K3X_E_INVALID_ARG, "route_topk: T %d < 0", T);
+  if (T == 0) return K3X_OK;
+  if (!x_bf16 || !idx_out || !gates_out)
+    return fail(K3X_E_INVALID_ARG, "route_topk: NULL x, idx or gates");
+  if (!aligned(x_bf16, 16)) return fail(K3X_E_UNSUPPORTED, "route_topk: x not 16-byte aligned");
+  const size_t need = k3x_route_workspace_size(r, T);
+  if (!ws || ws_bytes < need || !aligned(ws, 256))
+    return fail(K3X_E_WORKSPACE, "route_topk: workspace %zu bytes, need %zu (256-byte aligned)",
+                ws_bytes, need);
+  hipError_t e = k3x::launch_route(*r, static_cast<const uint16_t*>(x_bf16), T, idx_out,
+                                   gates_out, static_cast<float*>(ws), (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "route_topk");
+  return K3X_OK;
+}
+
+size_t k3x_moe_workspace_size(const k3x_pool* p, int32_t T, int32_t topk) {
+  if (!p || T < 0 || topk < 1 || topk > 64) return 0;
+  if ((int64_t)T * topk > (int64_t)1 << 26) return 0;
+  return k3x::moe_layout(p->E, p->H, p->I, T, topk).total;
+}
+
+k3x_status k3x_moe_forward(const k3x_pool* p, const void* x_bf16, int32_t T, const int32_t* idx,
+                           const float* gates, int32_t topk, float* y, void* ws,
+                           size_t ws_bytes, void* stream) {
+  if (!p) return fail(K3X_E_INVALID_ARG, "moe_forward: NULL pool");
+  if (T < 0) return fail(K3X_E_INVALID_ARG, "moe_forward: T %d < 0", T);
+  if (topk < 1 || topk > 64) return fail(K3X_E_INVALID_ARG, "moe_forward: topk %d not in 1..64", topk);
+  if ((int64_t)T * topk > (int64_t)1 << 26)
+    return fail(K3X_E_UNSUPPORTED, "moe_forward: T * topk above 2^26");
+  const size_t need = k3x_moe_workspace_size(p, T, topk);
+  if (!ws || ws_bytes < need || !aligned(ws, 256))
+    return fail(K3X_E_WORKSPACE, "moe_forward: workspace %zu bytes, need %zu (256-byte aligned)",
+                ws_bytes, need);
+  if (T > 0) {
+    if (!x_bf16 || !idx || !gates || !y)
+      return fail(K3X_E_INVALID_ARG, "moe_forward: NULL x, idx, gates or y");
+    if (!aligned(x_bf16, 16) || !aligned(y, 16))
+      return fail(K3X_E_UNSUPPORTED, "moe_forward: x and y must be 16-byte aligned");
+  }
+  const k3x::MoeLayout L = k3x::moe_layout(p->E, p->H, p->I, T, topk);
+  hipError_t e = k3x::launch_moe(*p, static_cast<const uint16_t*>(x_bf16), T, idx, gates, topk,
+                                 y, static_cast<uint8_t*>(ws), L, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "moe_forward");
+  return K3X_OK;
+}
+
+k3x_status k3x_fetch_drops(const void* ws, int64_t* n, void* stream) {
+  if (!ws || !n) return fail(K3X_E_INVALID_ARG, "fetch_drops: NULL ws or n");
+  int64_t v = 0;
+  hipError_t e = hipMemcpyAsync(&v, ws, sizeof(v), hipMemcpyDeviceToHost, (hipStream_t)stream);
+  if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "fetch_drops");
+  *n = v;
+  return v > 0 ? K3X_E_DROPS : K3X_OK;
+}
+
+k3x_status k3x_rmsnorm_bf16(const void* x, int32_t T, int32_t H, float eps, void* out,
+                            void* stream) {
+  if (T < 0 || H <= 0) return fail(K3X_E_INVALID_ARG, "rmsnorm: T %d, H %d", T, H);
+  if (H % 8 || H > 16384) return fail(K3X_E_UNSUPPORTED, "rmsnorm: H %d must be a multiple of 8, <= 16384", H);
+  if (T == 0) return K3X_OK;
+  if (!x || !out) return fail(K3X_E_INVALID_ARG, "rmsnorm: NULL x or out");
+  if (!aligned(x, 16) || !aligned(out, 16)) return fail(K3X_E_UNSUPPORTED, "rmsnorm: 16-byte alignment");
+  hipError_t e = k3x::launch_rmsnorm(static_cast<const uint16_t*>(x), T, H, eps,
+                                     static_cast<uint16_t*>(out), (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "rmsnorm");
+  return K3X_OK;
+}
+
+k3x_status k3x_residual_add_bf16(void* x, const float* y, int32_t T, int32_t H, void* stream) {
+  if (T < 0 || H <= 0) return fail(K3X_E_INVALID_ARG, "residual_add: T %d, H %d", T, H);
+  if (H % 8) return fail(K3X_E_UNSUPPORTED, "residual_add: H %d must be a multiple of 8", H);
+  if (T == 0) return K3X_OK;
+  if (!x || !y) return fail(K3X_E_INVALID_ARG, "residual_add: NULL x or y");
+  if (!aligned(x, 16) || !aligned(y, 16)) return fail(K3X_E_UNSUPPORTED, "residual_add: 16-byte alignment");
+  hipError_t e = k3x::launch_residual(static_cast<uint16_t*>(x), y, T, H, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "residual_add");
+  return K3X_OK;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------------------
+// Kernel timing
+// ---------------------------------------------------------------------------------------
+struct k3x_profiler {
+  int32_t capacity = 0;
+  int32_t n = 0;
+  hipEvent_t* start = nullptr;
+  hipEvent_t* stop = nullptr;
+  const char** name = nullptr;
+};
+
+namespace {
+thread_local k3x_profiler* g_prof = nullptr;
+}
+
+namespace k3x {
+
+LaunchTimer::LaunchTimer(const char* name, hipStream_t s) {
+  k3x_profiler* p = g_prof;
+  if (!p || p->n >= p->capacity) return;
+  const int i = p->n++;
+  p->name[i] = name;
+  if (hipEventRecord(p->start[i], s) != hipSuccess) return;
+  stop_ = p->stop[i];
+  s_ = s;
+}
+
+LaunchTimer::~LaunchTimer() {
+  if (stop_) (void)hipEventRecord(stop_, s_);
+}
+
+}  // namespace k3x
+
+extern "C" {
+
+k3x_status k3x_profiler_create(int32_t capacity, k3x_profiler** out) {
+  if (!out || capacity < 1 || capacity > (1 << 20))
+    return fail(K3X_E_INVALID_ARG, "profiler_create: capacity %d not in 1..2^20", capacity);
+  *out = nullptr;
+  k3x_profiler* p = new (std::nothrow) k3x_profiler;
+  if (!p) return fail(K3X_E_INVALID_ARG, "profiler_create: out of host memory");
+  p->start = new (std::nothrow) hipEvent_t[capacity]();
+  p->stop = new (std::nothrow) hipEvent_t[capacity]();
+  p->name = new (std::nothrow) const char*[capacity]();
+  if (!p->start || !p->stop || !p->name) {
+    k3x_profiler_destroy(p);
+    return fail(K3X_E_INVALID_ARG, "profiler_create: out of host memory");
+  }
+  p->capacity = capacity;
+  for (int i = 0; i < capacity; ++i) {
+    hipError_t e = hipEventCreate(&p->start[i]);
+    if (e == hipSuccess) e = hipEventCreate(&p->stop[i]);
+    if (e != hipSuccess) {
+      k3x_profiler_destroy(p);
+      return hip_fail(e, "profiler_create");
+    }
+  }
+  *out = p;
+  return K3X_OK;
+}
+
+void k3x_profiler_destroy(k3x_profiler* p) {
+  if (!p) return;
+  if (g_prof == p) g_prof = nullptr;
+  for (int i = 0; i < p->capacity; ++i) {
+    if (p->start && p->start[i]) (void)hipEventDestroy(p->start[i]);
+    if (p->stop && p->stop[i]) (void)hipEventDestroy(p->stop[i]);
+  }
+  delete[] p->start;
+  delete[] p->stop;
+  delete[] p->name;
+  delete p;
+}
+
+k3x_status k3x_profiler_attach(k3x_profiler* p) {
+  g_prof = p;
+  return K3X_OK;
+}
+
+k3x_status k3x_profiler_reset(k3x_profiler* p) {
+  if (!p) return fail(K3X_E_INVALID_ARG, "profiler_reset: NULL");
+  p->n = 0;
+  return K3X_OK;
+}
+
+int32_t k3x_profiler_count(const k3x_profiler* p) { return p ? p->n : 0; }
+
+k3x_status k3x_profiler_read(k3x_profiler* p, int32_t i, const char** name, float* ms) {
+  if (!p || !name || !ms || i < 0 || i >= p->n)
+    return fail(K3X_E_INVALID_ARG, "profiler_read: bad index %d", i);
+  hipError_t e = hipEventSynchronize(p->stop[i]);
+  if (e == hipSuccess) e = hipEventElapsedTime(ms, p->start[i], p->stop[i]);
+  if (e != hipSuccess) return hip_fail(e, "profiler_read");
+  *name = p->name[i];
+  return K3X_OK;
+}
+
+}  // extern "C"

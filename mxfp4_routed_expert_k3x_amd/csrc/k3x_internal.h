@@ -1,0 +1,134 @@
+// Internal declarations of the k3x HIP library (gfx950 only).
+//
+// Nothing here is shared with the CPU oracle: conversions, decoders and reductions below
+// are this library's own.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/k3x.h"
+
+namespace k3x {
+
+// ---------------------------------------------------------------------------------------
+// Vector types used by the gfx950 builtins
+// ---------------------------------------------------------------------------------------
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kGroup = 32;   // MX group along K
+constexpr int kKBlock = 128; // K per main-loop step: 4 groups, one per lane quarter
+constexpr int kNumXcd = 8;   // MI355X: 8 accelerator complex dies, workgroups dealt round-robin
+
+// ---------------------------------------------------------------------------------------
+// bf16 <-> f32
+// ---------------------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) {
+  return __uint_as_float(b16 << 16);
+}
+
+// Round-to-nearest-even narrowing of a float to bf16 bits.  NaN -> canonical quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// ---------------------------------------------------------------------------------------
+// MXFP4 decode: one E8M0 byte -> the float 2^(s-127); byte 255 -> 0 (zeroes the group).
+// ---------------------------------------------------------------------------------------
+__device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
+  // s in 1..254 is a normal float exponent field; s = 0 gives 2^-127 (subnormal)
+  const float v = s ? __uint_as_float(s << 23) : __uint_as_float(0x00400000u);
+  return s == 255u ? 0.0f : v;
+}
+
+// Eight consecutive E2M1 elements (the four bytes of one dword, low nibble = even element)
+// times a power-of-two scale, as eight bf16 in element order.  The products are exact for
+// scale bytes 2..253.
+__device__ __forceinline__ bf16x8 dequant8(uint32_t dw, float scale) {
+  const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, scale, 0);
+  const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, scale, 1);
+  const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, scale, 2);
+  const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, scale, 3);
+  return bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// XCD-aware placement: workgroups are dealt to the 8 dies round-robin, so workgroup b runs
+// on die b % 8.  Returns this workgroup's die and its rank among the die's workgroups.
+__device__ __forceinline__ void xcd_rank(int& die, int& rank, int& per_die) {
+  die = blockIdx.x % kNumXcd;
+  rank = blockIdx.x / kNumXcd;
+  per_die = gridDim.x / kNumXcd;  // grids are launched as a multiple of 8
+}
+
+// ---------------------------------------------------------------------------------------
+// Workspace layout of k3x_moe_forward (byte offsets; every region 256-byte aligned)
+// ---------------------------------------------------------------------------------------
+struct MoeLayout {
+  size_t drops;       // int64 drop counter (+ int32 n_tiles at +8)
+  size_t offsets;     // int32 [E + 1] start of each expert's slots in perm
+  size_t tiles;       // int32 [max_tiles][4] = expert, first slot in perm, count, pad
+  size_t perm;        // int32 [T * topk] slot ids (t * topk + j) grouped by expert
+  size_t h;           // bf16 [T * topk][I]
+  size_t d;           // fp32 [T * topk][H]
+  size_t total;
+  int32_t max_tiles;
+  int32_t tile_tokens;
+};
+
+MoeLayout moe_layout(int32_t E, int32_t H, int32_t I, int32_t T, int32_t topk);
+
+// ---------------------------------------------------------------------------------------
+// Pool handle
+// ---------------------------------------------------------------------------------------
+}  // namespace k3x
+
+struct k3x_pool {
+  int32_t E, H, I;
+  const uint8_t* base[6];
+  int64_t stride[6];
+};
+
+namespace k3x {
+
+// ---------------------------------------------------------------------------------------
+// Launchers (each returns hipSuccess or the launch error)
+// ---------------------------------------------------------------------------------------
+hipError_t launch_route(const k3x_router_desc& r, const uint16_t* x, int32_t T, int32_t* idx,
+                        float* gates, float* scores, hipStream_t s);
+
+hipError_t launch_moe(const k3x_pool& p, const uint16_t* x, int32_t T, const int32_t* idx,
+                      const float* gates, int32_t topk, float* y, uint8_t* ws,
+                      const MoeLayout& L, hipStream_t s);
+
+hipError_t launch_rmsnorm(const uint16_t* x, int32_t T, int32_t H, float eps, uint16_t* out,
+                          hipStream_t s);
+
+hipError_t launch_residual(uint16_t* x, const float* y, int32_t T, int32_t H, hipStream_t s);
+
+int device_cu_count();
+
+// Brackets one kernel launch with the attached profiler's events (no-op when none is
+// attached to this thread).  Construct right before the launch, destroy right after it.
+class LaunchTimer {
+ public:
+  LaunchTimer(const char* name, hipStream_t s);
+  ~LaunchTimer();
+
+ private:
+  hipEvent_t stop_ = nullptr;
+  hipStream_t s_ = nullptr;
+};
+
+}  // namespace k3x

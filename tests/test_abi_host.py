@@ -1,0 +1,153 @@
+"""The C ABI without a GPU: the library loads, exports every symbol the header declares, and
+rejects bad arguments on the host before enqueueing anything (no device work is started)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "k3x.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"\b(k3x_[a-z0-9_]+)\s*\(", src)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def k3x():
+    import mxfp4_routed_expert_k3x_amd as k
+
+    k.load_library()
+    return k
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("k3x_expert_pool_create", "k3x_route_topk", "k3x_moe_forward"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(k3x):
+    lib = k3x.lib()
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+    assert set(k3x.EXPORTS) == set(declared_functions())
+
+
+def test_python_binding_has_the_c_names(k3x):
+    for n in declared_functions():
+        assert hasattr(k3x, n), n
+
+
+def _desc(k3x, **kw):
+    d = k3x.k3x_pool_desc()
+    d.n_experts, d.hidden, d.inter, d.group = 8, 256, 384, 32
+    base = 1 << 40  # fake, never dereferenced: validation is host-only
+    for i, n in enumerate(k3x.TENSOR_ORDER):
+        setattr(d, n, base + i * (1 << 32))
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def _create(k3x, d):
+    h = ctypes.c_void_p()
+    st = k3x.lib().k3x_expert_pool_create(ctypes.byref(d), ctypes.byref(h))
+    return st, h.value
+
+
+def test_pool_create_accepts_valid_desc(k3x):
+    st, h = _create(k3x, _desc(k3x))
+    assert st == k3x.K3X_OK and h
+    k3x.lib().k3x_expert_pool_destroy(h)
+    k3x.lib().k3x_expert_pool_destroy(None)  # no-op
+
+
+@pytest.mark.parametrize("kw,want", [
+    ({"group": 16}, -2),
+    ({"group": 64}, -2),
+    ({"hidden": 3500}, -2),
+    ({"inter": 100}, -2),
+    ({"hidden": 0}, -1),
+    ({"n_experts": 0}, -1),
+    ({"n_experts": 20000}, -1),
+    ({"w2_scale": None}, -1),
+    ({"w1_packed": (1 << 40) + 8}, -2),
+])
+def test_pool_create_refuses(k3x, kw, want):
+    st, h = _create(k3x, _desc(k3x, **kw))
+    assert st == want and not h
+    assert k3x.k3x_last_error() != ""
+
+
+def test_pool_create_refuses_small_or_misaligned_stride(k3x):
+    d = _desc(k3x)
+    d.stride_bytes[0] = 100  # below the dense size of w1_packed
+    assert _create(k3x, d)[0] == k3x.K3X_E_INVALID_ARG
+    d = _desc(k3x)
+    d.stride_bytes[4] = 384 * 256 // 2 + 8  # packed stride must keep 16-byte alignment
+    assert _create(k3x, d)[0] == k3x.K3X_E_UNSUPPORTED
+    assert _create(k3x, _desc(k3x))[0] == k3x.K3X_OK
+
+
+def test_moe_forward_host_validation(k3x):
+    lib = k3x.lib()
+    st, h = _create(k3x, _desc(k3x))
+    assert st == 0
+    try:
+        need = lib.k3x_moe_workspace_size(h, 4, 16)
+        assert need > 0
+        assert lib.k3x_moe_workspace_size(h, 4, 65) == 0
+        assert lib.k3x_moe_workspace_size(h, -1, 16) == 0
+        fake = 1 << 40
+        # bad topk, negative T, missing or small or misaligned workspace: no launch happens
+        assert lib.k3x_moe_forward(h, fake, 4, fake, fake, 0, fake, fake, need, None) == -1
+        assert lib.k3x_moe_forward(h, fake, -1, fake, fake, 16, fake, fake, need, None) == -1
+        assert lib.k3x_moe_forward(h, fake, 4, fake, fake, 16, fake, None, need, None) == -3
+        assert lib.k3x_moe_forward(h, fake, 4, fake, fake, 16, fake, fake, need - 1, None) == -3
+        assert lib.k3x_moe_forward(h, fake, 4, fake, fake, 16, fake, fake + 8, need, None) == -3
+        assert lib.k3x_moe_forward(h, None, 4, fake, fake, 16, fake, fake, need, None) == -1
+        assert lib.k3x_moe_forward(h, fake + 2, 4, fake, fake, 16, fake, fake, need, None) == -2
+        assert lib.k3x_moe_forward(None, fake, 4, fake, fake, 16, fake, fake, need, None) == -1
+    finally:
+        lib.k3x_expert_pool_destroy(h)
+
+
+def test_router_host_validation(k3x):
+    lib = k3x.lib()
+    fake = 1 << 40
+    r = k3x.k3x_router_desc()
+    r.weight, r.bias, r.n_experts, r.hidden, r.topk, r.renorm, r.routed_scale = fake, None, 896, 3584, 16, 1, 1.0
+    need = lib.k3x_route_workspace_size(ctypes.byref(r), 4)
+    assert need >= 4 * 896 * 4
+    # T = 0 is a no-op that succeeds
+    assert lib.k3x_route_topk(ctypes.byref(r), fake, 0, fake, fake, fake, need, None) == 0
+    assert lib.k3x_route_topk(ctypes.byref(r), fake, 4, fake, fake, fake, need - 4, None) == -3
+    for field, val, want in (("topk", 0, -1), ("topk", 897, -1), ("hidden", 3583, -2),
+                             ("n_experts", 5000, -1), ("weight", None, -1)):
+        r2 = k3x.k3x_router_desc()
+        ctypes.pointer(r2)[0] = r
+        setattr(r2, field, val)
+        assert lib.k3x_route_topk(ctypes.byref(r2), fake, 4, fake, fake, fake, need, None) == want
+        assert lib.k3x_route_workspace_size(ctypes.byref(r2), 4) == 0
+
+
+def test_norm_helpers_host_validation(k3x):
+    lib = k3x.lib()
+    fake = 1 << 40
+    assert lib.k3x_rmsnorm_bf16(fake, 1, 3583, 1e-6, fake, None) == -2
+    assert lib.k3x_rmsnorm_bf16(fake, -1, 3584, 1e-6, fake, None) == -1
+    assert lib.k3x_rmsnorm_bf16(fake, 0, 3584, 1e-6, fake, None) == 0
+    assert lib.k3x_residual_add_bf16(fake, fake, 1, 3583, None) == -2
+    assert lib.k3x_residual_add_bf16(None, fake, 1, 3584, None) == -1
+    assert lib.k3x_fetch_drops(None, None, None) == -1
+
+
+def test_status_strings(k3x):
+    for s in (0, -1, -2, -3, -4, -5):
+        assert k3x.k3x_status_str(s)
+    assert k3x.k3x_status_str(7) == "unknown status"

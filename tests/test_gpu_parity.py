@@ -1,0 +1,327 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle.
+
+Routing indices must equal the oracle's element by element and gates bit for bit; y must
+reach relative L2 <= 1e-4 and max-abs <= 1e-3 * max|y_ref| (tests/cases.py).  Inputs are
+seeded (k3x_synth); expected values come from the oracle only.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import k3x_synth as S
+from cases import assert_y_close, oracle_forward_sampled, y_errors
+
+pytestmark = pytest.mark.gpu
+
+
+def _log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import mxfp4_routed_expert_k3x_amd as k3x
+
+    k3x.load_library()
+    return torch, k3x
+
+
+def _t(torch, a):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).cuda()
+
+
+def _np(t, dtype=None):
+    a = t.detach().cpu().numpy()
+    return a.view(dtype) if dtype is not None else a
+
+
+def _pool(torch, k3x, dev_tensors, E, H, I):
+    return k3x.k3x_expert_pool_create(dev_tensors, hidden=H, inter=I, n_experts=E)
+
+
+# ------------------------------------------------------------------------------------------
+# generator twin
+# ------------------------------------------------------------------------------------------
+def test_synth_device_bytes_equal_host_bytes(dev):
+    torch, _ = dev
+    _log("case: synth device vs host, E=3 H=256 I=384")
+    E, H, I = 3, 256, 384
+    d = S.device_pool(99, 2, E, H, I)
+    h = S.host_pool(99, 2, E, H, I)
+    for n in S.TENSOR_NAMES:
+        assert np.array_equal(_np(d[n]), h[n]), n
+    _log("case: synth device vs host, sampled windows of full-size experts")
+    big = S.device_pool(7, 1, 4, S.H_K3, S.I_K3)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(0)
+    for t, n in enumerate(S.TENSOR_NAMES):
+        arr = _np(big[n]).reshape(4, -1)
+        for _ in range(3):
+            e = int(rng.integers(0, 4))
+            b0 = int(rng.integers(0, arr.shape[1] - 64))
+            if t % 2 == 0:
+                want = S.packed_bytes(7, 1, e, t, 64, b0=b0)
+            else:
+                want = S.scale_bytes(7, 1, e, t, 64, s0=b0)
+            assert np.array_equal(arr[e, b0:b0 + 64], want), (n, e, b0)
+
+
+# ------------------------------------------------------------------------------------------
+# expert forward, small shapes (several tiles, ragged tails, duplicates, drops)
+# ------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("E,H,I,T,k", [(8, 256, 384, 5, 3), (6, 128, 128, 7, 5), (16, 384, 256, 40, 4)])
+def test_moe_small_parity(dev, orc, E, H, I, T, k):
+    torch, k3x = dev
+    _log(f"case: moe small E={E} H={H} I={I} T={T} k={k}")
+    seed = 1000 + E + H + I + T
+    host = S.host_pool(seed, 0, E, H, I)
+    pool = _pool(torch, k3x, S.device_pool(seed, 0, E, H, I), E, H, I)
+    x = S.normal_bf16(seed, S.P_X, 0, (T, H))
+    idx, gates = S.uniform_routing(seed, T, E, k)
+    y, ws = k3x.moe_forward(pool, _t(torch, x), _t(torch, idx), _t(torch, gates))
+    torch.cuda.synchronize()
+    assert k3x.k3x_fetch_drops(ws) == 0
+    y_ref, drops = orc.moe_forward(host, x, idx, gates)
+    assert drops == 0
+    assert_y_close(_np(y), y_ref, f"E={E} H={H} I={I} T={T} k={k}")
+
+
+def test_moe_duplicates_and_drops(dev, orc):
+    torch, k3x = dev
+    E, H, I, T, k = 6, 256, 256, 9, 6
+    _log(f"case: moe duplicates and drops E={E} T={T} k={k}")
+    host = S.host_pool(5, 0, E, H, I)
+    pool = _pool(torch, k3x, S.device_pool(5, 0, E, H, I), E, H, I)
+    x = S.normal_bf16(5, S.P_X, 0, (T, H))
+    rng = np.random.default_rng(5)
+    idx = rng.integers(0, E, (T, k)).astype(np.int32)  # duplicates within tokens
+    idx[0, 0] = -1
+    idx[3, 5] = E
+    idx[8, 2] = 1 << 30
+    _, gates = S.uniform_routing(5, T, k, k)
+    y, ws = k3x.moe_forward(pool, _t(torch, x), _t(torch, idx), _t(torch, gates))
+    torch.cuda.synchronize()
+    assert k3x.k3x_fetch_drops(ws) == 3
+    y_ref, drops = orc.moe_forward(host, x, idx, gates)
+    assert drops == 3
+    assert_y_close(_np(y), y_ref, "duplicates/drops")
+    # the next call resets the counter
+    idx2 = np.clip(idx, 0, E - 1).astype(np.int32)
+    k3x.moe_forward(pool, _t(torch, x), _t(torch, idx2), _t(torch, gates), ws=ws)
+    assert k3x.k3x_fetch_drops(ws) == 0
+
+
+def test_moe_zero_tokens(dev):
+    torch, k3x = dev
+    _log("case: moe T=0")
+    E, H, I = 4, 128, 128
+    pool = _pool(torch, k3x, S.device_pool(1, 0, E, H, I), E, H, I)
+    ws = k3x.alloc_workspace(k3x.k3x_moe_workspace_size(pool, 0, 16))
+    ws.fill_(0xFF)
+    x = torch.empty((0, H), dtype=torch.int16, device="cuda")
+    idx = torch.empty((0, 16), dtype=torch.int32, device="cuda")
+    g = torch.empty((0, 16), dtype=torch.float32, device="cuda")
+    y = torch.empty((0, H), dtype=torch.float32, device="cuda")
+    k3x.k3x_moe_forward(pool, x, 0, idx, g, 16, y, ws)
+    assert k3x.k3x_fetch_drops(ws) == 0
+
+
+# ------------------------------------------------------------------------------------------
+# router
+# ------------------------------------------------------------------------------------------
+def _route_both(torch, k3x, orc, x, W, b, topk, renorm=1, scale=1.0):
+    idx, gates, _ = k3x.route_topk(_t(torch, W), None if b is None else _t(torch, b),
+                                   _t(torch, x), topk, renorm, scale)
+    torch.cuda.synchronize()
+    i_ref, g_ref = orc.route(x, W, b, topk, renorm, scale)
+    return _np(idx), _np(gates), i_ref, g_ref
+
+
+def test_router_parity_k3_shape(dev, orc):
+    torch, k3x = dev
+    w = S.WORKLOADS[2]
+    _log("case: router E=896 H=3584 T=96 topk=16")
+    W, b = S.router_inputs(w)
+    x = S.normal_bf16(4242, S.P_X, 0, (96, w.H))
+    idx, gates, i_ref, g_ref = _route_both(torch, k3x, orc, x, W, b, 16)
+    assert np.array_equal(idx, i_ref)
+    assert np.array_equal(gates.view(np.uint32), g_ref.view(np.uint32))
+
+
+def test_router_parity_zipf_bias(dev, orc):
+    torch, k3x = dev
+    w = S.WORKLOADS[3]
+    _log("case: router Zipf bias T=64")
+    W, b = S.router_inputs(w)
+    x = S.normal_bf16(77, S.P_X, 0, (64, w.H))
+    idx, gates, i_ref, g_ref = _route_both(torch, k3x, orc, x, W, b, 16)
+    assert np.array_equal(idx, i_ref)
+    assert np.array_equal(gates.view(np.uint32), g_ref.view(np.uint32))
+
+
+def test_router_ties_full_k_and_options(dev, orc):
+    torch, k3x = dev
+    _log("case: router ties / k=E / renorm off / scale")
+    E, H = 96, 256
+    W = S.normal_bf16(3, S.P_WR, 0, (E, H), std=0.05)
+    W[17] = W[4]
+    b = S.normal_f32(3, S.P_BIAS, 0, (E,), std=0.01)
+    b[4] = b[17] = 5.0
+    x = S.normal_bf16(3, S.P_X, 0, (5, H))
+    idx, gates, i_ref, g_ref = _route_both(torch, k3x, orc, x, W, b, 4)
+    assert np.array_equal(idx, i_ref) and np.all(idx[:, 0] == 4) and np.all(idx[:, 1] == 17)
+    assert np.array_equal(gates.view(np.uint32), g_ref.view(np.uint32))
+    idx, gates, i_ref, g_ref = _route_both(torch, k3x, orc, x, W, b, E)
+    assert np.array_equal(idx, i_ref)
+    assert np.array_equal(gates.view(np.uint32), g_ref.view(np.uint32))
+    idx, gates, i_ref, g_ref = _route_both(torch, k3x, orc, x, W, None, 8, renorm=0, scale=2.5)
+    assert np.array_equal(idx, i_ref)
+    assert np.array_equal(gates.view(np.uint32), g_ref.view(np.uint32))
+
+
+# ------------------------------------------------------------------------------------------
+# the five workloads at full size (sampled tokens where the oracle would take minutes)
+# ------------------------------------------------------------------------------------------
+def test_workload1_decode_e64(dev, orc):
+    torch, k3x = dev
+    w = S.WORKLOADS[1]
+    _log(f"case: workload {w.name}")
+    pool = _pool(torch, k3x, S.device_pool(w.seed, 0, w.E, w.H, w.I), w.E, w.H, w.I)
+    x = S.activations(w)
+    idx, gates = S.uniform_routing(w.seed, w.T, w.E, w.topk)
+    y, ws = k3x.moe_forward(pool, _t(torch, x), _t(torch, idx), _t(torch, gates))
+    torch.cuda.synchronize()
+    y_ref = oracle_forward_sampled(orc, w.seed, 0, w.H, w.I, x, idx, gates, range(w.T))
+    r = assert_y_close(_np(y), y_ref, w.name)
+    _log(f"  rel_l2={r[0]:.3e} max_abs={r[1]:.3e}")
+
+
+def test_workload2_decode_e896_router(dev, orc):
+    torch, k3x = dev
+    w = S.WORKLOADS[2]
+    _log(f"case: workload {w.name}")
+    pool = _pool(torch, k3x, S.device_pool(w.seed, 0, w.E, w.H, w.I), w.E, w.H, w.I)
+    W, b = S.router_inputs(w)
+    x = S.activations(w)
+    xd = _t(torch, x)
+    idx, gates, _ = k3x.route_topk(_t(torch, W), _t(torch, b), xd, w.topk)
+    y, ws = k3x.moe_forward(pool, xd, idx, gates)
+    torch.cuda.synchronize()
+    i_ref, g_ref = orc.route(x, W, b, w.topk)
+    assert np.array_equal(_np(idx), i_ref)
+    assert np.array_equal(_np(gates).view(np.uint32), g_ref.view(np.uint32))
+    y_ref = oracle_forward_sampled(orc, w.seed, 0, w.H, w.I, x, i_ref, g_ref, range(w.T))
+    r = assert_y_close(_np(y), y_ref, w.name)
+    _log(f"  rel_l2={r[0]:.3e} max_abs={r[1]:.3e}")
+    del pool
+    torch.cuda.empty_cache()
+
+
+def test_workload3_decode_t32_zipf(dev, orc):
+    torch, k3x = dev
+    w = S.WORKLOADS[3]
+    _log(f"case: workload {w.name}")
+    pool = _pool(torch, k3x, S.device_pool(w.seed, 0, w.E, w.H, w.I), w.E, w.H, w.I)
+    W, b = S.router_inputs(w)
+    x = S.activations(w)
+    xd = _t(torch, x)
+    idx, gates, _ = k3x.route_topk(_t(torch, W), _t(torch, b), xd, w.topk)
+    y, ws = k3x.moe_forward(pool, xd, idx, gates)
+    torch.cuda.synchronize()
+    i_ref, g_ref = orc.route(x, W, b, w.topk)
+    assert np.array_equal(_np(idx), i_ref)
+    assert np.array_equal(_np(gates).view(np.uint32), g_ref.view(np.uint32))
+    U = len(np.unique(i_ref))
+    tokens = [0, 13, 31]
+    y_ref = oracle_forward_sampled(orc, w.seed, 0, w.H, w.I, x, i_ref, g_ref, tokens)
+    r = assert_y_close(_np(y)[tokens], y_ref, w.name)
+    _log(f"  distinct experts U={U} rel_l2={r[0]:.3e} max_abs={r[1]:.3e}")
+    del pool
+    torch.cuda.empty_cache()
+
+
+def test_workload4_prefill_t4096(dev, orc):
+    torch, k3x = dev
+    w = S.WORKLOADS[4]
+    _log(f"case: workload {w.name}")
+    pool = _pool(torch, k3x, S.device_pool(w.seed, 0, w.E, w.H, w.I), w.E, w.H, w.I)
+    x = S.activations(w)
+    idx, gates = S.uniform_routing(w.seed, w.T, w.E, w.topk)
+    y, ws = k3x.moe_forward(pool, _t(torch, x), _t(torch, idx), _t(torch, gates))
+    torch.cuda.synchronize()
+    assert k3x.k3x_fetch_drops(ws) == 0
+    tokens = [0, 1, 2047, 4095]
+    y_ref = oracle_forward_sampled(orc, w.seed, 0, w.H, w.I, x, idx, gates, tokens)
+    r = assert_y_close(_np(y)[tokens], y_ref, w.name)
+    _log(f"  rel_l2={r[0]:.3e} max_abs={r[1]:.3e}")
+    del pool, ws
+    torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------------------------------------
+# RMSNorm / residual and a chained decode (teacher-forced per layer)
+# ------------------------------------------------------------------------------------------
+def test_rmsnorm_and_residual_bitwise(dev, orc):
+    torch, k3x = dev
+    _log("case: rmsnorm / residual T=33 H=3584")
+    T, H = 33, 3584
+    x = S.normal_bf16(8, S.P_X, 0, (T, H))
+    xd = _t(torch, x)
+    out = torch.empty_like(xd)
+    k3x.k3x_rmsnorm_bf16(xd, T, H, 1e-6, out)
+    y = np.random.default_rng(8).standard_normal((T, H)).astype(np.float32) * 30
+    yd = _t(torch, y)
+    xr = xd.clone()
+    k3x.k3x_residual_add_bf16(xr, yd, T, H)
+    torch.cuda.synchronize()
+    assert np.array_equal(_np(out, np.uint16), orc.rmsnorm_bf16(x, 1e-6))
+    assert np.array_equal(_np(xr, np.uint16), orc.residual_add_bf16(x, y))
+
+
+def _chain(torch, k3x, orc, L, E, log_every=True):
+    w = S.WORKLOADS[5]
+    H, I, k = w.H, w.I, w.topk
+    x = S.activations(w)
+    xd = _t(torch, x)
+    worst = 0.0
+    for layer in range(L):
+        pool = _pool(torch, k3x, S.device_pool(w.seed, layer, E, H, I), E, H, I)
+        W = S.normal_bf16(w.seed, S.P_WR, layer, (E, H), std=0.02)
+        b = S.zipf_bias(w.seed, E, layer)
+        x_in = _np(xd, np.uint16).copy()
+        xn = torch.empty_like(xd)
+        k3x.k3x_rmsnorm_bf16(xd, 1, H, 1e-6, xn)
+        idx, gates, _ = k3x.route_topk(_t(torch, W), _t(torch, b), xn, k)
+        y, _ = k3x.moe_forward(pool, xn, idx, gates)
+        k3x.k3x_residual_add_bf16(xd, y, 1, H)
+        torch.cuda.synchronize()
+        # teacher forcing: the oracle takes this layer's GPU input
+        xn_ref = orc.rmsnorm_bf16(x_in, 1e-6)
+        assert np.array_equal(_np(xn, np.uint16), xn_ref), layer
+        i_ref, g_ref = orc.route(xn_ref, W, b, k)
+        assert np.array_equal(_np(idx), i_ref), layer
+        assert np.array_equal(_np(gates).view(np.uint32), g_ref.view(np.uint32)), layer
+        y_ref = oracle_forward_sampled(orc, w.seed, layer, H, I, xn_ref, i_ref, g_ref, [0])
+        rel, mx = assert_y_close(_np(y), y_ref, f"layer {layer}")
+        worst = max(worst, rel)
+        if log_every:
+            _log(f"  layer {layer}: rel_l2={rel:.3e} max_abs={mx:.3e}")
+        del pool
+    return worst
+
+
+def test_chain12_reduced_pool(dev, orc):
+    """Twelve chained layers (RMSNorm -> router -> experts -> residual) with 64 experts per
+    layer; every layer is checked against the oracle on the GPU's own layer input."""
+    torch, k3x = dev
+    _log("case: chain of 12 layers, E=64")
+    _chain(torch, k3x, orc, 12, 64)
