@@ -20,8 +20,10 @@
  *  - Kimi K3 artifact audit, section 4.3: the six packed/scale tensors of one expert.
  *
  * Readings taken where the pages leave a step open (each also listed in the design notes):
- *  - Activation: SwiGLU, h = silu(g) * u with silu(g) = g / (1 + expf(-g)) in fp32, and h
- *    rounded to bf16 (round to nearest even) before W2.
+ *  - Activation: SwiGLU, h = silu(g) * u with silu(g) = g / (1 + E) in fp32, E the float
+ *    exponential of -g taken as the float nearest to the exact value (evaluated in double
+ *    and rounded once, so every conforming implementation gets the same E), and h rounded to
+ *    bf16 (round to nearest even) before W2.
  *  - Expert dot products: each group of 32 is summed sequentially in ACC, multiplied by its
  *    exact power-of-two scale, and the group partials are summed by a pairwise tree (zero
  *    padded to a power of two).  ACC = float is the verdict oracle; ACC = double is its
@@ -228,7 +230,8 @@ void ORC(oracle_mxfp4_matvec)(const float *x, const uint8_t *packed, const uint8
   }
 }
 
-/* One routed expert on one activation: g = W1.x, u = W3.x, h = bf16(silu(g) * u), d = W2.h.
+/* One routed expert on one activation: g = W1.x, u = W3.x, h = bf16(silu(g) * u), d = W2.h,
+ * silu(g) = g / (1 + E) with E the float nearest to exp(-g).
  * x bf16 [H]; h_out bf16 [I] (may be NULL); g_out/u_out fp32 [I] (may be NULL);
  * d_out fp32 [H]. */
 void ORC(oracle_expert_forward)(const uint16_t *x, int64_t H, int64_t I, const uint8_t *w1p,
@@ -243,7 +246,8 @@ void ORC(oracle_expert_forward)(const uint16_t *x, int64_t H, int64_t I, const u
   ORC(oracle_mxfp4_matvec)(xf, w1p, w1s, I, H, g);
   ORC(oracle_mxfp4_matvec)(xf, w3p, w3s, I, H, u);
   for (int64_t r = 0; r < I; ++r) {
-    const float silu = g[r] / (1.0f + expf(-g[r]));
+    const float ex = (float)exp(-(double)g[r]);
+    const float silu = g[r] / (1.0f + ex);
     const uint16_t hb = float_to_bf16(silu * u[r]);
     if (h_out) h_out[r] = hb;
     hf[r] = bf16_to_float(hb);

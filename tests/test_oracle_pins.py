@@ -225,6 +225,7 @@ def test_brute_force_tiny(orc, H, I, acc):
             assert np.max(np.abs(g - g64)) <= 1e-6 * scale_g
             assert np.max(np.abs(u - u64)) <= 1e-6 * (np.max(np.abs(u64)) + 1e-30)
             # h = bf16(silu(g) * u): against the exact value built from the oracle's own g and u
+            # (the float exponential inside silu is the float nearest to exp(-g))
             # (g and u were pinned above), h may miss the exact rounding only next to a midpoint
             g64o, u64o = g.astype(np.float64), u.astype(np.float64)
             v = g64o / (1.0 + np.exp(-g64o)) * u64o
@@ -232,7 +233,7 @@ def test_brute_force_tiny(orc, H, I, acc):
             want = bf16_rne_from64(v)
             for r in np.nonzero(hf != want)[0]:
                 if abs(v[r]) < 2.0 ** -100:
-                    # for g < -88.7 expf(-g) overflows float32, so silu(g) is -0 there
+                    # for g < -88.7 exp(-g) overflows float32, so silu(g) is -0 there
                     assert abs(hf[r] - v[r]) <= 2.0 ** -100
                     continue
                 ulp = 2.0 ** (math.frexp(v[r])[1] - 8)
