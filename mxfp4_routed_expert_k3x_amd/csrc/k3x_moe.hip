@@ -5,11 +5,12 @@
 // h rounded to bf16 before W2.
 //
 // Pipeline of one forward (all on the caller's stream):
-//   1. moe_sort       slots (t, j) counted per expert, laid out expert by expert, and cut
-//                     into tiles of at most `tile_tokens` slots of one expert
-//   2. w13            per tile: g = W1 x, u = W3 x for 32 rows at a time, h = bf16(silu(g) u)
-//   3. w2             per tile: d = W2 h for 64 rows at a time
-//   4. combine        y[t] = sum_j gate[t][j] * d[t][j], slot order, invalid slots skipped
+//   1. moe_sort   (T > 1 only) slots (t, j) counted per expert, laid out expert by expert,
+//                 cut into tiles of at most 16 slots of one expert; counts drops.  With
+//                 T = 1 every slot is its own tile and the W13 kernel counts the drops.
+//   2. w13        per tile and 32 rows: g = W1 x, u = W3 x, h = bf16(silu(g) * u)
+//   3. w2         per tile and 64 rows: d = W2 h
+//   4. combine    y[t] = sum_j gate[t][j] * d[t][j] in slot order, invalid slots skipped
 //
 // The expert GEMMs run on bf16 MFMA (16x16x32, fp32 accumulate).  Packed weights stream from
 // HBM straight into the MFMA A operand: each lane loads 16 bytes = 32 nibbles = one whole
@@ -17,7 +18,9 @@
 // group's power-of-two scale folded in (exact).  Lane quarter q of a wave takes group
 // 4 kb + q, so one 16-byte load per lane feeds four MFMAs that together cover 16 rows x 128
 // K.  The activations (x or h) form the B operand; the MFMA's K order is a permutation shared
-// by A and B, so the product is unchanged.
+// by A and B, so the product is unchanged.  The four waves of a workgroup split K in four
+// contiguous ranges and their partial sums are added in a fixed order, (p0 + p1) + (p2 + p3),
+// which keeps every serial fp32 chain short.
 #include "k3x_internal.h"
 
 namespace k3x {
@@ -55,26 +58,30 @@ namespace {
 // ---------------------------------------------------------------------------------------
 constexpr int kSortThreads = 1024;
 
-__global__ __launch_bounds__(kSortThreads) void moe_sort(const int32_t* __restrict__ idx,
-                                                         int32_t n_slots, int32_t E,
-                                                         int32_t tile_tokens,
-                                                         uint8_t* __restrict__ ws,
-                                                         size_t off_offsets, size_t off_tiles,
-                                                         size_t off_perm) {
+struct SortArgs {
+  const int32_t* idx;
+  int32_t T, topk, E, tile_tokens;
+  uint8_t* ws;
+  size_t off_offsets, off_tiles, off_perm;
+};
+
+__global__ __launch_bounds__(kSortThreads) void moe_sort(SortArgs a) {
   extern __shared__ int32_t counts[];  // [E]
   __shared__ int32_t scan_c[kSortThreads];
   __shared__ int32_t scan_t[kSortThreads];
   __shared__ int32_t drop_cnt;
   const int tid = threadIdx.x;
-  int32_t* offsets = reinterpret_cast<int32_t*>(ws + off_offsets);
-  int32_t* tiles = reinterpret_cast<int32_t*>(ws + off_tiles);
-  int32_t* perm = reinterpret_cast<int32_t*>(ws + off_perm);
+  const int n_slots = a.T * a.topk;
+  const int E = a.E;
+  int32_t* offsets = reinterpret_cast<int32_t*>(a.ws + a.off_offsets);
+  int32_t* tiles = reinterpret_cast<int32_t*>(a.ws + a.off_tiles);
+  int32_t* perm = reinterpret_cast<int32_t*>(a.ws + a.off_perm);
 
   for (int e = tid; e < E; e += kSortThreads) counts[e] = 0;
   if (tid == 0) drop_cnt = 0;
   __syncthreads();
   for (int p = tid; p < n_slots; p += kSortThreads) {
-    const int e = idx[p];
+    const int e = a.idx[p];
     if (e >= 0 && e < E)
       atomicAdd(&counts[e], 1);
     else
@@ -88,7 +95,7 @@ __global__ __launch_bounds__(kSortThreads) void moe_sort(const int32_t* __restri
   for (int e = e0; e < e1; ++e) {
     const int c = counts[e];
     csum += c;
-    tsum += (c + tile_tokens - 1) / tile_tokens;
+    tsum += (c + a.tile_tokens - 1) / a.tile_tokens;
   }
   scan_c[tid] = csum;
   scan_t[tid] = tsum;
@@ -106,12 +113,12 @@ __global__ __launch_bounds__(kSortThreads) void moe_sort(const int32_t* __restri
   for (int e = e0; e < e1; ++e) {
     const int c = counts[e];
     offsets[e] = bc;
-    const int nt = (c + tile_tokens - 1) / tile_tokens;
+    const int nt = (c + a.tile_tokens - 1) / a.tile_tokens;
     for (int i = 0; i < nt; ++i) {
       int4 tv;
       tv.x = e;
-      tv.y = bc + i * tile_tokens;
-      tv.z = min(tile_tokens, c - i * tile_tokens);
+      tv.y = bc + i * a.tile_tokens;
+      tv.z = min(a.tile_tokens, c - i * a.tile_tokens);
       tv.w = 0;
       reinterpret_cast<int4*>(tiles)[bt + i] = tv;
     }
@@ -121,18 +128,18 @@ __global__ __launch_bounds__(kSortThreads) void moe_sort(const int32_t* __restri
   }
   if (tid == kSortThreads - 1) {
     offsets[E] = scan_c[kSortThreads - 1];
-    *reinterpret_cast<int64_t*>(ws) = (int64_t)drop_cnt;
-    *reinterpret_cast<int32_t*>(ws + 8) = scan_t[kSortThreads - 1];
+    *reinterpret_cast<int64_t*>(a.ws) = (int64_t)drop_cnt;
+    *reinterpret_cast<int32_t*>(a.ws + 8) = scan_t[kSortThreads - 1];
   }
   __syncthreads();
   for (int p = tid; p < n_slots; p += kSortThreads) {
-    const int e = idx[p];
+    const int e = a.idx[p];
     if (e >= 0 && e < E) perm[atomicAdd(&counts[e], 1)] = p;
   }
 }
 
 // ---------------------------------------------------------------------------------------
-// Shared pieces of the expert GEMMs
+// Decode-sized grouped GEMM
 // ---------------------------------------------------------------------------------------
 struct GemmArgs {
   const uint8_t* wa;   // first weight tensor (W1 or W2) packed, expert 0
@@ -144,193 +151,242 @@ struct GemmArgs {
   int32_t rows;        // output rows per expert (I for W1/W3, H for W2)
   const uint16_t* act; // B operand rows: x [T][H] (by token) or h [slots][I] (by slot)
   int32_t act_by_token;  // 1: row = slot / topk (x); 0: row = slot (h)
-  int32_t topk;
-  const uint8_t* ws;   // workspace: n_tiles at +8, tiles, perm
+  const int32_t* idx;  // [T][topk]
+  const float* gates;  // [T][topk]
+  int32_t T, topk, E;
+  int32_t implicit_tiles;  // 1 (T == 1): tile j is slot j, no sort ran
+  uint8_t* ws;         // workspace
   size_t off_tiles, off_perm;
   void* out;           // h (bf16 [slots][I]) or d (fp32 [slots][H])
 };
 
-// Load one K block (128 K) of the A operand for one 16-row block: this lane's 16 packed
-// bytes (group 4 kb + q of row `row`) and the group's scale as a float.
-struct AFrag {
-  uint4 q;
-  float scale;
+// One K block (128 K) of operands for one lane: the packed bytes of 4 row blocks (group
+// 4 kb + q of this lane's row), their 4 scale dwords (scales of groups 4 kb .. 4 kb + 3),
+// and the 4 B fragments (8 activations each) of this lane's column.
+struct Stage {
+  uint4 w[4];
+  uint32_t sc[4];
+  uint4 x[4];
 };
-
-__device__ __forceinline__ AFrag load_a(const uint8_t* __restrict__ wrow,
-                                        const uint8_t* __restrict__ srow, int grp) {
-  AFrag f;
-  f.q = *reinterpret_cast<const uint4*>(wrow + (size_t)grp * 16);
-  f.scale = e8m0_to_f32(srow[grp]);
-  return f;
-}
 
 __device__ __forceinline__ uint32_t dword_of(const uint4& v, int s) {
   return s == 0 ? v.x : s == 1 ? v.y : s == 2 ? v.z : v.w;
 }
 
-// ---------------------------------------------------------------------------------------
-// 2/3. Decode-sized grouped GEMM: tiles of at most 16 slots.  Work item = one wave, 4
-// row blocks of 16 (W1/W3 mode: W1 rows r0..r0+31 and W3 rows r0..r0+31; W2 mode: W2 rows
-// r0..r0+63), the full K.  The B operand comes straight from global memory (the tile's
-// activation rows are few and cache-resident).  Items are split over the 8 dies in
-// contiguous ranges and dealt to waves so that every workgroup gets a share.
-// ---------------------------------------------------------------------------------------
+// Operand addresses of one lane: two uniform expert bases (W1/W3 mode: W1 for row blocks
+// 0-1 and W3 for 2-3; W2 mode: both W2) plus 32-bit per-lane offsets, so the bases live in
+// scalar registers.
+struct Addr {
+  const uint8_t* wlo;  // packed base of row blocks 0-1
+  const uint8_t* whi;  // packed base of row blocks 2-3
+  const uint8_t* slo;  // scale base of row blocks 0-1
+  const uint8_t* shi;  // scale base of row blocks 2-3
+  uint32_t woff[4];    // byte offset of this lane's row in each row block (+ 16 q)
+  uint32_t soff[4];    // byte offset of this lane's scale row in each row block
+  const uint16_t* brow;
+};
+
+__device__ __forceinline__ void load_stage(Stage& st, const Addr& ad, bool valid, int kb, int q) {
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) {
+    const uint8_t* wb = rb < 2 ? ad.wlo : ad.whi;
+    const uint8_t* sb = rb < 2 ? ad.slo : ad.shi;
+    st.w[rb] = *reinterpret_cast<const uint4*>(wb + ad.woff[rb] + (uint32_t)kb * 64u);
+    st.sc[rb] = *reinterpret_cast<const uint32_t*>(sb + ad.soff[rb] + (uint32_t)kb * 4u);
+  }
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+    st.x[s] = valid ? *reinterpret_cast<const uint4*>(ad.brow + kKBlock * kb + 32 * q + 8 * s)
+                    : make_uint4(0, 0, 0, 0);
+}
+
+__device__ __forceinline__ void compute_stage(const Stage& st, f32x4 (&acc)[4], int q) {
+  float scale[4];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) scale[rb] = e8m0_to_f32((st.sc[rb] >> (8 * q)) & 0xFFu);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const bf16x8 b = as_bf16x8(st.x[s]);
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+      acc[rb] = mfma16x16x32(dequant8(dword_of(st.w[rb], s), scale[rb]), b, acc[rb]);
+  }
+}
+
+__device__ __forceinline__ bool expert_ok(int e, int E) { return e >= 0 && e < E; }
+
+// Work item = (tile, row chunk): W1/W3 mode covers W1 rows r0..r0+31 and W3 rows r0..r0+31
+// (row blocks 0,1 of W1 and 2,3 of W3); W2 mode covers W2 rows r0..r0+63.  Items are split
+// over the 8 dies in contiguous ranges (a die's workgroups then share the tiles' activation
+// rows in its L2) and strided over the die's workgroups.
 template <bool kSwiGLU>
 __global__ __launch_bounds__(256) void gemm_decode(GemmArgs a) {
+  __shared__ f32x4 part[4][4][kWave];  // [wave][row block][lane] partial sums
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
   const int n = lane % 16;  // B column / A row within a 16-row block
   const int q = lane / 16;  // lane quarter: which group of the K block
-  const int32_t n_tiles = *reinterpret_cast<const int32_t*>(a.ws + 8);
+  int n_tiles;
+  if (a.implicit_tiles) {
+    n_tiles = a.T * a.topk;
+    if (kSwiGLU && blockIdx.x == 0) {
+      // upkeep of the sortless path (T == 1): the drop count
+      if (threadIdx.x == 0) {
+        int bad = 0;
+        for (int j = 0; j < n_tiles; ++j) bad += expert_ok(a.idx[j], a.E) ? 0 : 1;
+        *reinterpret_cast<int64_t*>(a.ws) = bad;
+      }
+    }
+  } else {
+    n_tiles = *reinterpret_cast<const int32_t*>(a.ws + 8);
+  }
   const int4* tiles = reinterpret_cast<const int4*>(a.ws + a.off_tiles);
   const int32_t* perm = reinterpret_cast<const int32_t*>(a.ws + a.off_perm);
   const int rows_per_item = kSwiGLU ? 32 : 64;
   const int items_per_tile = a.rows / rows_per_item;
   const int items = n_tiles * items_per_tile;
+  const int nk = a.K / kKBlock;
+  const int kb0 = (wave * nk) / 4;
+  const int kb1 = ((wave + 1) * nk) / 4;
+  const size_t wrow_bytes = (size_t)a.K / 2;
+  const size_t srow_bytes = (size_t)a.K / kGroup;
 
   int die, rank, per_die;
   xcd_rank(die, rank, per_die);
   const int chunk = (items + kNumXcd - 1) / kNumXcd;
   const int lo = die * chunk;
   const int hi = min(items, lo + chunk);
-  const int wave_rank = wave * per_die + rank;
-  const int waves_per_die = per_die * (blockDim.x / kWave);
-  const int nk = a.K / kKBlock;
-  const size_t wrow_bytes = (size_t)a.K / 2;
-  const size_t srow_bytes = (size_t)a.K / kGroup;
 
-  for (int it = lo + wave_rank; it < hi; it += waves_per_die) {
+  for (int it = lo + rank; it < hi; it += per_die) {
     const int tile = it / items_per_tile;
     const int r0 = (it % items_per_tile) * rows_per_item;
-    const int4 tv = tiles[tile];
-    const int e = tv.x, start = tv.y, m = tv.z;
+    int e, start, m;
+    if (a.implicit_tiles) {
+      e = a.idx[tile];
+      start = tile;
+      m = 1;
+      if (!expert_ok(e, a.E)) continue;  // a dropped slot (uniform across the workgroup)
+    } else {
+      const int4 tv = tiles[tile];
+      e = tv.x;
+      start = tv.y;
+      m = tv.z;
+    }
 
-    // B column n of this tile
     const bool valid = n < m;
-    const int slot = valid ? perm[start + n] : 0;
+    const int slot = valid ? (a.implicit_tiles ? start + n : perm[start + n]) : 0;
     const int arow = a.act_by_token ? slot / a.topk : slot;
-    const uint16_t* brow = a.act + (size_t)arow * a.K;
 
-    // A rows of the 4 row blocks
-    const uint8_t* wp[4];
-    const uint8_t* sp[4];
+    Addr ad;
+    ad.brow = a.act + (size_t)arow * a.K;
+    if (kSwiGLU) {
+      ad.wlo = a.wa + (size_t)e * a.st_wa;
+      ad.whi = a.wb + (size_t)e * a.st_wb;
+      ad.slo = a.sa + (size_t)e * a.st_sa;
+      ad.shi = a.sb + (size_t)e * a.st_sb;
+    } else {
+      ad.wlo = ad.whi = a.wa + (size_t)e * a.st_wa;
+      ad.slo = ad.shi = a.sa + (size_t)e * a.st_sa;
+    }
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
-      int row;
-      const uint8_t *wbase, *sbase;
-      if (kSwiGLU) {
-        row = r0 + 16 * (rb & 1) + n;
-        wbase = (rb < 2) ? a.wa + (size_t)e * a.st_wa : a.wb + (size_t)e * a.st_wb;
-        sbase = (rb < 2) ? a.sa + (size_t)e * a.st_sa : a.sb + (size_t)e * a.st_sb;
-      } else {
-        row = r0 + 16 * rb + n;
-        wbase = a.wa + (size_t)e * a.st_wa;
-        sbase = a.sa + (size_t)e * a.st_sa;
-      }
-      wp[rb] = wbase + (size_t)row * wrow_bytes;
-      sp[rb] = sbase + (size_t)row * srow_bytes;
+      const int row = kSwiGLU ? r0 + 16 * (rb & 1) + n : r0 + 16 * rb + n;
+      ad.woff[rb] = (uint32_t)(row * wrow_bytes) + 16u * (uint32_t)q;
+      ad.soff[rb] = (uint32_t)(row * srow_bytes);
     }
 
     f32x4 acc[4];
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) acc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    AFrag cur[4];
-    uint4 xb[4];
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) cur[rb] = load_a(wp[rb], sp[rb], q);
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-      xb[s] = valid ? *reinterpret_cast<const uint4*>(brow + 32 * q + 8 * s) : make_uint4(0, 0, 0, 0);
-
-    for (int kb = 0; kb < nk; ++kb) {
-      AFrag nxt[4];
-      uint4 xn[4];
-      const bool more = kb + 1 < nk;
-      if (more) {
-        const int g = 4 * (kb + 1) + q;
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb) nxt[rb] = load_a(wp[rb], sp[rb], g);
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-          xn[s] = valid ? *reinterpret_cast<const uint4*>(brow + 128 * (kb + 1) + 32 * q + 8 * s)
-                        : make_uint4(0, 0, 0, 0);
-      }
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const bf16x8 b = as_bf16x8(xb[s]);
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb)
-          acc[rb] = mfma16x16x32(dequant8(dword_of(cur[rb].q, s), cur[rb].scale), b, acc[rb]);
-      }
-      if (more) {
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb) cur[rb] = nxt[rb];
-#pragma unroll
-        for (int s = 0; s < 4; ++s) xb[s] = xn[s];
-      }
+    // K range of this wave, loads issued one K block ahead of the MFMAs; two named stages
+    // alternate so that no register copy waits on a load still in flight
+    Stage s0, s1;
+    if (kb0 < kb1) load_stage(s0, ad, valid, kb0, q);
+    for (int kb = kb0; kb < kb1; kb += 2) {
+      if (kb + 1 < kb1) load_stage(s1, ad, valid, kb + 1, q);
+      compute_stage(s0, acc, q);
+      if (kb + 1 >= kb1) break;
+      if (kb + 2 < kb1) load_stage(s0, ad, valid, kb + 2, q);
+      compute_stage(s1, acc, q);
     }
 
-    // epilogue: lane holds rows 4q..4q+3 of each row block, column n
-    if (valid) {
-      if (kSwiGLU) {
-        uint16_t* h = static_cast<uint16_t*>(a.out);
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-          uint32_t packed[2];
+    for (int rb = 0; rb < 4; ++rb) part[wave][rb][lane] = acc[rb];
+    __syncthreads();
+
+    if (kSwiGLU) {
+      if (wave < 2 && valid) {
+        // lane holds rows 4q..4q+3 of row block `wave`, column n
+        const int rb = wave;
+        const f32x4 g = (part[0][rb][lane] + part[1][rb][lane]) + (part[2][rb][lane] + part[3][rb][lane]);
+        const f32x4 u = (part[0][rb + 2][lane] + part[1][rb + 2][lane]) +
+                        (part[2][rb + 2][lane] + part[3][rb + 2][lane]);
+        uint32_t hv[2];
 #pragma unroll
-          for (int i = 0; i < 4; i += 2) {
-            uint32_t two = 0;
+        for (int i = 0; i < 4; i += 2) {
+          uint32_t two = 0;
 #pragma unroll
-            for (int k2 = 0; k2 < 2; ++k2) {
-              const float g = acc[rb][i + k2];
-              const float u = acc[rb + 2][i + k2];
-              const float v = (g / (1.0f + expf(-g))) * u;
-              two |= f32_to_bf16_bits(v) << (16 * k2);
-            }
-            packed[i / 2] = two;
+          for (int k2 = 0; k2 < 2; ++k2) {
+            const float gi = g[i + k2];
+            const float v = (gi / (1.0f + expf(-gi))) * u[i + k2];
+            two |= f32_to_bf16_bits(v) << (16 * k2);
           }
-          const int row = r0 + 16 * rb + 4 * q;
-          *reinterpret_cast<uint2*>(h + (size_t)slot * a.rows + row) = make_uint2(packed[0], packed[1]);
+          hv[i / 2] = two;
         }
-      } else {
-        float* d = static_cast<float*>(a.out);
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
-          const int row = r0 + 16 * rb + 4 * q;
-          *reinterpret_cast<float4*>(d + (size_t)slot * a.rows + row) =
-              make_float4(acc[rb][0], acc[rb][1], acc[rb][2], acc[rb][3]);
-        }
+        uint16_t* h = static_cast<uint16_t*>(a.out);
+        const int row = r0 + 16 * rb + 4 * q;
+        *reinterpret_cast<uint2*>(h + (size_t)slot * a.rows + row) = make_uint2(hv[0], hv[1]);
+      }
+    } else {
+      const int rb = wave;
+      if (valid) {
+        const f32x4 d = (part[0][rb][lane] + part[1][rb][lane]) + (part[2][rb][lane] + part[3][rb][lane]);
+        float* dout = static_cast<float*>(a.out);
+        const int row = r0 + 16 * rb + 4 * q;
+        *reinterpret_cast<float4*>(dout + (size_t)slot * a.rows + row) = make_float4(d[0], d[1], d[2], d[3]);
       }
     }
+    __syncthreads();  // part[] is reused by the next item
   }
 }
 
 // ---------------------------------------------------------------------------------------
 // 4. Combine: y[t][r] = sum_j gates[t][j] * d[t*topk + j][r], slots in order, slots whose
-// expert id is invalid skipped.  One thread per 4 consecutive rows.
+// expert id is invalid skipped (a token without a valid slot gets 0).  Grid (row blocks, T):
+// each thread owns 4 consecutive rows; the slot loop is unrolled 16 at a time so the
+// independent loads of d overlap.
 // ---------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void moe_combine(const float* __restrict__ d,
                                                    const int32_t* __restrict__ idx,
                                                    const float* __restrict__ gates,
-                                                   int32_t T, int32_t topk, int32_t H,
-                                                   int32_t E, float* __restrict__ y) {
-  const int per_tok = H / 4;
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= (int64_t)T * per_tok) return;
-  const int t = (int)(i / per_tok);
-  const int r = (int)(i % per_tok) * 4;
+                                                   int32_t topk, int32_t H, int32_t E,
+                                                   float* __restrict__ y) {
+  const int t = blockIdx.y;
+  const int r = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  if (r >= H) return;
+  const int32_t* it = idx + (size_t)t * topk;
+  const float* gt = gates + (size_t)t * topk;
+  const float* dt = d + (size_t)t * topk * H + r;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int j = 0; j < topk; ++j) {
-    const int e = idx[(size_t)t * topk + j];
-    if (e < 0 || e >= E) continue;
-    const float g = gates[(size_t)t * topk + j];
-    const float4 v = *reinterpret_cast<const float4*>(d + ((size_t)t * topk + j) * H + r);
-    acc.x = acc.x + g * v.x;
-    acc.y = acc.y + g * v.y;
-    acc.z = acc.z + g * v.z;
-    acc.w = acc.w + g * v.w;
+  for (int j0 = 0; j0 < topk; j0 += 16) {
+    float4 v[16];
+    float g[16];
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) {
+      const int j = j0 + jj;
+      const bool ok = j < topk && expert_ok(it[j], E);
+      g[jj] = ok ? gt[j] : 0.0f;
+      v[jj] = ok ? *reinterpret_cast<const float4*>(dt + (size_t)j * H) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) {
+      if (j0 + jj >= topk || !expert_ok(it[j0 + jj], E)) continue;
+      acc.x = acc.x + g[jj] * v[jj].x;
+      acc.y = acc.y + g[jj] * v[jj].y;
+      acc.z = acc.z + g[jj] * v[jj].z;
+      acc.w = acc.w + g[jj] * v[jj].w;
+    }
   }
   *reinterpret_cast<float4*>(y + (size_t)t * H + r) = acc;
 }
@@ -340,17 +396,31 @@ __global__ __launch_bounds__(256) void moe_combine(const float* __restrict__ d,
 hipError_t launch_moe(const k3x_pool& p, const uint16_t* x, int32_t T, const int32_t* idx,
                       const float* gates, int32_t topk, float* y, uint8_t* ws,
                       const MoeLayout& L, hipStream_t s) {
-  const int n_slots = T * topk;
-  const size_t sort_lds = sizeof(int32_t) * (size_t)p.E;
-  {
-    LaunchTimer lt("moe_sort", s);
-    hipLaunchKernelGGL(moe_sort, dim3(1), dim3(kSortThreads), sort_lds, s, idx, n_slots, p.E,
-                       L.tile_tokens, ws, L.offsets, L.tiles, L.perm);
+  if (decode_exact_supported(p, T, topk))
+    return launch_decode_exact(p, x, idx, gates, topk, y, ws, s);
+  hipError_t err;
+  const bool implicit = (T == 1);
+  if (!implicit) {
+    SortArgs sa{};
+    sa.idx = idx;
+    sa.T = T;
+    sa.topk = topk;
+    sa.E = p.E;
+    sa.tile_tokens = L.tile_tokens;
+    sa.ws = ws;
+    sa.off_offsets = L.offsets;
+    sa.off_tiles = L.tiles;
+    sa.off_perm = L.perm;
+    const size_t sort_lds = sizeof(int32_t) * (size_t)p.E;
+    {
+      LaunchTimer lt("moe_sort", s);
+      hipLaunchKernelGGL(moe_sort, dim3(1), dim3(kSortThreads), sort_lds, s, sa);
+    }
+    if ((err = hipGetLastError()) != hipSuccess || T == 0) return err;
   }
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess || T == 0) return err;
 
-  const int grid = device_cu_count() * 2;  // two 4-wave workgroups per CU; multiple of 8
+  // persistent grids: two 4-wave workgroups per CU (the occupancy the registers allow)
+  const int max_grid = device_cu_count() * 2;
 
   GemmArgs a13{};
   a13.wa = p.base[0];
@@ -365,14 +435,26 @@ hipError_t launch_moe(const k3x_pool& p, const uint16_t* x, int32_t T, const int
   a13.rows = p.I;
   a13.act = x;
   a13.act_by_token = 1;
+  a13.idx = idx;
+  a13.gates = gates;
+  a13.T = T;
   a13.topk = topk;
+  a13.E = p.E;
+  a13.implicit_tiles = implicit ? 1 : 0;
   a13.ws = ws;
   a13.off_tiles = L.tiles;
   a13.off_perm = L.perm;
   a13.out = ws + L.h;
+  const int64_t max_tiles = implicit ? (int64_t)topk : (int64_t)L.max_tiles;
+  auto grid_for = [&](int64_t items) {
+    int64_t g = (items + kNumXcd - 1) / kNumXcd * kNumXcd;
+    if (g > max_grid) g = max_grid;
+    return (int)(g < kNumXcd ? kNumXcd : g);
+  };
   {
     LaunchTimer lt("w13_decode", s);
-    hipLaunchKernelGGL(gemm_decode<true>, dim3(grid), dim3(256), 0, s, a13);
+    hipLaunchKernelGGL(gemm_decode<true>, dim3(grid_for(max_tiles * (p.I / 32))), dim3(256), 0,
+                       s, a13);
   }
   if ((err = hipGetLastError()) != hipSuccess) return err;
 
@@ -390,16 +472,14 @@ hipError_t launch_moe(const k3x_pool& p, const uint16_t* x, int32_t T, const int
   a2.out = ws + L.d;
   {
     LaunchTimer lt("w2_decode", s);
-    hipLaunchKernelGGL(gemm_decode<false>, dim3(grid), dim3(256), 0, s, a2);
+    hipLaunchKernelGGL(gemm_decode<false>, dim3(grid_for(max_tiles * (p.H / 64))), dim3(256), 0,
+                       s, a2);
   }
   if ((err = hipGetLastError()) != hipSuccess) return err;
-
-  const int64_t threads = (int64_t)T * (p.H / 4);
   {
     LaunchTimer lt("moe_combine", s);
-    hipLaunchKernelGGL(moe_combine, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
-                       reinterpret_cast<const float*>(ws + L.d), idx, gates, T, topk, p.H, p.E,
-                       y);
+    hipLaunchKernelGGL(moe_combine, dim3((p.H / 4 + 255) / 256, T), dim3(256), 0, s,
+                       reinterpret_cast<const float*>(ws + L.d), idx, gates, topk, p.H, p.E, y);
   }
   return hipGetLastError();
 }

@@ -203,6 +203,8 @@ def test_workload1_decode_e64(dev, orc):
     y_ref = oracle_forward_sampled(orc, w.seed, 0, w.H, w.I, x, idx, gates, range(w.T))
     r = assert_y_close(_np(y), y_ref, w.name)
     _log(f"  rel_l2={r[0]:.3e} max_abs={r[1]:.3e}")
+    # single-token decode follows the oracle's arithmetic order: equal values
+    assert np.array_equal(_np(y), y_ref), "single-token decode differs from the fp32 oracle"
 
 
 def test_workload2_decode_e896_router(dev, orc):
@@ -222,8 +224,32 @@ def test_workload2_decode_e896_router(dev, orc):
     y_ref = oracle_forward_sampled(orc, w.seed, 0, w.H, w.I, x, i_ref, g_ref, range(w.T))
     r = assert_y_close(_np(y), y_ref, w.name)
     _log(f"  rel_l2={r[0]:.3e} max_abs={r[1]:.3e}")
+    assert np.array_equal(_np(y), y_ref), "single-token decode differs from the fp32 oracle"
     del pool
     torch.cuda.empty_cache()
+
+
+def test_decode_single_token_equals_oracle_many(dev, orc):
+    """Single-token decode over 24 different tokens and routings of a 64-expert pool:
+    every output equals the fp32 oracle's (same arithmetic order)."""
+    torch, k3x = dev
+    w = S.WORKLOADS[1]
+    _log("case: single-token decode, 24 tokens, E=64, full shapes")
+    pool = _pool(torch, k3x, S.device_pool(w.seed, 0, w.E, w.H, w.I), w.E, w.H, w.I)
+    x = S.normal_bf16(31337, S.P_X, 0, (24, w.H))
+    idx, gates = S.uniform_routing(31337, 24, w.E, w.topk)
+    cache = {}
+    ws = None
+    worst = 0.0
+    for t in range(24):
+        y, ws = k3x.moe_forward(pool, _t(torch, x[t:t + 1]), _t(torch, idx[t:t + 1]),
+                                _t(torch, gates[t:t + 1]), ws=ws)
+        torch.cuda.synchronize()
+        y_ref = oracle_forward_sampled(orc, w.seed, 0, w.H, w.I, x[t:t + 1], idx[t:t + 1],
+                                       gates[t:t + 1], [0], cache=cache)
+        worst = max(worst, y_errors(_np(y), y_ref)[0])
+        assert np.array_equal(_np(y), y_ref), f"token {t}"
+    _log(f"  worst rel_l2 over 24 tokens: {worst:.3e}")
 
 
 def test_workload3_decode_t32_zipf(dev, orc):
@@ -312,6 +338,7 @@ def _chain(torch, k3x, orc, L, E, log_every=True):
         assert np.array_equal(_np(gates).view(np.uint32), g_ref.view(np.uint32)), layer
         y_ref = oracle_forward_sampled(orc, w.seed, layer, H, I, xn_ref, i_ref, g_ref, [0])
         rel, mx = assert_y_close(_np(y), y_ref, f"layer {layer}")
+        assert np.array_equal(_np(y), y_ref), f"layer {layer}: differs from the fp32 oracle"
         worst = max(worst, rel)
         if log_every:
             _log(f"  layer {layer}: rel_l2={rel:.3e} max_abs={mx:.3e}")
