@@ -46,9 +46,9 @@ def per_kernel_work(name, H, I, E, T, topk, U):
     """Algorithmic (bytes, flops) of one launch: U distinct experts, T tokens, T*topk slots."""
     w13, w2 = expert_tensor_bytes(H, I)
     slots = T * topk
-    if name == "w13_decode" or name == "w13_prefill":
+    if name in ("w13_decode", "w13_grouped", "w13_prefill"):
         return U * w13 + T * H * 2 + slots * I * 2, slots * 4.0 * I * H
-    if name == "w2_decode" or name == "w2_prefill":
+    if name in ("w2_decode", "w2_grouped", "w2_prefill"):
         return U * w2 + slots * I * 2 + slots * H * 4, slots * 2.0 * H * I
     if name == "route_scores":
         return E * H * 2 + T * H * 2 + T * E * 4, 2.0 * T * E * H

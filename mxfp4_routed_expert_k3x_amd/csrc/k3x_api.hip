@@ -230,18 +230,14 @@ thread_local k3x_profiler* g_prof = nullptr;
 
 namespace k3x {
 
-LaunchTimer::LaunchTimer(const char* name, hipStream_t s) {
+bool profiler_events(const char* name, hipEvent_t* start, hipEvent_t* stop) {
   k3x_profiler* p = g_prof;
-  if (!p || p->n >= p->capacity) return;
+  if (!p || p->n >= p->capacity) return false;
   const int i = p->n++;
   p->name[i] = name;
-  if (hipEventRecord(p->start[i], s) != hipSuccess) return;
-  stop_ = p->stop[i];
-  s_ = s;
-}
-
-LaunchTimer::~LaunchTimer() {
-  if (stop_) (void)hipEventRecord(stop_, s_);
+  *start = p->start[i];
+  *stop = p->stop[i];
+  return true;
 }
 
 }  // namespace k3x

@@ -22,8 +22,8 @@
 // Decode is bound by HBM: each lane streams 32 contiguous bytes (two whole MX groups) of a
 // weight row per load pair, so a wave reads whole rows with fully coalesced 16-byte loads;
 // dequantization is in registers (gfx950 FP4 -> f32 conversion, two weights per
-// instruction) and nothing dequantized is ever written.  Sixteen rows of one slot form a work
-// item; loads run three rows ahead of the arithmetic, and lane r keeps row r's sum.
+// instruction) and nothing dequantized is ever written.  Each wave streams a contiguous run
+// of rows (over all slots), with loads running three rows ahead of the arithmetic.
 #include "k3x_internal.h"
 
 // Products and sums below are rounded one at a time unless written as an explicit fma.
@@ -33,8 +33,6 @@ namespace k3x {
 namespace {
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
-
-constexpr int kRows = 16;  // rows per work item
 
 struct DecodeArgs {
   const uint8_t* wa;  // W1 (w13) or W2 (w2) packed, expert 0
@@ -108,21 +106,6 @@ struct RowBits {
   uint32_t sc;  // two scale bytes (groups 2L, 2L+1) in the low 16 bits
 };
 
-__device__ __forceinline__ RowBits load_row(const uint8_t* wrow, const uint8_t* srow, int lane,
-                                            bool ok) {
-  RowBits r;
-  if (ok) {
-    const uint4* p = reinterpret_cast<const uint4*>(wrow + 32 * lane);
-    r.q0 = p[0];
-    r.q1 = p[1];
-    r.sc = *reinterpret_cast<const uint16_t*>(srow + 2 * lane);
-  } else {
-    r.q0 = r.q1 = make_uint4(0, 0, 0, 0);
-    r.sc = 0;
-  }
-  return r;
-}
-
 // Leaf of the tree for this lane: (group 2L sum * scale) + (group 2L+1 sum * scale).
 __device__ __forceinline__ float row_leaf(const RowBits& r, const float (&x0)[32],
                                           const float (&x1)[32]) {
@@ -131,143 +114,124 @@ __device__ __forceinline__ float row_leaf(const RowBits& r, const float (&x0)[32
   return p0 + p1;
 }
 
-// Sum of one row's lane leaves in tree order: partners at distance 1, 2, ..., 32.  Every
-// lane ends with the same total.
-__device__ __forceinline__ float tree_sum(float v) {
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) v = v + __shfl_xor(v, d, kWave);
-  return v;
-}
-
-__device__ __forceinline__ void keep_row(int lane, int r, float gv, float uv, float& g, float& u) {
-  if (lane == r) {
-    g = gv;
-    u = uv;
-  }
-}
-
-// Work items of one wave: the die's contiguous share of the items, cut into contiguous runs
-// per wave, so a wave keeps its slot (and its activation registers) for long stretches.
-__device__ __forceinline__ void wave_items(int items, int& i0, int& i1) {
+// Rows of one wave.  The rows of all slots form one sequence g = slot * rows + r; each die
+// takes a contiguous, balanced share of it, and each wave of the die a contiguous, balanced
+// run of that share, so every wave streams nearly the same number of rows and the expert
+// (and, for W2, the slot's activations) changes at most a few times along a run.
+__device__ __forceinline__ void wave_rows(int total, int& g0, int& g1) {
   int die, rank, per_die;
   xcd_rank(die, rank, per_die);
-  const int wave = threadIdx.x / kWave;
-  const int waves_per_die = per_die * (blockDim.x / kWave);
-  const int wave_rank = rank * (blockDim.x / kWave) + wave;
-  const int chunk = (items + kNumXcd - 1) / kNumXcd;
-  const int lo = die * chunk;
-  const int hi = min(items, lo + chunk);
-  const int n = max(0, hi - lo);
-  const int per = (n + waves_per_die - 1) / waves_per_die;
-  i0 = min(hi, lo + wave_rank * per);
-  i1 = min(hi, i0 + per);
+  const int wpb = blockDim.x / kWave;
+  const int W = per_die * wpb;
+  const int w = rank * wpb + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lo = (int)((int64_t)total * die / kNumXcd);
+  const int hi = (int)((int64_t)total * (die + 1) / kNumXcd);
+  const int n = hi - lo;
+  g0 = lo + (int)((int64_t)n * w / W);
+  g1 = lo + (int)((int64_t)n * (w + 1) / W);
 }
 
-// g = W1 x and u = W3 x for 16 rows of one slot, then h = bf16(silu(g) * u).
-__global__ __launch_bounds__(256) void w13_decode_exact(DecodeArgs a) {
-  const int lane = threadIdx.x % kWave;
-  if (blockIdx.x == 0 && threadIdx.x == 0) {
-    int bad = 0;
-    for (int j = 0; j < a.topk; ++j) bad += expert_ok(a.idx[j], a.E) ? 0 : 1;
-    *reinterpret_cast<int64_t*>(a.ws) = bad;
-  }
-  const int ngroups = a.K / kGroup;
-  const bool lane_ok = 2 * lane < ngroups;
-  float x0[32], x1[32];
-  load_act(a.act, 64 * lane, lane_ok, x0, x1);
+// Loads row r of one matrix of expert e: wave-uniform row addresses plus a per-lane
+// offset.  Lanes past the last group re-read the row's last 32 bytes; their activations are
+// zero, so their leaves are zero.  The load is unconditional (callers clamp r to a real
+// row), so the loop body has no branches and loads stay in flight across rows.
+__device__ __forceinline__ void load_row(RowBits& b, const uint8_t* wexp, const uint8_t* sexp,
+                                         int r, uint32_t wrow, uint32_t srow, uint32_t loff,
+                                         uint32_t soff) {
+  const uint4* p = reinterpret_cast<const uint4*>(wexp + (size_t)r * wrow + loff);
+  b.q0 = p[0];
+  b.q1 = p[1];
+  b.sc = *reinterpret_cast<const uint16_t*>(sexp + (size_t)r * srow + soff);
+}
 
-  const int per_slot = a.rows / kRows;
-  int i0, i1;
-  wave_items(a.topk * per_slot, i0, i1);
-  const size_t wrow = (size_t)a.K / 2, srow = (size_t)ngroups;
-  for (int it = i0; it < i1; ++it) {
-    const int slot = it / per_slot;
-    const int r0 = (it % per_slot) * kRows;
-    const int e = a.idx[slot];
-    if (!expert_ok(e, a.E)) continue;
-    const uint8_t* w1 = a.wa + (size_t)e * a.st_wa + (size_t)r0 * wrow;
-    const uint8_t* s1 = a.sa + (size_t)e * a.st_sa + (size_t)r0 * srow;
-    const uint8_t* w3 = a.wb + (size_t)e * a.st_wb + (size_t)r0 * wrow;
-    const uint8_t* s3 = a.sb + (size_t)e * a.st_sb + (size_t)r0 * srow;
-
-    // rows r0..r0+15, loads issued three rows ahead; lane r keeps row r's sums
-    float g = 0.0f, u = 0.0f;
-    RowBits a0, a1, a2, a3, c0, c1, c2, c3;
-    a0 = load_row(w1, s1, lane, lane_ok);
-    c0 = load_row(w3, s3, lane, lane_ok);
-    a1 = load_row(w1 + wrow, s1 + srow, lane, lane_ok);
-    c1 = load_row(w3 + wrow, s3 + srow, lane, lane_ok);
-    a2 = load_row(w1 + 2 * wrow, s1 + 2 * srow, lane, lane_ok);
-    c2 = load_row(w3 + 2 * wrow, s3 + 2 * srow, lane, lane_ok);
-#pragma unroll 1
-    for (int r = 0; r < kRows; r += 4) {
-      a3 = load_row(w1 + (r + 3) * wrow, s1 + (r + 3) * srow, lane, lane_ok);
-      c3 = load_row(w3 + (r + 3) * wrow, s3 + (r + 3) * srow, lane, lane_ok);
-      keep_row(lane, r, tree_sum(row_leaf(a0, x0, x1)), tree_sum(row_leaf(c0, x0, x1)), g, u);
-      if (r + 4 < kRows) {
-        a0 = load_row(w1 + (r + 4) * wrow, s1 + (r + 4) * srow, lane, lane_ok);
-        c0 = load_row(w3 + (r + 4) * wrow, s3 + (r + 4) * srow, lane, lane_ok);
-      }
-      keep_row(lane, r + 1, tree_sum(row_leaf(a1, x0, x1)), tree_sum(row_leaf(c1, x0, x1)), g, u);
-      if (r + 5 < kRows) {
-        a1 = load_row(w1 + (r + 5) * wrow, s1 + (r + 5) * srow, lane, lane_ok);
-        c1 = load_row(w3 + (r + 5) * wrow, s3 + (r + 5) * srow, lane, lane_ok);
-      }
-      keep_row(lane, r + 2, tree_sum(row_leaf(a2, x0, x1)), tree_sum(row_leaf(c2, x0, x1)), g, u);
-      if (r + 6 < kRows) {
-        a2 = load_row(w1 + (r + 6) * wrow, s1 + (r + 6) * srow, lane, lane_ok);
-        c2 = load_row(w3 + (r + 6) * wrow, s3 + (r + 6) * srow, lane, lane_ok);
-      }
-      keep_row(lane, r + 3, tree_sum(row_leaf(a3, x0, x1)), tree_sum(row_leaf(c3, x0, x1)), g, u);
-    }
-    if (lane < kRows) {
-      const float ex = (float)exp(-(double)g);
-      const float hv = (g / (1.0f + ex)) * u;
-      uint16_t* h = static_cast<uint16_t*>(a.out);
-      h[(size_t)slot * a.rows + r0 + lane] = (uint16_t)f32_to_bf16_bits(hv);
-    }
+// Reduce-scatter of four row leaves per vector across the wave, in tree order: distances 1
+// and 2 halve the rows, distances 4 .. 32 finish the sums.  On return v[m][0] of lane L is
+// the full sum of row (L & 3) of vector m.
+template <int NV>
+__device__ __forceinline__ void reduce4(float (&v)[NV][4], int lane) {
+  const bool b0 = lane & 1, b1 = (lane >> 1) & 1;
+#pragma unroll
+  for (int m = 0; m < NV; ++m) {
+    const float k0 = b0 ? v[m][1] : v[m][0], s0 = b0 ? v[m][0] : v[m][1];
+    const float k1 = b0 ? v[m][3] : v[m][2], s1 = b0 ? v[m][2] : v[m][3];
+    const float r0 = k0 + __shfl_xor(s0, 1, kWave);  // rows 0/1 -> row b0
+    const float r1 = k1 + __shfl_xor(s1, 1, kWave);  // rows 2/3 -> row 2 + b0
+    const float k = b1 ? r1 : r0, sd = b1 ? r0 : r1;
+    float t = k + __shfl_xor(sd, 2, kWave);  // row 2 b1 + b0
+#pragma unroll
+    for (int d = 4; d < kWave; d <<= 1) t = t + __shfl_xor(t, d, kWave);
+    v[m][0] = t;
   }
 }
 
-// d = W2 h for 16 rows of one slot.
-__global__ __launch_bounds__(256) void w2_decode_exact(DecodeArgs a) {
+// W1/W3 mode (kW13): g = W1 x, u = W3 x, h = bf16(silu(g) * u) for every row of the run.
+// W2 mode: d = W2 h with the slot's activations h.  A run is cut at slot boundaries into
+// segments of one expert; within a segment rows are loaded three ahead of the arithmetic
+// and finished four at a time.  A dropped slot's segment is skipped.
+template <bool kW13>
+__global__ __launch_bounds__(256) void decode_rows(DecodeArgs a) {
   const int lane = threadIdx.x % kWave;
+  const int my_idx = lane < a.topk ? a.idx[lane] : -1;
+  if (kW13 && blockIdx.x == 0 && threadIdx.x < kWave) {
+    const unsigned long long bad = __ballot(lane < a.topk && !expert_ok(my_idx, a.E));
+    if (lane == 0) *reinterpret_cast<int64_t*>(a.ws) = __popcll(bad);
+  }
   const int ngroups = a.K / kGroup;
   const bool lane_ok = 2 * lane < ngroups;
-  const int per_slot = a.rows / kRows;
-  int i0, i1;
-  wave_items(a.topk * per_slot, i0, i1);
-  const size_t wrow = (size_t)a.K / 2, srow = (size_t)ngroups;
+  const uint32_t wrow = (uint32_t)a.K / 2, srow = (uint32_t)ngroups;
+  const uint32_t loff = lane_ok ? 32u * lane : wrow - 32u;
+  const uint32_t soff = lane_ok ? 2u * lane : srow - 2u;
+  int g0, g1;
+  wave_rows(a.topk * a.rows, g0, g1);
+
   float x0[32], x1[32];
-  int have = -1;
-  for (int it = i0; it < i1; ++it) {
-    const int slot = it / per_slot;
-    const int r0 = (it % per_slot) * kRows;
-    const int e = a.idx[slot];
+  if (kW13) load_act(a.act, 64 * lane, lane_ok, x0, x1);
+
+  for (int gs = g0; gs < g1;) {
+    const int slot = gs / a.rows;
+    const int r0 = gs - slot * a.rows;
+    const int n = min(g1 - gs, a.rows - r0);  // rows of this segment
+    const int e = __builtin_amdgcn_readlane(my_idx, slot);
+    gs += n;
     if (!expert_ok(e, a.E)) continue;
-    if (slot != have) {
-      load_act(a.act + (size_t)slot * a.K, 64 * lane, lane_ok, x0, x1);
-      have = slot;
-    }
-    const uint8_t* w2 = a.wa + (size_t)e * a.st_wa + (size_t)r0 * wrow;
-    const uint8_t* s2 = a.sa + (size_t)e * a.st_sa + (size_t)r0 * srow;
-    float dsum = 0.0f, dummy = 0.0f;
-    RowBits b0, b1, b2, b3;
-    b0 = load_row(w2, s2, lane, lane_ok);
-    b1 = load_row(w2 + wrow, s2 + srow, lane, lane_ok);
-    b2 = load_row(w2 + 2 * wrow, s2 + 2 * srow, lane, lane_ok);
+    if (!kW13) load_act(a.act + (size_t)slot * a.K, 64 * lane, lane_ok, x0, x1);
+    const uint8_t* wa = a.wa + (size_t)e * a.st_wa;
+    const uint8_t* sa = a.sa + (size_t)e * a.st_sa;
+    const uint8_t* wb = kW13 ? a.wb + (size_t)e * a.st_wb : nullptr;
+    const uint8_t* sb = kW13 ? a.sb + (size_t)e * a.st_sb : nullptr;
+    const int rlast = r0 + n - 1;
+
+    RowBits A[4] = {}, C[4] = {};
+    auto load = [&](int i, int r) {  // row r into buffer i (rows past the segment re-read rlast)
+      const int rr = r <= rlast ? r : rlast;
+      load_row(A[i], wa, sa, rr, wrow, srow, loff, soff);
+      if (kW13) load_row(C[i], wb, sb, rr, wrow, srow, loff, soff);
+    };
+    load(0, r0);
+    load(1, r0 + 1);
+    load(2, r0 + 2);
 #pragma unroll 1
-    for (int r = 0; r < kRows; r += 4) {
-      b3 = load_row(w2 + (r + 3) * wrow, s2 + (r + 3) * srow, lane, lane_ok);
-      keep_row(lane, r, tree_sum(row_leaf(b0, x0, x1)), 0.0f, dsum, dummy);
-      if (r + 4 < kRows) b0 = load_row(w2 + (r + 4) * wrow, s2 + (r + 4) * srow, lane, lane_ok);
-      keep_row(lane, r + 1, tree_sum(row_leaf(b1, x0, x1)), 0.0f, dsum, dummy);
-      if (r + 5 < kRows) b1 = load_row(w2 + (r + 5) * wrow, s2 + (r + 5) * srow, lane, lane_ok);
-      keep_row(lane, r + 2, tree_sum(row_leaf(b2, x0, x1)), 0.0f, dsum, dummy);
-      if (r + 6 < kRows) b2 = load_row(w2 + (r + 6) * wrow, s2 + (r + 6) * srow, lane, lane_ok);
-      keep_row(lane, r + 3, tree_sum(row_leaf(b3, x0, x1)), 0.0f, dsum, dummy);
+    for (int r = r0; r <= rlast; r += 4) {
+      float v[kW13 ? 2 : 1][4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        load((i + 3) % 4, r + i + 3);
+        v[0][i] = row_leaf(A[i], x0, x1);
+        if (kW13) v[kW13 ? 1 : 0][i] = row_leaf(C[i], x0, x1);
+      }
+      reduce4(v, lane);
+      if (lane < 4 && r + lane <= rlast) {
+        const size_t out = (size_t)slot * a.rows + r + lane;
+        if (kW13) {
+          const float gv = v[0][0], uv = v[kW13 ? 1 : 0][0];
+          const float ex = (float)exp(-(double)gv);
+          const float hv = (gv / (1.0f + ex)) * uv;
+          static_cast<uint16_t*>(a.out)[out] = (uint16_t)f32_to_bf16_bits(hv);
+        } else {
+          static_cast<float*>(a.out)[out] = v[0][0];
+        }
+      }
     }
-    if (lane < kRows) static_cast<float*>(a.out)[(size_t)slot * a.rows + r0 + lane] = dsum;
   }
 }
 
@@ -293,7 +257,7 @@ __global__ __launch_bounds__(256) void combine_exact(const float* __restrict__ d
 
 int decode_grid(const void* fn) {
   static int cached[2] = {0, 0};
-  const int which = fn == reinterpret_cast<const void*>(&w13_decode_exact) ? 0 : 1;
+  const int which = fn == reinterpret_cast<const void*>(&decode_rows<true>) ? 0 : 1;
   if (!cached[which]) {
     int per_cu = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 256, 0) != hipSuccess || per_cu < 1)
@@ -306,8 +270,7 @@ int decode_grid(const void* fn) {
 }  // namespace
 
 bool decode_exact_supported(const k3x_pool& p, int32_t T, int32_t topk) {
-  return T == 1 && topk <= 64 && p.H / kGroup <= 128 && p.I / kGroup <= 128 &&
-         p.H % kRows == 0 && p.I % kRows == 0;
+  return T == 1 && topk <= 64 && p.H / kGroup <= 128 && p.I / kGroup <= 128;
 }
 
 size_t decode_exact_ws(const k3x_pool& p, int32_t topk, size_t* off_h, size_t* off_d) {
@@ -342,13 +305,9 @@ hipError_t launch_decode_exact(const k3x_pool& p, const uint16_t* x, const int32
   a.E = p.E;
   a.ws = ws;
   a.out = ws + off_h;
-  {
-    LaunchTimer lt("w13_decode", s);
-    hipLaunchKernelGGL(w13_decode_exact,
-                       dim3(decode_grid(reinterpret_cast<const void*>(&w13_decode_exact))),
-                       dim3(256), 0, s, a);
-  }
-  hipError_t err = hipGetLastError();
+  hipError_t err = launch("w13_decode", decode_rows<true>,
+                          dim3(decode_grid(reinterpret_cast<const void*>(&decode_rows<true>))),
+                          dim3(256), 0, s, a);
   if (err != hipSuccess) return err;
   DecodeArgs b = a;
   b.wa = p.base[4];
@@ -361,19 +320,12 @@ hipError_t launch_decode_exact(const k3x_pool& p, const uint16_t* x, const int32
   b.rows = p.H;
   b.act = reinterpret_cast<const uint16_t*>(ws + off_h);
   b.out = ws + off_d;
-  {
-    LaunchTimer lt("w2_decode", s);
-    hipLaunchKernelGGL(w2_decode_exact,
-                       dim3(decode_grid(reinterpret_cast<const void*>(&w2_decode_exact))),
-                       dim3(256), 0, s, b);
-  }
-  if ((err = hipGetLastError()) != hipSuccess) return err;
-  {
-    LaunchTimer lt("moe_combine", s);
-    hipLaunchKernelGGL(combine_exact, dim3((p.H + 255) / 256), dim3(256), 0, s,
-                       reinterpret_cast<const float*>(ws + off_d), idx, gates, topk, p.H, p.E, y);
-  }
-  return hipGetLastError();
+  err = launch("w2_decode", decode_rows<false>,
+               dim3(decode_grid(reinterpret_cast<const void*>(&decode_rows<false>))), dim3(256), 0,
+               s, b);
+  if (err != hipSuccess) return err;
+  return launch("moe_combine", combine_exact, dim3((p.H + 255) / 256), dim3(256), 0, s,
+                reinterpret_cast<const float*>(ws + off_d), idx, gates, topk, p.H, p.E, y);
 }
 
 }  // namespace k3x

@@ -4,6 +4,7 @@
 // are this library's own.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -126,16 +127,21 @@ hipError_t launch_residual(uint16_t* x, const float* y, int32_t T, int32_t H, hi
 
 int device_cu_count();
 
-// Brackets one kernel launch with the attached profiler's events (no-op when none is
-// attached to this thread).  Construct right before the launch, destroy right after it.
-class LaunchTimer {
- public:
-  LaunchTimer(const char* name, hipStream_t s);
-  ~LaunchTimer();
+// When a profiler is attached to the calling thread and has room, reserves the next record
+// for kernel `name` and returns its start/stop events.
+bool profiler_events(const char* name, hipEvent_t* start, hipEvent_t* stop);
 
- private:
-  hipEvent_t stop_ = nullptr;
-  hipStream_t s_ = nullptr;
-};
+// Enqueues one kernel.  With a profiler attached the launch carries the record's events,
+// which the runtime stamps at the start and end of that dispatch itself.
+template <typename F, typename... Args>
+inline hipError_t launch(const char* name, F kernel, dim3 grid, dim3 block, uint32_t shm,
+                         hipStream_t s, Args... args) {
+  hipEvent_t start, stop;
+  if (profiler_events(name, &start, &stop))
+    hipExtLaunchKernelGGL(kernel, grid, block, shm, s, start, stop, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, shm, s, args...);
+  return hipGetLastError();
+}
 
 }  // namespace k3x

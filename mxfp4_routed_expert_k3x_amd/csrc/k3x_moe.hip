@@ -412,11 +412,8 @@ hipError_t launch_moe(const k3x_pool& p, const uint16_t* x, int32_t T, const int
     sa.off_tiles = L.tiles;
     sa.off_perm = L.perm;
     const size_t sort_lds = sizeof(int32_t) * (size_t)p.E;
-    {
-      LaunchTimer lt("moe_sort", s);
-      hipLaunchKernelGGL(moe_sort, dim3(1), dim3(kSortThreads), sort_lds, s, sa);
-    }
-    if ((err = hipGetLastError()) != hipSuccess || T == 0) return err;
+    err = launch("moe_sort", moe_sort, dim3(1), dim3(kSortThreads), (uint32_t)sort_lds, s, sa);
+    if (err != hipSuccess || T == 0) return err;
   }
 
   // persistent grids: two 4-wave workgroups per CU (the occupancy the registers allow)
@@ -451,12 +448,9 @@ hipError_t launch_moe(const k3x_pool& p, const uint16_t* x, int32_t T, const int
     if (g > max_grid) g = max_grid;
     return (int)(g < kNumXcd ? kNumXcd : g);
   };
-  {
-    LaunchTimer lt("w13_decode", s);
-    hipLaunchKernelGGL(gemm_decode<true>, dim3(grid_for(max_tiles * (p.I / 32))), dim3(256), 0,
-                       s, a13);
-  }
-  if ((err = hipGetLastError()) != hipSuccess) return err;
+  err = launch("w13_grouped", gemm_decode<true>, dim3(grid_for(max_tiles * (p.I / 32))),
+               dim3(256), 0, s, a13);
+  if (err != hipSuccess) return err;
 
   GemmArgs a2 = a13;
   a2.wa = p.base[4];
@@ -470,18 +464,11 @@ hipError_t launch_moe(const k3x_pool& p, const uint16_t* x, int32_t T, const int
   a2.act = reinterpret_cast<const uint16_t*>(ws + L.h);
   a2.act_by_token = 0;
   a2.out = ws + L.d;
-  {
-    LaunchTimer lt("w2_decode", s);
-    hipLaunchKernelGGL(gemm_decode<false>, dim3(grid_for(max_tiles * (p.H / 64))), dim3(256), 0,
-                       s, a2);
-  }
-  if ((err = hipGetLastError()) != hipSuccess) return err;
-  {
-    LaunchTimer lt("moe_combine", s);
-    hipLaunchKernelGGL(moe_combine, dim3((p.H / 4 + 255) / 256, T), dim3(256), 0, s,
-                       reinterpret_cast<const float*>(ws + L.d), idx, gates, topk, p.H, p.E, y);
-  }
-  return hipGetLastError();
+  err = launch("w2_grouped", gemm_decode<false>, dim3(grid_for(max_tiles * (p.H / 64))),
+               dim3(256), 0, s, a2);
+  if (err != hipSuccess) return err;
+  return launch("moe_combine", moe_combine, dim3((p.H / 4 + 255) / 256, T), dim3(256), 0, s,
+                reinterpret_cast<const float*>(ws + L.d), idx, gates, topk, p.H, p.E, y);
 }
 
 }  // namespace k3x

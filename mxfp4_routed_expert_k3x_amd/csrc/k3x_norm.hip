@@ -73,18 +73,15 @@ __global__ __launch_bounds__(256) void residual_add_bf16(uint16_t* __restrict__ 
 hipError_t launch_rmsnorm(const uint16_t* x, int32_t T, int32_t H, float eps, uint16_t* out,
                           hipStream_t s) {
   if (T == 0) return hipSuccess;
-  LaunchTimer lt("rmsnorm_bf16", s);
-  hipLaunchKernelGGL(rmsnorm_bf16, dim3((T + 3) / 4), dim3(256), 0, s, x, T, H, eps, out);
-  return hipGetLastError();
+  return launch("rmsnorm_bf16", rmsnorm_bf16, dim3((T + 3) / 4), dim3(256), 0, s, x, T, H, eps,
+                out);
 }
 
 hipError_t launch_residual(uint16_t* x, const float* y, int32_t T, int32_t H, hipStream_t s) {
   const int64_t n8 = (int64_t)T * H / 8;
   if (n8 == 0) return hipSuccess;
-  LaunchTimer lt("residual_add_bf16", s);
-  hipLaunchKernelGGL(residual_add_bf16, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, x,
-                     y, n8);
-  return hipGetLastError();
+  return launch("residual_add_bf16", residual_add_bf16, dim3((unsigned)((n8 + 255) / 256)),
+                dim3(256), 0, s, x, y, n8);
 }
 
 }  // namespace k3x

@@ -10,10 +10,10 @@
 // down-shuffles.  The float logit goes through a double sigmoid rounded once to float.
 // This fixes the summation order completely, so the scores are reproducible bit for bit.
 //
-// Kernel 2 (route_select): one wave per token.  The selection scores c = s + bias live in
-// LDS; each of the topk rounds takes every lane's best untaken expert and reduces them with
-// a butterfly under the total order (larger c first, then lower index), so ties go to the
-// lower expert and -0 equals +0 as in an IEEE compare.
+// Kernel 2 (route_select): one workgroup per token.  A radix select finds the selection
+// score of the topk-th expert under the total order (larger c first, then lower index), so
+// ties go to the lower expert and -0 equals +0 as in an IEEE compare; the chosen experts
+// are then put in selection order by their rank.
 #include "k3x_internal.h"
 
 namespace k3x {
@@ -83,62 +83,165 @@ __device__ __forceinline__ bool beats(float cb, int ib, float ca, int ia) {
   return cb > ca || (cb == ca && ib < ia);
 }
 
-__global__ __launch_bounds__(64) void route_select(const float* __restrict__ scores,
-                                                   const float* __restrict__ bias, int32_t E,
-                                                   int32_t topk, int32_t renorm, float rscale,
-                                                   int32_t* __restrict__ idx_out,
-                                                   float* __restrict__ gates_out) {
-  extern __shared__ float lds[];
-  float* c = lds;       // [E] selection scores
-  float* sel = lds + E; // [topk] chosen unbiased scores, selection order
-  const int t = blockIdx.x;
-  const int lane = threadIdx.x;
-  const float* s_t = scores + (size_t)t * E;
-  for (int e = lane; e < E; e += kWave) c[e] = s_t[e] + (bias ? bias[e] : 0.0f);
-  __syncthreads();
+// Order-preserving 32-bit key of a selection score: a larger float gives a larger key, and
+// -0 is first made +0 so that the two compare equal, as in an IEEE compare.
+__device__ __forceinline__ uint32_t score_key(float c) {
+  const uint32_t b = c == 0.0f ? 0u : __float_as_uint(c);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
 
-  uint64_t taken = 0;  // bit m: expert lane + 64 m already chosen
-  const int per_lane = (E + kWave - 1) / kWave;
-  for (int j = 0; j < topk; ++j) {
-    float bc = 0.0f;
-    int bi = -1;
-    for (int m = 0; m < per_lane; ++m) {
-      const int e = lane + kWave * m;
-      if (e < E && !((taken >> m) & 1ull)) {
-        const float v = c[e];
-        if (beats(v, e, bc, bi)) {
-          bc = v;
-          bi = e;
-        }
-      }
-    }
+constexpr int kSelThreads = 256;
+constexpr int kMaxEqual = 256;  // experts sharing the threshold key handled at once
+
+// One workgroup of 256 threads per token; thread i owns experts i + 256 m (m < M).
+//  1. The key of the topk-th largest selection score is found by a radix select: four
+//     passes over 8-bit digits, each building a 256-bin LDS histogram of the keys that
+//     match the digits fixed so far and walking it from the top.
+//  2. The chosen set is every expert whose key is larger, plus, among the experts whose key
+//     equals it, the ones of lowest index until topk are taken -- exactly the experts the
+//     repeated argmax (larger score first, lower index on ties) would pick.
+//  3. Each chosen expert's slot is its rank in that total order; the gates are the unbiased
+//     scores in slot order, renormalised by their float sum (added in slot order).
+template <int M>
+__global__ __launch_bounds__(kSelThreads) void route_select(const float* __restrict__ scores,
+                                                            const float* __restrict__ bias,
+                                                            int32_t E, int32_t topk,
+                                                            int32_t renorm, float rscale,
+                                                            int32_t* __restrict__ idx_out,
+                                                            float* __restrict__ gates_out) {
+  extern __shared__ float dyn[];  // [topk] c, [topk] s, [topk] e (as int), [topk] ranked s
+  float* sel_c = dyn;
+  float* sel_s = dyn + topk;
+  int* sel_e = reinterpret_cast<int*>(dyn + 2 * topk);
+  float* ranked = dyn + 3 * topk;
+  __shared__ uint32_t hist[256];
+  __shared__ int eq_e[kMaxEqual];
+  __shared__ uint32_t s_prefix, s_rem;
+  __shared__ int s_nsel, s_neq;
+  __shared__ float s_sum;
+  const int tid = threadIdx.x;
+  const int t = blockIdx.x;
+  const float* s_t = scores + (size_t)t * E;
+
+  float sc[M], c[M];
+  uint32_t key[M];
 #pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) {
-      const float oc = __shfl_xor(bc, s, kWave);
-      const int oi = __shfl_xor(bi, s, kWave);
-      if (beats(oc, oi, bc, bi)) {
-        bc = oc;
-        bi = oi;
+  for (int m = 0; m < M; ++m) {
+    const int e = tid + kSelThreads * m;
+    sc[m] = e < E ? s_t[e] : 0.0f;
+    c[m] = e < E ? sc[m] + (bias ? bias[e] : 0.0f) : 0.0f;
+    key[m] = score_key(c[m]);
+  }
+
+  uint32_t prefix = 0, mask = 0, rem = (uint32_t)topk;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    hist[tid] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+      if (tid + kSelThreads * m < E && (key[m] & mask) == prefix)
+        atomicAdd(&hist[(key[m] >> shift) & 255u], 1u);
+    __syncthreads();
+    if (tid < kWave) {
+      // lane l sums bins 255-4l .. 252-4l (descending); an inclusive scan over lanes gives
+      // the number of keys in all bins from 255 down to the lane's lowest bin
+      uint32_t hb[4], local = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        hb[i] = hist[255 - 4 * tid - i];
+        local += hb[i];
+      }
+      uint32_t incl = local;
+#pragma unroll
+      for (int d = 1; d < kWave; d <<= 1) {
+        const uint32_t o = __shfl_up(incl, d, kWave);
+        if (tid >= d) incl += o;
+      }
+      const uint32_t excl = incl - local;
+      if (excl < rem && rem <= incl) {  // exactly one lane
+        uint32_t above = excl;
+        int bin = 255 - 4 * tid - 3;
+        uint32_t left = rem - above;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (above < rem && rem <= above + hb[i]) {
+            bin = 255 - 4 * tid - i;
+            left = rem - above;
+            break;
+          }
+          above += hb[i];
+        }
+        s_prefix = prefix | ((uint32_t)bin << shift);
+        s_rem = left;
       }
     }
-    // every lane now holds the same winner
-    if ((bi % kWave) == lane) taken |= 1ull << (bi / kWave);
-    if (lane == 0) {
-      idx_out[(size_t)t * topk + j] = bi;
-      sel[j] = s_t[bi];
+    __syncthreads();
+    prefix = s_prefix;
+    rem = s_rem;
+    mask |= 255u << shift;
+    __syncthreads();
+  }
+
+  // prefix is now the key of the topk-th expert; rem of the experts with that key are
+  // taken, those of lowest index
+  if (tid == 0) {
+    s_nsel = 0;
+    s_neq = 0;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const int e = tid + kSelThreads * m;
+    if (e < E && key[m] == prefix) {
+      const int pos = atomicAdd(&s_neq, 1);
+      if (pos < kMaxEqual) eq_e[pos] = e;
     }
   }
   __syncthreads();
-  if (lane == 0) {
+  const int neq = s_neq < kMaxEqual ? s_neq : kMaxEqual;
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const int e = tid + kSelThreads * m;
+    if (e >= E) continue;
+    bool take = key[m] > prefix;
+    if (key[m] == prefix) {
+      uint32_t below = 0;
+      if (s_neq <= kMaxEqual) {
+        for (int i = 0; i < neq; ++i) below += eq_e[i] < e ? 1u : 0u;
+      } else {  // very many equal scores: count them from the inputs
+        for (int e2 = 0; e2 < e; ++e2)
+          below += score_key(s_t[e2] + (bias ? bias[e2] : 0.0f)) == prefix ? 1u : 0u;
+      }
+      take = below < rem;
+    }
+    if (take) {
+      const int pos = atomicAdd(&s_nsel, 1);
+      sel_c[pos] = c[m];
+      sel_s[pos] = sc[m];
+      sel_e[pos] = e;
+    }
+  }
+  __syncthreads();
+  // slot of each chosen expert = its rank under (larger c, then lower index)
+  for (int i = tid; i < topk; i += kSelThreads) {
+    const float ci = sel_c[i];
+    const int ei = sel_e[i];
+    int r = 0;
+    for (int j = 0; j < topk; ++j) r += beats(sel_c[j], sel_e[j], ci, ei) ? 1 : 0;
+    idx_out[(size_t)t * topk + r] = ei;
+    ranked[r] = sel_s[i];
+  }
+  __syncthreads();
+  if (tid == 0) {
     float sum = 0.0f;
     if (renorm)
-      for (int j = 0; j < topk; ++j) sum = sum + sel[j];
-    sel[topk] = sum;  // slot reserved past the chosen scores
+      for (int j = 0; j < topk; ++j) sum = sum + ranked[j];
+    s_sum = sum;
   }
   __syncthreads();
-  const float sum = sel[topk];
-  for (int j = lane; j < topk; j += kWave) {
-    float w = sel[j];
+  const float sum = s_sum;
+  for (int j = tid; j < topk; j += kSelThreads) {
+    float w = ranked[j];
     if (renorm && sum > 0.0f) w = w / sum;
     gates_out[(size_t)t * topk + j] = w * rscale;
   }
@@ -152,22 +255,18 @@ hipError_t launch_route(const k3x_router_desc& r, const uint16_t* x, int32_t T, 
   const int E = r.n_experts, H = r.hidden;
   dim3 g1((E + 3) / 4, (T + kRouteTokBlock - 1) / kRouteTokBlock);
   const uint16_t* W = static_cast<const uint16_t*>(r.weight);
-  {
-    LaunchTimer lt("route_scores", s);
-    if (H <= 64 * 8 * 8)
-      hipLaunchKernelGGL(route_scores<8>, g1, dim3(256), 0, s, x, W, T, H, E, scores);
-    else
-      hipLaunchKernelGGL(route_scores<32>, g1, dim3(256), 0, s, x, W, T, H, E, scores);
-  }
-  hipError_t err = hipGetLastError();
+  hipError_t err;
+  if (H <= 64 * 8 * 8)
+    err = launch("route_scores", route_scores<8>, g1, dim3(256), 0, s, x, W, T, H, E, scores);
+  else
+    err = launch("route_scores", route_scores<32>, g1, dim3(256), 0, s, x, W, T, H, E, scores);
   if (err != hipSuccess) return err;
-  const size_t lds = sizeof(float) * ((size_t)E + (size_t)r.topk + 1);
-  {
-    LaunchTimer lt("route_select", s);
-    hipLaunchKernelGGL(route_select, dim3(T), dim3(64), lds, s, scores, r.bias, E, r.topk,
-                       r.renorm, r.routed_scale, idx, gates);
-  }
-  return hipGetLastError();
+  const uint32_t lds = (uint32_t)(sizeof(float) * 4 * (size_t)r.topk);
+  if (E <= kSelThreads * 4)
+    return launch("route_select", route_select<4>, dim3(T), dim3(kSelThreads), lds, s, scores,
+                  r.bias, E, r.topk, r.renorm, r.routed_scale, idx, gates);
+  return launch("route_select", route_select<16>, dim3(T), dim3(kSelThreads), lds, s, scores,
+                r.bias, E, r.topk, r.renorm, r.routed_scale, idx, gates);
 }
 
 }  // namespace k3x

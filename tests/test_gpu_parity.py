@@ -188,6 +188,24 @@ def test_router_ties_full_k_and_options(dev, orc):
     assert np.array_equal(gates.view(np.uint32), g_ref.view(np.uint32))
 
 
+def test_router_many_equal_scores(dev, orc):
+    """Whole blocks of identical router rows and biases: selection falls back on the lower
+    index among equal scores, including more equal scores than one LDS list holds."""
+    torch, k3x = dev
+    _log("case: router with 300 identical experts, E=700")
+    E, H = 700, 128
+    W = S.normal_bf16(11, S.P_WR, 0, (E, H), std=0.05)
+    W[100:400] = W[100]
+    b = S.normal_f32(11, S.P_BIAS, 0, (E,), std=0.01)
+    b[100:400] = 3.0
+    x = S.normal_bf16(11, S.P_X, 0, (3, H))
+    for k in (16, 64, 333):
+        idx, gates, i_ref, g_ref = _route_both(torch, k3x, orc, x, W, b, k)
+        assert np.array_equal(idx, i_ref), k
+        assert np.array_equal(gates.view(np.uint32), g_ref.view(np.uint32)), k
+    assert list(i_ref[0, :16]) == list(range(100, 116))
+
+
 # ------------------------------------------------------------------------------------------
 # the five workloads at full size (sampled tokens where the oracle would take minutes)
 # ------------------------------------------------------------------------------------------
