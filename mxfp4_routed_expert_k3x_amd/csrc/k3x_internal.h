@@ -120,6 +120,17 @@ hipError_t launch_decode_exact(const k3x_pool& p, const uint16_t* x, const int32
                                const float* gates, int32_t topk, float* y, uint8_t* ws,
                                hipStream_t s);
 
+// Prefill-sized grouped GEMMs (k3x_prefill.hip): expert tiles of up to 128 slots.
+int prefill_tile_tokens();
+hipError_t launch_prefill_gemms(const k3x_pool& p, const uint16_t* x, int32_t topk, uint8_t* ws,
+                                const MoeLayout& L, hipStream_t s);
+
+// True when a batch has enough slots per expert (16 on average) for the prefill kernels and
+// the shapes fit their tiling (hidden a multiple of 256).
+inline bool use_prefill(int32_t E, int32_t H, int32_t I, int32_t T, int32_t topk) {
+  return (int64_t)T * topk >= 16 * (int64_t)E && H % 256 == 0 && I % 128 == 0;
+}
+
 hipError_t launch_rmsnorm(const uint16_t* x, int32_t T, int32_t H, float eps, uint16_t* out,
                           hipStream_t s);
 

@@ -29,7 +29,8 @@ MoeLayout moe_layout(int32_t E, int32_t H, int32_t I, int32_t T, int32_t topk) {
   auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
   MoeLayout L{};
   const size_t slots = (size_t)T * topk;
-  L.tile_tokens = 16;  // decode tiles: one 16-column MFMA block
+  // decode-sized batches: tiles of one 16-column MFMA block; prefill: tiles of 128 slots
+  L.tile_tokens = use_prefill(E, H, I, T, topk) ? prefill_tile_tokens() : 16;
   const size_t nonempty = slots < (size_t)E ? slots : (size_t)E;
   L.max_tiles = (int32_t)(nonempty + (slots + L.tile_tokens - 1) / L.tile_tokens + 1);
   size_t off = 0;
@@ -414,6 +415,13 @@ hipError_t launch_moe(const k3x_pool& p, const uint16_t* x, int32_t T, const int
     const size_t sort_lds = sizeof(int32_t) * (size_t)p.E;
     err = launch("moe_sort", moe_sort, dim3(1), dim3(kSortThreads), (uint32_t)sort_lds, s, sa);
     if (err != hipSuccess || T == 0) return err;
+  }
+
+  if (L.tile_tokens > 16) {
+    err = launch_prefill_gemms(p, x, topk, ws, L, s);
+    if (err != hipSuccess) return err;
+    return launch("moe_combine", moe_combine, dim3((p.H / 4 + 255) / 256, T), dim3(256), 0, s,
+                  reinterpret_cast<const float*>(ws + L.d), idx, gates, topk, p.H, p.E, y);
   }
 
   // persistent grids: two 4-wave workgroups per CU (the occupancy the registers allow)

@@ -95,6 +95,29 @@ def test_moe_small_parity(dev, orc, E, H, I, T, k):
     assert_y_close(_np(y), y_ref, f"E={E} H={H} I={I} T={T} k={k}")
 
 
+@pytest.mark.parametrize("E,H,I,T,k", [(4, 256, 256, 40, 2), (2, 512, 384, 300, 1), (8, 256, 128, 200, 3)])
+def test_prefill_path_parity(dev, orc, E, H, I, T, k):
+    """Batches with >= 16 slots per expert take the prefill kernels (tiles of up to 128 slots):
+    several tiles per expert, ragged last tiles."""
+    torch, k3x = dev
+    _log(f"case: prefill path E={E} H={H} I={I} T={T} k={k}")
+    seed = 2000 + E + H + I + T
+    host = S.host_pool(seed, 0, E, H, I)
+    pool = _pool(torch, k3x, S.device_pool(seed, 0, E, H, I), E, H, I)
+    x = S.normal_bf16(seed, S.P_X, 0, (T, H))
+    rng = np.random.default_rng(seed)
+    idx = rng.integers(0, E, (T, k)).astype(np.int32)  # duplicates allowed
+    if T > 100:
+        idx[7, 0] = -5  # a dropped slot
+    _, gates = S.uniform_routing(seed, T, k, k)
+    y, ws = k3x.moe_forward(pool, _t(torch, x), _t(torch, idx), _t(torch, gates))
+    torch.cuda.synchronize()
+    y_ref, drops = orc.moe_forward(host, x, idx, gates)
+    assert k3x.k3x_fetch_drops(ws) == drops
+    r = assert_y_close(_np(y), y_ref, f"prefill E={E} H={H} I={I} T={T} k={k}")
+    _log(f"  rel_l2={r[0]:.3e} max_abs={r[1]:.3e}")
+
+
 def test_moe_duplicates_and_drops(dev, orc):
     torch, k3x = dev
     E, H, I, T, k = 6, 256, 256, 9, 6
