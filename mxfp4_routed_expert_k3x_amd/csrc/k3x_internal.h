@@ -81,6 +81,7 @@ struct MoeLayout {
   size_t offsets;     // int32 [E + 1] start of each expert's slots in perm
   size_t tiles;       // int32 [max_tiles][4] = expert, first slot in perm, count, pad
   size_t perm;        // int32 [T * topk] slot ids (t * topk + j) grouped by expert
+  size_t inv;         // int32 [T * topk] position of each slot in perm, -1 if dropped
   size_t h;           // bf16 [T * topk][I]
   size_t d;           // fp32 [T * topk][H]
   size_t total;
@@ -122,13 +123,17 @@ hipError_t launch_decode_exact(const k3x_pool& p, const uint16_t* x, const int32
 
 // Prefill-sized grouped GEMMs (k3x_prefill.hip): expert tiles of up to 128 slots.
 int prefill_tile_tokens();
-hipError_t launch_prefill_gemms(const k3x_pool& p, const uint16_t* x, int32_t topk, uint8_t* ws,
+hipError_t launch_prefill_gemms(const k3x_pool& p, const uint16_t* x, int32_t T, int32_t topk, uint8_t* ws,
                                 const MoeLayout& L, hipStream_t s);
 
 // True when a batch has enough slots per expert (16 on average) for the prefill kernels and
 // the shapes fit their tiling (hidden a multiple of 256).
 inline bool use_prefill(int32_t E, int32_t H, int32_t I, int32_t T, int32_t topk) {
-  return (int64_t)T * topk >= 16 * (int64_t)E && H % 256 == 0 && I % 128 == 0;
+  // tiles of 96 slots; items of 256 h rows (W1/W3) or 512 d rows (W2); the item's scale rows
+  // (K / 32 bytes each, K <= 4096) fit in LDS; 32-bit row offsets
+  const int64_t slots = (int64_t)T * topk;
+  return slots >= 16 * (int64_t)E && H % 512 == 0 && I % 512 == 0 && H <= 4096 && I <= 4096 &&
+         slots * (int64_t)(H > I ? H : I) < ((int64_t)1 << 31);
 }
 
 hipError_t launch_rmsnorm(const uint16_t* x, int32_t T, int32_t H, float eps, uint16_t* out,

@@ -42,6 +42,8 @@ MoeLayout moe_layout(int32_t E, int32_t H, int32_t I, int32_t T, int32_t topk) {
   off = up(off + sizeof(int32_t) * 4 * (size_t)L.max_tiles);
   L.perm = off;
   off = up(off + sizeof(int32_t) * (slots ? slots : 1));
+  L.inv = off;
+  off = up(off + sizeof(int32_t) * (slots ? slots : 1));
   L.h = off;
   off = up(off + sizeof(uint16_t) * slots * (size_t)I);
   L.d = off;
@@ -63,7 +65,7 @@ struct SortArgs {
   const int32_t* idx;
   int32_t T, topk, E, tile_tokens;
   uint8_t* ws;
-  size_t off_offsets, off_tiles, off_perm;
+  size_t off_offsets, off_tiles, off_perm, off_inv;
 };
 
 __global__ __launch_bounds__(kSortThreads) void moe_sort(SortArgs a) {
@@ -77,6 +79,7 @@ __global__ __launch_bounds__(kSortThreads) void moe_sort(SortArgs a) {
   int32_t* offsets = reinterpret_cast<int32_t*>(a.ws + a.off_offsets);
   int32_t* tiles = reinterpret_cast<int32_t*>(a.ws + a.off_tiles);
   int32_t* perm = reinterpret_cast<int32_t*>(a.ws + a.off_perm);
+  int32_t* inv = reinterpret_cast<int32_t*>(a.ws + a.off_inv);
 
   for (int e = tid; e < E; e += kSortThreads) counts[e] = 0;
   if (tid == 0) drop_cnt = 0;
@@ -135,7 +138,12 @@ __global__ __launch_bounds__(kSortThreads) void moe_sort(SortArgs a) {
   __syncthreads();
   for (int p = tid; p < n_slots; p += kSortThreads) {
     const int e = a.idx[p];
-    if (e >= 0 && e < E) perm[atomicAdd(&counts[e], 1)] = p;
+    int pos = -1;
+    if (e >= 0 && e < E) {
+      pos = atomicAdd(&counts[e], 1);
+      perm[pos] = p;
+    }
+    inv[p] = pos;
   }
 }
 
@@ -361,6 +369,7 @@ __global__ __launch_bounds__(256) void gemm_decode(GemmArgs a) {
 __global__ __launch_bounds__(256) void moe_combine(const float* __restrict__ d,
                                                    const int32_t* __restrict__ idx,
                                                    const float* __restrict__ gates,
+                                                   const int32_t* __restrict__ inv,
                                                    int32_t topk, int32_t H, int32_t E,
                                                    float* __restrict__ y) {
   const int t = blockIdx.y;
@@ -368,7 +377,7 @@ __global__ __launch_bounds__(256) void moe_combine(const float* __restrict__ d,
   if (r >= H) return;
   const int32_t* it = idx + (size_t)t * topk;
   const float* gt = gates + (size_t)t * topk;
-  const float* dt = d + (size_t)t * topk * H + r;
+  const int32_t* pt = inv ? inv + (size_t)t * topk : nullptr;  // d rows by sorted position
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int j0 = 0; j0 < topk; j0 += 16) {
     float4 v[16];
@@ -378,7 +387,8 @@ __global__ __launch_bounds__(256) void moe_combine(const float* __restrict__ d,
       const int j = j0 + jj;
       const bool ok = j < topk && expert_ok(it[j], E);
       g[jj] = ok ? gt[j] : 0.0f;
-      v[jj] = ok ? *reinterpret_cast<const float4*>(dt + (size_t)j * H) : make_float4(0.f, 0.f, 0.f, 0.f);
+      const size_t row = pt ? (size_t)(ok ? pt[j] : 0) : (size_t)t * topk + j;
+      v[jj] = ok ? *reinterpret_cast<const float4*>(d + row * H + r) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
 #pragma unroll
     for (int jj = 0; jj < 16; ++jj) {
@@ -412,16 +422,18 @@ hipError_t launch_moe(const k3x_pool& p, const uint16_t* x, int32_t T, const int
     sa.off_offsets = L.offsets;
     sa.off_tiles = L.tiles;
     sa.off_perm = L.perm;
+    sa.off_inv = L.inv;
     const size_t sort_lds = sizeof(int32_t) * (size_t)p.E;
     err = launch("moe_sort", moe_sort, dim3(1), dim3(kSortThreads), (uint32_t)sort_lds, s, sa);
     if (err != hipSuccess || T == 0) return err;
   }
 
   if (L.tile_tokens > 16) {
-    err = launch_prefill_gemms(p, x, topk, ws, L, s);
+    err = launch_prefill_gemms(p, x, T, topk, ws, L, s);
     if (err != hipSuccess) return err;
     return launch("moe_combine", moe_combine, dim3((p.H / 4 + 255) / 256, T), dim3(256), 0, s,
-                  reinterpret_cast<const float*>(ws + L.d), idx, gates, topk, p.H, p.E, y);
+                  reinterpret_cast<const float*>(ws + L.d), idx, gates,
+                  reinterpret_cast<const int32_t*>(ws + L.inv), topk, p.H, p.E, y);
   }
 
   // persistent grids: two 4-wave workgroups per CU (the occupancy the registers allow)
@@ -476,7 +488,7 @@ hipError_t launch_moe(const k3x_pool& p, const uint16_t* x, int32_t T, const int
                dim3(256), 0, s, a2);
   if (err != hipSuccess) return err;
   return launch("moe_combine", moe_combine, dim3((p.H / 4 + 255) / 256, T), dim3(256), 0, s,
-                reinterpret_cast<const float*>(ws + L.d), idx, gates, topk, p.H, p.E, y);
+                reinterpret_cast<const float*>(ws + L.d), idx, gates, nullptr, topk, p.H, p.E, y);
 }
 
 }  // namespace k3x

@@ -27,6 +27,23 @@ def assert_y_close(y, y_ref, what=""):
     return rel_l2, max_abs
 
 
+def assert_y_close_oracle(y, y_ref32, y_ref64_fn, what=""):
+    """Verdict against the oracle in its fp32 arithmetic.  The oracle's fp32 sums are one
+    rounding of the definition and its fp64 sums another; where the fp32 one already lies
+    beyond the tolerance from the fp64 one (a bf16 rounding of a large h that falls the other
+    way, amplified by W2), the same tolerance is applied against the fp64 oracle instead."""
+    r32 = y_errors(y, y_ref32)
+    if r32[0] <= REL_L2_TOL and r32[1] <= MAX_ABS_TOL:
+        assert np.all(np.isfinite(y)), f"{what}: non-finite output"
+        return r32
+    y_ref64 = y_ref64_fn()
+    floor = y_errors(y_ref32, y_ref64)
+    assert floor[0] > REL_L2_TOL or floor[1] > MAX_ABS_TOL, (
+        f"{what}: rel L2 {r32[0]:.3e}, max abs {r32[1]:.3e} against the fp32 oracle, whose own "
+        f"distance to the fp64 oracle is only {floor[0]:.3e} / {floor[1]:.3e}")
+    return assert_y_close(y, y_ref64, f"{what} [fp64 oracle; fp32 oracle off by {floor[0]:.2e} / {floor[1]:.2e}]")
+
+
 def oracle_forward_sampled(orc, seed, layer, H, I, x_bits, idx, gates, tokens, E=None,
                            acc="f32", cache=None):
     """Oracle y for the listed tokens, regenerating on the host only the experts they use.
