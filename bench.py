@@ -10,8 +10,11 @@ device memory and resident before timing.  Successive steps rotate over 64 diffe
 tokens, so each step reads a different set of 16 experts and the 256 MB Infinity Cache
 cannot serve them from a previous step.
 
-Prints ONE JSON line.  Kernel durations come from HIP events the library records around
-each of its launches inside the timed region (k3x_profiler_*).
+Prints ONE JSON line.  The timed region replays one HIP graph per rotated batch (captured
+once, each replay checked bit for bit against the eager result first), so `value` and
+`ms_per_step` are the path's throughput without host launch gaps.  Kernel durations for the
+roofline come from HIP events the library records around each of its launches
+(k3x_profiler_*) in a second timed pass over the same steps, launched eagerly.
 """
 from __future__ import annotations
 
@@ -65,46 +68,42 @@ def per_kernel_work(name, H, I, E, T, topk, U):
     return 0, 0.0
 
 
-def cpu_baseline(w, x, W, b, dev_idx, dev_gates, budget_s=12.0):
+def cpu_baseline(w, x, W, b, dev_idx, dev_gates, pool_dev, budget_s=12.0):
     """The oracle as it stands, on this host's cores, over a bounded sample of the same
-    workload's tokens (expert bytes generated beforehand, outside the timing)."""
+    workload's tokens, repeated until about budget_s seconds of oracle time.  Each token's
+    expert bytes are copied from the generator's device pool (k3x_synth writes the same
+    bytes on the device and the host) outside the timing."""
     import k3x_synth as S
     import oracle
 
-    tokens = []
-    t_used = 0.0
-    cache = {}
-    i = 0
-    while i < len(x) and (t_used < budget_s or not tokens):
-        xt = x[i:i + 1]
+    n_tok, t_used, i = 0, 0.0, 0
+    while t_used < budget_s:
+        t = i % len(x)
+        i += 1
+        xt = x[t:t + 1]
         if w.router:
             t0 = time.perf_counter()
             idx, gates = oracle.route(xt, W, b, w.topk)
             t_used += time.perf_counter() - t0
         else:
-            idx, gates = dev_idx[i:i + 1], dev_gates[i:i + 1]
+            idx, gates = dev_idx[t:t + 1], dev_gates[t:t + 1]
         exps = []
         for e in idx[0]:
-            key = int(e)
-            if key not in cache:
-                cache[key] = S.expert_bytes(w.seed, 0, key, w.H, w.I)
-            exps.append(cache[key])
+            e = int(e)
+            exps.append(S.ExpertBytes(*[pool_dev[nm][e].cpu().numpy() for nm in S.TENSOR_NAMES]))
         t0 = time.perf_counter()
         d = np.stack([oracle.expert_forward(xt[0], ex) for ex in exps])[None]
         oracle.combine(gates, d)
         t_used += time.perf_counter() - t0
-        tokens.append(i)
-        i += 1
-        if len(cache) > 256:
-            cache.clear()
+        n_tok += 1
     return {
-        "value": len(tokens) / t_used,
+        "value": n_tok / t_used,
         "unit": "tokens/s",
         "cores": oracle.threads(),
         "kind": "oracle",
-        "sample": f"{len(tokens)} token(s) of the same workload ({'router + ' if w.router else ''}"
-                  f"{w.topk} experts each + combine), {t_used:.1f} s of oracle time, expert byte "
-                  f"generation excluded",
+        "sample": f"{n_tok} token(s) of the same workload ({'router + ' if w.router else ''}"
+                  f"{w.topk} experts each + combine), {t_used:.1f} s of oracle time; expert bytes "
+                  f"copied to the host outside the timing",
     }
 
 
@@ -140,8 +139,8 @@ def main():
     dev = torch.device("cuda:0")
 
     log(f"generating pool: E={w.E} H={w.H} I={w.I}")
-    pool = k3x.k3x_expert_pool_create(S.device_pool(w.seed, 0, w.E, w.H, w.I), hidden=w.H,
-                                      inter=w.I, n_experts=w.E)
+    pool_dev = S.device_pool(w.seed, 0, w.E, w.H, w.I)
+    pool = k3x.k3x_expert_pool_create(pool_dev, hidden=w.H, inter=w.I, n_experts=w.E)
     R = 1 if prefill else ROTATE
     x = S.normal_bf16(w.seed, S.P_X, 0, (R * w.T, w.H))
     xs = [torch.from_numpy(x[r * w.T:(r + 1) * w.T].view(np.int16)).to(dev) for r in range(R)]
@@ -171,28 +170,58 @@ def main():
             i_, g_ = routes[r]
             k3x.k3x_moe_forward(pool, xs[r], w.T, i_, g_, w.topk, y, ws)
 
-    # distinct experts per rotated batch (from the GPU's own routing)
-    U = []
+    # distinct experts per rotated batch (from the GPU's own routing), eager results kept
+    U, y_eager = [], []
     for r in range(R):
         step(r)
         torch.cuda.synchronize()
         ids = (idx if w.router else routes[r][0]).cpu().numpy()
         U.append(len(np.unique(ids)))
+        y_eager.append(y.clone())
     drops = k3x.k3x_fetch_drops(ws)
     if drops:
         sys.exit(f"run invalid: {drops} dropped slots")
 
+    # one graph per rotated batch; every graph is replayed and checked against the eager
+    # result, with eager steps in between
+    graphs = []
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(0)
+    torch.cuda.current_stream().wait_stream(side)
+    for r in range(R):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(r)
+        graphs.append(g)
+    for r in range(R):
+        graphs[r].replay()
+        torch.cuda.synchronize()
+        if not torch.equal(y, y_eager[r]):
+            sys.exit(f"graph replay of batch {r} differs from the eager result")
+        step((r + 1) % R)
+        torch.cuda.synchronize()
+
     for i in range(warmup):
-        step(i % R)
+        graphs[i % R].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        graphs[i % R].replay()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    # kernel durations: the same steps launched eagerly, HIP events around each launch
     kernels_per_step = 6 if w.router else 4
     prof = k3x.k3x_profiler_create(steps * kernels_per_step + 16)
     torch.cuda.synchronize()
     k3x.k3x_profiler_attach(prof)
-    t0 = time.perf_counter()
+    t1 = time.perf_counter()
     for i in range(steps):
         step(i % R)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    wall_eager = time.perf_counter() - t1
     k3x.k3x_profiler_attach(None)
     durs = k3x.profiler_durations(prof)
     k3x.k3x_profiler_destroy(prof)
@@ -249,7 +278,9 @@ def main():
                  "hbm_gbps_kernel_sum": round(path_bytes / ksum / 1e9, 1),
                  "hbm_frac_kernel_sum": round(path_bytes / ksum / 1e9 / PEAK_HBM_GBS, 4),
                  "tflops_kernel_sum": round(path_flops / ksum / 1e12, 2),
-                 "hbm_gbps_wall": round(path_bytes / (wall / steps) / 1e9, 1)},
+                 "hbm_gbps_wall": round(path_bytes / (wall / steps) / 1e9, 1),
+                 "timed_region": "HIP graph replay, one graph per rotated batch",
+                 "eager_ms_per_step": round(wall_eager / steps * 1e3, 5)},
         "kernels": kernels,
         "cpu_baseline": None,
     }
@@ -257,7 +288,7 @@ def main():
         log("timing the oracle on the host (bounded sample)")
         di = np.concatenate([r_[0] for r_ in routes_np]) if routes_np else None
         dg = np.concatenate([r_[1] for r_ in routes_np]) if routes_np else None
-        out["cpu_baseline"] = cpu_baseline(w, x, W, b, di, dg)
+        out["cpu_baseline"] = cpu_baseline(w, x, W, b, di, dg, pool_dev)
     print(json.dumps(out), flush=True)
 
 
