@@ -167,11 +167,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_prefill(PrefillArgs a, const
   };
 
   // ---- operand staging ----
-  // Activation and weight blocks both run two K blocks ahead, in rings of three register
-  // sets (block kb in set kb % 3), issued as one group per block: activations, then weights.
-  // Scheduling barriers keep the groups in that order, so the memory-counter wait that the
-  // store of activation block kb + 1 needs (at the end of step kb) never covers a weight
-  // block that is still ahead of the MFMAs.
+  // Weight blocks run two K blocks ahead in a ring of three register sets (block kb in set
+  // kb % 3), activation blocks one block ahead in two sets.  Each step issues its activation
+  // loads before its weight loads; scheduling barriers keep that order, so the
+  // memory-counter wait that the store of activation block kb + 1 needs at the end of step kb
+  // covers only loads issued before it (weights up to block kb + 1, which step kb + 1 needs
+  // anyway), never the weight block kb + 2 issued in the same step.
   auto load_x = [&](int kb, uint4 (&xv)[kXPass]) __attribute__((always_inline)) {
 #pragma unroll
     for (int p = 0; p < kXPass; ++p) xv[p] = buf_load16(xrs, xoff[p], (uint32_t)(2 * kKBlock * kb));
@@ -227,7 +228,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_prefill(PrefillArgs a, const
                 : (uint32_t)(16 * rb) * srow;
   };
 
-  uint4 x0[kXPass], x1[kXPass], x2[kXPass];
+  uint4 x0[kXPass], x1[kXPass];
   uint4 w0[kRB], w1[kRB], w2[kRB];
   {
     int te, ts, tm, tc;
@@ -238,7 +239,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_prefill(PrefillArgs a, const
   }
   load_x(0, x0);
   load_w(0, w0);
-  load_x(min(1, nk - 1), x1);
   load_w(min(1, nk - 1), w1);
   copy_scales();
 
@@ -283,19 +283,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_prefill(PrefillArgs a, const
             for (int rb = 0; rb < kRB; ++rb) acc[rb][tb] = mfma16x16x32(av[rb], bq[f % 3], acc[rb][tb]);
           }
         }
-        // keep the dequantized fragments of one 32-wide K step live at a time
-        __builtin_amdgcn_sched_barrier(0);
       }
     };
 
     // one K block: loads for later blocks, MFMAs, the next activation block into LDS, and
     // one barrier.  The body has no branches, so the compiler's memory-counter waits stay
     // exact (the last blocks re-read block nk - 1 instead of skipping the loads).
-    // step kb: MFMAs on set kb % 3, store activation block kb + 1 (set (kb + 1) % 3) to LDS,
-    // load block kb + 2 into set (kb + 2) % 3
-    auto step = [&](int kb, const uint4 (&wc)[kRB], const uint4 (&xn)[kXPass], uint4 (&xl)[kXPass],
-                    uint4 (&wn)[kRB]) __attribute__((always_inline)) {
-      load_x(min(kb + 2, nk - 1), xl);
+    // step kb: load activation block kb + 1 into xn and weight block kb + 2 into wn, MFMAs on
+    // wc (block kb), then activation block kb + 1 into LDS
+    auto step = [&](int kb, const uint4 (&wc)[kRB], uint4 (&xn)[kXPass], uint4 (&wn)[kRB]) __attribute__((always_inline)) {
+      load_x(min(kb + 1, nk - 1), xn);
       load_w(min(kb + 2, nk - 1), wn);
       compute(kb, wc);
       store_x((kb + 1) & 1, xn);
@@ -304,21 +301,31 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_prefill(PrefillArgs a, const
 
     store_x(0, x0);
     __syncthreads();
-    // the first three steps are peeled so that the loop is only entered in the steady state
+    // the first six steps are peeled so that the loop is only entered in the steady state
     // (the compiler then keeps every wait in the loop down to the block it needs)
     int kb = 0;
-    if (nk >= 3) {
-      step(0, w0, x1, x2, w2);
-      step(1, w1, x2, x0, w0);
-      step(2, w2, x0, x1, w1);
-      for (kb = 3; kb + 3 <= nk; kb += 3) {
-        step(kb, w0, x1, x2, w2);
-        step(kb + 1, w1, x2, x0, w0);
-        step(kb + 2, w2, x0, x1, w1);
+    if (nk >= 6) {
+      step(0, w0, x1, w2);
+      step(1, w1, x0, w0);
+      step(2, w2, x1, w1);
+      step(3, w0, x0, w2);
+      step(4, w1, x1, w0);
+      step(5, w2, x0, w1);
+      for (kb = 6; kb + 6 <= nk; kb += 6) {
+        step(kb, w0, x1, w2);
+        step(kb + 1, w1, x0, w0);
+        step(kb + 2, w2, x1, w1);
+        step(kb + 3, w0, x0, w2);
+        step(kb + 4, w1, x1, w0);
+        step(kb + 5, w2, x0, w1);
       }
     }
-    if (kb < nk) step(kb, w0, x1, x2, w2);
-    if (kb + 1 < nk) step(kb + 1, w1, x2, x0, w0);
+    // remaining 0..5 blocks (the ring sets follow kb % 3, the activation sets kb % 2)
+    if (kb < nk) step(kb, w0, x1, w2);
+    if (kb + 1 < nk) step(kb + 1, w1, x0, w0);
+    if (kb + 2 < nk) step(kb + 2, w2, x1, w1);
+    if (kb + 3 < nk) step(kb + 3, w0, x0, w2);
+    if (kb + 4 < nk) step(kb + 4, w1, x1, w0);
   };
 
   // epilogue: lane holds rows 4q..4q+3 of each row block for column 16 tb + n
@@ -367,7 +374,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_prefill(PrefillArgs a, const
       enter(ne, nstart, nm, nchunk, nslot);
       load_x(0, x0);
       load_w(0, w0);
-      load_x(min(1, nk - 1), x1);
       load_w(min(1, nk - 1), w1);
       // every wave finished the last K block (barrier) before the scales are replaced; the
       // next item's first barrier publishes them
