@@ -10,6 +10,15 @@ device memory and resident before timing.  Successive steps rotate over 64 diffe
 tokens, so each step reads a different set of 16 experts and the 256 MB Infinity Cache
 cannot serve them from a previous step.
 
+Two helper modes support `roofline.traffic` (HBM bytes from rocprofv3 counters):
+    python bench.py --copy-probe                 # a plain device copy of 1 GiB, run under
+                                                 # rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE)
+    python bench.py --traffic-from F W CF CW     # counter CSVs of the workload (F, W) and of
+                                                 # the copy (CF, CW) -> profiles/traffic_<workload>.txt
+The copy's readings give the scale of each counter (bytes moved / bytes counted); the
+summary records the hash of the kernel sources, and a normal run reports the traffic only
+while those sources are unchanged.
+
 Prints ONE JSON line.  The timed region replays one HIP graph per rotated batch (captured
 once, each replay checked bit for bit against the eager result first), so `value` and
 `ms_per_step` are the path's throughput without host launch gaps.  Kernel durations for the
@@ -33,6 +42,13 @@ METRIC = "MoE-layer tokens/s + achieved HBM GB/s (decode), TFLOP/s (prefill)"
 PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
 ROTATE = 64
+COPY_PROBE_BYTES = 1 << 30
+KERNEL_SOURCES = ("k3x_decode.hip", "k3x_moe.hip", "k3x_prefill.hip", "k3x_router.hip")
+# rocprofv3 kernel names of the library's launch names
+KERNEL_SYMBOLS = {"w13_decode": "decode_rows<true>", "w2_decode": "decode_rows<false>",
+                  "w13_prefill": "gemm_prefill<true>", "w2_prefill": "gemm_prefill<false>",
+                  "w13_grouped": "gemm_decode<true>", "w2_grouped": "gemm_decode<false>",
+                  "route_scores": "route_scores", "route_select": "route_select"}
 
 
 def log(*a):
@@ -107,6 +123,81 @@ def cpu_baseline(w, x, W, b, dev_idx, dev_gates, pool_dev, budget_s=12.0):
     }
 
 
+def sources_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "mxfp4_routed_expert_k3x_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def copy_probe():
+    import torch
+    a = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device="cuda:0")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": COPY_PROBE_BYTES, "dispatches": 3}))
+
+
+def _counter_rows(path, counter):
+    import csv
+    out = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] == counter:
+                out.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    return out
+
+
+def traffic_from(f_csv, w_csv, cf_csv, cw_csv, workload):
+    """Per-launch HBM bytes of the library's kernels from FETCH_SIZE / WRITE_SIZE (KiB per
+    dispatch), each scaled by bytes / counted bytes of the plain copy."""
+    def copy_scale(path, counter):
+        vals = [v for k, v in _counter_rows(path, counter) if "copy" in k.lower()]
+        vals = [v for v in vals if v > 0.5 * COPY_PROBE_BYTES / 1024]  # the 1 GiB copies
+        return COPY_PROBE_BYTES / (1024.0 * float(np.median(vals))), len(vals)
+    sf, nf = copy_scale(cf_csv, "FETCH_SIZE")
+    sw, nw = copy_scale(cw_csv, "WRITE_SIZE")
+    lines = [f"# HBM traffic of {workload} from rocprofv3 counters",
+             f"sources_hash={sources_hash()}",
+             f"copy_fetch_scale={sf:.4f} (from {nf} copies of {COPY_PROBE_BYTES} B)",
+             f"copy_write_scale={sw:.4f} (from {nw} copies)"]
+    fetch = _counter_rows(f_csv, "FETCH_SIZE")
+    write = _counter_rows(w_csv, "WRITE_SIZE")
+    for name, sym in KERNEL_SYMBOLS.items():
+        fv = [v for k, v in fetch if sym in k]
+        wv = [v for k, v in write if sym in k]
+        if not fv or not wv:
+            continue
+        b = 1024.0 * (float(np.mean(fv)) * sf + float(np.mean(wv)) * sw)
+        lines.append(f"traffic {name} {b:.0f} fetch_kib={np.mean(fv):.0f} write_kib={np.mean(wv):.0f} "
+                     f"dispatches={len(fv)}/{len(wv)}")
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def traffic_for(workload, kernel):
+    """Calibrated HBM bytes per launch of `kernel`, or None (no summary, or kernels changed)."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    vals, ok = {}, False
+    for line in open(path):
+        if line.startswith("sources_hash="):
+            ok = line.strip().split("=", 1)[1] == sources_hash()
+        elif line.startswith("traffic "):
+            parts = line.split()
+            vals[parts[1]] = float(parts[2])
+    return vals.get(kernel) if ok else None
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -114,7 +205,13 @@ def main():
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="decode_t1_e896_router")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"))
     args = ap.parse_args()
+    if args.copy_probe:
+        return copy_probe()
+    if args.traffic_from:
+        return traffic_from(*args.traffic_from, args.workload)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path is "
               f"built and measured for a single MI355X", file=sys.stderr)
@@ -240,13 +337,16 @@ def main():
         }
     dominant = max(kernels, key=lambda n: kernels[n]["avg_us"] * kernels[n]["launches"])
     dk = kernels[dominant]
+    traffic = traffic_for(w.name, dominant)
+    traffic = int(traffic) if traffic is not None else None
     if prefill:
         roof = {"bound": "mfma", "achieved": dk["tflops"], "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(dk["tflops"] / PEAK_BF16_TFLOPS, 4),
-                "traffic": None, "kernel": dominant}
+                "traffic": traffic, "kernel": dominant, "alg_bytes": dk["alg_bytes"]}
     else:
         roof = {"bound": "hbm", "achieved": dk["gbps"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(dk["gbps"] / PEAK_HBM_GBS, 4), "traffic": None, "kernel": dominant}
+                "frac": round(dk["gbps"] / PEAK_HBM_GBS, 4), "traffic": traffic, "kernel": dominant,
+                "alg_bytes": dk["alg_bytes"]}
 
     w13, w2 = expert_tensor_bytes(w.H, w.I)
     path_bytes = mean_U * (w13 + w2) + w.T * (w.H * 2 + w.H * 4)
