@@ -3,8 +3,8 @@
 // for selection only, repeated argmax with ties to the lower expert, gates from the unbiased
 // scores renormalised by their float sum and scaled by routed_scale.
 //
-// Kernel 1 (route_scores): one wave per (expert, token block).  The expert's weight row
-// stays in registers while the wave walks its tokens.  Lane L owns the 8-element chunks
+// Kernel 1 (route_scores): one wave per (expert, block of 4 tokens).  The expert's weight row
+// stays in registers while the wave sums the block's tokens side by side.  Lane L owns the 8-element chunks
 // whose index is L mod 64 and sums their exact bf16*bf16 products in double, in ascending
 // order; the 64 lane partials are then folded p[L] += p[L + s] for s = 32 .. 1 with
 // down-shuffles.  The float logit goes through a double sigmoid rounded once to float.
@@ -19,7 +19,7 @@
 namespace k3x {
 namespace {
 
-constexpr int kRouteTokBlock = 32;  // tokens per wave in route_scores
+constexpr int kRouteTokBlock = 4;  // tokens per wave in route_scores, summed side by side
 
 // NC = 8-element chunks each lane keeps in registers: hidden <= 64 * 8 * NC
 template <int NC>
@@ -47,31 +47,42 @@ __global__ __launch_bounds__(256) void route_scores(const uint16_t* __restrict__
     }
   }
 
-  for (int t = t0; t < t1; ++t) {
-    const uint4* xrow = reinterpret_cast<const uint4*>(x + (size_t)t * H);
-    double acc = 0.0;
+  // the block's tokens are summed side by side (independent chains, each in the fixed order)
+  double acc[kRouteTokBlock];
 #pragma unroll
-    for (int i = 0; i < NC; ++i) {
-      if (i < nmine) {
-        const uint4 xv = xrow[lane + kWave * i];
-        const uint32_t xs[4] = {xv.x, xv.y, xv.z, xv.w};
-        const uint32_t ws[4] = {wv[i].x, wv[i].y, wv[i].z, wv[i].w};
+  for (int k = 0; k < kRouteTokBlock; ++k) acc[k] = 0.0;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const double xl = (double)bf16_bits_to_f32(xs[j] & 0xFFFFu);
-          const double wl = (double)bf16_bits_to_f32(ws[j] & 0xFFFFu);
-          acc = acc + xl * wl;  // the product is exact in double
-          const double xh = (double)bf16_bits_to_f32(xs[j] >> 16);
-          const double wh = (double)bf16_bits_to_f32(ws[j] >> 16);
-          acc = acc + xh * wh;
+  for (int i = 0; i < NC; ++i) {
+    if (i < nmine) {
+      const uint32_t ws[4] = {wv[i].x, wv[i].y, wv[i].z, wv[i].w};
+#pragma unroll
+      for (int k = 0; k < kRouteTokBlock; ++k) {
+        if (t0 + k < t1) {
+          const uint4 xv = reinterpret_cast<const uint4*>(x + (size_t)(t0 + k) * H)[lane + kWave * i];
+          const uint32_t xs[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const double xl = (double)bf16_bits_to_f32(xs[j] & 0xFFFFu);
+            const double wl = (double)bf16_bits_to_f32(ws[j] & 0xFFFFu);
+            acc[k] = acc[k] + xl * wl;  // the product is exact in double
+            const double xh = (double)bf16_bits_to_f32(xs[j] >> 16);
+            const double wh = (double)bf16_bits_to_f32(ws[j] >> 16);
+            acc[k] = acc[k] + xh * wh;
+          }
         }
       }
     }
+  }
 #pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) acc = acc + __shfl_down(acc, s, kWave);
-    if (lane == 0) {
-      const float l = (float)acc;
-      scores[(size_t)t * E + e] = (float)(1.0 / (1.0 + exp(-(double)l)));
+  for (int k = 0; k < kRouteTokBlock; ++k) {
+    if (t0 + k < t1) {
+      double a = acc[k];
+#pragma unroll
+      for (int s = 32; s >= 1; s >>= 1) a = a + __shfl_down(a, s, kWave);
+      if (lane == 0) {
+        const float l = (float)a;
+        scores[(size_t)(t0 + k) * E + e] = (float)(1.0 / (1.0 + exp(-(double)l)));
+      }
     }
   }
 }

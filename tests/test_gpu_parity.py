@@ -96,9 +96,10 @@ def test_moe_small_parity(dev, orc, E, H, I, T, k):
 
 
 @pytest.mark.parametrize("E,H,I,T,k", [(4, 512, 512, 40, 2), (2, 512, 1536, 300, 1),
-                                       (3, 1536, 1024, 100, 2), (8, 1024, 512, 200, 3)])
+                                       (3, 1536, 1024, 100, 2), (8, 1024, 512, 200, 3),
+                                       (64, 512, 512, 3, 4), (16, 1024, 512, 2, 8)])
 def test_prefill_path_parity(dev, orc, E, H, I, T, k):
-    """Batches with >= 16 slots per expert take the prefill kernels (tiles of up to 96 slots,
+    """Batches of two or more tokens take the sorted-tile kernels (tiles of up to 96 slots,
     items of 256 h rows and 512 d rows): several tiles per expert, ragged last tiles, several
     row chunks per tile, K loops of every length modulo the three-stage weight ring."""
     torch, k3x = dev
