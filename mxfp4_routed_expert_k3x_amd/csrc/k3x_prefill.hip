@@ -255,11 +255,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_prefill(PrefillArgs a, const
 #pragma unroll
       for (int tb = 0; tb < NB; ++tb) acc[rb][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    // the scales of K block kb, decoded before the barrier that starts it (the item's scale
+    // rows do not change while its K loop runs)
+    float scl[kRB];
+    auto read_scales = [&](int kb) __attribute__((always_inline)) {
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb) scl[rb] = e8m0_to_f32(ss[sbase + rb_off(rb) + 4u * (uint32_t)kb]);
+    };
     auto compute = [&](int kb, const uint4 (&w)[kRB]) __attribute__((always_inline)) {
       const int buf = kb & 1;
       float scale[kRB];
 #pragma unroll
-      for (int rb = 0; rb < kRB; ++rb) scale[rb] = e8m0_to_f32(ss[sbase + rb_off(rb) + 4u * (uint32_t)kb]);
+      for (int rb = 0; rb < kRB; ++rb) scale[rb] = scl[rb];
       // B fragments in (s, tb) order, read two fragments ahead of the MFMAs that use them
       const uint16_t* xb = &xs[buf][n][32 * q];
       auto read_b = [&](int f) __attribute__((always_inline)) {
@@ -296,11 +303,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_prefill(PrefillArgs a, const
       load_w(min(kb + 2, nk - 1), wn);
       compute(kb, wc);
       store_x((kb + 1) & 1, xn);
+      read_scales(min(kb + 1, nk - 1));
       __syncthreads();
     };
 
     store_x(0, x0);
     __syncthreads();
+    // after the barrier: the item's scale rows were copied into LDS by all waves
+    read_scales(0);
     // the first six steps are peeled so that the loop is only entered in the steady state
     // (the compiler then keeps every wait in the loop down to the block it needs)
     int kb = 0;
