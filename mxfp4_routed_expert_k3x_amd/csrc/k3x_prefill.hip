@@ -1,4 +1,5 @@
-// Prefill-sized grouped GEMMs of the routed experts (many slots per expert).
+// Grouped GEMMs of the routed experts for batches of two or more tokens (prefill, and small
+// decode batches, where they stream lightly shared experts' weights fastest).
 //
 // Sources: kimi-k3-in-c README, Part II section 4 "Reduction one: the experts already ship at
 // half a byte" (MXFP4 weights taken straight from the nibbles: E2M1 value times 2^(scale -
@@ -19,7 +20,9 @@
 // n) and converts it with the gfx950 scaled FP4 -> bf16 instruction, the group's power-of-two
 // scale folded in (exact).  One 16-byte load feeds four bf16 MFMAs (16x16x32) that together
 // cover 16 rows x 128 K.  Weights run two K blocks ahead of the MFMAs in a ring of three
-// register sets.  The tile's activations (x rows by token, or h rows by position) are the B
+// register sets.  The item's scale rows are copied into LDS once per item (direct-to-LDS
+// loads), and each K block's four scales are decoded from there before the barrier that
+// starts the block.  The tile's activations (x rows by token, or h rows by position) are the B
 // operand: each 128-wide K block of the tile's rows is staged in LDS one block ahead (double
 // buffered, rows padded by 16 bytes so the 16 lanes of one read hit distinct banks) and every
 // B fragment is used by the wave's four row blocks.  The MFMA's K order is a permutation
