@@ -237,20 +237,22 @@ __global__ __launch_bounds__(256) void decode_rows(DecodeArgs a) {
 
 // y[r] = sum_j gates[j] * d[j][r] over valid slots in slot order, each product and each sum
 // rounded separately.  One thread per row.
-__global__ __launch_bounds__(256) void combine_exact(const float* __restrict__ d,
-                                                     const int32_t* __restrict__ idx,
-                                                     const float* __restrict__ gates,
-                                                     int32_t topk, int32_t H, int32_t E,
-                                                     float* __restrict__ y) {
+template <int KMAX>
+__global__ __launch_bounds__(64) void combine_exact(const float* __restrict__ d,
+                                                    const int32_t* __restrict__ idx,
+                                                    const float* __restrict__ gates,
+                                                    int32_t topk, int32_t H, int32_t E,
+                                                    float* __restrict__ y) {
   const int r = blockIdx.x * blockDim.x + threadIdx.x;
   if (r >= H) return;
-  float dv[64];
+  // all loads first and unconditional (slots past topk re-read the last one), so they are in
+  // flight together; the sum then takes the valid slots in order
+  float dv[KMAX];
 #pragma unroll
-  for (int j = 0; j < 64; ++j)
-    if (j < topk) dv[j] = expert_ok(idx[j], E) ? d[(size_t)j * H + r] : 0.0f;
+  for (int j = 0; j < KMAX; ++j) dv[j] = d[(size_t)min(j, topk - 1) * H + r];
   float acc = 0.0f;
 #pragma unroll
-  for (int j = 0; j < 64; ++j)
+  for (int j = 0; j < KMAX; ++j)
     if (j < topk && expert_ok(idx[j], E)) acc = acc + gates[j] * dv[j];
   y[r] = acc;
 }
@@ -324,7 +326,11 @@ hipError_t launch_decode_exact(const k3x_pool& p, const uint16_t* x, const int32
                dim3(decode_grid(reinterpret_cast<const void*>(&decode_rows<false>))), dim3(256), 0,
                s, b);
   if (err != hipSuccess) return err;
-  return launch("moe_combine", combine_exact, dim3((p.H + 255) / 256), dim3(256), 0, s,
+  // 64 rows per workgroup spread the rows' loads over many CUs
+  if (topk <= 16)
+    return launch("moe_combine", combine_exact<16>, dim3((p.H + 63) / 64), dim3(64), 0, s,
+                  reinterpret_cast<const float*>(ws + off_d), idx, gates, topk, p.H, p.E, y);
+  return launch("moe_combine", combine_exact<64>, dim3((p.H + 63) / 64), dim3(64), 0, s,
                 reinterpret_cast<const float*>(ws + off_d), idx, gates, topk, p.H, p.E, y);
 }
 
