@@ -12,15 +12,17 @@
 //     bits as a multiply followed by an add);
 //   - the group sum is multiplied by its exact power-of-two scale;
 //   - the group sums are added by a pairwise tree over groups in index order, zero-padded to
-//     a power of two: lane L holds groups 2L and 2L+1 and adds them; lanes then combine with
-//     partners at distance 1, 2, 4, 8, 16, 32, so each addition joins two adjacent subtrees
-//     (IEEE addition is commutative, so which lane holds which operand does not matter).
+//     128 leaves (a zero leaf leaves every sum unchanged, so this is the tree over the groups
+//     padded to any power of two): lane L holds groups L and 64 + L; each half of the tree is
+//     formed by lanes combining with partners at distance 1, 2, 4, 8, 16, 32, so each
+//     addition joins two adjacent subtrees, and the root adds the two halves (IEEE addition
+//     is commutative, so which lane holds which operand does not matter).
 // The exponential inside silu is the float nearest to exp(-g) (evaluated in double), and the
 // combine multiplies and adds with separate roundings.  With these rules the result is a
 // function of the inputs alone, independent of the launch shape.
 //
-// Decode is bound by HBM: each lane streams 32 contiguous bytes (two whole MX groups) of a
-// weight row per load pair, so a wave reads whole rows with fully coalesced 16-byte loads;
+// Decode is bound by HBM: lane L reads group L of a weight row, then group 64 + L, so each
+// load instruction of a wave covers up to 1 KB of the row contiguously (whole cache lines);
 // dequantization is in registers (gfx950 FP4 -> f32 conversion, two weights per
 // instruction) and nothing dequantized is ever written.  Each wave streams a contiguous run
 // of rows (over all slots), with loads running three rows ahead of the arithmetic.
@@ -83,35 +85,41 @@ __device__ __forceinline__ float group_sum(const uint4& q, const float (&x)[32])
   return p;
 }
 
-// bf16 activations of two groups (64 elements at e0) -> floats.
-__device__ __forceinline__ void load_act(const uint16_t* __restrict__ row, int e0, bool ok,
+// bf16 activations of this lane's groups L (x0) and 64 + L (x1) -> floats; zero past the
+// last group.
+__device__ __forceinline__ void load_act(const uint16_t* __restrict__ row, int lane, int ngroups,
                                          float (&x0)[32], float (&x1)[32]) {
 #pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const uint4 v = ok ? *reinterpret_cast<const uint4*>(row + e0 + 8 * c) : make_uint4(0, 0, 0, 0);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    float* dst = c < 4 ? x0 : x1;
-    const int o = (c % 4) * 8;
+  for (int h = 0; h < 2; ++h) {
+    const int g = lane + 64 * h;
+    const bool ok = g < ngroups;
+    float* dst = h ? x1 : x0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      dst[o + 2 * j] = bf16_bits_to_f32(w[j] & 0xFFFFu);
-      dst[o + 2 * j + 1] = bf16_bits_to_f32(w[j] >> 16);
+    for (int c = 0; c < 4; ++c) {
+      const uint4 v =
+          ok ? *reinterpret_cast<const uint4*>(row + 32 * g + 8 * c) : make_uint4(0, 0, 0, 0);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        dst[8 * c + 2 * j] = bf16_bits_to_f32(w[j] & 0xFFFFu);
+        dst[8 * c + 2 * j + 1] = bf16_bits_to_f32(w[j] >> 16);
+      }
     }
   }
 }
 
-// One row of one matrix for this lane: its two groups and their scale bytes.
+// One row of one matrix for this lane: groups L and 64 + L and their scale bytes.
 struct RowBits {
   uint4 q0, q1;
-  uint32_t sc;  // two scale bytes (groups 2L, 2L+1) in the low 16 bits
+  uint32_t s0, s1;
 };
 
-// Leaf of the tree for this lane: (group 2L sum * scale) + (group 2L+1 sum * scale).
-__device__ __forceinline__ float row_leaf(const RowBits& r, const float (&x0)[32],
-                                          const float (&x1)[32]) {
-  const float p0 = group_sum(r.q0, x0) * e8m0_to_f32(r.sc & 0xFFu);
-  const float p1 = group_sum(r.q1, x1) * e8m0_to_f32((r.sc >> 8) & 0xFFu);
-  return p0 + p1;
+// The two leaves of this lane: group L sum * scale (half A) and group 64 + L sum * scale
+// (half B).
+__device__ __forceinline__ void row_leaves(const RowBits& r, const float (&x0)[32],
+                                           const float (&x1)[32], float& la, float& lb) {
+  la = group_sum(r.q0, x0) * e8m0_to_f32(r.s0);
+  lb = group_sum(r.q1, x1) * e8m0_to_f32(r.s1);
 }
 
 // Rows of one wave.  The rows of all slots form one sequence g = slot * rows + r; each die
@@ -131,36 +139,52 @@ __device__ __forceinline__ void wave_rows(int total, int& g0, int& g1) {
   g1 = lo + (int)((int64_t)n * (w + 1) / W);
 }
 
-// Loads row r of one matrix of expert e: wave-uniform row addresses plus a per-lane
-// offset.  Lanes past the last group re-read the row's last 32 bytes; their activations are
-// zero, so their leaves are zero.  The load is unconditional (callers clamp r to a real
-// row), so the loop body has no branches and loads stay in flight across rows.
+// Loads row r of one matrix of expert e: wave-uniform row addresses plus per-lane offsets.
+// Lanes past the last group re-read the row's last 16 bytes (and last scale byte); their
+// activations are zero, so their leaves are zero.  The load is unconditional (callers clamp
+// r to a real row), so the loop body has no branches and loads stay in flight across rows.
+struct LaneOffsets {
+  uint32_t wa, wb, sa, sb;  // weight bytes and scale bytes of groups L and 64 + L
+};
+
 __device__ __forceinline__ void load_row(RowBits& b, const uint8_t* wexp, const uint8_t* sexp,
-                                         int r, uint32_t wrow, uint32_t srow, uint32_t loff,
-                                         uint32_t soff) {
-  const uint4* p = reinterpret_cast<const uint4*>(wexp + (size_t)r * wrow + loff);
-  b.q0 = p[0];
-  b.q1 = p[1];
-  b.sc = *reinterpret_cast<const uint16_t*>(sexp + (size_t)r * srow + soff);
+                                         int r, uint32_t wrow, uint32_t srow,
+                                         const LaneOffsets& o) {
+  const uint8_t* w = wexp + (size_t)r * wrow;
+  const uint8_t* sc = sexp + (size_t)r * srow;
+  b.q0 = *reinterpret_cast<const uint4*>(w + o.wa);
+  b.q1 = *reinterpret_cast<const uint4*>(w + o.wb);
+  b.s0 = sc[o.sa];
+  b.s1 = sc[o.sb];
 }
 
-// Reduce-scatter of four row leaves per vector across the wave, in tree order: distances 1
-// and 2 halve the rows, distances 4 .. 32 finish the sums.  On return v[m][0] of lane L is
-// the full sum of row (L & 3) of vector m.
+// Reduce-scatter of eight leaves per vector (rows 0..3 of half A, then rows 0..3 of half B)
+// across the wave, in tree order: distances 1, 2, 4 halve the set (lane L keeps entry
+// L & 7), distances 8 .. 32 finish each half's tree, and a last exchange at distance 4 adds
+// the two halves of a row.  On return v[m][0] of lane L is the full sum of row (L & 3).
 template <int NV>
-__device__ __forceinline__ void reduce4(float (&v)[NV][4], int lane) {
-  const bool b0 = lane & 1, b1 = (lane >> 1) & 1;
+__device__ __forceinline__ void reduce8(float (&v)[NV][8], int lane) {
+  const bool b0 = lane & 1, b1 = (lane >> 1) & 1, b2 = (lane >> 2) & 1;
 #pragma unroll
   for (int m = 0; m < NV; ++m) {
-    const float k0 = b0 ? v[m][1] : v[m][0], s0 = b0 ? v[m][0] : v[m][1];
-    const float k1 = b0 ? v[m][3] : v[m][2], s1 = b0 ? v[m][2] : v[m][3];
-    const float r0 = k0 + __shfl_xor(s0, 1, kWave);  // rows 0/1 -> row b0
-    const float r1 = k1 + __shfl_xor(s1, 1, kWave);  // rows 2/3 -> row 2 + b0
-    const float k = b1 ? r1 : r0, sd = b1 ? r0 : r1;
-    float t = k + __shfl_xor(sd, 2, kWave);  // row 2 b1 + b0
+    float a[4], c[2];
 #pragma unroll
-    for (int d = 4; d < kWave; d <<= 1) t = t + __shfl_xor(t, d, kWave);
-    v[m][0] = t;
+    for (int j = 0; j < 4; ++j) {  // entries 2j, 2j+1 -> entry 2j + b0
+      const float k = b0 ? v[m][2 * j + 1] : v[m][2 * j];
+      const float s = b0 ? v[m][2 * j] : v[m][2 * j + 1];
+      a[j] = k + __shfl_xor(s, 1, kWave);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {  // -> entry 4j + 2 b1 + b0
+      const float k = b1 ? a[2 * j + 1] : a[2 * j];
+      const float s = b1 ? a[2 * j] : a[2 * j + 1];
+      c[j] = k + __shfl_xor(s, 2, kWave);
+    }
+    const float k = b2 ? c[1] : c[0], s = b2 ? c[0] : c[1];
+    float t = k + __shfl_xor(s, 4, kWave);  // entry L & 7
+#pragma unroll
+    for (int d = 8; d < kWave; d <<= 1) t = t + __shfl_xor(t, d, kWave);
+    v[m][0] = t + __shfl_xor(t, 4, kWave);  // half A + half B of row L & 3
   }
 }
 
@@ -177,15 +201,17 @@ __global__ __launch_bounds__(256) void decode_rows(DecodeArgs a) {
     if (lane == 0) *reinterpret_cast<int64_t*>(a.ws) = __popcll(bad);
   }
   const int ngroups = a.K / kGroup;
-  const bool lane_ok = 2 * lane < ngroups;
   const uint32_t wrow = (uint32_t)a.K / 2, srow = (uint32_t)ngroups;
-  const uint32_t loff = lane_ok ? 32u * lane : wrow - 32u;
-  const uint32_t soff = lane_ok ? 2u * lane : srow - 2u;
+  LaneOffsets lo;
+  lo.wa = lane < ngroups ? 16u * lane : wrow - 16u;
+  lo.wb = lane + 64 < ngroups ? 16u * (lane + 64) : wrow - 16u;
+  lo.sa = lane < ngroups ? (uint32_t)lane : srow - 1u;
+  lo.sb = lane + 64 < ngroups ? (uint32_t)lane + 64u : srow - 1u;
   int g0, g1;
   wave_rows(a.topk * a.rows, g0, g1);
 
   float x0[32], x1[32];
-  if (kW13) load_act(a.act, 64 * lane, lane_ok, x0, x1);
+  if (kW13) load_act(a.act, lane, ngroups, x0, x1);
 
   for (int gs = g0; gs < g1;) {
     const int slot = gs / a.rows;
@@ -194,7 +220,7 @@ __global__ __launch_bounds__(256) void decode_rows(DecodeArgs a) {
     const int e = __builtin_amdgcn_readlane(my_idx, slot);
     gs += n;
     if (!expert_ok(e, a.E)) continue;
-    if (!kW13) load_act(a.act + (size_t)slot * a.K, 64 * lane, lane_ok, x0, x1);
+    if (!kW13) load_act(a.act + (size_t)slot * a.K, lane, ngroups, x0, x1);
     const uint8_t* wa = a.wa + (size_t)e * a.st_wa;
     const uint8_t* sa = a.sa + (size_t)e * a.st_sa;
     const uint8_t* wb = kW13 ? a.wb + (size_t)e * a.st_wb : nullptr;
@@ -202,24 +228,28 @@ __global__ __launch_bounds__(256) void decode_rows(DecodeArgs a) {
     const int rlast = r0 + n - 1;
 
     RowBits A[4] = {}, C[4] = {};
-    auto load = [&](int i, int r) {  // row r into buffer i (rows past the segment re-read rlast)
+    // row r into buffer i (rows past the segment re-read rlast); the scheduling barriers keep
+    // the loads where they stand, three rows ahead of the arithmetic
+    auto load = [&](int i, int r) {
       const int rr = r <= rlast ? r : rlast;
-      load_row(A[i], wa, sa, rr, wrow, srow, loff, soff);
-      if (kW13) load_row(C[i], wb, sb, rr, wrow, srow, loff, soff);
+      __builtin_amdgcn_sched_barrier(0);
+      load_row(A[i], wa, sa, rr, wrow, srow, lo);
+      if (kW13) load_row(C[i], wb, sb, rr, wrow, srow, lo);
+      __builtin_amdgcn_sched_barrier(0);
     };
     load(0, r0);
     load(1, r0 + 1);
     load(2, r0 + 2);
 #pragma unroll 1
     for (int r = r0; r <= rlast; r += 4) {
-      float v[kW13 ? 2 : 1][4];
+      float v[kW13 ? 2 : 1][8];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         load((i + 3) % 4, r + i + 3);
-        v[0][i] = row_leaf(A[i], x0, x1);
-        if (kW13) v[kW13 ? 1 : 0][i] = row_leaf(C[i], x0, x1);
+        row_leaves(A[i], x0, x1, v[0][i], v[0][4 + i]);
+        if (kW13) row_leaves(C[i], x0, x1, v[kW13 ? 1 : 0][i], v[kW13 ? 1 : 0][4 + i]);
       }
-      reduce4(v, lane);
+      reduce8(v, lane);
       if (lane < 4 && r + lane <= rlast) {
         const size_t out = (size_t)slot * a.rows + r + lane;
         if (kW13) {
