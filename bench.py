@@ -45,7 +45,7 @@ ROTATE = 64
 COPY_PROBE_BYTES = 1 << 30
 KERNEL_SOURCES = ("k3x_decode.hip", "k3x_moe.hip", "k3x_prefill.hip", "k3x_router.hip")
 # rocprofv3 kernel names of the library's launch names
-KERNEL_SYMBOLS = {"w13_decode": "decode_rows<true>", "w2_decode": "decode_rows<false>",
+KERNEL_SYMBOLS = {"w13_decode": "decode_w13", "w2_combine_decode": "decode_w2_combine",
                   "w13_prefill": "gemm_prefill<true>", "w2_prefill": "gemm_prefill<false>",
                   "w13_grouped": "gemm_decode<true>", "w2_grouped": "gemm_decode<false>",
                   "route_scores": "route_scores", "route_select": "route_select"}
@@ -67,8 +67,11 @@ def per_kernel_work(name, H, I, E, T, topk, U):
     slots = T * topk
     if name in ("w13_decode", "w13_grouped", "w13_prefill"):
         return U * w13 + T * H * 2 + slots * I * 2, slots * 4.0 * I * H
-    if name in ("w2_decode", "w2_grouped", "w2_prefill"):
+    if name in ("w2_grouped", "w2_prefill"):
         return U * w2 + slots * I * 2 + slots * H * 4, slots * 2.0 * H * I
+    if name == "w2_combine_decode":
+        return (U * w2 + slots * I * 2 + slots * 8 + T * H * 4,
+                slots * 2.0 * H * I + 2.0 * slots * H)
     if name == "route_scores":
         return E * H * 2 + T * H * 2 + T * E * 4, 2.0 * T * E * H
     if name == "route_select":

@@ -147,8 +147,8 @@ size_t k3x_moe_workspace_size(const k3x_pool* p, int32_t T, int32_t topk) {
   if (!p || T < 0 || topk < 1 || topk > 64) return 0;
   if ((int64_t)T * topk > (int64_t)1 << 26) return 0;
   const size_t general = k3x::moe_layout(p->E, p->H, p->I, T, topk).total;
-  size_t off_h, off_d;
-  const size_t exact = k3x::decode_exact_ws(*p, topk, &off_h, &off_d);
+  size_t off_h;
+  const size_t exact = k3x::decode_exact_ws(*p, topk, &off_h);
   return general > exact ? general : exact;
 }
 

@@ -24,8 +24,11 @@
 // Decode is bound by HBM: lane L reads group L of a weight row, then group 64 + L, so each
 // load instruction of a wave covers up to 1 KB of the row contiguously (whole cache lines);
 // dequantization is in registers (gfx950 FP4 -> f32 conversion, two weights per
-// instruction) and nothing dequantized is ever written.  Each wave streams a contiguous run
-// of rows (over all slots), with loads running three rows ahead of the arithmetic.
+// instruction) and nothing dequantized is ever written.  Two launches: W1/W3 (each wave
+// streams a contiguous run of rows over all slots and writes h), then W2 with the weighted
+// combine in its epilogue (each workgroup owns a block of output rows of every slot, so the
+// slot-order sum happens in LDS and the per-slot W2 outputs never reach memory).  Loads run
+// three rows ahead of the arithmetic.
 #include "k3x_internal.h"
 
 // Products and sums below are rounded one at a time unless written as an explicit fma.
@@ -188,30 +191,73 @@ __device__ __forceinline__ void reduce8(float (&v)[NV][8], int lane) {
   }
 }
 
-// W1/W3 mode (kW13): g = W1 x, u = W3 x, h = bf16(silu(g) * u) for every row of the run.
-// W2 mode: d = W2 h with the slot's activations h.  A run is cut at slot boundaries into
-// segments of one expert; within a segment rows are loaded three ahead of the arithmetic
-// and finished four at a time.  A dropped slot's segment is skipped.
-template <bool kW13>
-__global__ __launch_bounds__(256) void decode_rows(DecodeArgs a) {
-  const int lane = threadIdx.x % kWave;
-  const int my_idx = lane < a.topk ? a.idx[lane] : -1;
-  if (kW13 && blockIdx.x == 0 && threadIdx.x < kWave) {
-    const unsigned long long bad = __ballot(lane < a.topk && !expert_ok(my_idx, a.E));
-    if (lane == 0) *reinterpret_cast<int64_t*>(a.ws) = __popcll(bad);
-  }
-  const int ngroups = a.K / kGroup;
-  const uint32_t wrow = (uint32_t)a.K / 2, srow = (uint32_t)ngroups;
+// Per-lane load offsets of a row of K/32 groups (lanes past the last group point at the
+// row's last 16 bytes and last scale byte).
+__device__ __forceinline__ LaneOffsets lane_offsets(int lane, int ngroups, uint32_t wrow,
+                                                    uint32_t srow) {
   LaneOffsets lo;
   lo.wa = lane < ngroups ? 16u * lane : wrow - 16u;
   lo.wb = lane + 64 < ngroups ? 16u * (lane + 64) : wrow - 16u;
   lo.sa = lane < ngroups ? (uint32_t)lane : srow - 1u;
   lo.sb = lane + 64 < ngroups ? (uint32_t)lane + 64u : srow - 1u;
+  return lo;
+}
+
+// Streams rows r0 .. rlast of one expert (one matrix, or W1 and W3 side by side when kW13)
+// against the activations x0/x1: rows are loaded three ahead of the arithmetic and finished
+// four at a time.  For each row, lane (row - r) & 3 of the group of four calls
+// emit(row, sum_a, sum_b) with the row's full dot products (sum_b only when kW13).
+template <bool kW13, typename Emit>
+__device__ __forceinline__ void stream_rows(const uint8_t* wa, const uint8_t* sa,
+                                            const uint8_t* wb, const uint8_t* sb, int r0,
+                                            int rlast, uint32_t wrow, uint32_t srow,
+                                            const LaneOffsets& lo, const float (&x0)[32],
+                                            const float (&x1)[32], int lane, Emit emit) {
+  RowBits A[4] = {}, C[4] = {};
+  // row r into buffer i (rows past the segment re-read rlast); the scheduling barriers keep
+  // the loads where they stand, three rows ahead of the arithmetic
+  auto load = [&](int i, int r) {
+    const int rr = r <= rlast ? r : rlast;
+    __builtin_amdgcn_sched_barrier(0);
+    load_row(A[i], wa, sa, rr, wrow, srow, lo);
+    if (kW13) load_row(C[i], wb, sb, rr, wrow, srow, lo);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  load(0, r0);
+  load(1, r0 + 1);
+  load(2, r0 + 2);
+#pragma unroll 1
+  for (int r = r0; r <= rlast; r += 4) {
+    float v[kW13 ? 2 : 1][8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      load((i + 3) % 4, r + i + 3);
+      row_leaves(A[i], x0, x1, v[0][i], v[0][4 + i]);
+      if (kW13) row_leaves(C[i], x0, x1, v[kW13 ? 1 : 0][i], v[kW13 ? 1 : 0][4 + i]);
+    }
+    reduce8(v, lane);
+    if (lane < 4 && r + lane <= rlast) emit(r + lane, v[0][0], v[kW13 ? 1 : 0][0]);
+  }
+}
+
+// g = W1 x, u = W3 x, h = bf16(silu(g) * u) for every (slot, row) of this wave's run.  A run
+// is cut at slot boundaries into segments of one expert; a dropped slot's segment is skipped.
+// Workgroup 0 also writes the number of dropped slots.
+__global__ __launch_bounds__(256) void decode_w13(DecodeArgs a) {
+  const int lane = threadIdx.x % kWave;
+  const int my_idx = lane < a.topk ? a.idx[lane] : -1;
+  if (blockIdx.x == 0 && threadIdx.x < kWave) {
+    const unsigned long long bad = __ballot(lane < a.topk && !expert_ok(my_idx, a.E));
+    if (lane == 0) *reinterpret_cast<int64_t*>(a.ws) = __popcll(bad);
+  }
+  const int ngroups = a.K / kGroup;
+  const uint32_t wrow = (uint32_t)a.K / 2, srow = (uint32_t)ngroups;
+  const LaneOffsets lo = lane_offsets(lane, ngroups, wrow, srow);
   int g0, g1;
   wave_rows(a.topk * a.rows, g0, g1);
 
   float x0[32], x1[32];
-  if (kW13) load_act(a.act, lane, ngroups, x0, x1);
+  load_act(a.act, lane, ngroups, x0, x1);
 
   for (int gs = g0; gs < g1;) {
     const int slot = gs / a.rows;
@@ -220,83 +266,72 @@ __global__ __launch_bounds__(256) void decode_rows(DecodeArgs a) {
     const int e = __builtin_amdgcn_readlane(my_idx, slot);
     gs += n;
     if (!expert_ok(e, a.E)) continue;
-    if (!kW13) load_act(a.act + (size_t)slot * a.K, lane, ngroups, x0, x1);
-    const uint8_t* wa = a.wa + (size_t)e * a.st_wa;
-    const uint8_t* sa = a.sa + (size_t)e * a.st_sa;
-    const uint8_t* wb = kW13 ? a.wb + (size_t)e * a.st_wb : nullptr;
-    const uint8_t* sb = kW13 ? a.sb + (size_t)e * a.st_sb : nullptr;
-    const int rlast = r0 + n - 1;
+    uint16_t* h = static_cast<uint16_t*>(a.out) + (size_t)slot * a.rows;
+    stream_rows<true>(a.wa + (size_t)e * a.st_wa, a.sa + (size_t)e * a.st_sa,
+                      a.wb + (size_t)e * a.st_wb, a.sb + (size_t)e * a.st_sb, r0, r0 + n - 1,
+                      wrow, srow, lo, x0, x1, lane, [&](int r, float gv, float uv) {
+                        const float ex = (float)exp(-(double)gv);
+                        const float hv = (gv / (1.0f + ex)) * uv;
+                        h[r] = (uint16_t)f32_to_bf16_bits(hv);
+                      });
+  }
+}
 
-    RowBits A[4] = {}, C[4] = {};
-    // row r into buffer i (rows past the segment re-read rlast); the scheduling barriers keep
-    // the loads where they stand, three rows ahead of the arithmetic
-    auto load = [&](int i, int r) {
-      const int rr = r <= rlast ? r : rlast;
-      __builtin_amdgcn_sched_barrier(0);
-      load_row(A[i], wa, sa, rr, wrow, srow, lo);
-      if (kW13) load_row(C[i], wb, sb, rr, wrow, srow, lo);
-      __builtin_amdgcn_sched_barrier(0);
-    };
-    load(0, r0);
-    load(1, r0 + 1);
-    load(2, r0 + 2);
-#pragma unroll 1
-    for (int r = r0; r <= rlast; r += 4) {
-      float v[kW13 ? 2 : 1][8];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        load((i + 3) % 4, r + i + 3);
-        row_leaves(A[i], x0, x1, v[0][i], v[0][4 + i]);
-        if (kW13) row_leaves(C[i], x0, x1, v[kW13 ? 1 : 0][i], v[kW13 ? 1 : 0][4 + i]);
-      }
-      reduce8(v, lane);
-      if (lane < 4 && r + lane <= rlast) {
-        const size_t out = (size_t)slot * a.rows + r + lane;
-        if (kW13) {
-          const float gv = v[0][0], uv = v[kW13 ? 1 : 0][0];
-          const float ex = (float)exp(-(double)gv);
-          const float hv = (gv / (1.0f + ex)) * uv;
-          static_cast<uint16_t*>(a.out)[out] = (uint16_t)f32_to_bf16_bits(hv);
-        } else {
-          static_cast<float*>(a.out)[out] = v[0][0];
-        }
-      }
+// y = sum_j gates[j] * (W2_j h_j) over valid slots in slot order, with the combine in the
+// epilogue: workgroup b owns output rows [b R, b R + R) of every slot, so it holds all the
+// terms of its rows.  Wave w streams the block's rows of slots w, w + 8, ... (one expert
+// each, against that slot's h) and parks d[slot][row] in LDS; after a barrier one thread per
+// row adds the slots in order, each product and each sum rounded separately.  d never
+// reaches memory.
+constexpr int kW2Waves = 8;
+
+__global__ __launch_bounds__(kW2Waves * kWave) void decode_w2_combine(DecodeArgs a,
+                                                                      const float* __restrict__ gates,
+                                                                      float* __restrict__ y,
+                                                                      int32_t R) {
+  extern __shared__ float dsh[];  // [topk][R]
+  const int lane = threadIdx.x % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int my_idx = lane < a.topk ? a.idx[lane] : -1;
+  const float my_gate = lane < a.topk ? gates[lane] : 0.0f;
+  const int rb0 = blockIdx.x * R;
+  const int rlast = rb0 + min(R, a.rows - rb0) - 1;
+  const int nr = rlast - rb0 + 1;
+  const int ngroups = a.K / kGroup;
+  const uint32_t wrow = (uint32_t)a.K / 2, srow = (uint32_t)ngroups;
+  const LaneOffsets lo = lane_offsets(lane, ngroups, wrow, srow);
+
+  float x0[32], x1[32];
+  for (int slot = wave; slot < a.topk; slot += kW2Waves) {
+    const int e = __builtin_amdgcn_readlane(my_idx, slot);
+    if (!expert_ok(e, a.E)) continue;
+    load_act(a.act + (size_t)slot * a.K, lane, ngroups, x0, x1);
+    float* d = dsh + slot * R - rb0;
+    stream_rows<false>(a.wa + (size_t)e * a.st_wa, a.sa + (size_t)e * a.st_sa, nullptr, nullptr,
+                       rb0, rlast, wrow, srow, lo, x0, x1, lane,
+                       [&](int r, float dv, float) { d[r] = dv; });
+  }
+  __syncthreads();
+  if (threadIdx.x < nr) {
+    float acc = 0.0f;
+    for (int j = 0; j < a.topk; ++j) {
+      const int e = __builtin_amdgcn_readlane(my_idx, j);
+      const float g = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_gate), j));
+      if (expert_ok(e, a.E)) acc = acc + g * dsh[j * R + threadIdx.x];
     }
+    y[rb0 + threadIdx.x] = acc;
   }
 }
 
-// y[r] = sum_j gates[j] * d[j][r] over valid slots in slot order, each product and each sum
-// rounded separately.  One thread per row.
-template <int KMAX>
-__global__ __launch_bounds__(64) void combine_exact(const float* __restrict__ d,
-                                                    const int32_t* __restrict__ idx,
-                                                    const float* __restrict__ gates,
-                                                    int32_t topk, int32_t H, int32_t E,
-                                                    float* __restrict__ y) {
-  const int r = blockIdx.x * blockDim.x + threadIdx.x;
-  if (r >= H) return;
-  // all loads first and unconditional (slots past topk re-read the last one), so they are in
-  // flight together; the sum then takes the valid slots in order
-  float dv[KMAX];
-#pragma unroll
-  for (int j = 0; j < KMAX; ++j) dv[j] = d[(size_t)min(j, topk - 1) * H + r];
-  float acc = 0.0f;
-#pragma unroll
-  for (int j = 0; j < KMAX; ++j)
-    if (j < topk && expert_ok(idx[j], E)) acc = acc + gates[j] * dv[j];
-  y[r] = acc;
-}
-
-int decode_grid(const void* fn) {
-  static int cached[2] = {0, 0};
-  const int which = fn == reinterpret_cast<const void*>(&decode_rows<true>) ? 0 : 1;
-  if (!cached[which]) {
-    int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 256, 0) != hipSuccess || per_cu < 1)
-      per_cu = 2;
-    cached[which] = per_cu;
+int decode_w13_grid() {
+  static int per_cu = 0;
+  if (!per_cu) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_w13, 256, 0) != hipSuccess || n < 1)
+      n = 2;
+    per_cu = n;
   }
-  return device_cu_count() * cached[which];
+  return device_cu_count() * per_cu;
 }
 
 }  // namespace
@@ -305,21 +340,19 @@ bool decode_exact_supported(const k3x_pool& p, int32_t T, int32_t topk) {
   return T == 1 && topk <= 64 && p.H / kGroup <= 128 && p.I / kGroup <= 128;
 }
 
-size_t decode_exact_ws(const k3x_pool& p, int32_t topk, size_t* off_h, size_t* off_d) {
+size_t decode_exact_ws(const k3x_pool& p, int32_t topk, size_t* off_h) {
   auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
   size_t off = up(16);
   *off_h = off;
   off = up(off + sizeof(uint16_t) * (size_t)topk * p.I);
-  *off_d = off;
-  off = up(off + sizeof(float) * (size_t)topk * p.H);
   return off;
 }
 
 hipError_t launch_decode_exact(const k3x_pool& p, const uint16_t* x, const int32_t* idx,
                                const float* gates, int32_t topk, float* y, uint8_t* ws,
                                hipStream_t s) {
-  size_t off_h, off_d;
-  decode_exact_ws(p, topk, &off_h, &off_d);
+  size_t off_h;
+  decode_exact_ws(p, topk, &off_h);
   DecodeArgs a{};
   a.wa = p.base[0];
   a.sa = p.base[1];
@@ -337,9 +370,7 @@ hipError_t launch_decode_exact(const k3x_pool& p, const uint16_t* x, const int32
   a.E = p.E;
   a.ws = ws;
   a.out = ws + off_h;
-  hipError_t err = launch("w13_decode", decode_rows<true>,
-                          dim3(decode_grid(reinterpret_cast<const void*>(&decode_rows<true>))),
-                          dim3(256), 0, s, a);
+  hipError_t err = launch("w13_decode", decode_w13, dim3(decode_w13_grid()), dim3(256), 0, s, a);
   if (err != hipSuccess) return err;
   DecodeArgs b = a;
   b.wa = p.base[4];
@@ -351,17 +382,13 @@ hipError_t launch_decode_exact(const k3x_pool& p, const uint16_t* x, const int32
   b.K = p.I;
   b.rows = p.H;
   b.act = reinterpret_cast<const uint16_t*>(ws + off_h);
-  b.out = ws + off_d;
-  err = launch("w2_decode", decode_rows<false>,
-               dim3(decode_grid(reinterpret_cast<const void*>(&decode_rows<false>))), dim3(256), 0,
-               s, b);
-  if (err != hipSuccess) return err;
-  // 64 rows per workgroup spread the rows' loads over many CUs
-  if (topk <= 16)
-    return launch("moe_combine", combine_exact<16>, dim3((p.H + 63) / 64), dim3(64), 0, s,
-                  reinterpret_cast<const float*>(ws + off_d), idx, gates, topk, p.H, p.E, y);
-  return launch("moe_combine", combine_exact<64>, dim3((p.H + 63) / 64), dim3(64), 0, s,
-                reinterpret_cast<const float*>(ws + off_d), idx, gates, topk, p.H, p.E, y);
+  b.out = nullptr;
+  // one workgroup per compute unit, each owning a block of R output rows
+  const int ncu = device_cu_count();
+  const int R = std::min((p.H + ncu - 1) / ncu, kW2Waves * kWave);  // one thread per row
+  const int nblk = (p.H + R - 1) / R;
+  return launch("w2_combine_decode", decode_w2_combine, dim3(nblk), dim3(kW2Waves * kWave),
+                (uint32_t)(sizeof(float) * topk * R), s, b, gates, y, R);
 }
 
 }  // namespace k3x

@@ -116,7 +116,7 @@ hipError_t launch_moe(const k3x_pool& p, const uint16_t* x, int32_t T, const int
 
 // Single-token decode in the reference arithmetic order (k3x_decode.hip).
 bool decode_exact_supported(const k3x_pool& p, int32_t T, int32_t topk);
-size_t decode_exact_ws(const k3x_pool& p, int32_t topk, size_t* off_h, size_t* off_d);
+size_t decode_exact_ws(const k3x_pool& p, int32_t topk, size_t* off_h);
 hipError_t launch_decode_exact(const k3x_pool& p, const uint16_t* x, const int32_t* idx,
                                const float* gates, int32_t topk, float* y, uint8_t* ws,
                                hipStream_t s);

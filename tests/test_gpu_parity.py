@@ -147,6 +147,29 @@ def test_moe_duplicates_and_drops(dev, orc):
     assert k3x.k3x_fetch_drops(ws) == 0
 
 
+@pytest.mark.parametrize("H,I,E,k", [(512, 384, 12, 1), (512, 384, 12, 9), (2560, 2304, 12, 17),
+                                       (2560, 2304, 12, 40), (512, 384, 12, 64)])
+def test_decode_exact_slot_counts(dev, orc, H, I, E, k):
+    """Single-token decode with 1 to 64 slots (duplicates and one dropped slot when k > 1):
+    every workgroup of the W2 + combine launch takes several slots per wave, and the
+    result equals the fp32 oracle's bit for bit."""
+    torch, k3x = dev
+    _log(f"case: exact decode H={H} I={I} E={E} k={k}")
+    host = S.host_pool(11, 0, E, H, I)
+    pool = _pool(torch, k3x, S.device_pool(11, 0, E, H, I), E, H, I)
+    x = S.normal_bf16(11, S.P_X, 0, (1, H))
+    rng = np.random.default_rng(k)
+    idx = rng.integers(0, E, (1, k)).astype(np.int32)
+    if k > 1:
+        idx[0, k // 2] = -1
+    _, gates = S.uniform_routing(11, 1, k, k)
+    y, ws = k3x.moe_forward(pool, _t(torch, x), _t(torch, idx), _t(torch, gates))
+    torch.cuda.synchronize()
+    y_ref, drops = orc.moe_forward(host, x, idx, gates)
+    assert k3x.k3x_fetch_drops(ws) == drops == (1 if k > 1 else 0)
+    assert np.array_equal(_np(y), y_ref)
+
+
 def test_moe_zero_tokens(dev):
     torch, k3x = dev
     _log("case: moe T=0")
