@@ -420,3 +420,13 @@ def test_chain12_reduced_pool(dev, orc):
     torch, k3x = dev
     _log("case: chain of 12 layers, E=64")
     _chain(torch, k3x, orc, 12, 64)
+
+
+def test_chain12_full_size(dev, orc):
+    """The chained workload at its full size: 12 layers of 896 experts with per-layer router
+    weights and Zipf-skewed bias.  Layers are generated one after another (one 15.7 GB pool
+    on the device at a time); each is checked against the oracle on the GPU's own input:
+    RMSNorm bitwise, routing bit-exact, y equal to the fp32 oracle bit for bit."""
+    torch, k3x = dev
+    _log("case: chain of 12 layers, E=896 (full size)")
+    _chain(torch, k3x, orc, 12, 896)
