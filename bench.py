@@ -8,7 +8,9 @@ one decode token through one layer of 896 experts with the router (E = 896, H = 
 I = 3072, top-16).  Inputs are synthetic and seeded (k3x_synth); pools are generated in
 device memory and resident before timing.  Successive steps rotate over 64 different
 tokens, so each step reads a different set of 16 experts and the 256 MB Infinity Cache
-cannot serve them from a previous step.
+cannot serve them from a previous step.  `--workload chain12_t1_e896` runs one decode token
+through 12 layers of 896 experts, all resident (about 188 GB): RMSNorm, router, experts and
+residual add per layer, one graph per starting token.
 
 Two helper modes support `roofline.traffic` (HBM bytes from rocprofv3 counters):
     python bench.py --copy-probe                 # a plain device copy of 1 GiB, run under
@@ -84,6 +86,8 @@ def per_kernel_work(name, H, I, E, T, topk, U):
         return T * H * 4, 3.0 * T * H
     if name == "residual_add_bf16":
         return T * H * 8, 1.0 * T * H
+    if name == "residual_rmsnorm_bf16":
+        return T * H * 10, 4.0 * T * H
     return 0, 0.0
 
 
@@ -124,6 +128,184 @@ def cpu_baseline(w, x, W, b, dev_idx, dev_gates, pool_dev, budget_s=12.0):
                   f"{w.topk} experts each + combine), {t_used:.1f} s of oracle time; expert bytes "
                   f"copied to the host outside the timing",
     }
+
+
+def chain_cpu_baseline(w, x, layers, budget_s=12.0):
+    """The oracle through the chained layers (RMSNorm, router, 16 experts, combine, residual)
+    for a bounded sample of starting tokens, on this host's cores.  Expert bytes are copied
+    from the device pools outside the timing."""
+    import k3x_synth as S
+    import oracle
+
+    n_tok, t_used, i = 0, 0.0, 0
+    while t_used < budget_s:
+        xt = x[i % len(x):i % len(x) + 1].copy()
+        i += 1
+        for lay in layers:
+            t0 = time.perf_counter()
+            xn = oracle.rmsnorm_bf16(xt, 1e-6)
+            idx, gates = oracle.route(xn, lay["W"], lay["b"], w.topk)
+            t_used += time.perf_counter() - t0
+            exps = [S.ExpertBytes(*[lay["pool"][nm][int(e)].cpu().numpy() for nm in S.TENSOR_NAMES])
+                    for e in idx[0]]
+            t0 = time.perf_counter()
+            d = np.stack([oracle.expert_forward(xn[0], ex) for ex in exps])[None]
+            y = oracle.combine(gates, d)
+            xt = oracle.residual_add_bf16(xt, y)
+            t_used += time.perf_counter() - t0
+        n_tok += 1
+    return {
+        "value": n_tok / t_used,
+        "unit": "tokens/s",
+        "cores": oracle.threads(),
+        "kind": "oracle",
+        "sample": f"{n_tok} token(s) through {len(layers)} layers (RMSNorm + router + {w.topk} "
+                  f"experts + combine + residual each), {t_used:.1f} s of oracle time; expert "
+                  f"bytes copied to the host outside the timing",
+    }
+
+
+def bench_chain(w, args, torch, S, k3x):
+    """One decode token through w.layers MoE layers, every layer's experts resident in HBM:
+    RMSNorm -> router -> experts -> residual add per layer, one HIP graph per starting token."""
+    steps = args.steps if args.steps is not None else 50
+    warmup = args.warmup if args.warmup is not None else 5
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    free, _ = torch.cuda.mem_get_info(dev)
+    need = w.layers * w.E * S.expert_bytes_per_expert(w.H, w.I)
+    if free < need + (2 << 30):
+        sys.exit(f"the chained workload needs {need / 1e9:.1f} GB of device memory, "
+                 f"{free / 1e9:.1f} GB free")
+    log(f"generating {w.layers} layers: E={w.E} H={w.H} I={w.I} ({need / 1e9:.1f} GB)")
+    layers = []
+    for layer in range(w.layers):
+        pool_dev = S.device_pool(w.seed, layer, w.E, w.H, w.I)
+        W, b = S.router_inputs(w, layer)
+        Wd = torch.from_numpy(W.view(np.int16)).to(dev)
+        bd = torch.from_numpy(b).to(dev)
+        layers.append({"pool_dev": pool_dev, "W": W, "b": b, "Wd": Wd, "bd": bd,
+                       "pool": k3x.k3x_expert_pool_create(pool_dev, hidden=w.H, inter=w.I,
+                                                          n_experts=w.E),
+                       "rdesc": k3x.router_desc(Wd, bd, w.topk)})
+    R = ROTATE
+    x = S.normal_bf16(w.seed, S.P_X, 0, (R, w.H))
+    xs = [torch.from_numpy(x[r:r + 1].view(np.int16)).to(dev) for r in range(R)]
+    xb = torch.empty((1, w.H), dtype=torch.int16, device=dev)   # residual stream
+    xn = torch.empty_like(xb)
+    idx = torch.empty((1, w.topk), dtype=torch.int32, device=dev)
+    gates = torch.empty((1, w.topk), dtype=torch.float32, device=dev)
+    y = torch.empty((1, w.H), dtype=torch.float32, device=dev)
+    ws = k3x.alloc_workspace(k3x.k3x_moe_workspace_size(layers[0]["pool"], 1, w.topk), dev)
+    rws = k3x.alloc_workspace(k3x.k3x_route_workspace_size(layers[0]["rdesc"], 1), dev)
+
+    def step(r):
+        # layer l's residual update and layer l + 1's RMSNorm are one fused launch
+        xb.copy_(xs[r])
+        k3x.k3x_rmsnorm_bf16(xb, 1, w.H, 1e-6, xn)
+        for li, lay in enumerate(layers):
+            k3x.k3x_route_topk(lay["rdesc"], xn, 1, idx, gates, rws)
+            k3x.k3x_moe_forward(lay["pool"], xn, 1, idx, gates, w.topk, y, ws)
+            if li + 1 < len(layers):
+                k3x.k3x_residual_add_rmsnorm_bf16(xb, y, 1, w.H, 1e-6, xn)
+            else:
+                k3x.k3x_residual_add_bf16(xb, y, 1, w.H)
+
+    out_eager = []
+    for r in range(R):
+        step(r)
+        torch.cuda.synchronize()
+        out_eager.append(xb.clone())
+    if k3x.k3x_fetch_drops(ws):
+        sys.exit("run invalid: dropped slots")
+    graphs = []
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(0)
+    torch.cuda.current_stream().wait_stream(side)
+    for r in range(R):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(r)
+        graphs.append(g)
+    for r in range(R):
+        graphs[r].replay()
+        torch.cuda.synchronize()
+        if not torch.equal(xb, out_eager[r]):
+            sys.exit(f"graph replay of token {r} differs from the eager result")
+        step((r + 1) % R)
+        torch.cuda.synchronize()
+
+    for i in range(warmup):
+        graphs[i % R].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        graphs[i % R].replay()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    prof = k3x.k3x_profiler_create(steps * w.layers * 8 + 16)
+    torch.cuda.synchronize()
+    k3x.k3x_profiler_attach(prof)
+    for i in range(steps):
+        step(i % R)
+    torch.cuda.synchronize()
+    k3x.k3x_profiler_attach(None)
+    durs = k3x.profiler_durations(prof)
+    k3x.k3x_profiler_destroy(prof)
+
+    kernels = {}
+    for name, ms in durs.items():
+        nbytes, flops = per_kernel_work(name, w.H, w.I, w.E, 1, w.topk, w.topk)
+        avg_s = float(np.mean(ms)) * 1e-3
+        kernels[name] = {"launches": len(ms), "avg_us": round(avg_s * 1e6, 3),
+                         "alg_bytes": int(nbytes), "gbps": round(nbytes / avg_s / 1e9, 1),
+                         "tflops": round(flops / avg_s / 1e12, 2)}
+    dominant = max(kernels, key=lambda n: kernels[n]["avg_us"] * kernels[n]["launches"])
+    dk = kernels[dominant]
+    traffic = traffic_for(w.name, dominant)
+    roof = {"bound": "hbm", "achieved": dk["gbps"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(dk["gbps"] / PEAK_HBM_GBS, 4),
+            "traffic": int(traffic) if traffic is not None else None, "kernel": dominant,
+            "alg_bytes": dk["alg_bytes"]}
+    w13, w2 = expert_tensor_bytes(w.H, w.I)
+    layer_bytes = w.topk * (w13 + w2) + w.E * w.H * 2 + w.E * 4 + w.H * (2 + 4)
+    path_bytes = w.layers * layer_bytes
+    ksum = sum(k["avg_us"] * k["launches"] for k in kernels.values()) / steps * 1e-6
+    out = {
+        "metric": METRIC,
+        "value": round(steps / wall, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(wall / steps * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "tokens": 1, "layers": w.layers, "experts": w.E,
+                   "hidden": w.H, "inter": w.I, "topk": w.topk, "router": True,
+                   "zipf_bias": w.zipf, "weights": "mxfp4 (e2m1 + e8m0 per 32)",
+                   "resident_expert_gb": round(need / 1e9, 1), "rotated_batches": R},
+        "roofline": roof,
+        "path": {"kernel_sum_us": round(ksum * 1e6, 3),
+                 "alg_bytes_per_step": int(path_bytes),
+                 "hbm_gbps_kernel_sum": round(path_bytes / ksum / 1e9, 1),
+                 "hbm_frac_kernel_sum": round(path_bytes / ksum / 1e9 / PEAK_HBM_GBS, 4),
+                 "hbm_gbps_wall": round(path_bytes / (wall / steps) / 1e9, 1),
+                 "timed_region": "HIP graph replay, one graph per starting token"},
+        "kernels": kernels,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the oracle on the host (bounded sample)")
+        out["cpu_baseline"] = chain_cpu_baseline(
+            w, x, [{"W": l_["W"], "b": l_["b"], "pool": l_["pool_dev"]} for l_ in layers])
+    print(json.dumps(out), flush=True)
 
 
 def sources_hash():
@@ -231,7 +413,7 @@ def main():
         sys.exit(f"unknown workload {args.workload}; one of {sorted(wl)}")
     w = wl[args.workload]
     if w.layers != 1:
-        sys.exit("the chained workload is a parity case; bench one of the single-layer workloads")
+        return bench_chain(w, args, torch, S, k3x)
     prefill = w.T > 64
     steps = args.steps if args.steps is not None else (20 if prefill else 200)
     warmup = args.warmup if args.warmup is not None else (3 if prefill else 20)

@@ -158,6 +158,16 @@ k3x_status k3x_rmsnorm_bf16(const void *x, int32_t T, int32_t H, float eps, void
  * multiple of 8. */
 k3x_status k3x_residual_add_bf16(void *x, const float *y, int32_t T, int32_t H, void *stream);
 
+/* The residual update of one layer fused with the RMSNorm that starts the next:
+ * x[t][h] <- bf16_rne(float(x[t][h]) + y[t][h]), then out[t] <- RMSNorm(x[t]) exactly as
+ * k3x_rmsnorm_bf16 computes it (same summation order), so the results equal those of
+ * k3x_residual_add_bf16 followed by k3x_rmsnorm_bf16 bit for bit, in one launch.
+ * x bf16 [T][H] (updated in place), y fp32 [T][H], out bf16 [T][H]; all 16-byte aligned;
+ * out must not overlap x or y (K3X_E_INVALID_ARG); H a multiple of 8, <= 16384
+ * (K3X_E_UNSUPPORTED). */
+k3x_status k3x_residual_add_rmsnorm_bf16(void *x, const float *y, int32_t T, int32_t H,
+                                         float eps, void *out, void *stream);
+
 /* ------------------------------------------------------------------------------------------
  * Kernel timing (instrumentation only; the work done is unchanged).  While a profiler is
  * attached to the calling thread, every kernel the library enqueues from that thread is

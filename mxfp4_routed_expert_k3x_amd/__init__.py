@@ -63,7 +63,7 @@ class k3x_router_desc(ctypes.Structure):
 EXPORTS = (
     "k3x_status_str", "k3x_last_error", "k3x_expert_pool_create", "k3x_expert_pool_destroy",
     "k3x_route_workspace_size", "k3x_route_topk", "k3x_moe_workspace_size", "k3x_moe_forward",
-    "k3x_fetch_drops", "k3x_rmsnorm_bf16", "k3x_residual_add_bf16",
+    "k3x_fetch_drops", "k3x_rmsnorm_bf16", "k3x_residual_add_bf16", "k3x_residual_add_rmsnorm_bf16",
     "k3x_profiler_create", "k3x_profiler_destroy", "k3x_profiler_attach", "k3x_profiler_reset",
     "k3x_profiler_count", "k3x_profiler_read",
 )
@@ -102,6 +102,8 @@ def load_library(path: str = LIB_PATH):
     L.k3x_rmsnorm_bf16.argtypes = [P, I32, I32, ctypes.c_float, P, P]
     L.k3x_residual_add_bf16.restype = ctypes.c_int
     L.k3x_residual_add_bf16.argtypes = [P, P, I32, I32, P]
+    L.k3x_residual_add_rmsnorm_bf16.restype = ctypes.c_int
+    L.k3x_residual_add_rmsnorm_bf16.argtypes = [P, P, I32, I32, ctypes.c_float, P, P]
     L.k3x_profiler_create.restype = ctypes.c_int
     L.k3x_profiler_create.argtypes = [I32, ctypes.POINTER(P)]
     L.k3x_profiler_destroy.restype = None
@@ -249,6 +251,11 @@ def k3x_rmsnorm_bf16(x, T: int, H: int, eps: float, out, stream=None):
 
 def k3x_residual_add_bf16(x, y, T: int, H: int, stream=None):
     _check(lib().k3x_residual_add_bf16(_ptr(x), _ptr(y), int(T), int(H), _stream(stream)))
+
+
+def k3x_residual_add_rmsnorm_bf16(x, y, T: int, H: int, eps: float, out, stream=None):
+    _check(lib().k3x_residual_add_rmsnorm_bf16(_ptr(x), _ptr(y), int(T), int(H), float(eps),
+                                               _ptr(out), _stream(stream)))
 
 
 # ------------------------------------------------------------------------------------------

@@ -211,6 +211,25 @@ k3x_status k3x_residual_add_bf16(void* x, const float* y, int32_t T, int32_t H, 
   return K3X_OK;
 }
 
+k3x_status k3x_residual_add_rmsnorm_bf16(void* x, const float* y, int32_t T, int32_t H,
+                                          float eps, void* out, void* stream) {
+  if (T < 0 || H <= 0) return fail(K3X_E_INVALID_ARG, "residual_add_rmsnorm: T %d, H %d", T, H);
+  if (H % 8 || H > 16384)
+    return fail(K3X_E_UNSUPPORTED, "residual_add_rmsnorm: H %d must be a multiple of 8, <= 16384", H);
+  if (T == 0) return K3X_OK;
+  if (!x || !y || !out) return fail(K3X_E_INVALID_ARG, "residual_add_rmsnorm: NULL x, y or out");
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(out, 16))
+    return fail(K3X_E_UNSUPPORTED, "residual_add_rmsnorm: 16-byte alignment");
+  const uintptr_t xb = (uintptr_t)T * (uintptr_t)H * 2, yb = (uintptr_t)T * (uintptr_t)H * 4;
+  const uintptr_t xo = (uintptr_t)x, yo = (uintptr_t)y, oo = (uintptr_t)out;
+  if ((oo < xo + xb && xo < oo + xb) || (oo < yo + yb && yo < oo + xb))
+    return fail(K3X_E_INVALID_ARG, "residual_add_rmsnorm: out overlaps x or y");
+  hipError_t e = k3x::launch_residual_rmsnorm(static_cast<uint16_t*>(x), y, T, H, eps,
+                                              static_cast<uint16_t*>(out), (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "residual_add_rmsnorm");
+  return K3X_OK;
+}
+
 }  // extern "C"
 
 // ---------------------------------------------------------------------------------------

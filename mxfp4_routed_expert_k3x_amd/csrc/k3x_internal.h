@@ -144,6 +144,8 @@ hipError_t launch_rmsnorm(const uint16_t* x, int32_t T, int32_t H, float eps, ui
                           hipStream_t s);
 
 hipError_t launch_residual(uint16_t* x, const float* y, int32_t T, int32_t H, hipStream_t s);
+hipError_t launch_residual_rmsnorm(uint16_t* x, const float* y, int32_t T, int32_t H, float eps,
+                                   uint16_t* out, hipStream_t s);
 
 int device_cu_count();
 

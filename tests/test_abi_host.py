@@ -144,6 +144,18 @@ def test_norm_helpers_host_validation(k3x):
     assert lib.k3x_rmsnorm_bf16(fake, 0, 3584, 1e-6, fake, None) == 0
     assert lib.k3x_residual_add_bf16(fake, fake, 1, 3583, None) == -2
     assert lib.k3x_residual_add_bf16(None, fake, 1, 3584, None) == -1
+    f = ctypes.c_float(1e-6)
+    fused = lib.k3x_residual_add_rmsnorm_bf16
+    assert fused(fake, fake + (1 << 20), 1, 3583, f, fake + (2 << 20), None) == -2
+    assert fused(fake, fake + (1 << 20), 1, 16392, f, fake + (2 << 20), None) == -2
+    assert fused(fake, fake + (1 << 20), -1, 3584, f, fake + (2 << 20), None) == -1
+    assert fused(fake, fake + (1 << 20), 0, 3584, f, fake + (2 << 20), None) == 0
+    assert fused(None, fake + (1 << 20), 1, 3584, f, fake + (2 << 20), None) == -1
+    assert fused(fake, fake + (1 << 20), 1, 3584, f, fake + 8, None) == -2  # misaligned out
+    # out overlapping x (same buffer, or partly) or y is refused before any launch
+    assert fused(fake, fake + (1 << 20), 1, 3584, f, fake, None) == -1
+    assert fused(fake, fake + (1 << 20), 2, 3584, f, fake + 7168, None) == -1
+    assert fused(fake, fake + (1 << 20), 1, 3584, f, fake + (1 << 20) + 4096, None) == -1
     assert lib.k3x_fetch_drops(None, None, None) == -1
 
 

@@ -379,6 +379,17 @@ def test_rmsnorm_and_residual_bitwise(dev, orc):
     torch.cuda.synchronize()
     assert np.array_equal(_np(out, np.uint16), orc.rmsnorm_bf16(x, 1e-6))
     assert np.array_equal(_np(xr, np.uint16), orc.residual_add_bf16(x, y))
+    # the fused residual + RMSNorm: both outputs equal the oracle's two steps bit for bit
+    for H2 in (H, 8200):  # 8200 > 64 * 8 * 8 takes the wide variant
+        x2 = S.normal_bf16(9, S.P_X, 0, (T, H2))
+        y2 = np.random.default_rng(9).standard_normal((T, H2)).astype(np.float32) * 30
+        xf, yf = _t(torch, x2), _t(torch, y2)
+        nf = torch.empty_like(xf)
+        k3x.k3x_residual_add_rmsnorm_bf16(xf, yf, T, H2, 1e-6, nf)
+        torch.cuda.synchronize()
+        x_ref = orc.residual_add_bf16(x2, y2)
+        assert np.array_equal(_np(xf, np.uint16), x_ref), H2
+        assert np.array_equal(_np(nf, np.uint16), orc.rmsnorm_bf16(x_ref, 1e-6)), H2
 
 
 def _chain(torch, k3x, orc, L, E, log_every=True):
@@ -387,16 +398,21 @@ def _chain(torch, k3x, orc, L, E, log_every=True):
     x = S.activations(w)
     xd = _t(torch, x)
     worst = 0.0
+    # layer l's residual update and layer l + 1's RMSNorm run as one fused launch
+    xn = torch.empty_like(xd)
+    k3x.k3x_rmsnorm_bf16(xd, 1, H, 1e-6, xn)
     for layer in range(L):
         pool = _pool(torch, k3x, S.device_pool(w.seed, layer, E, H, I), E, H, I)
         W = S.normal_bf16(w.seed, S.P_WR, layer, (E, H), std=0.02)
         b = S.zipf_bias(w.seed, E, layer)
         x_in = _np(xd, np.uint16).copy()
-        xn = torch.empty_like(xd)
-        k3x.k3x_rmsnorm_bf16(xd, 1, H, 1e-6, xn)
         idx, gates, _ = k3x.route_topk(_t(torch, W), _t(torch, b), xn, k)
         y, _ = k3x.moe_forward(pool, xn, idx, gates)
-        k3x.k3x_residual_add_bf16(xd, y, 1, H)
+        if layer + 1 < L:
+            xn_next = torch.empty_like(xd)
+            k3x.k3x_residual_add_rmsnorm_bf16(xd, y, 1, H, 1e-6, xn_next)
+        else:
+            k3x.k3x_residual_add_bf16(xd, y, 1, H)
         torch.cuda.synchronize()
         # teacher forcing: the oracle takes this layer's GPU input
         xn_ref = orc.rmsnorm_bf16(x_in, 1e-6)
@@ -407,6 +423,9 @@ def _chain(torch, k3x, orc, L, E, log_every=True):
         y_ref = oracle_forward_sampled(orc, w.seed, layer, H, I, xn_ref, i_ref, g_ref, [0])
         rel, mx = assert_y_close(_np(y), y_ref, f"layer {layer}")
         assert np.array_equal(_np(y), y_ref), f"layer {layer}: differs from the fp32 oracle"
+        assert np.array_equal(_np(xd, np.uint16), orc.residual_add_bf16(x_in, y_ref)), layer
+        if layer + 1 < L:
+            xn = xn_next
         worst = max(worst, rel)
         if log_every:
             _log(f"  layer {layer}: rel_l2={rel:.3e} max_abs={mx:.3e}")
