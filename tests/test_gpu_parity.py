@@ -256,6 +256,34 @@ def test_router_many_equal_scores(dev, orc):
     assert list(i_ref[0, :16]) == list(range(100, 116))
 
 
+def test_router_selection_paths(dev, orc):
+    """Selection at the boundaries of its register layouts (E up to 1024 and beyond, topk up
+    to 64 and beyond), ragged token counts, and biases that make +0 and -0 selection
+    scores compare equal."""
+    torch, k3x = dev
+    for E, k, T in ((1024, 64, 7), (1024, 65, 3), (1025, 16, 5), (64, 64, 6), (2048, 16, 9)):
+        _log(f"case: router selection E={E} topk={k} T={T}")
+        H = 256
+        W = S.normal_bf16(E + k, S.P_WR, 0, (E, H), std=0.05)
+        b = S.normal_f32(E + k, S.P_BIAS, 0, (E,), std=0.01)
+        x = S.normal_bf16(E + k, S.P_X, 0, (T, H))
+        idx, gates, i_ref, g_ref = _route_both(torch, k3x, orc, x, W, b, k)
+        assert np.array_equal(idx, i_ref), (E, k, T)
+        assert np.array_equal(gates.view(np.uint32), g_ref.view(np.uint32)), (E, k, T)
+    # zero router rows with zero bias next to equal ones with bias -0.0: score + bias is +0.5
+    # or 0.5 + -0.0 = +0.5, so the keys tie and the lower index wins
+    E, H = 128, 64
+    W = S.normal_bf16(5, S.P_WR, 0, (E, H), std=0.05)
+    W[10:20] = 0
+    b = np.zeros(E, dtype=np.float32)
+    b[10:15] = np.float32(-0.0)
+    b[20:] = -1.0
+    x = S.normal_bf16(5, S.P_X, 0, (4, H))
+    idx, gates, i_ref, g_ref = _route_both(torch, k3x, orc, x, W, b, 8)
+    assert np.array_equal(idx, i_ref)
+    assert np.array_equal(gates.view(np.uint32), g_ref.view(np.uint32))
+
+
 # ------------------------------------------------------------------------------------------
 # the five workloads at full size (sampled tokens where the oracle would take minutes)
 # ------------------------------------------------------------------------------------------
