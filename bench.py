@@ -82,6 +82,10 @@ def per_kernel_work(name, H, I, E, T, topk, U):
         return slots * H * 4 + T * H * 4 + slots * 8, 2.0 * slots * H
     if name == "moe_sort":
         return slots * 4 * 2, 0.0
+    if name in ("sort_count", "sort_scatter"):
+        return slots * 4 * (1 if name == "sort_count" else 3), 0.0
+    if name == "sort_scan":
+        return 64 * E * 4 * 2, 0.0
     if name == "rmsnorm_bf16":
         return T * H * 4, 3.0 * T * H
     if name == "residual_add_bf16":

@@ -84,9 +84,11 @@ struct MoeLayout {
   size_t inv;         // int32 [T * topk] position of each slot in perm, -1 if dropped
   size_t h;           // bf16 [T * topk][I]
   size_t d;           // fp32 [T * topk][H]
+  size_t sort_parts;  // int32 [sort_n][E] per-part expert counts (then cursors) + [sort_n] drops
   size_t total;
   int32_t max_tiles;
   int32_t tile_tokens;
+  int32_t sort_n;     // parts of the split sort (0: one workgroup sorts everything)
 };
 
 MoeLayout moe_layout(int32_t E, int32_t H, int32_t I, int32_t T, int32_t topk);

@@ -6,8 +6,8 @@
 //
 // Pipeline of one forward (all on the caller's stream):
 //   1. moe_sort   (T > 1 only) slots (t, j) counted per expert, laid out expert by expert,
-//                 cut into tiles of at most 16 slots of one expert; counts drops.  With
-//                 T = 1 every slot is its own tile and the W13 kernel counts the drops.
+//                 cut into tiles of one expert; counts drops.  Batches of 8192 slots or more
+//                 take the split sort (count per slice, one scan, scatter per slice).
 //   2. w13        per tile and 32 rows: g = W1 x, u = W3 x, h = bf16(silu(g) * u)
 //   3. w2         per tile and 64 rows: d = W2 h
 //   4. combine    y[t] = sum_j gate[t][j] * d[t][j] in slot order, invalid slots skipped
@@ -24,6 +24,11 @@
 #include "k3x_internal.h"
 
 namespace k3x {
+
+// Large batches sort in three launches over kSortParts slices of the slots (count per slice,
+// one scan, scatter per slice); smaller ones in one workgroup.
+constexpr int kSortParts = 64;
+constexpr int kSortSplitMin = 8192;
 
 MoeLayout moe_layout(int32_t E, int32_t H, int32_t I, int32_t T, int32_t topk) {
   auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
@@ -48,6 +53,9 @@ MoeLayout moe_layout(int32_t E, int32_t H, int32_t I, int32_t T, int32_t topk) {
   off = up(off + sizeof(uint16_t) * slots * (size_t)I);
   L.d = off;
   off = up(off + sizeof(float) * slots * (size_t)H);
+  L.sort_n = slots >= (size_t)kSortSplitMin ? kSortParts : 0;
+  L.sort_parts = off;
+  off = up(off + sizeof(int32_t) * (size_t)L.sort_n * ((size_t)E + 1));
   L.total = off;
   return L;
 }
@@ -141,6 +149,133 @@ __global__ __launch_bounds__(kSortThreads) void moe_sort(SortArgs a) {
     int pos = -1;
     if (e >= 0 && e < E) {
       pos = atomicAdd(&counts[e], 1);
+      perm[pos] = p;
+    }
+    inv[p] = pos;
+  }
+}
+
+// Split sort for large batches.  Slice g of the slots (kSortParts slices) is counted by
+// workgroup g into parts[g][e]; one workgroup then forms the expert totals, offsets and tiles
+// as moe_sort does and turns parts[g][e] into the first position of slice g's slots of expert
+// e; workgroup g finally scatters its slice from those cursors.  No workgroup waits on
+// another inside a launch.
+constexpr int kSplitThreads = 256;
+
+struct SplitArgs {
+  const int32_t* idx;
+  int32_t n_slots, E, tile_tokens;
+  uint8_t* ws;
+  size_t off_offsets, off_tiles, off_perm, off_inv, off_parts;
+};
+
+__device__ __forceinline__ void slice_of(int n_slots, int& p0, int& p1) {
+  const int chunk = (n_slots + kSortParts - 1) / kSortParts;
+  p0 = min(n_slots, (int)blockIdx.x * chunk);
+  p1 = min(n_slots, p0 + chunk);
+}
+
+__global__ __launch_bounds__(kSplitThreads) void sort_count(SplitArgs a) {
+  extern __shared__ int32_t cnt[];  // [E]
+  __shared__ int32_t drops;
+  int32_t* parts = reinterpret_cast<int32_t*>(a.ws + a.off_parts);
+  for (int e = threadIdx.x; e < a.E; e += kSplitThreads) cnt[e] = 0;
+  if (threadIdx.x == 0) drops = 0;
+  __syncthreads();
+  int p0, p1;
+  slice_of(a.n_slots, p0, p1);
+  for (int p = p0 + threadIdx.x; p < p1; p += kSplitThreads) {
+    const int e = a.idx[p];
+    if (e >= 0 && e < a.E)
+      atomicAdd(&cnt[e], 1);
+    else
+      atomicAdd(&drops, 1);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < a.E; e += kSplitThreads) parts[(size_t)blockIdx.x * a.E + e] = cnt[e];
+  if (threadIdx.x == 0) parts[(size_t)kSortParts * a.E + blockIdx.x] = drops;
+}
+
+__global__ __launch_bounds__(kSortThreads) void sort_scan(SplitArgs a) {
+  __shared__ int32_t scan_c[kSortThreads];
+  __shared__ int32_t scan_t[kSortThreads];
+  const int tid = threadIdx.x;
+  const int E = a.E;
+  int32_t* offsets = reinterpret_cast<int32_t*>(a.ws + a.off_offsets);
+  int32_t* tiles = reinterpret_cast<int32_t*>(a.ws + a.off_tiles);
+  int32_t* parts = reinterpret_cast<int32_t*>(a.ws + a.off_parts);
+  const int per = (E + kSortThreads - 1) / kSortThreads;
+  const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
+  auto total_of = [&](int e) {
+    int c = 0;
+#pragma unroll 16
+    for (int g = 0; g < kSortParts; ++g) c += parts[(size_t)g * E + e];
+    return c;
+  };
+  int csum = 0, tsum = 0;
+  for (int e = e0; e < e1; ++e) {
+    const int c = total_of(e);
+    csum += c;
+    tsum += (c + a.tile_tokens - 1) / a.tile_tokens;
+  }
+  scan_c[tid] = csum;
+  scan_t[tid] = tsum;
+  __syncthreads();
+  for (int o = 1; o < kSortThreads; o <<= 1) {
+    const int vc = tid >= o ? scan_c[tid - o] : 0;
+    const int vt = tid >= o ? scan_t[tid - o] : 0;
+    __syncthreads();
+    scan_c[tid] += vc;
+    scan_t[tid] += vt;
+    __syncthreads();
+  }
+  int bc = scan_c[tid] - csum;
+  int bt = scan_t[tid] - tsum;
+  for (int e = e0; e < e1; ++e) {
+    offsets[e] = bc;
+    int run = bc;
+#pragma unroll 16
+    for (int g = 0; g < kSortParts; ++g) {  // slice g's first position among expert e's slots
+      const int c = parts[(size_t)g * E + e];
+      parts[(size_t)g * E + e] = run;
+      run += c;
+    }
+    const int c = run - bc;
+    const int nt = (c + a.tile_tokens - 1) / a.tile_tokens;
+    for (int i = 0; i < nt; ++i) {
+      int4 tv;
+      tv.x = e;
+      tv.y = bc + i * a.tile_tokens;
+      tv.z = min(a.tile_tokens, c - i * a.tile_tokens);
+      tv.w = 0;
+      reinterpret_cast<int4*>(tiles)[bt + i] = tv;
+    }
+    bc += c;
+    bt += nt;
+  }
+  if (tid == kSortThreads - 1) {
+    offsets[E] = scan_c[kSortThreads - 1];
+    int64_t dr = 0;
+    for (int g = 0; g < kSortParts; ++g) dr += parts[(size_t)kSortParts * E + g];
+    *reinterpret_cast<int64_t*>(a.ws) = dr;
+    *reinterpret_cast<int32_t*>(a.ws + 8) = scan_t[kSortThreads - 1];
+  }
+}
+
+__global__ __launch_bounds__(kSplitThreads) void sort_scatter(SplitArgs a) {
+  extern __shared__ int32_t cur[];  // [E]
+  int32_t* perm = reinterpret_cast<int32_t*>(a.ws + a.off_perm);
+  int32_t* inv = reinterpret_cast<int32_t*>(a.ws + a.off_inv);
+  const int32_t* parts = reinterpret_cast<const int32_t*>(a.ws + a.off_parts);
+  for (int e = threadIdx.x; e < a.E; e += kSplitThreads) cur[e] = parts[(size_t)blockIdx.x * a.E + e];
+  __syncthreads();
+  int p0, p1;
+  slice_of(a.n_slots, p0, p1);
+  for (int p = p0 + threadIdx.x; p < p1; p += kSplitThreads) {
+    const int e = a.idx[p];
+    int pos = -1;
+    if (e >= 0 && e < a.E) {
+      pos = atomicAdd(&cur[e], 1);
       perm[pos] = p;
     }
     inv[p] = pos;
@@ -424,8 +559,21 @@ hipError_t launch_moe(const k3x_pool& p, const uint16_t* x, int32_t T, const int
     sa.off_perm = L.perm;
     sa.off_inv = L.inv;
     const size_t sort_lds = sizeof(int32_t) * (size_t)p.E;
-    err = launch("moe_sort", moe_sort, dim3(1), dim3(kSortThreads), (uint32_t)sort_lds, s, sa);
-    if (err != hipSuccess || T == 0) return err;
+    if (L.sort_n) {
+      SplitArgs b{idx, T * topk, p.E, L.tile_tokens, ws, L.offsets, L.tiles, L.perm, L.inv,
+                  L.sort_parts};
+      err = launch("sort_count", sort_count, dim3(kSortParts), dim3(kSplitThreads),
+                   (uint32_t)sort_lds, s, b);
+      if (err == hipSuccess)
+        err = launch("sort_scan", sort_scan, dim3(1), dim3(kSortThreads), 0, s, b);
+      if (err == hipSuccess)
+        err = launch("sort_scatter", sort_scatter, dim3(kSortParts), dim3(kSplitThreads),
+                     (uint32_t)sort_lds, s, b);
+      if (err != hipSuccess) return err;
+    } else {
+      err = launch("moe_sort", moe_sort, dim3(1), dim3(kSortThreads), (uint32_t)sort_lds, s, sa);
+      if (err != hipSuccess || T == 0) return err;
+    }
   }
 
   if (L.tile_tokens > 16) {

@@ -170,6 +170,30 @@ def test_decode_exact_slot_counts(dev, orc, H, I, E, k):
     assert np.array_equal(_np(y), y_ref)
 
 
+@pytest.mark.parametrize("T,H,I,E,k", [(1030, 256, 256, 6, 8), (1100, 512, 512, 40, 8)])
+def test_moe_split_sort(dev, orc, T, H, I, E, k):
+    """Batches of 8192 slots or more are sorted in slices (count, scan, scatter): duplicates
+    within tokens, out-of-range ids counted as drops, on the grouped path (H = 256) and the
+    prefill path (H = 512)."""
+    torch, k3x = dev
+    _log(f"case: split sort T={T} H={H} I={I} E={E} k={k}")
+    host = S.host_pool(17, 0, E, H, I)
+    pool = _pool(torch, k3x, S.device_pool(17, 0, E, H, I), E, H, I)
+    x = S.normal_bf16(17, S.P_X, 0, (T, H))
+    rng = np.random.default_rng(T)
+    idx = rng.integers(0, E, (T, k)).astype(np.int32)
+    idx[5, 3] = -1
+    idx[700, 0] = E
+    idx[T - 1, k - 1] = 1 << 20
+    _, gates = S.uniform_routing(17, T, k, k)
+    y, ws = k3x.moe_forward(pool, _t(torch, x), _t(torch, idx), _t(torch, gates))
+    torch.cuda.synchronize()
+    assert k3x.k3x_fetch_drops(ws) == 3
+    y_ref, drops = orc.moe_forward(host, x, idx, gates)
+    assert drops == 3
+    assert_y_close(_np(y), y_ref, "split sort")
+
+
 def test_moe_zero_tokens(dev):
     torch, k3x = dev
     _log("case: moe T=0")
