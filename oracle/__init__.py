@@ -72,6 +72,8 @@ def lib():
         L.oracle_rmsnorm_bf16.argtypes = [P, ci, ci, ctypes.c_float, P]
         L.oracle_residual_add_bf16.restype = ci
         L.oracle_residual_add_bf16.argtypes = [P, P, ci, ci]
+        L.oracle_glu.restype = ci
+        L.oracle_glu.argtypes = [P, P, i64, ci, ctypes.c_float, ctypes.c_float, P]
         for sfx in ("f32", "f64"):
             f = getattr(L, f"oracle_mxfp4_matvec_{sfx}")
             f.restype = None
@@ -85,6 +87,14 @@ def lib():
             f = getattr(L, f"oracle_moe_forward_{sfx}")
             f.restype = i64
             f.argtypes = [i64, i64, i64, P, P, P, P, P, P, P, i64, P, P, P, i64, P]
+            f = getattr(L, f"oracle_expert_forward_act_{sfx}")
+            f.restype = None
+            f.argtypes = [P, i64, i64, P, P, P, P, P, P, ci, ctypes.c_float, ctypes.c_float,
+                          P, P, P, P]
+            f = getattr(L, f"oracle_moe_forward_act_{sfx}")
+            f.restype = i64
+            f.argtypes = [i64, i64, i64, P, P, P, P, P, P, P, ci, ctypes.c_float, ctypes.c_float,
+                          i64, P, P, P, i64, P]
         _lib = L
     return _lib
 
@@ -141,9 +151,32 @@ def mxfp4_matvec(x, packed, scales, acc="f32"):
     return y
 
 
-def expert_forward(x_bf16, ex, acc="f32", want_hidden=False):
+ACTIVATIONS = {"swiglu": 0, "situ": 1}
+
+
+def _act(act):
+    """act: "swiglu", or ("situ", b1, b2)."""
+    if act == "swiglu" or act is None:
+        return 0, 0.0, 0.0
+    name, b1, b2 = act
+    assert name == "situ"
+    return 1, float(b1), float(b2)
+
+
+def glu(g, u, act=("situ", 4.0, 25.0)):
+    """The gated activation in fp32 before the bf16 rounding of h (oracle_glu)."""
+    g = _c(g, np.float32)
+    u = _c(u, np.float32)
+    out = np.empty_like(g)
+    a, b1, b2 = _act(act)
+    if lib().oracle_glu(_p(g), _p(u), g.size, a, b1, b2, _p(out)) != 0:
+        raise ValueError("oracle_glu: bad arguments")
+    return out
+
+
+def expert_forward(x_bf16, ex, acc="f32", want_hidden=False, act="swiglu"):
     """One expert on one activation.  ex has w1_packed..w2_scale (numpy u8).  Returns d
-    (float32 [H]) or (h_bf16 [I], g [I], u [I], d [H])."""
+    (float32 [H]) or (h_bf16 [I], g [I], u [I], d [H]).  act: "swiglu" or ("situ", b1, b2)."""
     x = _c(x_bf16, np.uint16)
     H = x.shape[0]
     I = ex.w1_packed.shape[0]
@@ -153,8 +186,9 @@ def expert_forward(x_bf16, ex, acc="f32", want_hidden=False):
     h = np.empty(I, dtype=np.uint16) if want_hidden else None
     g = np.empty(I, dtype=np.float32) if want_hidden else None
     u = np.empty(I, dtype=np.float32) if want_hidden else None
-    getattr(lib(), f"oracle_expert_forward_{_sfx(acc)}")(
-        _p(x), H, I, *[_p(a) for a in t], _p(h), _p(g), _p(u), _p(d))
+    a_, b1, b2 = _act(act)
+    getattr(lib(), f"oracle_expert_forward_act_{_sfx(acc)}")(
+        _p(x), H, I, *[_p(a) for a in t], a_, b1, b2, _p(h), _p(g), _p(u), _p(d))
     return (h, g, u, d) if want_hidden else d
 
 
@@ -170,7 +204,7 @@ def combine(gates, d, valid=None, acc="f32"):
     return y
 
 
-def moe_forward(pool, x_bf16, idx, gates, acc="f32"):
+def moe_forward(pool, x_bf16, idx, gates, acc="f32", act="swiglu"):
     """Whole forward over a host pool: pool = dict of six u8 arrays [E][rows][cols].
     Returns (y float32 [T][H], drops)."""
     x = _c(x_bf16, np.uint16)
@@ -183,8 +217,9 @@ def moe_forward(pool, x_bf16, idx, gates, acc="f32"):
     E, I = t[0].shape[0], t[0].shape[1]
     assert t[0].shape == (E, I, H // 2) and t[4].shape == (E, H, I // 2)
     y = np.empty((T, H), dtype=np.float32)
-    drops = getattr(lib(), f"oracle_moe_forward_{_sfx(acc)}")(
-        E, H, I, *[_p(a) for a in t], None, T, _p(x), _p(idx), _p(gates), k, _p(y))
+    a_, b1, b2 = _act(act)
+    drops = getattr(lib(), f"oracle_moe_forward_act_{_sfx(acc)}")(
+        E, H, I, *[_p(a) for a in t], None, a_, b1, b2, T, _p(x), _p(idx), _p(gates), k, _p(y))
     return y, int(drops)
 
 

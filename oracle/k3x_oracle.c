@@ -24,6 +24,12 @@
  *    exponential of -g taken as the float nearest to the exact value (evaluated in double
  *    and rounded once, so every conforming implementation gets the same E), and h rounded to
  *    bf16 (round to nearest even) before W2.
+ *  - Optional activation SiTU-GLU, the engine's own (README Part II section 9, the routed-
+ *    expert loop and its activation listing; default b1 = 4, b2 = 25 from the config
+ *    header): a = b1 * T(g / b1) * s(g) with the sigmoid on the uncapped gate, v = b2 *
+ *    T(u / b2), h = a * v, where T(q) is the float nearest to tanh(q) (evaluated in double,
+ *    rounded once, as E above) and s(g) = 1 / (1 + E); quotients and products in fp32, left
+ *    to right as the listing writes them.
  *  - Expert dot products: each group of 32 is summed sequentially in ACC, multiplied by its
  *    exact power-of-two scale, and the group partials are summed by a pairwise tree (zero
  *    padded to a power of two).  ACC = float is the verdict oracle; ACC = double is its
@@ -230,14 +236,45 @@ void ORC(oracle_mxfp4_matvec)(const float *x, const uint8_t *packed, const uint8
   }
 }
 
-/* One routed expert on one activation: g = W1.x, u = W3.x, h = bf16(silu(g) * u), d = W2.h,
- * silu(g) = g / (1 + E) with E the float nearest to exp(-g).
+/* The gated activation of one (g, u) pair before h is rounded to bf16.  act 0: SwiGLU,
+ * silu(g) * u with silu(g) = g / (1 + E), E the float nearest to exp(-g).  act 1: SiTU-GLU
+ * with caps b1 (gate) and b2 (up): (b1 * T(g / b1) * s(g)) * (b2 * T(u / b2)), T(q) the float
+ * nearest to tanh(q), s(g) = 1 / (1 + E). */
+static float glu_one(float g, float u, int act, float b1, float b2) {
+  const float ex = (float)exp(-(double)g);
+  if (act == 1) {
+    const float tg = (float)tanh((double)(g / b1));
+    const float sg = 1.0f / (1.0f + ex);
+    const float a = b1 * tg * sg;
+    const float tu = (float)tanh((double)(u / b2));
+    const float v = b2 * tu;
+    return a * v;
+  }
+  const float silu = g / (1.0f + ex);
+  return silu * u;
+}
+
+#ifdef ORACLE_COMMON
+/* out[i] = the activation of (g[i], u[i]) in fp32 (before the bf16 rounding of h).
+ * Returns -1 for an unknown act or, with act 1, caps that are not finite and positive. */
+int oracle_glu(const float *g, const float *u, int64_t n, int act, float b1, float b2,
+               float *out) {
+  if (act != 0 && act != 1) return -1;
+  if (act == 1 && !(b1 > 0.0f && b2 > 0.0f && isfinite(b1) && isfinite(b2))) return -1;
+  for (int64_t i = 0; i < n; ++i) out[i] = glu_one(g[i], u[i], act, b1, b2);
+  return 0;
+}
+#endif
+
+/* One routed expert on one activation: g = W1.x, u = W3.x, h = bf16(act(g, u)), d = W2.h
+ * (act as in glu_one).
  * x bf16 [H]; h_out bf16 [I] (may be NULL); g_out/u_out fp32 [I] (may be NULL);
  * d_out fp32 [H]. */
-void ORC(oracle_expert_forward)(const uint16_t *x, int64_t H, int64_t I, const uint8_t *w1p,
-                                const uint8_t *w1s, const uint8_t *w3p, const uint8_t *w3s,
-                                const uint8_t *w2p, const uint8_t *w2s, uint16_t *h_out,
-                                float *g_out, float *u_out, float *d_out) {
+void ORC(oracle_expert_forward_act)(const uint16_t *x, int64_t H, int64_t I, const uint8_t *w1p,
+                                    const uint8_t *w1s, const uint8_t *w3p, const uint8_t *w3s,
+                                    const uint8_t *w2p, const uint8_t *w2s, int act, float b1,
+                                    float b2, uint16_t *h_out, float *g_out, float *u_out,
+                                    float *d_out) {
   float *xf = (float *)malloc(sizeof(float) * (size_t)H);
   float *g = (float *)malloc(sizeof(float) * (size_t)I);
   float *u = (float *)malloc(sizeof(float) * (size_t)I);
@@ -246,9 +283,7 @@ void ORC(oracle_expert_forward)(const uint16_t *x, int64_t H, int64_t I, const u
   ORC(oracle_mxfp4_matvec)(xf, w1p, w1s, I, H, g);
   ORC(oracle_mxfp4_matvec)(xf, w3p, w3s, I, H, u);
   for (int64_t r = 0; r < I; ++r) {
-    const float ex = (float)exp(-(double)g[r]);
-    const float silu = g[r] / (1.0f + ex);
-    const uint16_t hb = float_to_bf16(silu * u[r]);
+    const uint16_t hb = float_to_bf16(glu_one(g[r], u[r], act, b1, b2));
     if (h_out) h_out[r] = hb;
     hf[r] = bf16_to_float(hb);
   }
@@ -259,6 +294,15 @@ void ORC(oracle_expert_forward)(const uint16_t *x, int64_t H, int64_t I, const u
   free(g);
   free(u);
   free(hf);
+}
+
+/* The SwiGLU expert (act 0). */
+void ORC(oracle_expert_forward)(const uint16_t *x, int64_t H, int64_t I, const uint8_t *w1p,
+                                const uint8_t *w1s, const uint8_t *w3p, const uint8_t *w3s,
+                                const uint8_t *w2p, const uint8_t *w2s, uint16_t *h_out,
+                                float *g_out, float *u_out, float *d_out) {
+  ORC(oracle_expert_forward_act)(x, H, I, w1p, w1s, w3p, w3s, w2p, w2s, 0, 0.0f, 0.0f, h_out,
+                                 g_out, u_out, d_out);
 }
 
 /* Slot-order weighted combine: y[t][r] = sum_j gates[t][j] * d[t][j][r] in ACC, j ascending,
@@ -279,11 +323,12 @@ void ORC(oracle_combine)(int64_t T, int64_t topk, int64_t H, const float *gates,
 /* Whole MoE forward over a pool held in host memory (small cases).  Pool tensors are
  * [E][rows][cols] with the per-expert byte strides given (0 = dense).  An expert id outside
  * [0, E) is a dropped slot: it contributes 0 and is counted.  Returns the drop count. */
-int64_t ORC(oracle_moe_forward)(int64_t E, int64_t H, int64_t I, const uint8_t *w1p,
-                                const uint8_t *w1s, const uint8_t *w3p, const uint8_t *w3s,
-                                const uint8_t *w2p, const uint8_t *w2s, const int64_t *strides,
-                                int64_t T, const uint16_t *x, const int32_t *idx,
-                                const float *gates, int64_t topk, float *y) {
+int64_t ORC(oracle_moe_forward_act)(int64_t E, int64_t H, int64_t I, const uint8_t *w1p,
+                                    const uint8_t *w1s, const uint8_t *w3p, const uint8_t *w3s,
+                                    const uint8_t *w2p, const uint8_t *w2s,
+                                    const int64_t *strides, int act, float b1, float b2,
+                                    int64_t T, const uint16_t *x, const int32_t *idx,
+                                    const float *gates, int64_t topk, float *y) {
   const int64_t dflt[6] = {I * H / 2, I * H / 32, I * H / 2, I * H / 32, H * I / 2, H * I / 32};
   int64_t st[6];
   for (int i = 0; i < 6; ++i) st[i] = (strides && strides[i]) ? strides[i] : dflt[i];
@@ -301,12 +346,22 @@ int64_t ORC(oracle_moe_forward)(int64_t E, int64_t H, int64_t I, const uint8_t *
         continue;
       }
       valid[t * topk + j] = 1;
-      ORC(oracle_expert_forward)(x + t * H, H, I, w1p + e * st[0], w1s + e * st[1],
-                                 w3p + e * st[2], w3s + e * st[3], w2p + e * st[4],
-                                 w2s + e * st[5], NULL, NULL, NULL, dj);
+      ORC(oracle_expert_forward_act)(x + t * H, H, I, w1p + e * st[0], w1s + e * st[1],
+                                     w3p + e * st[2], w3s + e * st[3], w2p + e * st[4],
+                                     w2s + e * st[5], act, b1, b2, NULL, NULL, NULL, dj);
     }
   ORC(oracle_combine)(T, topk, H, gates, d, valid, y);
   free(d);
   free(valid);
   return drops;
+}
+
+/* The SwiGLU forward (act 0). */
+int64_t ORC(oracle_moe_forward)(int64_t E, int64_t H, int64_t I, const uint8_t *w1p,
+                                const uint8_t *w1s, const uint8_t *w3p, const uint8_t *w3s,
+                                const uint8_t *w2p, const uint8_t *w2s, const int64_t *strides,
+                                int64_t T, const uint16_t *x, const int32_t *idx,
+                                const float *gates, int64_t topk, float *y) {
+  return ORC(oracle_moe_forward_act)(E, H, I, w1p, w1s, w3p, w3s, w2p, w2s, strides, 0, 0.0f,
+                                     0.0f, T, x, idx, gates, topk, y);
 }

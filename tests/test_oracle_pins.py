@@ -484,3 +484,93 @@ def test_residual_add(orc):
     out = orc.residual_add_bf16(x, y)
     want = S.f32_to_bf16_bits((S.bf16_bits_to_f32(x) + y).astype(np.float32))
     assert np.array_equal(out, want)
+
+
+# ------------------------------------------------------------------------------------------
+# SiTU-GLU (kimi-k3-in-c README Part II section 9, the routed-expert loop's activation
+# listing; caps b1 = 4, b2 = 25 from the config header)
+# ------------------------------------------------------------------------------------------
+SITU = ("situ", 4.0, 25.0)
+
+
+def test_situ_saturates_at_the_cap_product(orc):
+    """The engine's self-test prints |out| = 100.000 = b1 * b2 for a saturated input; the
+    float tanh of a large argument is 1 and the sigmoid of a large gate is 1."""
+    g = np.array([100.0, 60.0, 1e4, 3e4], np.float32)
+    u = np.array([1e4, 1e3, 1e5, 2e3], np.float32)
+    assert np.all(orc.glu(g, u, SITU) == 100.0)
+    assert np.all(orc.glu(g, -u, SITU) == -100.0)
+    assert np.all(orc.glu(g, u, ("situ", 2.0, 3.0)) == 6.0)
+
+
+def test_situ_bounded_by_the_cap_product(orc):
+    rng = np.random.default_rng(5)
+    g = (rng.standard_normal(200000) * rng.choice([0.1, 3.0, 100.0], 200000)).astype(np.float32)
+    u = (rng.standard_normal(200000) * rng.choice([0.1, 30.0, 1000.0], 200000)).astype(np.float32)
+    h = orc.glu(g, u, SITU)
+    assert np.all(np.isfinite(h)) and np.all(np.abs(h) <= 100.0)
+
+
+def test_situ_zero_gate_and_odd_in_the_up_projection(orc):
+    rng = np.random.default_rng(6)
+    g = (rng.standard_normal(50000) * 5).astype(np.float32)
+    u = (rng.standard_normal(50000) * 50).astype(np.float32)
+    assert np.all(orc.glu(np.zeros_like(g), u, SITU) == 0.0)
+    # tanh and the fp32 quotient are odd, so flipping u flips h exactly
+    assert np.array_equal(orc.glu(g, -u, SITU), -orc.glu(g, u, SITU))
+
+
+def test_situ_tends_to_swiglu_for_large_caps(orc):
+    """b * tanh(q / b) -> q as b -> infinity, so the activation becomes silu(g) * u."""
+    rng = np.random.default_rng(7)
+    g = (rng.standard_normal(50000) * 4).astype(np.float32)
+    u = (rng.standard_normal(50000) * 4).astype(np.float32)
+    big = orc.glu(g, u, ("situ", 1e7, 1e7))
+    sw = orc.glu(g, u, "swiglu")
+    assert np.allclose(big, sw, rtol=2e-6, atol=1e-37)
+
+
+def test_situ_within_the_pages_tolerance_of_the_exact_value(orc):
+    """The engine checks this kernel at atol 1e-5, rtol 1e-4; the oracle's fp32 rounding
+    steps stay far inside that against the exact value (float64 math)."""
+    rng = np.random.default_rng(8)
+    g = (rng.standard_normal(100000) * 6).astype(np.float32)
+    u = (rng.standard_normal(100000) * 60).astype(np.float32)
+    h = orc.glu(g, u, SITU).astype(np.float64)
+    g64, u64 = g.astype(np.float64), u.astype(np.float64)
+    exact = 4.0 * np.tanh(g64 / 4.0) / (1.0 + np.exp(-g64)) * (25.0 * np.tanh(u64 / 25.0))
+    assert np.allclose(h, exact, atol=1e-5, rtol=1e-4)
+    assert np.max(np.abs(h - exact) / (np.abs(exact) + 1e-30)) < 1e-5
+
+
+def test_situ_rejects_bad_caps(orc):
+    g = np.ones(4, np.float32)
+    for b1, b2 in ((0.0, 25.0), (4.0, -1.0), (float("inf"), 25.0), (4.0, float("nan"))):
+        with pytest.raises(ValueError):
+            orc.glu(g, g, ("situ", b1, b2))
+
+
+@pytest.mark.parametrize("acc", ["f32", "f64"])
+def test_situ_expert_against_brute_force(orc, acc):
+    """A whole expert with SiTU-GLU on tiny shapes: h equals bf16 of the activation of the
+    oracle's own g and u, and d, y follow numpy's float64 algebra."""
+    E, H, I, k, T = 6, 64, 96, 3, 4
+    pool = _tiny_pool(4242, E, H, I)
+    x = S.normal_bf16(9, S.P_X, 0, (T, H))
+    idx, gates = S.uniform_routing(13, T, E, k)
+    y, drops = orc.moe_forward(pool, x, idx, gates, acc=acc, act=SITU)
+    assert drops == 0
+    y_ref = np.zeros((T, H))
+    for t in range(T):
+        for j in range(k):
+            e = int(idx[t, j])
+            ex = S.ExpertBytes(*[pool[n][e] for n in S.TENSOR_NAMES])
+            h, g, u, d = orc.expert_forward(x[t], ex, acc=acc, want_hidden=True, act=SITU)
+            assert np.array_equal(bits_to_f(h), bf16_rne_from64(orc.glu(g, u, SITU)))
+            d64 = dequant64(pool["w2_packed"][e], pool["w2_scale"][e]) @ bits_to_f(h)
+            assert np.max(np.abs(d - d64)) <= 1e-6 * (np.max(np.abs(d64)) + 1e-30)
+            y_ref[t] += float(gates[t, j]) * d64
+    assert np.linalg.norm(y - y_ref) / np.linalg.norm(y_ref) <= 1e-6
+    # the SiTU forward differs from the SwiGLU one (the option reaches the activation)
+    y_sw, _ = orc.moe_forward(pool, x, idx, gates, acc=acc)
+    assert not np.allclose(y, y_sw)
