@@ -69,6 +69,14 @@ const char *k3x_last_error(void);
  * base_k + e * stride_bytes[k]; stride 0 means dense (the tensor's own size).
  * Tensor order in stride_bytes: w1_packed, w1_scale, w3_packed, w3_scale, w2_packed, w2_scale.
  * ---------------------------------------------------------------------------------------- */
+/* The gated activation between W1/W3 and W2 (h is rounded to bf16 after it):
+ * K3X_ACT_SWIGLU: silu(g) * u.
+ * K3X_ACT_SITU:   SiTU-GLU, the engine's own routed-expert activation (README Part II
+ *                 section 9, the activation listing): (b1 tanh(g / b1) sigmoid(g)) *
+ *                 (b2 tanh(u / b2)), the sigmoid on the uncapped gate; the checkpoint's caps
+ *                 are b1 = 4, b2 = 25, so |h| <= 100. */
+typedef enum { K3X_ACT_SWIGLU = 0, K3X_ACT_SITU = 1 } k3x_activation;
+
 typedef struct k3x_pool_desc {
   int32_t n_experts; /* 1..8192                                                    */
   int32_t hidden;    /* H: multiple of 128 (e.g. 3584)                              */
@@ -76,14 +84,18 @@ typedef struct k3x_pool_desc {
   int32_t group;     /* must be 32                                                  */
   const void *w1_packed, *w1_scale, *w3_packed, *w3_scale, *w2_packed, *w2_scale;
   int64_t stride_bytes[6];
+  int32_t activation; /* k3x_activation; 0 (a zeroed desc) is SwiGLU               */
+  float situ_b1;      /* K3X_ACT_SITU: gate cap, finite and > 0 (4.0 in the checkpoint) */
+  float situ_b2;      /* K3X_ACT_SITU: up cap, finite and > 0 (25.0 in the checkpoint)  */
 } k3x_pool_desc;
 
 typedef struct k3x_pool k3x_pool;
 
 /* Validates d and creates a host-side handle in *out.  Refuses (K3X_E_UNSUPPORTED)
  * group != 32, hidden or inter not a multiple of 128, packed pointers or strides not
- * 16-byte aligned; refuses (K3X_E_INVALID_ARG) NULL pointers, n_experts out of range and
- * strides smaller than the dense tensor size.  Allocates host memory only; the device
+ * 16-byte aligned; refuses (K3X_E_INVALID_ARG) NULL pointers, n_experts out of range,
+ * strides smaller than the dense tensor size, an unknown activation and, for SiTU-GLU,
+ * caps that are not finite and positive.  Allocates host memory only; the device
  * tensors are borrowed and must outlive the pool.  Scale bytes are read as given: bytes
  * 2..253 give normal weights; 255 zeroes a group; 0, 1 and 254 are outside the range this
  * build promises to reproduce exactly. */

@@ -6,6 +6,8 @@
 
 #include <new>
 
+#include <cmath>
+
 #include "k3x_internal.h"
 
 namespace {
@@ -70,6 +72,13 @@ k3x_status k3x_expert_pool_create(const k3x_pool_desc* d, k3x_pool** out) {
                 d->hidden, d->inter);
   if (d->hidden > 65536 || d->inter > 65536)
     return fail(K3X_E_UNSUPPORTED, "pool_create: hidden/inter above 65536");
+  if (d->activation != K3X_ACT_SWIGLU && d->activation != K3X_ACT_SITU)
+    return fail(K3X_E_INVALID_ARG, "pool_create: unknown activation %d", d->activation);
+  if (d->activation == K3X_ACT_SITU &&
+      !(std::isfinite(d->situ_b1) && std::isfinite(d->situ_b2) && d->situ_b1 > 0.0f &&
+        d->situ_b2 > 0.0f))
+    return fail(K3X_E_INVALID_ARG, "pool_create: SiTU caps %g, %g must be finite and > 0",
+                (double)d->situ_b1, (double)d->situ_b2);
   const void* ptrs[6] = {d->w1_packed, d->w1_scale, d->w3_packed, d->w3_scale, d->w2_packed, d->w2_scale};
   const int64_t H = d->hidden, I = d->inter;
   const int64_t dense[6] = {I * H / 2, I * H / 32, I * H / 2, I * H / 32, H * I / 2, H * I / 32};
@@ -78,6 +87,9 @@ k3x_status k3x_expert_pool_create(const k3x_pool_desc* d, k3x_pool** out) {
   p->E = d->n_experts;
   p->H = d->hidden;
   p->I = d->inter;
+  p->act = d->activation;
+  p->b1 = d->activation == K3X_ACT_SITU ? d->situ_b1 : 0.0f;
+  p->b2 = d->activation == K3X_ACT_SITU ? d->situ_b2 : 0.0f;
   for (int k = 0; k < 6; ++k) {
     if (!ptrs[k]) {
       delete p;

@@ -52,6 +52,8 @@ struct DecodeArgs {
   int32_t topk, E;
   uint8_t* ws;          // w13 writes the drop count at offset 0
   void* out;            // w13: h bf16 [topk][I]; w2: d fp32 [topk][H]
+  int32_t gact;         // k3x_activation of the W1/W3 epilogue
+  float b1, b2;         // SiTU-GLU caps
 };
 
 __device__ __forceinline__ bool expert_ok(int e, int E) { return e >= 0 && e < E; }
@@ -240,7 +242,9 @@ __device__ __forceinline__ void stream_rows(const uint8_t* wa, const uint8_t* sa
   }
 }
 
-// g = W1 x, u = W3 x, h = bf16(silu(g) * u) for every (slot, row) of this wave's run.  A run
+// g = W1 x, u = W3 x, h = bf16(silu(g) * u) (or of SiTU-GLU, with each tanh the float nearest
+// to its double value, products and quotients in fp32 left to right) for every (slot, row)
+// of this wave's run.  A run
 // is cut at slot boundaries into segments of one expert; a dropped slot's segment is skipped.
 // Workgroup 0 also writes the number of dropped slots.
 __global__ __launch_bounds__(256) void decode_w13(DecodeArgs a) {
@@ -271,7 +275,16 @@ __global__ __launch_bounds__(256) void decode_w13(DecodeArgs a) {
                       a.wb + (size_t)e * a.st_wb, a.sb + (size_t)e * a.st_sb, r0, r0 + n - 1,
                       wrow, srow, lo, x0, x1, lane, [&](int r, float gv, float uv) {
                         const float ex = (float)exp(-(double)gv);
-                        const float hv = (gv / (1.0f + ex)) * uv;
+                        float hv;
+                        if (a.gact == K3X_ACT_SITU) {
+                          const float tg = (float)tanh((double)(gv / a.b1));
+                          const float sg = 1.0f / (1.0f + ex);
+                          const float av = a.b1 * tg * sg;
+                          const float tu = (float)tanh((double)(uv / a.b2));
+                          hv = av * (a.b2 * tu);
+                        } else {
+                          hv = (gv / (1.0f + ex)) * uv;
+                        }
                         h[r] = (uint16_t)f32_to_bf16_bits(hv);
                       });
   }
@@ -370,6 +383,9 @@ hipError_t launch_decode_exact(const k3x_pool& p, const uint16_t* x, const int32
   a.E = p.E;
   a.ws = ws;
   a.out = ws + off_h;
+  a.gact = p.act;
+  a.b1 = p.b1;
+  a.b2 = p.b2;
   hipError_t err = launch("w13_decode", decode_w13, dim3(decode_w13_grid()), dim3(256), 0, s, a);
   if (err != hipSuccess) return err;
   DecodeArgs b = a;

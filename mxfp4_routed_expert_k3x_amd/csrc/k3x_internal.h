@@ -59,6 +59,28 @@ __device__ __forceinline__ bf16x8 dequant8(uint32_t dw, float scale) {
   return bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
+// tanh for the GEMM epilogues (h is rounded to bf16 right after): the odd series to x^7 for
+// |x| < 1/8 (next term below 2e-10), else (1 - e) / (1 + e) with e = exp(-2|x|) from the
+// hardware exponential; the sign is copied back.
+__device__ __forceinline__ float tanh_fast(float x) {
+  const float ax = fabsf(x);
+  const float x2 = x * x;
+  const float p =
+      ax * (1.0f + x2 * (-1.0f / 3.0f + x2 * (2.0f / 15.0f + x2 * (-17.0f / 315.0f))));
+  const float e = __expf(-2.0f * ax);
+  const float q = (1.0f - e) * __builtin_amdgcn_rcpf(1.0f + e);
+  return copysignf(ax < 0.125f ? p : q, x);
+}
+
+// SiTU-GLU for the GEMM epilogues: (b1 tanh(g / b1) sigmoid(g)) * (b2 tanh(u / b2)), the
+// sigmoid on the uncapped gate (kimi-k3-in-c README, Part II section 9, the activation
+// listing), with the hardware exponential and reciprocal.
+__device__ __forceinline__ float situ_fast(float g, float u, float b1, float b2) {
+  const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+  const float a = b1 * tanh_fast(__fdividef(g, b1)) * sg;
+  return a * (b2 * tanh_fast(__fdividef(u, b2)));
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -102,6 +124,8 @@ struct k3x_pool {
   int32_t E, H, I;
   const uint8_t* base[6];
   int64_t stride[6];
+  int32_t act;   // k3x_activation
+  float b1, b2;  // SiTU-GLU caps
 };
 
 namespace k3x {

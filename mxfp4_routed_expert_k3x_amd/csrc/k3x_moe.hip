@@ -302,6 +302,8 @@ struct GemmArgs {
   uint8_t* ws;         // workspace
   size_t off_tiles, off_perm;
   void* out;           // h (bf16 [slots][I]) or d (fp32 [slots][H])
+  int32_t gact;        // k3x_activation of the W1/W3 epilogue
+  float b1, b2;        // SiTU-GLU caps
 };
 
 // One K block (128 K) of operands for one lane: the packed bytes of 4 row blocks (group
@@ -473,7 +475,8 @@ __global__ __launch_bounds__(256) void gemm_decode(GemmArgs a) {
 #pragma unroll
           for (int k2 = 0; k2 < 2; ++k2) {
             const float gi = g[i + k2];
-            const float v = (gi / (1.0f + expf(-gi))) * u[i + k2];
+            const float v = a.gact == K3X_ACT_SITU ? situ_fast(gi, u[i + k2], a.b1, a.b2)
+                                                   : (gi / (1.0f + expf(-gi))) * u[i + k2];
             two |= f32_to_bf16_bits(v) << (16 * k2);
           }
           hv[i / 2] = two;
@@ -610,6 +613,9 @@ hipError_t launch_moe(const k3x_pool& p, const uint16_t* x, int32_t T, const int
   a13.off_tiles = L.tiles;
   a13.off_perm = L.perm;
   a13.out = ws + L.h;
+  a13.gact = p.act;
+  a13.b1 = p.b1;
+  a13.b2 = p.b2;
   const int64_t max_tiles = implicit ? (int64_t)topk : (int64_t)L.max_tiles;
   auto grid_for = [&](int64_t items) {
     int64_t g = (items + kNumXcd - 1) / kNumXcd * kNumXcd;

@@ -10,7 +10,7 @@
 // Slots are sorted by expert into tiles of at most 96 slots of one expert.  An item is one
 // tile against a chunk of output rows, computed by one workgroup of 8 waves (2 per SIMD):
 //   - W1/W3 mode: 256 rows of h (each wave 32 rows of W1 and the same 32 rows of W3),
-//     epilogue h = bf16(silu(g) * u);
+//     epilogue h = bf16(silu(g) * u), or of SiTU-GLU when the pool asks for it;
 //   - W2 mode: 512 rows of d (each wave 64 rows of W2).
 // h and d are stored by sorted position (row = the slot's index in the sorted order), so W2
 // reads its tile's h rows contiguously and the combine gathers d through the inverse order.
@@ -62,6 +62,8 @@ struct PrefillArgs {
   uint32_t act_bytes;
   int32_t topk;
   void* out;          // h bf16 [positions][I] or d fp32 [positions][H]
+  int32_t gact;       // k3x_activation of the W1/W3 epilogue
+  float b1, b2;       // SiTU-GLU caps
 };
 
 // output rows of one item: W1/W3 mode 32 h rows per wave (32 W1 + 32 W3 rows), W2 mode 64
@@ -355,8 +357,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_prefill(PrefillArgs a, const
             uint32_t hv[2];
 #pragma unroll
             for (int i = 0; i < 4; i += 2) {
-              const float h0 = swiglu_fast(acc[rb][tb][i], acc[rb + kRB / 2][tb][i]);
-              const float h1 = swiglu_fast(acc[rb][tb][i + 1], acc[rb + kRB / 2][tb][i + 1]);
+              const float g0 = acc[rb][tb][i], u0 = acc[rb + kRB / 2][tb][i];
+              const float g1 = acc[rb][tb][i + 1], u1 = acc[rb + kRB / 2][tb][i + 1];
+              const bool situ = a.gact == K3X_ACT_SITU;
+              const float h0 = situ ? situ_fast(g0, u0, a.b1, a.b2) : swiglu_fast(g0, u0);
+              const float h1 = situ ? situ_fast(g1, u1, a.b1, a.b2) : swiglu_fast(g1, u1);
               hv[i / 2] = f32_to_bf16_bits(h0) | (f32_to_bf16_bits(h1) << 16);
             }
             *reinterpret_cast<uint2*>(h + 16 * rb) = make_uint2(hv[0], hv[1]);
@@ -431,6 +436,9 @@ hipError_t launch_prefill_gemms(const k3x_pool& p, const uint16_t* x, int32_t T,
   a.act_bytes = (uint32_t)((size_t)T * p.H * 2);
   a.topk = topk;
   a.out = ws + L.h;
+  a.gact = p.act;
+  a.b1 = p.b1;
+  a.b2 = p.b2;
   const int32_t* n_tiles = reinterpret_cast<const int32_t*>(ws + 8);
   const int4* tiles = reinterpret_cast<const int4*>(ws + L.tiles);
   const int32_t* perm = reinterpret_cast<const int32_t*>(ws + L.perm);

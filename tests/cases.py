@@ -45,7 +45,7 @@ def assert_y_close_oracle(y, y_ref32, y_ref64_fn, what=""):
 
 
 def oracle_forward_sampled(orc, seed, layer, H, I, x_bits, idx, gates, tokens, E=None,
-                           acc="f32", cache=None):
+                           acc="f32", cache=None, act="swiglu"):
     """Oracle y for the listed tokens, regenerating on the host only the experts they use.
     Slots with expert ids outside [0, E) contribute nothing."""
     tokens = list(tokens)
@@ -67,6 +67,6 @@ def oracle_forward_sampled(orc, seed, layer, H, I, x_bits, idx, gates, tokens, E
             if cache is not None:
                 cache[key] = ex
         for ti, j in uses:
-            d[ti, j] = orc.expert_forward(x_bits[tokens[ti]], ex, acc=acc)
+            d[ti, j] = orc.expert_forward(x_bits[tokens[ti]], ex, acc=acc, act=act)
             valid[ti, j] = 1
     return orc.combine(gates[tokens], d, valid, acc=acc)

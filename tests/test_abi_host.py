@@ -65,6 +65,12 @@ def test_pool_create_accepts_valid_desc(k3x):
     assert st == k3x.K3X_OK and h
     k3x.lib().k3x_expert_pool_destroy(h)
     k3x.lib().k3x_expert_pool_destroy(None)  # no-op
+    # SiTU-GLU with the checkpoint's caps; SwiGLU ignores the caps
+    for kw in ({"activation": 1, "situ_b1": 4.0, "situ_b2": 25.0},
+               {"activation": 0, "situ_b1": -1.0, "situ_b2": float("nan")}):
+        st, h = _create(k3x, _desc(k3x, **kw))
+        assert st == k3x.K3X_OK and h, kw
+        k3x.lib().k3x_expert_pool_destroy(h)
 
 
 @pytest.mark.parametrize("kw,want", [
@@ -77,6 +83,12 @@ def test_pool_create_accepts_valid_desc(k3x):
     ({"n_experts": 20000}, -1),
     ({"w2_scale": None}, -1),
     ({"w1_packed": (1 << 40) + 8}, -2),
+    ({"activation": 2}, -1),
+    ({"activation": -1}, -1),
+    ({"activation": 1, "situ_b1": 0.0, "situ_b2": 25.0}, -1),
+    ({"activation": 1, "situ_b1": 4.0, "situ_b2": -25.0}, -1),
+    ({"activation": 1, "situ_b1": float("inf"), "situ_b2": 25.0}, -1),
+    ({"activation": 1, "situ_b1": 4.0, "situ_b2": float("nan")}, -1),
 ])
 def test_pool_create_refuses(k3x, kw, want):
     st, h = _create(k3x, _desc(k3x, **kw))

@@ -44,8 +44,15 @@ def _np(t, dtype=None):
     return a.view(dtype) if dtype is not None else a
 
 
-def _pool(torch, k3x, dev_tensors, E, H, I):
-    return k3x.k3x_expert_pool_create(dev_tensors, hidden=H, inter=I, n_experts=E)
+def _pool(torch, k3x, dev_tensors, E, H, I, act="swiglu"):
+    if act == "swiglu":
+        return k3x.k3x_expert_pool_create(dev_tensors, hidden=H, inter=I, n_experts=E)
+    _, b1, b2 = act
+    return k3x.k3x_expert_pool_create(dev_tensors, hidden=H, inter=I, n_experts=E,
+                                      activation="situ", situ_b1=b1, situ_b2=b2)
+
+
+SITU = ("situ", 4.0, 25.0)
 
 
 # ------------------------------------------------------------------------------------------
@@ -408,6 +415,83 @@ def test_workload4_prefill_t4096(dev, orc):
     tokens = [0, 1, 2047, 4095]
     y_ref = oracle_forward_sampled(orc, w.seed, 0, w.H, w.I, x, idx, gates, tokens)
     r = assert_y_close(_np(y)[tokens], y_ref, w.name)
+    _log(f"  rel_l2={r[0]:.3e} max_abs={r[1]:.3e}")
+    del pool, ws
+    torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------------------------------------
+# SiTU-GLU (the engine's own activation) on every path
+# ------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("caps", [(4.0, 25.0), (0.5, 3.0)])
+def test_situ_decode_bit_exact(dev, orc, caps):
+    """Single-token decode with SiTU-GLU at full shapes (E = 64, 16 slots) and with small
+    caps that saturate often: y equals the fp32 oracle bit for bit."""
+    torch, k3x = dev
+    w = S.WORKLOADS[1]
+    act = ("situ",) + caps
+    _log(f"case: SiTU decode caps={caps}")
+    pool = _pool(torch, k3x, S.device_pool(w.seed, 0, w.E, w.H, w.I), w.E, w.H, w.I, act)
+    x = S.normal_bf16(w.seed + 3, S.P_X, 0, (1, w.H))
+    idx, gates = S.uniform_routing(w.seed + 3, 1, w.E, w.topk)
+    y, _ = k3x.moe_forward(pool, _t(torch, x), _t(torch, idx), _t(torch, gates))
+    torch.cuda.synchronize()
+    y_ref = oracle_forward_sampled(orc, w.seed, 0, w.H, w.I, x, idx, gates, [0], act=act)
+    assert np.array_equal(_np(y), y_ref)
+    y_sw = oracle_forward_sampled(orc, w.seed, 0, w.H, w.I, x, idx, gates, [0])
+    assert not np.allclose(y_ref, y_sw)
+
+
+@pytest.mark.parametrize("E,H,I,T,k", [(5, 256, 384, 8, 3), (4, 512, 512, 40, 2),
+                                       (16, 1024, 512, 2, 8)])
+def test_situ_grouped_and_prefill_paths(dev, orc, E, H, I, T, k):
+    """Batches with SiTU-GLU on the small-batch grouped kernels (H = 256) and on the
+    sorted-tile kernels (H = 512, 1024), against the oracle with the same activation."""
+    torch, k3x = dev
+    _log(f"case: SiTU E={E} H={H} I={I} T={T} k={k}")
+    seed = 3000 + E + H + I + T
+    host = S.host_pool(seed, 0, E, H, I)
+    pool = _pool(torch, k3x, S.device_pool(seed, 0, E, H, I), E, H, I, SITU)
+    x = S.normal_bf16(seed, S.P_X, 0, (T, H))
+    rng = np.random.default_rng(seed)
+    idx = rng.integers(0, E, (T, k)).astype(np.int32)
+    _, gates = S.uniform_routing(seed, T, k, k)
+    y, _ = k3x.moe_forward(pool, _t(torch, x), _t(torch, idx), _t(torch, gates))
+    torch.cuda.synchronize()
+    y_ref, _ = orc.moe_forward(host, x, idx, gates, act=SITU)
+    r = assert_y_close_oracle(
+        _np(y), y_ref, lambda: orc.moe_forward(host, x, idx, gates, acc="f64", act=SITU)[0],
+        f"SiTU E={E} H={H} I={I} T={T} k={k}")
+    _log(f"  rel_l2={r[0]:.3e} max_abs={r[1]:.3e}")
+
+
+def test_situ_workload2_and_prefill_full_size(dev, orc):
+    """Full shapes with SiTU-GLU: one routed decode token over 896 experts (bit-exact) and
+    the 4096-token prefill (sampled tokens, tolerance)."""
+    torch, k3x = dev
+    w = S.WORKLOADS[2]
+    _log("case: SiTU workload decode_t1_e896_router")
+    pool = _pool(torch, k3x, S.device_pool(w.seed, 0, w.E, w.H, w.I), w.E, w.H, w.I, SITU)
+    W, b = S.router_inputs(w)
+    x = S.activations(w)
+    xd = _t(torch, x)
+    idx, gates, _ = k3x.route_topk(_t(torch, W), _t(torch, b), xd, w.topk)
+    y, _ = k3x.moe_forward(pool, xd, idx, gates)
+    torch.cuda.synchronize()
+    y_ref = oracle_forward_sampled(orc, w.seed, 0, w.H, w.I, x, _np(idx), _np(gates), [0],
+                                   act=SITU)
+    assert np.array_equal(_np(y), y_ref)
+    del pool
+    w = S.WORKLOADS[4]
+    _log("case: SiTU workload prefill_t4096_e896")
+    pool = _pool(torch, k3x, S.device_pool(w.seed, 0, w.E, w.H, w.I), w.E, w.H, w.I, SITU)
+    x = S.activations(w)
+    idx, gates = S.uniform_routing(w.seed, w.T, w.E, w.topk)
+    y, ws = k3x.moe_forward(pool, _t(torch, x), _t(torch, idx), _t(torch, gates))
+    torch.cuda.synchronize()
+    tokens = [0, 1, 2047, 4095]
+    y_ref = oracle_forward_sampled(orc, w.seed, 0, w.H, w.I, x, idx, gates, tokens, act=SITU)
+    r = assert_y_close(_np(y)[tokens], y_ref, "SiTU prefill")
     _log(f"  rel_l2={r[0]:.3e} max_abs={r[1]:.3e}")
     del pool, ws
     torch.cuda.empty_cache()
