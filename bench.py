@@ -1,9 +1,11 @@
 """Benchmark of the routed-expert hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+                    [--activation swiglu|situ]
 
 A step is one pass of the whole path over one batch: the router (when the workload has one)
-and the expert forward (sort, fused W1/W3 + SwiGLU, W2, combine).  The default workload is
+and the expert forward (sort, fused W1/W3 + SwiGLU (or SiTU-GLU with --activation situ), W2,
+combine).  The default workload is
 one decode token through one layer of 896 experts with the router (E = 896, H = 3584,
 I = 3072, top-16).  Inputs are synthetic and seeded (k3x_synth); pools are generated in
 device memory and resident before timing.  Successive steps rotate over 64 different
@@ -44,6 +46,7 @@ METRIC = "MoE-layer tokens/s + achieved HBM GB/s (decode), TFLOP/s (prefill)"
 PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
 ROTATE = 64
+ORACLE_ACT = {"swiglu": "swiglu", "situ": ("situ", 4.0, 25.0)}
 COPY_PROBE_BYTES = 1 << 30
 KERNEL_SOURCES = ("k3x_decode.hip", "k3x_moe.hip", "k3x_prefill.hip", "k3x_router.hip")
 # rocprofv3 kernel names of the library's launch names
@@ -95,7 +98,7 @@ def per_kernel_work(name, H, I, E, T, topk, U):
     return 0, 0.0
 
 
-def cpu_baseline(w, x, W, b, dev_idx, dev_gates, pool_dev, budget_s=12.0):
+def cpu_baseline(w, x, W, b, dev_idx, dev_gates, pool_dev, budget_s=12.0, act="swiglu"):
     """The oracle as it stands, on this host's cores, over a bounded sample of the same
     workload's tokens, repeated until about budget_s seconds of oracle time.  Each token's
     expert bytes are copied from the generator's device pool (k3x_synth writes the same
@@ -119,7 +122,7 @@ def cpu_baseline(w, x, W, b, dev_idx, dev_gates, pool_dev, budget_s=12.0):
             e = int(e)
             exps.append(S.ExpertBytes(*[pool_dev[nm][e].cpu().numpy() for nm in S.TENSOR_NAMES]))
         t0 = time.perf_counter()
-        d = np.stack([oracle.expert_forward(xt[0], ex) for ex in exps])[None]
+        d = np.stack([oracle.expert_forward(xt[0], ex, act=act) for ex in exps])[None]
         oracle.combine(gates, d)
         t_used += time.perf_counter() - t0
         n_tok += 1
@@ -134,7 +137,7 @@ def cpu_baseline(w, x, W, b, dev_idx, dev_gates, pool_dev, budget_s=12.0):
     }
 
 
-def chain_cpu_baseline(w, x, layers, budget_s=12.0):
+def chain_cpu_baseline(w, x, layers, budget_s=12.0, act="swiglu"):
     """The oracle through the chained layers (RMSNorm, router, 16 experts, combine, residual)
     for a bounded sample of starting tokens, on this host's cores.  Expert bytes are copied
     from the device pools outside the timing."""
@@ -153,7 +156,7 @@ def chain_cpu_baseline(w, x, layers, budget_s=12.0):
             exps = [S.ExpertBytes(*[lay["pool"][nm][int(e)].cpu().numpy() for nm in S.TENSOR_NAMES])
                     for e in idx[0]]
             t0 = time.perf_counter()
-            d = np.stack([oracle.expert_forward(xn[0], ex) for ex in exps])[None]
+            d = np.stack([oracle.expert_forward(xn[0], ex, act=act) for ex in exps])[None]
             y = oracle.combine(gates, d)
             xt = oracle.residual_add_bf16(xt, y)
             t_used += time.perf_counter() - t0
@@ -190,7 +193,8 @@ def bench_chain(w, args, torch, S, k3x):
         bd = torch.from_numpy(b).to(dev)
         layers.append({"pool_dev": pool_dev, "W": W, "b": b, "Wd": Wd, "bd": bd,
                        "pool": k3x.k3x_expert_pool_create(pool_dev, hidden=w.H, inter=w.I,
-                                                          n_experts=w.E),
+                                                          n_experts=w.E,
+                                                          activation=args.activation),
                        "rdesc": k3x.router_desc(Wd, bd, w.topk)})
     R = ROTATE
     x = S.normal_bf16(w.seed, S.P_X, 0, (R, w.H))
@@ -291,7 +295,8 @@ def bench_chain(w, args, torch, S, k3x):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": w.name, "tokens": 1, "layers": w.layers, "experts": w.E,
+        "config": {"workload": w.name, "activation": args.activation, "tokens": 1,
+                   "layers": w.layers, "experts": w.E,
                    "hidden": w.H, "inter": w.I, "topk": w.topk, "router": True,
                    "zipf_bias": w.zipf, "weights": "mxfp4 (e2m1 + e8m0 per 32)",
                    "resident_expert_gb": round(need / 1e9, 1), "rotated_batches": R},
@@ -308,7 +313,8 @@ def bench_chain(w, args, torch, S, k3x):
     if not args.no_cpu_baseline:
         log("timing the oracle on the host (bounded sample)")
         out["cpu_baseline"] = chain_cpu_baseline(
-            w, x, [{"W": l_["W"], "b": l_["b"], "pool": l_["pool_dev"]} for l_ in layers])
+            w, x, [{"W": l_["W"], "b": l_["b"], "pool": l_["pool_dev"]} for l_ in layers],
+            act=ORACLE_ACT[args.activation])
     print(json.dumps(out), flush=True)
 
 
@@ -394,6 +400,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="decode_t1_e896_router")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--activation", choices=("swiglu", "situ"), default="swiglu",
+                    help="gated activation of the expert pool (situ: SiTU-GLU, caps 4 and 25)")
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"))
     args = ap.parse_args()
@@ -426,7 +434,8 @@ def main():
 
     log(f"generating pool: E={w.E} H={w.H} I={w.I}")
     pool_dev = S.device_pool(w.seed, 0, w.E, w.H, w.I)
-    pool = k3x.k3x_expert_pool_create(pool_dev, hidden=w.H, inter=w.I, n_experts=w.E)
+    pool = k3x.k3x_expert_pool_create(pool_dev, hidden=w.H, inter=w.I, n_experts=w.E,
+                                      activation=args.activation)
     R = 1 if prefill else ROTATE
     x = S.normal_bf16(w.seed, S.P_X, 0, (R * w.T, w.H))
     xs = [torch.from_numpy(x[r * w.T:(r + 1) * w.T].view(np.int16)).to(dev) for r in range(R)]
@@ -557,7 +566,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": w.name, "tokens": w.T, "experts": w.E, "hidden": w.H,
+        "config": {"workload": w.name, "activation": args.activation, "tokens": w.T,
+                   "experts": w.E, "hidden": w.H,
                    "inter": w.I, "topk": w.topk, "router": w.router, "zipf_bias": w.zipf,
                    "weights": "mxfp4 (e2m1 + e8m0 per 32)", "rotated_batches": R,
                    "distinct_experts_per_step": round(mean_U, 2)},
@@ -577,7 +587,7 @@ def main():
         log("timing the oracle on the host (bounded sample)")
         di = np.concatenate([r_[0] for r_ in routes_np]) if routes_np else None
         dg = np.concatenate([r_[1] for r_ in routes_np]) if routes_np else None
-        out["cpu_baseline"] = cpu_baseline(w, x, W, b, di, dg, pool_dev)
+        out["cpu_baseline"] = cpu_baseline(w, x, W, b, di, dg, pool_dev, act=ORACLE_ACT[args.activation])
     print(json.dumps(out), flush=True)
 
 

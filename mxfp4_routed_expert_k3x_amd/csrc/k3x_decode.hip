@@ -207,8 +207,10 @@ __device__ __forceinline__ LaneOffsets lane_offsets(int lane, int ngroups, uint3
 
 // Streams rows r0 .. rlast of one expert (one matrix, or W1 and W3 side by side when kW13)
 // against the activations x0/x1: rows are loaded three ahead of the arithmetic and finished
-// four at a time.  For each row, lane (row - r) & 3 of the group of four calls
-// emit(row, sum_a, sum_b) with the row's full dot products (sum_b only when kW13).
+// four at a time.  After each group of four rows r .. r + 3 every lane calls
+// emit(r + lane, sum_a, sum_b, valid, n): lanes 0..3 with valid set hold the full dot
+// products of row r + lane (sum_b only when kW13), and n (the same on every lane) is the
+// number of valid rows in the group.
 template <bool kW13, typename Emit>
 __device__ __forceinline__ void stream_rows(const uint8_t* wa, const uint8_t* sa,
                                             const uint8_t* wb, const uint8_t* sb, int r0,
@@ -238,15 +240,18 @@ __device__ __forceinline__ void stream_rows(const uint8_t* wa, const uint8_t* sa
       if (kW13) row_leaves(C[i], x0, x1, v[kW13 ? 1 : 0][i], v[kW13 ? 1 : 0][4 + i]);
     }
     reduce8(v, lane);
-    if (lane < 4 && r + lane <= rlast) emit(r + lane, v[0][0], v[kW13 ? 1 : 0][0]);
+    emit(r + lane, v[0][0], v[kW13 ? 1 : 0][0], lane < 4 && r + lane <= rlast,
+         min(4, rlast - r + 1));
   }
 }
 
 // g = W1 x, u = W3 x, h = bf16(silu(g) * u) (or of SiTU-GLU, with each tanh the float nearest
 // to its double value, products and quotients in fp32 left to right) for every (slot, row)
-// of this wave's run.  A run
-// is cut at slot boundaries into segments of one expert; a dropped slot's segment is skipped.
-// Workgroup 0 also writes the number of dropped slots.
+// of this wave's run.  A run is cut at slot boundaries into segments of one expert; a dropped
+// slot's segment is skipped.  The finished (g, u) pairs are parked in the wave's LDS slice
+// and their activations evaluated up to 64 at a time, one per lane, so the double-precision
+// exponentials and tanh do not hold up the row loop.  Workgroup 0 also writes the number of
+// dropped slots.
 __global__ __launch_bounds__(256) void decode_w13(DecodeArgs a) {
   const int lane = threadIdx.x % kWave;
   const int my_idx = lane < a.topk ? a.idx[lane] : -1;
@@ -263,6 +268,32 @@ __global__ __launch_bounds__(256) void decode_w13(DecodeArgs a) {
   float x0[32], x1[32];
   load_act(a.act, lane, ngroups, x0, x1);
 
+  __shared__ float s_g[4][kWave], s_u[4][kWave];
+  __shared__ int32_t s_o[4][kWave];
+  const int wv = threadIdx.x / kWave;
+  uint16_t* hout = static_cast<uint16_t*>(a.out);
+  int nbuf = 0;  // parked rows of this wave (the same on every lane)
+  auto flush = [&]() {
+    __builtin_amdgcn_wave_barrier();
+    if (lane < nbuf) {
+      const float gv = s_g[wv][lane], uv = s_u[wv][lane];
+      const float ex = (float)exp(-(double)gv);
+      float hv;
+      if (a.gact == K3X_ACT_SITU) {
+        const float tg = (float)tanh((double)(gv / a.b1));
+        const float sg = 1.0f / (1.0f + ex);
+        const float av = a.b1 * tg * sg;
+        const float tu = (float)tanh((double)(uv / a.b2));
+        hv = av * (a.b2 * tu);
+      } else {
+        hv = (gv / (1.0f + ex)) * uv;
+      }
+      hout[s_o[wv][lane]] = (uint16_t)f32_to_bf16_bits(hv);
+    }
+    __builtin_amdgcn_wave_barrier();
+    nbuf = 0;
+  };
+
   for (int gs = g0; gs < g1;) {
     const int slot = gs / a.rows;
     const int r0 = gs - slot * a.rows;
@@ -270,24 +301,21 @@ __global__ __launch_bounds__(256) void decode_w13(DecodeArgs a) {
     const int e = __builtin_amdgcn_readlane(my_idx, slot);
     gs += n;
     if (!expert_ok(e, a.E)) continue;
-    uint16_t* h = static_cast<uint16_t*>(a.out) + (size_t)slot * a.rows;
+    const int obase = slot * a.rows;
     stream_rows<true>(a.wa + (size_t)e * a.st_wa, a.sa + (size_t)e * a.st_sa,
                       a.wb + (size_t)e * a.st_wb, a.sb + (size_t)e * a.st_sb, r0, r0 + n - 1,
-                      wrow, srow, lo, x0, x1, lane, [&](int r, float gv, float uv) {
-                        const float ex = (float)exp(-(double)gv);
-                        float hv;
-                        if (a.gact == K3X_ACT_SITU) {
-                          const float tg = (float)tanh((double)(gv / a.b1));
-                          const float sg = 1.0f / (1.0f + ex);
-                          const float av = a.b1 * tg * sg;
-                          const float tu = (float)tanh((double)(uv / a.b2));
-                          hv = av * (a.b2 * tu);
-                        } else {
-                          hv = (gv / (1.0f + ex)) * uv;
+                      wrow, srow, lo, x0, x1, lane,
+                      [&](int r, float gv, float uv, bool valid, int nv) {
+                        if (valid) {
+                          s_g[wv][nbuf + lane] = gv;
+                          s_u[wv][nbuf + lane] = uv;
+                          s_o[wv][nbuf + lane] = obase + r;
                         }
-                        h[r] = (uint16_t)f32_to_bf16_bits(hv);
+                        nbuf += nv;
+                        if (nbuf > kWave - 4) flush();
                       });
   }
+  flush();
 }
 
 // y = sum_j gates[j] * (W2_j h_j) over valid slots in slot order, with the combine in the
@@ -322,7 +350,9 @@ __global__ __launch_bounds__(kW2Waves * kWave) void decode_w2_combine(DecodeArgs
     float* d = dsh + slot * R - rb0;
     stream_rows<false>(a.wa + (size_t)e * a.st_wa, a.sa + (size_t)e * a.st_sa, nullptr, nullptr,
                        rb0, rlast, wrow, srow, lo, x0, x1, lane,
-                       [&](int r, float dv, float) { d[r] = dv; });
+                       [&](int r, float dv, float, bool valid, int) {
+                         if (valid) d[r] = dv;
+                       });
   }
   __syncthreads();
   if (threadIdx.x < nr) {
