@@ -201,6 +201,67 @@ def test_moe_split_sort(dev, orc, T, H, I, E, k):
     assert_y_close(_np(y), y_ref, "split sort")
 
 
+def test_strided_pool(dev, orc):
+    """Experts laid out with padding between them (per-tensor byte strides larger than the
+    dense size, as when experts sit inside a bigger arena): single-token decode stays
+    bit-exact and the multi-token paths match the oracle."""
+    torch, k3x = dev
+    E, H, I = 6, 512, 512
+    _log(f"case: strided pool E={E} H={H} I={I}")
+    host = S.host_pool(23, 0, E, H, I)
+    dense = S.device_pool(23, 0, E, H, I)
+    tensors, strides = {}, []
+    for t, name in enumerate(S.TENSOR_NAMES):
+        per = dense[name][0].numel()
+        stride = per + 256 * (t + 1)  # every stride a multiple of 16, all different
+        buf = torch.full((E * stride,), 0xA5, dtype=torch.uint8, device="cuda")
+        for e in range(E):
+            buf[e * stride:e * stride + per] = dense[name][e].reshape(-1)
+        tensors[name] = buf
+        strides.append(stride)
+    pool = k3x.k3x_expert_pool_create(tensors, hidden=H, inter=I, n_experts=E, strides=strides)
+    for T, k in ((1, 4), (9, 3), (40, 2)):
+        x = S.normal_bf16(23 + T, S.P_X, 0, (T, H))
+        rng = np.random.default_rng(T)
+        idx = rng.integers(0, E, (T, k)).astype(np.int32)
+        _, gates = S.uniform_routing(23 + T, T, k, k)
+        y, _ = k3x.moe_forward(pool, _t(torch, x), _t(torch, idx), _t(torch, gates))
+        torch.cuda.synchronize()
+        y_ref, _ = orc.moe_forward(host, x, idx, gates)
+        if T == 1:
+            assert np.array_equal(_np(y), y_ref)
+        else:
+            assert_y_close_oracle(_np(y), y_ref,
+                                  lambda: orc.moe_forward(host, x, idx, gates, acc="f64")[0],
+                                  f"strided pool T={T}")
+
+
+def test_largest_rows(dev, orc):
+    """Rows of 128 groups (H = I = 4096, the largest the exact decode kernel and the LDS
+    scale buffer of the sorted-tile kernels take): decode bit-exact, prefill path within
+    tolerance."""
+    torch, k3x = dev
+    E, H, I = 6, 4096, 4096
+    _log(f"case: largest rows E={E} H={H} I={I}")
+    host = S.host_pool(29, 0, E, H, I)
+    pool = _pool(torch, k3x, S.device_pool(29, 0, E, H, I), E, H, I)
+    for T, k in ((1, 6), (24, 2)):
+        x = S.normal_bf16(29 + T, S.P_X, 0, (T, H))
+        rng = np.random.default_rng(29 + T)
+        idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+        _, gates = S.uniform_routing(29 + T, T, k, k)
+        y, _ = k3x.moe_forward(pool, _t(torch, x), _t(torch, idx), _t(torch, gates))
+        torch.cuda.synchronize()
+        y_ref, _ = orc.moe_forward(host, x, idx, gates)
+        if T == 1:
+            assert np.array_equal(_np(y), y_ref)
+        else:
+            r = assert_y_close_oracle(_np(y), y_ref,
+                                      lambda: orc.moe_forward(host, x, idx, gates, acc="f64")[0],
+                                      f"largest rows T={T}")
+            _log(f"  rel_l2={r[0]:.3e} max_abs={r[1]:.3e}")
+
+
 def test_moe_zero_tokens(dev):
     torch, k3x = dev
     _log("case: moe T=0")
