@@ -191,6 +191,7 @@ def _rng(*key) -> np.random.Generator:
 
 # draw purposes (part of the PCG64 seed key)
 P_X, P_WR, P_BIAS, P_ROUTE, P_GATE, P_ZIPF = 1, 2, 3, 4, 5, 6
+P_DOWN, P_UP, P_SH1, P_SH3, P_SH2, P_NORMW = 7, 8, 9, 10, 11, 12
 
 
 def normal_bf16(seed, purpose, layer, shape, std=1.0) -> np.ndarray:
@@ -375,3 +376,41 @@ def host_pool(seed, layer, E, H, I, experts=None, lo=SCALE_LO, count=SCALE_COUNT
     ids = range(E) if experts is None else experts
     exps = [expert_bytes(seed, layer, e, H, I, lo=lo, count=count) for e in ids]
     return {n: np.stack([getattr(ex, n) for ex in exps]) for n in TENSOR_NAMES}
+
+
+# ------------------------------------------------------------------------------------------
+# The latent MoE block around the routed experts (kimi-k3-in-c README, Part II section 9):
+# full width D, latent L (the routed experts' hidden), routed inter I, S = n_shared * I.
+# ------------------------------------------------------------------------------------------
+@dataclass(frozen=True)
+class LatentShape:
+    D: int = 7168
+    L: int = H_K3
+    I: int = I_K3
+    n_shared: int = 2
+    E: int = 896
+    topk: int = TOPK_K3
+
+    @property
+    def S(self) -> int:
+        return self.n_shared * self.I
+
+
+LATENT_K3 = LatentShape()
+LATENT_SEED = 0x4B335800 + 6
+
+
+def latent_inputs(seed, layer, D, L, S, E):
+    """Dense bf16 weights of one latent block, each N(0, 1/fan_in) so activations keep unit
+    scale: router Wr [E][D] (std 0.02, as the routed workloads), bias N(0, 0.01), down [L][D],
+    up [D][L], shared sh1, sh3 [S][D], sh2 [D][S]; the latent RMSNorm weight 1 + N(0, 0.1)."""
+    return {
+        "Wr": normal_bf16(seed, P_WR, layer, (E, D), std=0.02),
+        "bias": normal_f32(seed, P_BIAS, layer, (E,), std=0.01),
+        "down": normal_bf16(seed, P_DOWN, layer, (L, D), std=D ** -0.5),
+        "up": normal_bf16(seed, P_UP, layer, (D, L), std=L ** -0.5),
+        "sh1": normal_bf16(seed, P_SH1, layer, (S, D), std=D ** -0.5),
+        "sh3": normal_bf16(seed, P_SH3, layer, (S, D), std=D ** -0.5),
+        "sh2": normal_bf16(seed, P_SH2, layer, (D, S), std=S ** -0.5),
+        "norm_w": (1.0 + normal_f32(seed, P_NORMW, layer, (L,), std=0.1)).astype(np.float32),
+    }

@@ -72,6 +72,8 @@ def lib():
         L.oracle_rmsnorm_bf16.argtypes = [P, ci, ci, ctypes.c_float, P]
         L.oracle_residual_add_bf16.restype = ci
         L.oracle_residual_add_bf16.argtypes = [P, P, ci, ci]
+        L.oracle_rmsnorm_w_f32.restype = ci
+        L.oracle_rmsnorm_w_f32.argtypes = [P, ci, ci, P, ctypes.c_float, P]
         L.oracle_glu.restype = ci
         L.oracle_glu.argtypes = [P, P, i64, ci, ctypes.c_float, ctypes.c_float, P]
         for sfx in ("f32", "f64"):
@@ -91,6 +93,11 @@ def lib():
             f.restype = None
             f.argtypes = [P, i64, i64, P, P, P, P, P, P, ci, ctypes.c_float, ctypes.c_float,
                           P, P, P, P]
+            f = getattr(L, f"oracle_latent_block_{sfx}")
+            f.restype = i64
+            f.argtypes = [i64] * 7 + [P, P, P, ci, ctypes.c_float, P, P, P, P, P, P,
+                                      ctypes.c_float, P, P, P, P, P, P, ci, ctypes.c_float,
+                                      ctypes.c_float, ci, P]
             f = getattr(L, f"oracle_moe_forward_act_{sfx}")
             f.restype = i64
             f.argtypes = [i64, i64, i64, P, P, P, P, P, P, P, ci, ctypes.c_float, ctypes.c_float,
@@ -265,3 +272,49 @@ def threads() -> int:
     """OpenMP threads the oracle's parallel loops use."""
     n = os.environ.get("OMP_NUM_THREADS")
     return int(n) if n and n.isdigit() else (os.cpu_count() or 1)
+
+
+def rmsnorm_w_f32(x, w, eps):
+    """Weighted RMSNorm of fp32 rows -> bf16 bits (w None: weight 1)."""
+    x = _c(x, np.float32)
+    T, n = x.shape
+    out = np.empty((T, n), dtype=np.uint16)
+    wp = None if w is None else _c(w, np.float32)
+    if lib().oracle_rmsnorm_w_f32(_p(x), T, n, _p(wp), eps, _p(out)) != 0:
+        raise ValueError("oracle_rmsnorm_w_f32: bad arguments")
+    return out
+
+
+def latent_block(x_bf16, Wr, bias, topk, down, up, sh1, sh3, sh2, norm_w, eps, pool,
+                 act="swiglu", act_shared=("situ", 4.0, 25.0), renorm=1, routed_scale=1.0,
+                 acc="f32"):
+    """Stable LatentMoE block for T tokens.  x bf16 [T][D]; Wr bf16 [E][D]; down bf16 [L][D];
+    up bf16 [D][L]; sh1, sh3 bf16 [S][D]; sh2 bf16 [D][S]; norm_w fp32 [L] or None; pool the
+    routed experts (dense host tensors, hidden = L).  Returns (out fp32 [T][D], drops)."""
+    x = _c(x_bf16, np.uint16)
+    T, D = x.shape
+    Wr = _c(Wr, np.uint16)
+    E = Wr.shape[0]
+    down, up = _c(down, np.uint16), _c(up, np.uint16)
+    sh1, sh3, sh2 = _c(sh1, np.uint16), _c(sh3, np.uint16), _c(sh2, np.uint16)
+    L, S = down.shape[0], sh1.shape[0]
+    names = ("w1_packed", "w1_scale", "w3_packed", "w3_scale", "w2_packed", "w2_scale")
+    t = [_c(pool[n], np.uint8) for n in names]
+    I = t[0].shape[1]
+    assert down.shape == (L, D) and up.shape == (D, L) and sh2.shape == (D, S)
+    assert t[0].shape[2] == L // 2
+    b = None if bias is None else _c(bias, np.float32)
+    nw = None if norm_w is None else _c(norm_w, np.float32)
+    a, b1, b2 = _act(act)
+    ash, sb1, sb2 = _act(act_shared)
+    if ash == 1 and a == 1:
+        assert (sb1, sb2) == (b1, b2), "one pair of caps for routed and shared experts"
+    if ash == 1:
+        b1, b2 = sb1, sb2
+    out = np.empty((T, D), dtype=np.float32)
+    drops = getattr(lib(), f"oracle_latent_block_{_sfx(acc)}")(
+        T, D, L, I, S, E, topk, _p(x), _p(Wr), _p(b), renorm, routed_scale, _p(down), _p(up),
+        _p(sh1), _p(sh3), _p(sh2), _p(nw), eps, *[_p(a_) for a_ in t], a, b1, b2, ash, _p(out))
+    if drops < 0:
+        raise ValueError("oracle_latent_block: bad arguments")
+    return out, int(drops)

@@ -41,6 +41,12 @@
  *    order of additions matters, and it is fixed here.
  *  - Router sigmoid: computed in double from the float logit and rounded once to float.
  *  - The combine y = sum_j gate_j * d_j runs in ACC in slot order and is rounded at the end.
+ *  - Latent MoE block (README Part II section 9, the k3_moe listing): every vector that enters
+ *    a bf16 matrix is rounded to bf16 first (the input x, the latent z, the normalised
+ *    aggregate, the shared experts' activation); dense products are summed in ACC in
+ *    ascending k; the aggregate's RMSNorm sums squares in double in the 64-way order above and
+ *    scales as (x * inv) * w; the shared experts' output is added to the up-projection once,
+ *    in fp32.
  *
  * Build: cc -O2 -ffp-contract=off -fno-fast-math -fopenmp, once with
  * -DORACLE_ACC=float -DORACLE_SFX=f32 -DORACLE_COMMON=1 and once with
@@ -62,6 +68,11 @@
 #define ORC(name) ORACLE_CAT(name, ORACLE_SFX)
 
 typedef ORACLE_ACC acc_t;
+
+int oracle_rmsnorm_w_f32(const float *x, int T, int n, const float *w, float eps, uint16_t *out);
+int oracle_route(const uint16_t *x, int T, int H, const uint16_t *Wr, const float *bias, int E,
+                 int topk, int renorm, float routed_scale, int32_t *idx, float *gates,
+                 float *logits_out, float *scores_out);
 
 /* ----------------------------------------------------------------------------------------
  * Tables and bit helpers (README section 4; section 5 for bf16 widening)
@@ -189,6 +200,23 @@ int oracle_rmsnorm_bf16(const uint16_t *x, int T, int H, float eps, uint16_t *ou
       const float v = bf16_to_float(x[(size_t)t * H + h]) * inv * 1.0f;
       out[(size_t)t * H + h] = float_to_bf16(v);
     }
+  }
+  free(xd);
+  return 0;
+}
+
+/* Weighted RMSNorm of fp32 rows (README section 5, the RMSNorm of the floating point
+ * contract): ss = sum of squares in double in the fixed 64-way order, inv = (float)(1 /
+ * sqrt(ss / n + eps)), out = bf16((x * inv) * w) (w NULL: weight 1).  n % 8 == 0. */
+int oracle_rmsnorm_w_f32(const float *x, int T, int n, const float *w, float eps, uint16_t *out) {
+  if (T < 0 || n <= 0 || n % 8) return -1;
+  double *xd = (double *)malloc(sizeof(double) * (size_t)n);
+  for (int t = 0; t < T; ++t) {
+    const float *xt = x + (size_t)t * n;
+    for (int h = 0; h < n; ++h) xd[h] = (double)xt[h];
+    const double ss = sum64_products(xd, xd, n);
+    const float inv = (float)(1.0 / sqrt(ss / (double)n + (double)eps));
+    for (int h = 0; h < n; ++h) out[(size_t)t * n + h] = float_to_bf16(xt[h] * inv * (w ? w[h] : 1.0f));
   }
   free(xd);
   return 0;
@@ -364,4 +392,85 @@ int64_t ORC(oracle_moe_forward)(int64_t E, int64_t H, int64_t I, const uint8_t *
                                 const float *gates, int64_t topk, float *y) {
   return ORC(oracle_moe_forward_act)(E, H, I, w1p, w1s, w3p, w3s, w2p, w2s, strides, 0, 0.0f,
                                      0.0f, T, x, idx, gates, topk, y);
+}
+
+/* ----------------------------------------------------------------------------------------
+ * Stable LatentMoE block (README Part II section 9, the k3_moe listing), T tokens:
+ *   1. route on the full width D;  2. z = bf16(down . x), down bf16 [L][D];
+ *   3. accL = routed experts on z (the MoE forward above, activation act with caps b1, b2);
+ *   4. a = RMSNorm_w(accL) (norm_w fp32 [L], or skipped when norm_w is NULL: a = bf16(accL));
+ *   5. o = up . a, up bf16 [D][L];
+ *   6. shared experts on the ORIGINAL x, added unweighted: g = sh1 . x, u = sh3 . x (sh1, sh3
+ *      bf16 [S][D]), s = bf16(act_sh(g, u)), out = o + sh2 . s (sh2 bf16 [D][S]).
+ * Returns the number of dropped routed slots, or -1 on bad arguments.
+ * ---------------------------------------------------------------------------------------- */
+static void ORC(dense_rows)(const uint16_t *W, const uint16_t *v, int64_t rows, int64_t K,
+                            float *y) {
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r) {
+    acc_t a = 0;
+    for (int64_t k = 0; k < K; ++k)
+      a += (acc_t)bf16_to_float(W[r * K + k]) * (acc_t)bf16_to_float(v[k]);
+    y[r] = (float)a;
+  }
+}
+
+int64_t ORC(oracle_latent_block)(int64_t T, int64_t D, int64_t L, int64_t I, int64_t S,
+                                 int64_t E, int64_t topk, const uint16_t *x, const uint16_t *Wr,
+                                 const float *bias, int renorm, float rscale,
+                                 const uint16_t *down, const uint16_t *up, const uint16_t *sh1,
+                                 const uint16_t *sh3, const uint16_t *sh2, const float *norm_w,
+                                 float eps, const uint8_t *w1p, const uint8_t *w1s,
+                                 const uint8_t *w3p, const uint8_t *w3s, const uint8_t *w2p,
+                                 const uint8_t *w2s, int act, float b1, float b2, int act_sh,
+                                 float *out) {
+  if (T < 0 || D <= 0 || L <= 0 || I <= 0 || S <= 0 || D % 8 || L % 32 || I % 32 || E <= 0 ||
+      topk < 1 || topk > E)
+    return -1;
+  if (T == 0) return 0;
+  int32_t *idx = (int32_t *)malloc(sizeof(int32_t) * (size_t)(T * topk));
+  float *gates = (float *)malloc(sizeof(float) * (size_t)(T * topk));
+  uint16_t *z = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)(T * L));
+  float *acc = (float *)malloc(sizeof(float) * (size_t)(T * L));
+  uint16_t *a = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)(T * L));
+  const int64_t fmax = D > S ? (D > L ? D : L) : (S > L ? S : L);
+  float *f = (float *)malloc(sizeof(float) * (size_t)fmax);
+  float *g = (float *)malloc(sizeof(float) * (size_t)S);
+  float *u = (float *)malloc(sizeof(float) * (size_t)S);
+  uint16_t *sb = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)S);
+  int64_t drops = -1;
+  if (oracle_route(x, (int)T, (int)D, Wr, bias, (int)E, (int)topk, renorm, rscale, idx, gates,
+                   NULL, NULL) != 0)
+    goto done;
+  for (int64_t t = 0; t < T; ++t) {
+    ORC(dense_rows)(down, x + t * D, L, D, f);
+    for (int64_t i = 0; i < L; ++i) z[t * L + i] = float_to_bf16(f[i]);
+  }
+  drops = ORC(oracle_moe_forward_act)(E, L, I, w1p, w1s, w3p, w3s, w2p, w2s, NULL, act, b1, b2, T,
+                                      z, idx, gates, topk, acc);
+  if (norm_w) {
+    oracle_rmsnorm_w_f32(acc, (int)T, (int)L, norm_w, eps, a);
+  } else {
+    for (int64_t i = 0; i < T * L; ++i) a[i] = float_to_bf16(acc[i]);
+  }
+  for (int64_t t = 0; t < T; ++t) {
+    float *ot = out + t * D;
+    ORC(dense_rows)(up, a + t * L, D, L, ot);
+    ORC(dense_rows)(sh1, x + t * D, S, D, g);
+    ORC(dense_rows)(sh3, x + t * D, S, D, u);
+    for (int64_t i = 0; i < S; ++i) sb[i] = float_to_bf16(glu_one(g[i], u[i], act_sh, b1, b2));
+    ORC(dense_rows)(sh2, sb, D, S, f);
+    for (int64_t i = 0; i < D; ++i) ot[i] = ot[i] + f[i];
+  }
+done:
+  free(idx);
+  free(gates);
+  free(z);
+  free(acc);
+  free(a);
+  free(f);
+  free(g);
+  free(u);
+  free(sb);
+  return drops;
 }

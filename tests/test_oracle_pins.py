@@ -574,3 +574,107 @@ def test_situ_expert_against_brute_force(orc, acc):
     # the SiTU forward differs from the SwiGLU one (the option reaches the activation)
     y_sw, _ = orc.moe_forward(pool, x, idx, gates, acc=acc)
     assert not np.allclose(y, y_sw)
+
+
+# ------------------------------------------------------------------------------------------
+# Latent MoE block (kimi-k3-in-c README, Part II section 9, the k3_moe listing)
+# ------------------------------------------------------------------------------------------
+def _latent_case(seed, T=3, D=96, L=64, I=64, n_shared=2, E=6, k=3):
+    S_ = n_shared * I
+    w = S.latent_inputs(seed, 0, D, L, S_, E)
+    pool = _tiny_pool(seed, E, L, I, nan_scales=False)
+    x = S.normal_bf16(seed, S.P_X, 0, (T, D))
+    return w, pool, x, k
+
+
+def _bf16_round64(v):
+    return bf16_rne_from64(v)
+
+
+def test_latent_block_against_float64_algebra(orc):
+    """The whole block recomputed with numpy float64 dense algebra and the pinned pieces
+    (router, SiTU-GLU, E2M1/E8M0 decode), rounding to bf16 at the same points."""
+    w, pool, x, k = _latent_case(31)
+    act = ("situ", 4.0, 25.0)
+    out, drops = orc.latent_block(x, w["Wr"], w["bias"], k, w["down"], w["up"], w["sh1"],
+                                  w["sh3"], w["sh2"], w["norm_w"], 1e-6, pool, act=act,
+                                  act_shared=act, acc="f64")
+    assert drops == 0
+    idx, gates = orc.route(x, w["Wr"], w["bias"], k)
+    f = lambda a: bits_to_f(a)
+    down, up, sh1, sh3, sh2 = (f(w[n]) for n in ("down", "up", "sh1", "sh3", "sh2"))
+    for t in range(x.shape[0]):
+        xt = f(x[t])
+        z = _bf16_round64(down @ xt)
+        acc = np.zeros(down.shape[0])
+        for j in range(k):
+            e = int(idx[t, j])
+            W1 = dequant64(pool["w1_packed"][e], pool["w1_scale"][e])
+            W3 = dequant64(pool["w3_packed"][e], pool["w3_scale"][e])
+            W2 = dequant64(pool["w2_packed"][e], pool["w2_scale"][e])
+            g, u = (W1 @ z).astype(np.float32), (W3 @ z).astype(np.float32)
+            h = _bf16_round64(orc.glu(g, u, act).astype(np.float64))
+            acc += float(gates[t, j]) * (W2 @ h)
+        ss = math.fsum(acc.astype(np.float32).astype(np.float64) ** 2)
+        inv = 1.0 / math.sqrt(ss / len(acc) + 1e-6)
+        a = _bf16_round64(acc * inv * w["norm_w"].astype(np.float64))
+        o = up @ a
+        g, u = (sh1 @ xt).astype(np.float32), (sh3 @ xt).astype(np.float32)
+        s_ = _bf16_round64(orc.glu(g, u, act).astype(np.float64))
+        ref = o + sh2 @ s_
+        rel = np.linalg.norm(out[t] - ref) / np.linalg.norm(ref)
+        assert rel < 1e-6, (t, rel)
+    out32, _ = orc.latent_block(x, w["Wr"], w["bias"], k, w["down"], w["up"], w["sh1"],
+                                w["sh3"], w["sh2"], w["norm_w"], 1e-6, pool, act=act,
+                                act_shared=act)
+    assert np.linalg.norm(out32 - out) / np.linalg.norm(out) < 1e-4
+
+
+def test_latent_norm_is_on_the_aggregate(orc):
+    """The RMSNorm acts on the weighted sum of the experts: scaling every gate (routed_scale)
+    leaves the block's output unchanged up to eps and rounding, while without the norm the
+    routed part scales with the gates exactly."""
+    w, pool, x, k = _latent_case(37)
+    zero = np.zeros_like(w["sh2"])
+    common = (w["Wr"], w["bias"], k, w["down"], w["up"], w["sh1"], w["sh3"])
+    o1, _ = orc.latent_block(x, *common, w["sh2"], w["norm_w"], 1e-6, pool, routed_scale=1.0)
+    o2, _ = orc.latent_block(x, *common, w["sh2"], w["norm_w"], 1e-6, pool, routed_scale=2.0)
+    assert np.linalg.norm(o2 - o1) / np.linalg.norm(o1) < 1e-2
+    # no norm, no shared experts: doubling the gates doubles the output exactly
+    n1, _ = orc.latent_block(x, *common, zero, None, 1e-6, pool, routed_scale=1.0)
+    n2, _ = orc.latent_block(x, *common, zero, None, 1e-6, pool, routed_scale=2.0)
+    assert np.array_equal(n2, 2.0 * n1)
+    assert not np.allclose(n1, o1)
+
+
+def test_latent_shared_experts_added_unweighted(orc):
+    """With the shared down-projection sh2 zeroed the output is exactly the routed part; the
+    shared part alone (router bias steering the routed experts elsewhere) is the same for
+    any routing."""
+    w, pool, x, k = _latent_case(41)
+    zero = np.zeros_like(w["sh2"])
+    args = (w["Wr"], w["bias"], k, w["down"], w["up"], w["sh1"], w["sh3"])
+    full, _ = orc.latent_block(x, *args, w["sh2"], w["norm_w"], 1e-6, pool)
+    routed, _ = orc.latent_block(x, *args, zero, w["norm_w"], 1e-6, pool)
+    shared = full - routed
+    b2 = w["bias"].copy()
+    b2[:3] += 10.0  # forces experts 0..2
+    full2, _ = orc.latent_block(x, w["Wr"], b2, k, w["down"], w["up"], w["sh1"], w["sh3"],
+                                w["sh2"], w["norm_w"], 1e-6, pool)
+    routed2, _ = orc.latent_block(x, w["Wr"], b2, k, w["down"], w["up"], w["sh1"], w["sh3"],
+                                  zero, w["norm_w"], 1e-6, pool)
+    assert not np.allclose(routed, routed2)
+    assert np.allclose(full2 - routed2, shared, rtol=1e-5, atol=1e-5 * np.abs(shared).max())
+
+
+def test_weighted_rmsnorm(orc):
+    """Unit weight equals the bf16 RMSNorm on bf16-valued rows; a weight of 2 doubles the
+    output exactly; the constant-vector closed form."""
+    x = bits_to_f(S.normal_bf16(3, S.P_X, 0, (4, 256))).astype(np.float32)
+    xb = S.f32_to_bf16_bits(x)
+    one = orc.rmsnorm_w_f32(x, None, 1e-6)
+    assert np.array_equal(one, orc.rmsnorm_bf16(xb, 1e-6))
+    two = orc.rmsnorm_w_f32(x, np.full(256, 2.0, np.float32), 1e-6)
+    assert np.array_equal(bits_to_f(two), 2.0 * bits_to_f(one))
+    c = np.full((1, 64), 3.0, np.float32)
+    assert np.all(bits_to_f(orc.rmsnorm_w_f32(c, None, 0.0)) == 1.0)
