@@ -64,6 +64,8 @@ def lib():
         L.oracle_bf16_to_f32.argtypes = [ctypes.c_uint16]
         L.oracle_f32_to_bf16.restype = ctypes.c_uint16
         L.oracle_f32_to_bf16.argtypes = [ctypes.c_float]
+        L.oracle_f32_to_bf16_n.restype = None
+        L.oracle_f32_to_bf16_n.argtypes = [P, i64, P]
         L.oracle_sum64.restype = ctypes.c_double
         L.oracle_sum64.argtypes = [P, P, i64]
         L.oracle_route.restype = ci
@@ -74,6 +76,8 @@ def lib():
         L.oracle_residual_add_bf16.argtypes = [P, P, ci, ci]
         L.oracle_rmsnorm_w_f32.restype = ci
         L.oracle_rmsnorm_w_f32.argtypes = [P, ci, ci, P, ctypes.c_float, P]
+        L.oracle_dense64_bf16.restype = ci
+        L.oracle_dense64_bf16.argtypes = [P, P, i64, i64, P]
         L.oracle_glu.restype = ci
         L.oracle_glu.argtypes = [P, P, i64, ci, ctypes.c_float, ctypes.c_float, P]
         for sfx in ("f32", "f64"):
@@ -136,6 +140,14 @@ def bf16_to_f32(bits: int) -> float:
 
 def f32_to_bf16(v: float) -> int:
     return int(lib().oracle_f32_to_bf16(float(v)))
+
+
+def bf16_round(a):
+    """fp32 array -> bf16 bits, round to nearest even (quiet NaNs kept)."""
+    a = _c(a, np.float32)
+    out = np.empty(a.shape, dtype=np.uint16)
+    lib().oracle_f32_to_bf16_n(_p(a), a.size, _p(out))
+    return out
 
 
 def sum64(a, b) -> float:
@@ -283,6 +295,19 @@ def rmsnorm_w_f32(x, w, eps):
     if lib().oracle_rmsnorm_w_f32(_p(x), T, n, _p(wp), eps, _p(out)) != 0:
         raise ValueError("oracle_rmsnorm_w_f32: bad arguments")
     return out
+
+
+def dense64_bf16(W, v):
+    """The contract's bf16 matmul in the fixed 64-way double order: y[r] = (float) sum64(W[r] . v),
+    W bf16 [rows][K], v bf16 [K] (K % 8 == 0) -> fp32 [rows]."""
+    W = _c(W, np.uint16)
+    v = _c(v, np.uint16)
+    rows, K = W.shape
+    assert v.shape == (K,)
+    y = np.empty(rows, dtype=np.float32)
+    if lib().oracle_dense64_bf16(_p(W), _p(v), rows, K, _p(y)) != 0:
+        raise ValueError("oracle_dense64_bf16: bad arguments")
+    return y
 
 
 def latent_block(x_bf16, Wr, bias, topk, down, up, sh1, sh3, sh2, norm_w, eps, pool,

@@ -43,10 +43,13 @@
  *  - The combine y = sum_j gate_j * d_j runs in ACC in slot order and is rounded at the end.
  *  - Latent MoE block (README Part II section 9, the k3_moe listing): every vector that enters
  *    a bf16 matrix is rounded to bf16 first (the input x, the latent z, the normalised
- *    aggregate, the shared experts' activation); dense products are summed in ACC in
- *    ascending k; the aggregate's RMSNorm sums squares in double in the 64-way order above and
- *    scales as (x * inv) * w; the shared experts' output is added to the up-projection once,
- *    in fp32.
+ *    aggregate, the shared experts' activation); the dense bf16 products follow the
+ *    contract's bf16 matmul (README Part II section 5: products and sums in double, the
+ *    result rounded once to float), with the double sum taken in the 64-way order above
+ *    instead of the contract's four interleaved accumulators (the same reading as the router
+ *    logits); the aggregate's RMSNorm sums squares in double in the 64-way order and scales as
+ *    (x * inv) * w; the shared experts' output is added to the up-projection once, in fp32.
+ *    Only the routed experts inside the block depend on ACC.
  *
  * Build: cc -O2 -ffp-contract=off -fno-fast-math -fopenmp, once with
  * -DORACLE_ACC=float -DORACLE_SFX=f32 -DORACLE_COMMON=1 and once with
@@ -70,6 +73,7 @@
 typedef ORACLE_ACC acc_t;
 
 int oracle_rmsnorm_w_f32(const float *x, int T, int n, const float *w, float eps, uint16_t *out);
+int oracle_dense64_bf16(const uint16_t *W, const uint16_t *v, int64_t rows, int64_t K, float *y);
 int oracle_route(const uint16_t *x, int T, int H, const uint16_t *Wr, const float *bias, int E,
                  int topk, int renorm, float routed_scale, int32_t *idx, float *gates,
                  float *logits_out, float *scores_out);
@@ -133,8 +137,39 @@ float oracle_e2m1(int code) { return e2m1_value((unsigned)code); }
 float oracle_e8m0(int s) { return e8m0_value((unsigned)s); }
 float oracle_bf16_to_f32(uint16_t b) { return bf16_to_float(b); }
 uint16_t oracle_f32_to_bf16(float f) { return float_to_bf16(f); }
+void oracle_f32_to_bf16_n(const float *x, int64_t n, uint16_t *out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = float_to_bf16(x[i]);
+}
 
 double oracle_sum64(const double *a, const double *b, int64_t n) { return sum64_products(a, b, n); }
+
+/* The contract's bf16 matmul (README Part II section 5) in the fixed 64-way order:
+ * y[r] = (float) sum64(W[r][k] * v[k]), W bf16 [rows][K], v bf16 [K], K % 8 == 0.  The
+ * products of two bf16 values are exact in double.  Returns -1 on bad arguments. */
+int oracle_dense64_bf16(const uint16_t *W, const uint16_t *v, int64_t rows, int64_t K, float *y) {
+  if (rows < 0 || K <= 0 || K % 8) return -1;
+  double *vd = (double *)malloc(sizeof(double) * (size_t)K);
+  if (!vd) return -1;
+  for (int64_t k = 0; k < K; ++k) vd[k] = (double)bf16_to_float(v[k]);
+  int bad = 0;
+#pragma omp parallel
+  {
+    double *wd = (double *)malloc(sizeof(double) * (size_t)K);
+    if (!wd) {
+#pragma omp atomic write
+      bad = 1;
+    } else {
+#pragma omp for schedule(static)
+      for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t k = 0; k < K; ++k) wd[k] = (double)bf16_to_float(W[r * K + k]);
+        y[r] = (float)sum64_products(wd, vd, K);
+      }
+      free(wd);
+    }
+  }
+  free(vd);
+  return bad ? -1 : 0;
+}
 
 /* --------------------------------------------------------------------------------------
  * Router (README section 9).  x bf16 [T][H], Wr bf16 [E][H], bias fp32 [E] or NULL.
@@ -404,17 +439,6 @@ int64_t ORC(oracle_moe_forward)(int64_t E, int64_t H, int64_t I, const uint8_t *
  *      bf16 [S][D]), s = bf16(act_sh(g, u)), out = o + sh2 . s (sh2 bf16 [D][S]).
  * Returns the number of dropped routed slots, or -1 on bad arguments.
  * ---------------------------------------------------------------------------------------- */
-static void ORC(dense_rows)(const uint16_t *W, const uint16_t *v, int64_t rows, int64_t K,
-                            float *y) {
-#pragma omp parallel for schedule(static)
-  for (int64_t r = 0; r < rows; ++r) {
-    acc_t a = 0;
-    for (int64_t k = 0; k < K; ++k)
-      a += (acc_t)bf16_to_float(W[r * K + k]) * (acc_t)bf16_to_float(v[k]);
-    y[r] = (float)a;
-  }
-}
-
 int64_t ORC(oracle_latent_block)(int64_t T, int64_t D, int64_t L, int64_t I, int64_t S,
                                  int64_t E, int64_t topk, const uint16_t *x, const uint16_t *Wr,
                                  const float *bias, int renorm, float rscale,
@@ -424,8 +448,8 @@ int64_t ORC(oracle_latent_block)(int64_t T, int64_t D, int64_t L, int64_t I, int
                                  const uint8_t *w3p, const uint8_t *w3s, const uint8_t *w2p,
                                  const uint8_t *w2s, int act, float b1, float b2, int act_sh,
                                  float *out) {
-  if (T < 0 || D <= 0 || L <= 0 || I <= 0 || S <= 0 || D % 8 || L % 32 || I % 32 || E <= 0 ||
-      topk < 1 || topk > E)
+  if (T < 0 || D <= 0 || L <= 0 || I <= 0 || S <= 0 || D % 8 || L % 32 || I % 32 || S % 8 ||
+      E <= 0 || topk < 1 || topk > E)
     return -1;
   if (T == 0) return 0;
   int32_t *idx = (int32_t *)malloc(sizeof(int32_t) * (size_t)(T * topk));
@@ -443,7 +467,10 @@ int64_t ORC(oracle_latent_block)(int64_t T, int64_t D, int64_t L, int64_t I, int
                    NULL, NULL) != 0)
     goto done;
   for (int64_t t = 0; t < T; ++t) {
-    ORC(dense_rows)(down, x + t * D, L, D, f);
+    if (oracle_dense64_bf16(down, x + t * D, L, D, f) != 0) {
+      drops = -1;
+      goto done;
+    }
     for (int64_t i = 0; i < L; ++i) z[t * L + i] = float_to_bf16(f[i]);
   }
   drops = ORC(oracle_moe_forward_act)(E, L, I, w1p, w1s, w3p, w3s, w2p, w2s, NULL, act, b1, b2, T,
@@ -455,11 +482,17 @@ int64_t ORC(oracle_latent_block)(int64_t T, int64_t D, int64_t L, int64_t I, int
   }
   for (int64_t t = 0; t < T; ++t) {
     float *ot = out + t * D;
-    ORC(dense_rows)(up, a + t * L, D, L, ot);
-    ORC(dense_rows)(sh1, x + t * D, S, D, g);
-    ORC(dense_rows)(sh3, x + t * D, S, D, u);
+    if (oracle_dense64_bf16(up, a + t * L, D, L, ot) != 0 ||
+        oracle_dense64_bf16(sh1, x + t * D, S, D, g) != 0 ||
+        oracle_dense64_bf16(sh3, x + t * D, S, D, u) != 0) {
+      drops = -1;
+      goto done;
+    }
     for (int64_t i = 0; i < S; ++i) sb[i] = float_to_bf16(glu_one(g[i], u[i], act_sh, b1, b2));
-    ORC(dense_rows)(sh2, sb, D, S, f);
+    if (oracle_dense64_bf16(sh2, sb, D, S, f) != 0) {
+      drops = -1;
+      goto done;
+    }
     for (int64_t i = 0; i < D; ++i) ot[i] = ot[i] + f[i];
   }
 done:

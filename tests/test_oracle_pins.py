@@ -123,6 +123,13 @@ def test_bf16_helpers(orc):
     want = bf16_rne_from64(v.astype(np.float64))
     got = np.array([orc.bf16_to_f32(orc.f32_to_bf16(float(a))) for a in v])
     assert np.array_equal(got, want)
+    # the array form: the same roundings, the ties, infinities and a NaN that stays a NaN
+    vv = np.concatenate([v, np.array([tie_down, tie_up, np.inf, -np.inf], dtype=np.float32)])
+    bits = orc.bf16_round(vv)
+    assert np.array_equal(bits_to_f(bits[:2000]), want)
+    assert list(bits[2000:]) == [0x3F80, 0x3F82, 0x7F80, 0xFF80]
+    nan = orc.bf16_round(np.array([np.nan], dtype=np.float32))[0]
+    assert (nan & 0x7F80) == 0x7F80 and (nan & 0x7F) != 0
 
 
 # ------------------------------------------------------------------------------------------
@@ -589,6 +596,53 @@ def _latent_case(seed, T=3, D=96, L=64, I=64, n_shared=2, E=6, k=3):
 
 def _bf16_round64(v):
     return bf16_rne_from64(v)
+
+
+def test_dense64_exact_on_integers(orc):
+    """The contract's bf16 matmul on small integers: every product and partial sum is exact,
+    so each row must equal its integer dot product whatever the order (a dropped term, a
+    swapped index or a transposed operand changes it)."""
+    rng = np.random.default_rng(5)
+    rows, K = 7, 1032
+    Wi = rng.integers(-8, 9, (rows, K))
+    vi = rng.integers(-8, 9, K)
+    W = S.f32_to_bf16_bits(Wi.astype(np.float32))
+    v = S.f32_to_bf16_bits(vi.astype(np.float32))
+    y = orc.dense64_bf16(W, v)
+    assert np.array_equal(y, (Wi @ vi).astype(np.float32))
+    assert not np.array_equal(orc.dense64_bf16(W[:, ::-1].copy(), v), y)
+
+
+def test_dense64_within_one_ulp_of_exact_sum(orc):
+    """Random bf16 rows: the double sum rounded to float lies within one float ulp of the
+    exactly rounded sum of the exact products (math.fsum)."""
+    rng = np.random.default_rng(6)
+    rows, K = 9, 3584
+    W = S.f32_to_bf16_bits(rng.standard_normal((rows, K)).astype(np.float32))
+    v = S.f32_to_bf16_bits(rng.standard_normal(K).astype(np.float32))
+    y = orc.dense64_bf16(W, v)
+    Wf, vf = bits_to_f(W), bits_to_f(v)
+    for r in range(rows):
+        exact = np.float32(math.fsum((Wf[r] * vf).tolist()))
+        assert abs(float(y[r]) - float(exact)) <= float(np.spacing(np.abs(exact))), r
+
+
+def test_dense64_fixed_64_way_order(orc):
+    """The order of the double sum is the fixed 64-way one: products 2^60, 1 and -2^60 in the
+    chunks of partials 0, 1 and 2 fold as (2^60 + -2^60) + 1 = 1, where ascending order (and
+    the contract's four interleaved accumulators) lose the 1 to rounding and give 0."""
+    K = 512
+    Wf = np.zeros(K, dtype=np.float32)
+    vf = np.zeros(K, dtype=np.float32)
+    Wf[0], vf[0] = 2.0 ** 30, 2.0 ** 30       # chunk 0 -> partial 0
+    Wf[8], vf[8] = 1.0, 1.0                   # chunk 1 -> partial 1
+    Wf[16], vf[16] = -(2.0 ** 30), 2.0 ** 30  # chunk 2 -> partial 2
+    y = orc.dense64_bf16(S.f32_to_bf16_bits(Wf)[None], S.f32_to_bf16_bits(vf))
+    assert y[0] == 1.0
+    seq = 0.0
+    for k in range(K):
+        seq += float(Wf[k]) * float(vf[k])
+    assert seq == 0.0
 
 
 def test_latent_block_against_float64_algebra(orc):
