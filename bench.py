@@ -49,11 +49,13 @@ ROTATE = 64
 ORACLE_ACT = {"swiglu": "swiglu", "situ": ("situ", 4.0, 25.0)}
 COPY_PROBE_BYTES = 1 << 30
 KERNEL_SOURCES = ("k3x_decode.hip", "k3x_moe.hip", "k3x_prefill.hip", "k3x_router.hip")
+LATENT_SOURCES = KERNEL_SOURCES + ("k3x_dense.hip",)
 # rocprofv3 kernel names of the library's launch names
 KERNEL_SYMBOLS = {"w13_decode": "decode_w13", "w2_combine_decode": "decode_w2_combine",
                   "w13_prefill": "gemm_prefill<true>", "w2_prefill": "gemm_prefill<false>",
                   "w13_grouped": "gemm_decode<true>", "w2_grouped": "gemm_decode<false>",
-                  "route_scores": "route_scores", "route_select": "route_select"}
+                  "route_scores": "route_scores", "route_select": "route_select",
+                  "latent_in": "latent_in", "latent_out": "latent_out"}
 
 
 def log(*a):
@@ -96,6 +98,20 @@ def per_kernel_work(name, H, I, E, T, topk, U):
     if name == "residual_rmsnorm_bf16":
         return T * H * 10, 4.0 * T * H
     return 0, 0.0
+
+
+def latent_kernel_work(name, sh, T):
+    """Algorithmic (bytes, flops) of one launch of the latent block's dense kernels (sh: a
+    k3x_synth.LatentShape), T tokens in the launch."""
+    D, L, Sx = sh.D, sh.L, sh.S
+    E = sh.E
+    if name == "latent_in":  # router, down, sh1, sh3 rows; x in; scores, z, s out
+        return ((E + L + 2 * Sx) * D * 2 + T * D * 2 + T * (E * 4 + L * 2 + Sx * 2),
+                2.0 * T * D * (E + L + 2 * Sx))
+    if name == "latent_out":  # up, sh2 rows; acc, s, norm weight in; out (fp32)
+        return (D * (L + Sx) * 2 + T * (L * 4 + Sx * 2) + L * 4 + T * D * 4,
+                2.0 * T * D * (L + Sx))
+    return per_kernel_work(name, L, sh.I, sh.E, T, sh.topk, min(sh.E, T * sh.topk))
 
 
 def cpu_baseline(w, x, W, b, dev_idx, dev_gates, pool_dev, budget_s=12.0, act="swiglu"):
@@ -318,10 +334,178 @@ def bench_chain(w, args, torch, S, k3x):
     print(json.dumps(out), flush=True)
 
 
-def sources_hash():
+LATENT_WORKLOADS = {"latent_t1_e896": 1, "latent_t8_e896": 8}
+
+
+def latent_cpu_baseline(sh, x, w, pool_dev, topk, budget_s=12.0):
+    """The oracle's latent block, one token at a time, for a bounded sample of the rotated
+    tokens, on this host's cores.  The bytes of the experts each token routes to are copied
+    from the device pool outside the timing (the others stay untouched zero pages)."""
+    import k3x_synth as S
+    import oracle
+
+    shapes = {n: tuple(pool_dev[n].shape) for n in S.TENSOR_NAMES}
+    n_tok, t_used, i = 0, 0.0, 0
+    while t_used < budget_s:
+        xt = x[i % len(x):i % len(x) + 1].copy()
+        i += 1
+        idx, _ = oracle.route(xt, w["Wr"], w["bias"], topk)
+        host = {n: np.zeros(shapes[n], dtype=np.uint8) for n in S.TENSOR_NAMES}
+        for e in set(int(v) for v in idx.ravel()):
+            for n in S.TENSOR_NAMES:
+                host[n][e] = pool_dev[n][e].cpu().numpy()
+        t0 = time.perf_counter()
+        oracle.latent_block(xt, w["Wr"], w["bias"], topk, w["down"], w["up"], w["sh1"],
+                            w["sh3"], w["sh2"], w["norm_w"], 1e-6, host, act="swiglu",
+                            act_shared=("situ", 4.0, 25.0))
+        t_used += time.perf_counter() - t0
+        n_tok += 1
+    return {
+        "value": n_tok / t_used,
+        "unit": "tokens/s",
+        "cores": oracle.threads(),
+        "kind": "oracle",
+        "sample": f"{n_tok} token(s) through the whole latent block (router on {sh.D}, down, "
+                  f"{topk} of {sh.E} experts, latent RMSNorm, up, 2 shared experts), "
+                  f"{t_used:.1f} s of oracle time; expert bytes copied to the host outside the "
+                  f"timing",
+    }
+
+
+def bench_latent(args, torch, S, k3x):
+    """The latent MoE block (router on the full width, down-projection, the routed experts
+    on the latent, RMSNorm of the aggregate, up-projection, two shared experts) on T decode
+    tokens, one HIP graph per rotated batch."""
+    T = LATENT_WORKLOADS[args.workload]
+    sh = S.LATENT_K3
+    steps = args.steps if args.steps is not None else 200
+    warmup = args.warmup if args.warmup is not None else 20
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    seed = S.LATENT_SEED
+    log(f"generating the latent block: D={sh.D} L={sh.L} S={sh.S} E={sh.E} I={sh.I}")
+    pool_dev = S.device_pool(seed, 0, sh.E, sh.L, sh.I)
+    pool = k3x.k3x_expert_pool_create(pool_dev, hidden=sh.L, inter=sh.I, n_experts=sh.E)
+    w = S.latent_inputs(seed, 0, sh.D, sh.L, sh.S, sh.E)
+    dv = {n: torch.from_numpy(w[n].view(np.int16) if w[n].dtype == np.uint16 else w[n]).to(dev)
+          for n in w}
+    d = k3x.latent_desc(dv["down"], dv["up"], dv["sh1"], dv["sh3"], dv["sh2"], dv["norm_w"],
+                        eps=1e-6, latent_norm=1, shared_activation="situ")
+    r = k3x.router_desc(dv["Wr"], dv["bias"], sh.topk)
+    R = ROTATE
+    x = S.normal_bf16(seed, S.P_X, 0, (R * T, sh.D))
+    xs = [torch.from_numpy(x[i * T:(i + 1) * T].view(np.int16)).to(dev) for i in range(R)]
+    out = torch.empty((T, sh.D), dtype=torch.float32, device=dev)
+    ws = k3x.alloc_workspace(k3x.k3x_latent_workspace_size(d, pool, r, T), dev)
+    moe_off = k3x.k3x_latent_ws_layout(d, pool, r, T)["moe"]
+
+    def step(i):
+        k3x.k3x_latent_forward(d, pool, r, xs[i], T, out, ws)
+
+    out_eager = []
+    for i in range(R):
+        step(i)
+        torch.cuda.synchronize()
+        out_eager.append(out.clone())
+    if k3x.k3x_fetch_drops(ws[moe_off:]):
+        sys.exit("run invalid: dropped slots")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(0)
+    torch.cuda.current_stream().wait_stream(side)
+    graphs = []
+    for i in range(R):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(i)
+        graphs.append(g)
+    for i in range(R):
+        graphs[i].replay()
+        torch.cuda.synchronize()
+        if not torch.equal(out, out_eager[i]):
+            sys.exit(f"graph replay of batch {i} differs from the eager result")
+        step((i + 1) % R)
+        torch.cuda.synchronize()
+
+    for i in range(warmup):
+        graphs[i % R].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        graphs[i % R].replay()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    prof = k3x.k3x_profiler_create(steps * 16 + 16)
+    torch.cuda.synchronize()
+    k3x.k3x_profiler_attach(prof)
+    for i in range(steps):
+        step(i % R)
+    torch.cuda.synchronize()
+    k3x.k3x_profiler_attach(None)
+    durs = k3x.profiler_durations(prof)
+    k3x.k3x_profiler_destroy(prof)
+
+    kernels = {}
+    for name, ms in durs.items():
+        nbytes, flops = latent_kernel_work(name, sh, T)
+        avg_s = float(np.mean(ms)) * 1e-3
+        kernels[name] = {"launches": len(ms), "avg_us": round(avg_s * 1e6, 3),
+                         "alg_bytes": int(nbytes), "gbps": round(nbytes / avg_s / 1e9, 1),
+                         "tflops": round(flops / avg_s / 1e12, 2)}
+    dominant = max(kernels, key=lambda n: kernels[n]["avg_us"] * kernels[n]["launches"])
+    dk = kernels[dominant]
+    traffic = traffic_for(args.workload, dominant)
+    roof = {"bound": "hbm", "achieved": dk["gbps"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(dk["gbps"] / PEAK_HBM_GBS, 4),
+            "traffic": int(traffic) if traffic is not None else None, "kernel": dominant,
+            "alg_bytes": dk["alg_bytes"]}
+    w13, w2 = expert_tensor_bytes(sh.L, sh.I)
+    dense = (sh.L * sh.D * 2 + sh.S * sh.D * 2) * 2 + sh.E * sh.D * 2
+    U = min(sh.E, T * sh.topk)
+    path_bytes = dense + U * (w13 + w2)
+    ksum = sum(k["avg_us"] * k["launches"] for k in kernels.values()) / steps * 1e-6
+    res = {
+        "metric": METRIC,
+        "value": round(steps * T / wall, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(wall / steps * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "tokens": T, "hidden": sh.D, "latent": sh.L,
+                   "shared_inter": sh.S, "experts": sh.E, "inter": sh.I, "topk": sh.topk,
+                   "router": True, "routed_activation": "swiglu", "shared_activation": "situ",
+                   "weights": "routed mxfp4 (e2m1 + e8m0 per 32), dense bf16",
+                   "rotated_batches": R},
+        "roofline": roof,
+        "path": {"kernel_sum_us": round(ksum * 1e6, 3),
+                 "alg_bytes_per_step": int(path_bytes),
+                 "hbm_gbps_kernel_sum": round(path_bytes / ksum / 1e9, 1),
+                 "hbm_frac_kernel_sum": round(path_bytes / ksum / 1e9 / PEAK_HBM_GBS, 4),
+                 "hbm_gbps_wall": round(path_bytes / (wall / steps) / 1e9, 1),
+                 "timed_region": "HIP graph replay, one graph per rotated batch"},
+        "kernels": kernels,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the oracle on the host (bounded sample)")
+        res["cpu_baseline"] = latent_cpu_baseline(sh, x, w, pool_dev, sh.topk)
+    print(json.dumps(res), flush=True)
+
+
+def sources_hash(workload=None):
+    """Hash of the kernel sources a workload runs (the routed path's, plus the dense kernels
+    for the latent block)."""
     import hashlib
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in LATENT_SOURCES if workload in LATENT_WORKLOADS else KERNEL_SOURCES:
         with open(os.path.join(ROOT, "mxfp4_routed_expert_k3x_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -359,7 +543,7 @@ def traffic_from(f_csv, w_csv, cf_csv, cw_csv, workload):
     sf, nf = copy_scale(cf_csv, "FETCH_SIZE")
     sw, nw = copy_scale(cw_csv, "WRITE_SIZE")
     lines = [f"# HBM traffic of {workload} from rocprofv3 counters",
-             f"sources_hash={sources_hash()}",
+             f"sources_hash={sources_hash(workload)}",
              f"copy_fetch_scale={sf:.4f} (from {nf} copies of {COPY_PROBE_BYTES} B)",
              f"copy_write_scale={sw:.4f} (from {nw} copies)"]
     fetch = _counter_rows(f_csv, "FETCH_SIZE")
@@ -386,7 +570,7 @@ def traffic_for(workload, kernel):
     vals, ok = {}, False
     for line in open(path):
         if line.startswith("sources_hash="):
-            ok = line.strip().split("=", 1)[1] == sources_hash()
+            ok = line.strip().split("=", 1)[1] == sources_hash(workload)
         elif line.startswith("traffic "):
             parts = line.split()
             vals[parts[1]] = float(parts[2])
@@ -420,9 +604,11 @@ def main():
     import mxfp4_routed_expert_k3x_amd as k3x
 
     k3x.load_library()
+    if args.workload in LATENT_WORKLOADS:
+        return bench_latent(args, torch, S, k3x)
     wl = {w.name: w for w in S.WORKLOADS.values()}
     if args.workload not in wl:
-        sys.exit(f"unknown workload {args.workload}; one of {sorted(wl)}")
+        sys.exit(f"unknown workload {args.workload}; one of {sorted(wl) + sorted(LATENT_WORKLOADS)}")
     w = wl[args.workload]
     if w.layers != 1:
         return bench_chain(w, args, torch, S, k3x)

@@ -181,6 +181,59 @@ k3x_status k3x_residual_add_rmsnorm_bf16(void *x, const float *y, int32_t T, int
                                          float eps, void *out, void *stream);
 
 /* ------------------------------------------------------------------------------------------
+ * Latent MoE block (README Part II section 9, the k3_moe listing): the routed experts inside
+ * the block that wraps them.  Per token:
+ *   1. route on the full width D (router desc with hidden = D);
+ *   2. z = bf16(down . x);
+ *   3. acc = the routed experts on z (pool with hidden = L, the latent), as k3x_moe_forward;
+ *   4. a = bf16 RMSNorm of the AGGREGATE acc with norm_weight (latent_norm != 0; the sum of
+ *      squares in double in a fixed order, (acc * inv) * w), or a = bf16(acc);
+ *   5. out = up . a;
+ *   6. out += sh2 . s, s = bf16(act(sh1 . x, sh3 . x)): the shared experts on the ORIGINAL x,
+ *      added unweighted (act = shared_activation with the caps).
+ * Dense products are bf16 x bf16 summed in fp32; the path is sized for decode batches (larger
+ * ones read the dense weights once per 8 tokens).
+ * ---------------------------------------------------------------------------------------- */
+typedef struct k3x_latent_desc {
+  int32_t hidden;           /* D: multiple of 512, <= 8192 (7168 in the checkpoint)        */
+  int32_t shared_inter;     /* S = n_shared * inter: multiple of 512, L + S <= 9728 (6144) */
+  const void *down;         /* bf16 [L][D], L = the routed pool's hidden                    */
+  const void *up;           /* bf16 [D][L]                                                  */
+  const void *sh1, *sh3;    /* bf16 [S][D]: gate and up rows of the shared experts          */
+  const void *sh2;          /* bf16 [D][S]                                                  */
+  int32_t latent_norm;      /* nonzero: RMSNorm of the aggregate (the checkpoint: 1)        */
+  const float *norm_weight; /* fp32 [L], or NULL for weight 1                               */
+  float eps;                /* RMSNorm eps, >= 0                                            */
+  int32_t shared_activation; /* k3x_activation of the shared experts                        */
+  float situ_b1, situ_b2;   /* K3X_ACT_SITU caps of the shared experts                      */
+} k3x_latent_desc;
+
+/* Bytes of device workspace k3x_latent_forward needs (0 if the arguments are invalid). */
+size_t k3x_latent_workspace_size(const k3x_latent_desc *d, const k3x_pool *p,
+                                 const k3x_router_desc *r, int32_t T);
+
+/* Runs the block on T tokens.  x_bf16 bf16 [T][D] -> out fp32 [T][D] (overwritten); all device
+ * pointers 16-byte aligned; ws: at least k3x_latent_workspace_size bytes, 256-byte aligned.
+ * Refuses (K3X_E_INVALID_ARG) NULL weights or mismatched widths (router hidden != D, pool
+ * hidden != L) and (K3X_E_UNSUPPORTED) D, L or S not multiples of 512 or above 8192, or
+ * L + S above 9728 (the K3 block: 3584 + 6144), or topk above 64.  Dropped
+ * routed slots are counted in the workspace as for k3x_moe_forward (k3x_fetch_drops on
+ * ws + offs[5] of k3x_latent_ws_layout). */
+k3x_status k3x_latent_forward(const k3x_latent_desc *d, const k3x_pool *p,
+                              const k3x_router_desc *r, const void *x_bf16, int32_t T,
+                              float *out, void *ws, size_t ws_bytes, void *stream);
+
+/* Byte offsets, inside the block's workspace for T tokens, of its intermediates (256-byte
+ * aligned), readable once k3x_latent_forward has completed on its stream:
+ *   offs[0] idx int32 [T][topk]   offs[1] gates fp32 [T][topk]   offs[2] z bf16 [T][L]
+ *   offs[3] acc fp32 [T][L] (the aggregate of the routed experts)
+ *   offs[4] s bf16 [T][S] (the shared experts' activation)
+ *   offs[5] the routed experts' workspace (its drop counter first, read by k3x_fetch_drops).
+ * Returns K3X_OK, or the error k3x_latent_forward would return for these arguments. */
+k3x_status k3x_latent_ws_layout(const k3x_latent_desc *d, const k3x_pool *p,
+                                const k3x_router_desc *r, int32_t T, size_t offs[6]);
+
+/* ------------------------------------------------------------------------------------------
  * Kernel timing (instrumentation only; the work done is unchanged).  While a profiler is
  * attached to the calling thread, every kernel the library enqueues from that thread is
  * bracketed by two HIP events recorded on the same stream, up to the profiler's capacity.

@@ -67,10 +67,29 @@ class k3x_router_desc(ctypes.Structure):
     ]
 
 
+class k3x_latent_desc(ctypes.Structure):
+    _fields_ = [
+        ("hidden", ctypes.c_int32),
+        ("shared_inter", ctypes.c_int32),
+        ("down", ctypes.c_void_p),
+        ("up", ctypes.c_void_p),
+        ("sh1", ctypes.c_void_p),
+        ("sh3", ctypes.c_void_p),
+        ("sh2", ctypes.c_void_p),
+        ("latent_norm", ctypes.c_int32),
+        ("norm_weight", ctypes.c_void_p),
+        ("eps", ctypes.c_float),
+        ("shared_activation", ctypes.c_int32),
+        ("situ_b1", ctypes.c_float),
+        ("situ_b2", ctypes.c_float),
+    ]
+
+
 EXPORTS = (
     "k3x_status_str", "k3x_last_error", "k3x_expert_pool_create", "k3x_expert_pool_destroy",
     "k3x_route_workspace_size", "k3x_route_topk", "k3x_moe_workspace_size", "k3x_moe_forward",
     "k3x_fetch_drops", "k3x_rmsnorm_bf16", "k3x_residual_add_bf16", "k3x_residual_add_rmsnorm_bf16",
+    "k3x_latent_workspace_size", "k3x_latent_forward", "k3x_latent_ws_layout",
     "k3x_profiler_create", "k3x_profiler_destroy", "k3x_profiler_attach", "k3x_profiler_reset",
     "k3x_profiler_count", "k3x_profiler_read",
 )
@@ -112,6 +131,13 @@ def load_library(path: str = LIB_PATH):
     L.k3x_residual_add_rmsnorm_bf16.restype = ctypes.c_int
     L.k3x_residual_add_rmsnorm_bf16.argtypes = [P, P, I32, I32, ctypes.c_float, P, P]
     L.k3x_profiler_create.restype = ctypes.c_int
+    LD, RD = ctypes.POINTER(k3x_latent_desc), ctypes.POINTER(k3x_router_desc)
+    L.k3x_latent_workspace_size.restype = SZ
+    L.k3x_latent_workspace_size.argtypes = [LD, P, RD, I32]
+    L.k3x_latent_ws_layout.restype = ctypes.c_int
+    L.k3x_latent_ws_layout.argtypes = [LD, P, RD, I32, ctypes.POINTER(SZ)]
+    L.k3x_latent_forward.restype = ctypes.c_int
+    L.k3x_latent_forward.argtypes = [LD, P, RD, P, I32, P, P, SZ, P]
     L.k3x_profiler_create.argtypes = [I32, ctypes.POINTER(P)]
     L.k3x_profiler_destroy.restype = None
     L.k3x_profiler_destroy.argtypes = [P]
@@ -267,6 +293,46 @@ def k3x_residual_add_bf16(x, y, T: int, H: int, stream=None):
 def k3x_residual_add_rmsnorm_bf16(x, y, T: int, H: int, eps: float, out, stream=None):
     _check(lib().k3x_residual_add_rmsnorm_bf16(_ptr(x), _ptr(y), int(T), int(H), float(eps),
                                                _ptr(out), _stream(stream)))
+
+
+# ------------------------------------------------------------------------------------------
+# Latent MoE block
+# ------------------------------------------------------------------------------------------
+def latent_desc(down, up, sh1, sh3, sh2, norm_weight=None, eps=1e-5, latent_norm=1,
+                shared_activation="situ", situ_b1=4.0, situ_b2=25.0) -> k3x_latent_desc:
+    """down bf16 [L][D], up [D][L], sh1/sh3 [S][D], sh2 [D][S] (device tensors of bf16 bits);
+    norm_weight fp32 [L] or None (weight 1)."""
+    d = k3x_latent_desc()
+    d.hidden, d.shared_inter = int(down.shape[1]), int(sh1.shape[0])
+    d.down, d.up, d.sh1, d.sh3, d.sh2 = (_ptr(t) for t in (down, up, sh1, sh3, sh2))
+    d.latent_norm = int(latent_norm)
+    d.norm_weight = _ptr(norm_weight)
+    d.eps = float(eps)
+    d.shared_activation = {"swiglu": K3X_ACT_SWIGLU, "situ": K3X_ACT_SITU}[shared_activation]
+    d.situ_b1, d.situ_b2 = float(situ_b1), float(situ_b2)
+    return d
+
+
+def k3x_latent_workspace_size(d: k3x_latent_desc, pool: Pool, r: k3x_router_desc, T: int) -> int:
+    return int(lib().k3x_latent_workspace_size(ctypes.byref(d), pool.handle, ctypes.byref(r),
+                                               int(T)))
+
+
+LATENT_WS_FIELDS = ("idx", "gates", "z", "acc", "s", "moe")
+
+
+def k3x_latent_ws_layout(d: k3x_latent_desc, pool: Pool, r: k3x_router_desc, T: int) -> dict:
+    """{name: byte offset} of the block's intermediates in its workspace."""
+    offs = (ctypes.c_size_t * 6)()
+    _check(lib().k3x_latent_ws_layout(ctypes.byref(d), pool.handle, ctypes.byref(r), int(T), offs))
+    return dict(zip(LATENT_WS_FIELDS, (int(v) for v in offs)))
+
+
+def k3x_latent_forward(d: k3x_latent_desc, pool: Pool, r: k3x_router_desc, x, T: int, out, ws,
+                       ws_bytes=None, stream=None):
+    nbytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    _check(lib().k3x_latent_forward(ctypes.byref(d), pool.handle, ctypes.byref(r), _ptr(x),
+                                    int(T), _ptr(out), _ptr(ws), int(nbytes), _stream(stream)))
 
 
 # ------------------------------------------------------------------------------------------

@@ -189,6 +189,90 @@ k3x_status k3x_moe_forward(const k3x_pool* p, const void* x_bf16, int32_t T, con
   return K3X_OK;
 }
 
+static k3x_status check_latent(const k3x_latent_desc* d, const k3x_pool* p,
+                               const k3x_router_desc* r, int32_t T) {
+  if (!d || !p) return fail(K3X_E_INVALID_ARG, "latent: NULL desc or pool");
+  k3x_status st = check_router(r);
+  if (st != K3X_OK) return st;
+  if (T < 0) return fail(K3X_E_INVALID_ARG, "latent: T %d < 0", T);
+  if (!d->down || !d->up || !d->sh1 || !d->sh3 || !d->sh2)
+    return fail(K3X_E_INVALID_ARG, "latent: NULL dense weight");
+  if (r->hidden != d->hidden)
+    return fail(K3X_E_INVALID_ARG, "latent: router hidden %d != block hidden %d", r->hidden,
+                d->hidden);
+  if (r->n_experts != p->E)
+    return fail(K3X_E_INVALID_ARG, "latent: router experts %d != pool experts %d", r->n_experts,
+                p->E);
+  if (r->topk > 64) return fail(K3X_E_UNSUPPORTED, "latent: topk %d above 64", r->topk);
+  const int32_t dims[3] = {d->hidden, p->H, d->shared_inter};
+  const char* names[3] = {"hidden", "latent", "shared_inter"};
+  for (int i = 0; i < 3; ++i)
+    if (dims[i] <= 0 || dims[i] % 512 || dims[i] > 8192)
+      return fail(K3X_E_UNSUPPORTED, "latent: %s %d must be a positive multiple of 512, <= 8192",
+                  names[i], dims[i]);
+  if (p->H + d->shared_inter > 9728)
+    return fail(K3X_E_UNSUPPORTED, "latent: latent %d + shared_inter %d above 9728", p->H,
+                d->shared_inter);
+  if (!(d->eps >= 0.0f) || !std::isfinite(d->eps))
+    return fail(K3X_E_INVALID_ARG, "latent: eps %g must be finite and >= 0", (double)d->eps);
+  if (d->shared_activation != K3X_ACT_SWIGLU && d->shared_activation != K3X_ACT_SITU)
+    return fail(K3X_E_INVALID_ARG, "latent: unknown shared activation %d", d->shared_activation);
+  if (d->shared_activation == K3X_ACT_SITU &&
+      !(std::isfinite(d->situ_b1) && std::isfinite(d->situ_b2) && d->situ_b1 > 0.0f &&
+        d->situ_b2 > 0.0f))
+    return fail(K3X_E_INVALID_ARG, "latent: SiTU caps %g, %g must be finite and > 0",
+                (double)d->situ_b1, (double)d->situ_b2);
+  const void* dense[5] = {d->down, d->up, d->sh1, d->sh3, d->sh2};
+  for (int i = 0; i < 5; ++i)
+    if (!aligned(dense[i], 16))
+      return fail(K3X_E_UNSUPPORTED, "latent: dense weight %d not 16-byte aligned", i);
+  if (d->norm_weight && !aligned(d->norm_weight, 16))
+    return fail(K3X_E_UNSUPPORTED, "latent: norm weight not 16-byte aligned");
+  if ((int64_t)T * r->topk > (int64_t)1 << 26)
+    return fail(K3X_E_UNSUPPORTED, "latent: T * topk above 2^26");
+  return K3X_OK;
+}
+
+k3x_status k3x_latent_ws_layout(const k3x_latent_desc* d, const k3x_pool* p,
+                                const k3x_router_desc* r, int32_t T, size_t offs[6]) {
+  k3x_status st = check_latent(d, p, r, T);
+  if (st != K3X_OK) return st;
+  if (!offs) return fail(K3X_E_INVALID_ARG, "latent_ws_layout: NULL offs");
+  const k3x::LatentLayout L = k3x::latent_layout(*d, *p, r->n_experts, T, r->topk);
+  const size_t o[6] = {L.idx, L.gates, L.z, L.acc, L.s, L.moe};
+  for (int i = 0; i < 6; ++i) offs[i] = o[i];
+  return K3X_OK;
+}
+
+size_t k3x_latent_workspace_size(const k3x_latent_desc* d, const k3x_pool* p,
+                                 const k3x_router_desc* r, int32_t T) {
+  if (check_latent(d, p, r, T) != K3X_OK) return 0;
+  const size_t moe = k3x_moe_workspace_size(p, T, r->topk);
+  if (!moe) return 0;
+  return k3x::latent_layout(*d, *p, r->n_experts, T, r->topk).moe + moe;
+}
+
+k3x_status k3x_latent_forward(const k3x_latent_desc* d, const k3x_pool* p,
+                              const k3x_router_desc* r, const void* x_bf16, int32_t T,
+                              float* out, void* ws, size_t ws_bytes, void* stream) {
+  k3x_status st = check_latent(d, p, r, T);
+  if (st != K3X_OK) return st;
+  const size_t need = k3x_latent_workspace_size(d, p, r, T);
+  if (!ws || ws_bytes < need || !aligned(ws, 256))
+    return fail(K3X_E_WORKSPACE, "latent_forward: workspace %zu bytes, need %zu (256-byte aligned)",
+                ws_bytes, need);
+  if (T == 0) return K3X_OK;
+  if (!x_bf16 || !out) return fail(K3X_E_INVALID_ARG, "latent_forward: NULL x or out");
+  if (!aligned(x_bf16, 16) || !aligned(out, 16))
+    return fail(K3X_E_UNSUPPORTED, "latent_forward: x and out must be 16-byte aligned");
+  const k3x::LatentLayout L = k3x::latent_layout(*d, *p, r->n_experts, T, r->topk);
+  const k3x::MoeLayout ML = k3x::moe_layout(p->E, p->H, p->I, T, r->topk);
+  hipError_t e = k3x::launch_latent(*d, *p, *r, static_cast<const uint16_t*>(x_bf16), T, out,
+                                    static_cast<uint8_t*>(ws), L, ML, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "latent_forward");
+  return K3X_OK;
+}
+
 k3x_status k3x_fetch_drops(const void* ws, int64_t* n, void* stream) {
   if (!ws || !n) return fail(K3X_E_INVALID_ARG, "fetch_drops: NULL ws or n");
   int64_t v = 0;

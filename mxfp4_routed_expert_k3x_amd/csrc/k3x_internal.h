@@ -135,6 +135,9 @@ namespace k3x {
 // ---------------------------------------------------------------------------------------
 hipError_t launch_route(const k3x_router_desc& r, const uint16_t* x, int32_t T, int32_t* idx,
                         float* gates, float* scores, hipStream_t s);
+// The selection alone, on scores fp32 [T][E] already computed (the latent block's own pass).
+hipError_t launch_route_select(const k3x_router_desc& r, int32_t T, const float* scores,
+                               int32_t* idx, float* gates, hipStream_t s);
 
 hipError_t launch_moe(const k3x_pool& p, const uint16_t* x, int32_t T, const int32_t* idx,
                       const float* gates, int32_t topk, float* y, uint8_t* ws,
@@ -146,6 +149,22 @@ size_t decode_exact_ws(const k3x_pool& p, int32_t topk, size_t* off_h);
 hipError_t launch_decode_exact(const k3x_pool& p, const uint16_t* x, const int32_t* idx,
                                const float* gates, int32_t topk, float* y, uint8_t* ws,
                                hipStream_t s);
+
+// Latent MoE block (k3x_dense.hip): workspace layout and launcher.
+struct LatentLayout {
+  size_t scores;  // router scores fp32 [T][E]
+  size_t idx;     // int32 [T][topk]
+  size_t gates;   // fp32 [T][topk]
+  size_t z;       // bf16 [T][L] latent input of the routed experts
+  size_t acc;     // fp32 [T][L] their aggregate
+  size_t s;       // bf16 [T][S] shared experts' activation
+  size_t moe;     // the routed experts' workspace
+};
+LatentLayout latent_layout(const k3x_latent_desc& d, const k3x_pool& p, int32_t E, int32_t T,
+                           int32_t topk);
+hipError_t launch_latent(const k3x_latent_desc& d, const k3x_pool& p, const k3x_router_desc& r,
+                         const uint16_t* x, int32_t T, float* out, uint8_t* ws,
+                         const LatentLayout& L, const MoeLayout& ML, hipStream_t s);
 
 // Prefill-sized grouped GEMMs (k3x_prefill.hip): expert tiles of up to 128 slots.
 int prefill_tile_tokens();

@@ -4,11 +4,14 @@
 // scores renormalised by their float sum and scaled by routed_scale.
 //
 // Kernel 1 (route_scores): one wave per (expert, block of 4 tokens).  The expert's weight row
-// stays in registers while the wave sums the block's tokens side by side.  Lane L owns the 8-element chunks
-// whose index is L mod 64 and sums their exact bf16*bf16 products in double, in ascending
-// order; the 64 lane partials are then folded p[L] += p[L + s] for s = 32 .. 1 with
-// down-shuffles.  The float logit goes through a double sigmoid rounded once to float.
+// stays in registers while the wave sums the block's tokens side by side.  Lane L owns the
+// 8-element chunks whose index is L mod 64 and sums their exact bf16*bf16 products in double,
+// in ascending order; the 64 lane partials are then folded p[L] += p[L + s] for s = 32 .. 1
+// with down-shuffles.  The float logit goes through a double sigmoid rounded once to float.
 // This fixes the summation order completely, so the scores are reproducible bit for bit.
+// For widths that are multiples of 512 (up to 8192) the row is loaded whole and at once (a
+// fixed number of 16-byte chunks per lane) and the block's tokens are staged in LDS while the
+// row is in flight; other widths take a guarded loop that reads the tokens from memory.
 //
 // Kernel 2 (route_select): one workgroup per token.  A radix select finds the selection
 // score of the topk-th expert under the total order (larger c first, then lower index), so
@@ -85,6 +88,76 @@ __global__ __launch_bounds__(256) void route_scores(const uint16_t* __restrict__
       }
     }
   }
+}
+
+// The same scores for H = 512 * NCH: the wave's weight row is requested first (NCH chunks per
+// lane, no guards), the NT-token block is staged in LDS meanwhile, then summed in the order
+// above.  Slots of tokens past T are zero-filled and their sums dropped.
+template <int NCH, int NT>
+__global__ __launch_bounds__(256) void route_scores_staged(const uint16_t* __restrict__ x,
+                                                           const uint16_t* __restrict__ W,
+                                                           int32_t T, int32_t H, int32_t E,
+                                                           float* __restrict__ scores) {
+  extern __shared__ uint4 xs[];  // [NT][H / 8]
+  const int lane = threadIdx.x % kWave;
+  const int e = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  const int t0 = blockIdx.y * NT;
+  const int nt = min(NT, T - t0);
+  const int cpr = NCH * kWave;
+  uint4 wv[NCH];
+  const uint4* wrow = reinterpret_cast<const uint4*>(W + (size_t)(e < E ? e : E - 1) * H);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) wv[i] = wrow[lane + kWave * i];
+  __builtin_amdgcn_sched_barrier(0);
+  for (int i = threadIdx.x; i < NT * cpr; i += blockDim.x)
+    xs[i] = i < nt * cpr ? reinterpret_cast<const uint4*>(x + (size_t)(t0 + i / cpr) * H)[i % cpr]
+                         : make_uint4(0, 0, 0, 0);
+  __syncthreads();
+  if (e >= E) return;
+  double acc[NT];
+#pragma unroll
+  for (int k = 0; k < NT; ++k) acc[k] = 0.0;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const uint32_t ws[4] = {wv[i].x, wv[i].y, wv[i].z, wv[i].w};
+#pragma unroll
+    for (int k = 0; k < NT; ++k) {
+      const uint4 xv = xs[k * cpr + lane + kWave * i];
+      const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc[k] = acc[k] + (double)bf16_bits_to_f32(xw[j] & 0xFFFFu) *
+                              (double)bf16_bits_to_f32(ws[j] & 0xFFFFu);
+        acc[k] = acc[k] + (double)bf16_bits_to_f32(xw[j] >> 16) *
+                              (double)bf16_bits_to_f32(ws[j] >> 16);
+      }
+    }
+    if (NT > 1) {  // one chunk's tokens live at a time
+#pragma unroll
+      for (int k = 0; k < NT; ++k) asm volatile("" : "+v"(acc[k]));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < NT; ++k) {
+    double a = acc[k];
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) a = a + __shfl_down(a, s, kWave);
+    if (lane == 0 && k < nt) {
+      const float l = (float)a;
+      scores[(size_t)(t0 + k) * E + e] = (float)(1.0 / (1.0 + exp(-(double)l)));
+    }
+  }
+}
+
+typedef void (*ScoresKernel)(const uint16_t*, const uint16_t*, int32_t, int32_t, int32_t, float*);
+
+template <int... N>
+ScoresKernel staged_kernel(int nch, int nt) {
+  constexpr ScoresKernel k1[] = {route_scores_staged<N, 1>...};
+  constexpr ScoresKernel k4[] = {route_scores_staged<N, kRouteTokBlock>...};
+  return (nt == 1 ? k1 : k4)[nch - 1];
 }
 
 // (c, index) total order: true when candidate b beats a.  Index -1 means "no candidate".
@@ -260,24 +333,40 @@ __global__ __launch_bounds__(kSelThreads) void route_select(const float* __restr
 
 }  // namespace
 
-hipError_t launch_route(const k3x_router_desc& r, const uint16_t* x, int32_t T, int32_t* idx,
-                        float* gates, float* scores, hipStream_t s) {
+hipError_t launch_route_select(const k3x_router_desc& r, int32_t T, const float* scores,
+                               int32_t* idx, float* gates, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  const int E = r.n_experts, H = r.hidden;
-  dim3 g1((E + 3) / 4, (T + kRouteTokBlock - 1) / kRouteTokBlock);
-  const uint16_t* W = static_cast<const uint16_t*>(r.weight);
-  hipError_t err;
-  if (H <= 64 * 8 * 8)
-    err = launch("route_scores", route_scores<8>, g1, dim3(256), 0, s, x, W, T, H, E, scores);
-  else
-    err = launch("route_scores", route_scores<32>, g1, dim3(256), 0, s, x, W, T, H, E, scores);
-  if (err != hipSuccess) return err;
+  const int E = r.n_experts;
   const uint32_t lds = (uint32_t)(sizeof(float) * 4 * (size_t)r.topk);
   if (E <= kSelThreads * 4)
     return launch("route_select", route_select<4>, dim3(T), dim3(kSelThreads), lds, s, scores,
                   r.bias, E, r.topk, r.renorm, r.routed_scale, idx, gates);
   return launch("route_select", route_select<16>, dim3(T), dim3(kSelThreads), lds, s, scores,
                 r.bias, E, r.topk, r.renorm, r.routed_scale, idx, gates);
+}
+
+hipError_t launch_route(const k3x_router_desc& r, const uint16_t* x, int32_t T, int32_t* idx,
+                        float* gates, float* scores, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const int E = r.n_experts, H = r.hidden;
+  const uint16_t* W = static_cast<const uint16_t*>(r.weight);
+  hipError_t err;
+  if (H % 512 == 0 && H <= 8192) {
+    const int nt = T == 1 ? 1 : kRouteTokBlock;
+    dim3 g((E + 3) / 4, (T + nt - 1) / nt);
+    err = launch("route_scores",
+                 staged_kernel<1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16>(H / 512, nt),
+                 g, dim3(256), (uint32_t)(sizeof(uint16_t) * (size_t)nt * H), s, x, W, T, H, E,
+                 scores);
+  } else {
+    dim3 g1((E + 3) / 4, (T + kRouteTokBlock - 1) / kRouteTokBlock);
+    if (H <= 64 * 8 * 8)
+      err = launch("route_scores", route_scores<8>, g1, dim3(256), 0, s, x, W, T, H, E, scores);
+    else
+      err = launch("route_scores", route_scores<32>, g1, dim3(256), 0, s, x, W, T, H, E, scores);
+  }
+  if (err != hipSuccess) return err;
+  return launch_route_select(r, T, scores, idx, gates, s);
 }
 
 }  // namespace k3x

@@ -171,6 +171,89 @@ def test_norm_helpers_host_validation(k3x):
     assert lib.k3x_fetch_drops(None, None, None) == -1
 
 
+def test_latent_block_host_validation(k3x):
+    lib = k3x.lib()
+    fake = 1 << 40
+    st, h = _create(k3x, _desc(k3x, hidden=512))  # routed experts on a 512-wide latent
+    assert st == 0
+    try:
+        def desc(**kw):
+            d = k3x.k3x_latent_desc()
+            d.hidden, d.shared_inter = 1024, 512
+            d.down, d.up, d.sh1, d.sh3, d.sh2 = (fake + i * (1 << 32) for i in range(5))
+            d.latent_norm, d.norm_weight, d.eps = 1, fake + (6 << 32), 1e-5
+            d.shared_activation, d.situ_b1, d.situ_b2 = k3x.K3X_ACT_SITU, 4.0, 25.0
+            for k, v in kw.items():
+                setattr(d, k, v)
+            return d
+
+        def router(**kw):
+            r = k3x.k3x_router_desc()
+            r.weight, r.bias, r.n_experts, r.hidden, r.topk, r.renorm, r.routed_scale = \
+                fake + (7 << 32), None, 8, 1024, 2, 1, 1.0
+            for k, v in kw.items():
+                setattr(r, k, v)
+            return r
+
+        def fwd(d, r, T=3, x=fake + (8 << 32), out=fake + (9 << 32), ws=fake + (10 << 32),
+                nbytes=None):
+            need = lib.k3x_latent_workspace_size(ctypes.byref(desc()), h, ctypes.byref(router()), T)
+            return lib.k3x_latent_forward(ctypes.byref(d), h, ctypes.byref(r), x, T, out, ws,
+                                          need if nbytes is None else nbytes, None)
+
+        need = lib.k3x_latent_workspace_size(ctypes.byref(desc()), h, ctypes.byref(router()), 3)
+        offs = (ctypes.c_size_t * 6)()
+        assert lib.k3x_latent_ws_layout(ctypes.byref(desc()), h, ctypes.byref(router()), 3,
+                                        offs) == 0
+        assert all(o % 256 == 0 for o in offs) and list(offs) == sorted(offs)
+        off = offs[5]
+        assert need > off > 0
+        # every intermediate fits before the next: idx, gates [3][2]; z [3][512] bf16;
+        # acc [3][512] fp32; s [3][512] bf16
+        sizes = [3 * 2 * 4, 3 * 2 * 4, 3 * 512 * 2, 3 * 512 * 4, 3 * 512 * 2]
+        assert all(offs[i] + sizes[i] <= offs[i + 1] for i in range(5))
+        assert lib.k3x_latent_ws_layout(ctypes.byref(desc(hidden=1000)), h,
+                                        ctypes.byref(router(hidden=1000)), 3, offs) == k3x.K3X_E_UNSUPPORTED
+        assert lib.k3x_latent_ws_layout(ctypes.byref(desc()), h, ctypes.byref(router()), 3,
+                                        None) == k3x.K3X_E_INVALID_ARG
+        assert need - off >= lib.k3x_moe_workspace_size(h, 3, 2)
+        assert fwd(desc(), router(), T=0) == 0  # nothing to do, nothing launched
+        E_ARG, E_UNS, E_WS = k3x.K3X_E_INVALID_ARG, k3x.K3X_E_UNSUPPORTED, k3x.K3X_E_WORKSPACE
+        cases = [
+            (desc(hidden=1536), router(), E_ARG),           # router width != block width
+            (desc(), router(n_experts=9, weight=fake), E_ARG),  # router experts != pool experts
+            (desc(), router(topk=9), E_ARG),
+            (desc(hidden=1000), router(hidden=1000), E_UNS),  # not a multiple of 512
+            (desc(hidden=8704), router(hidden=8704), E_UNS),  # above 8192
+            (desc(shared_inter=768), router(), E_UNS),
+            (desc(shared_inter=9728), router(), E_UNS),      # L + S above 9728
+            (desc(down=None), router(), E_ARG),
+            (desc(sh2=None), router(), E_ARG),
+            (desc(up=fake + 8), router(), E_UNS),            # misaligned weight
+            (desc(norm_weight=fake + 4), router(), E_UNS),
+            (desc(eps=-1.0), router(), E_ARG),
+            (desc(eps=float("nan")), router(), E_ARG),
+            (desc(shared_activation=2), router(), E_ARG),
+            (desc(situ_b1=0.0), router(), E_ARG),
+            (desc(situ_b2=float("inf")), router(), E_ARG),
+        ]
+        for d, r, want in cases:
+            assert fwd(d, r) == want, (d.hidden, d.shared_inter, want)
+            assert lib.k3x_latent_workspace_size(ctypes.byref(d), h, ctypes.byref(r), 3) == 0
+        assert fwd(desc(), router(), T=-1) == E_ARG
+        assert fwd(desc(), router(), nbytes=need - 1) == E_WS
+        assert fwd(desc(), router(), ws=None) == E_WS
+        assert fwd(desc(), router(), ws=fake + 64) == E_WS
+        assert fwd(desc(), router(), x=None) == E_ARG
+        assert fwd(desc(), router(), out=fake + 4) == E_UNS
+        assert lib.k3x_latent_forward(None, h, ctypes.byref(router()), fake, 3, fake, fake, need,
+                                      None) == E_ARG
+        assert lib.k3x_latent_forward(ctypes.byref(desc()), None, ctypes.byref(router()), fake, 3,
+                                      fake, fake, need, None) == E_ARG
+    finally:
+        lib.k3x_expert_pool_destroy(h)
+
+
 def test_status_strings(k3x):
     for s in (0, -1, -2, -3, -4, -5):
         assert k3x.k3x_status_str(s)
