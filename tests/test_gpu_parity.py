@@ -376,6 +376,31 @@ def test_router_selection_paths(dev, orc):
     assert np.array_equal(gates.view(np.uint32), g_ref.view(np.uint32))
 
 
+def test_router_shared_key_digits(dev, orc):
+    """Selection scores that share their leading bytes: zero router rows give every expert
+    the score 0.5 exactly, and biases that are multiples of its ulp (2^-24) or of 2^-16 make
+    the keys differ only in their last byte, or only from the second byte down; with no bias
+    every key is equal and the lowest indices are taken in order."""
+    torch, k3x = dev
+    E, H = 896, 512
+    W = np.zeros((E, H), dtype=np.uint16)
+    x = S.normal_bf16(3, S.P_X, 0, (2, H))
+    rng = np.random.default_rng(3)
+    cases = {
+        "all equal": None,
+        "last byte": (rng.integers(0, 256, E) * 2.0 ** -24).astype(np.float32),
+        "two bytes": (rng.integers(0, 65536, E) * 2.0 ** -24).astype(np.float32),
+    }
+    for name, b in cases.items():
+        _log(f"case: router keys sharing leading digits ({name})")
+        for k in (16, 64):
+            idx, gates, i_ref, g_ref = _route_both(torch, k3x, orc, x, W, b, k)
+            assert np.array_equal(idx, i_ref), (name, k)
+            assert np.array_equal(gates.view(np.uint32), g_ref.view(np.uint32)), (name, k)
+            if b is None:
+                assert list(i_ref[0]) == list(range(k))
+
+
 # ------------------------------------------------------------------------------------------
 # the five workloads at full size (sampled tokens where the oracle would take minutes)
 # ------------------------------------------------------------------------------------------
