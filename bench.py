@@ -5,7 +5,7 @@
 
 A step is one pass of the whole path over one batch: the router (when the workload has one)
 and the expert forward (sort, fused W1/W3 + SwiGLU (or SiTU-GLU with --activation situ), W2,
-combine).  The default workload is
+combine); with a router both run as one k3x_route_moe_forward call.  The default workload is
 one decode token through one layer of 896 experts with the router (E = 896, H = 3584,
 I = 3072, top-16).  Inputs are synthetic and seeded (k3x_synth); pools are generated in
 device memory and resident before timing.  Successive steps rotate over 64 different
@@ -220,16 +220,16 @@ def bench_chain(w, args, torch, S, k3x):
     idx = torch.empty((1, w.topk), dtype=torch.int32, device=dev)
     gates = torch.empty((1, w.topk), dtype=torch.float32, device=dev)
     y = torch.empty((1, w.H), dtype=torch.float32, device=dev)
-    ws = k3x.alloc_workspace(k3x.k3x_moe_workspace_size(layers[0]["pool"], 1, w.topk), dev)
-    rws = k3x.alloc_workspace(k3x.k3x_route_workspace_size(layers[0]["rdesc"], 1), dev)
+    # router + experts in one call per layer
+    ws = k3x.alloc_workspace(
+        k3x.k3x_route_moe_workspace_size(layers[0]["rdesc"], layers[0]["pool"], 1), dev)
 
     def step(r):
         # layer l's residual update and layer l + 1's RMSNorm are one fused launch
         xb.copy_(xs[r])
         k3x.k3x_rmsnorm_bf16(xb, 1, w.H, 1e-6, xn)
         for li, lay in enumerate(layers):
-            k3x.k3x_route_topk(lay["rdesc"], xn, 1, idx, gates, rws)
-            k3x.k3x_moe_forward(lay["pool"], xn, 1, idx, gates, w.topk, y, ws)
+            k3x.k3x_route_moe_forward(lay["rdesc"], lay["pool"], xn, 1, idx, gates, y, ws)
             if li + 1 < len(layers):
                 k3x.k3x_residual_add_rmsnorm_bf16(xb, y, 1, w.H, 1e-6, xn)
             else:
@@ -639,14 +639,14 @@ def main():
     idx = torch.empty((w.T, w.topk), dtype=torch.int32, device=dev)
     gates = torch.empty((w.T, w.topk), dtype=torch.float32, device=dev)
     y = torch.empty((w.T, w.H), dtype=torch.float32, device=dev)
-    ws = k3x.alloc_workspace(k3x.k3x_moe_workspace_size(pool, w.T, w.topk), dev)
     rdesc = k3x.router_desc(Wd, bd, w.topk) if w.router else None
-    rws = k3x.alloc_workspace(k3x.k3x_route_workspace_size(rdesc, w.T), dev) if w.router else None
+    # with a router: router + experts in one call
+    ws = k3x.alloc_workspace(k3x.k3x_route_moe_workspace_size(rdesc, pool, w.T) if w.router
+                             else k3x.k3x_moe_workspace_size(pool, w.T, w.topk), dev)
 
     def step(r):
         if w.router:
-            k3x.k3x_route_topk(rdesc, xs[r], w.T, idx, gates, rws)
-            k3x.k3x_moe_forward(pool, xs[r], w.T, idx, gates, w.topk, y, ws)
+            k3x.k3x_route_moe_forward(rdesc, pool, xs[r], w.T, idx, gates, y, ws)
         else:
             i_, g_ = routes[r]
             k3x.k3x_moe_forward(pool, xs[r], w.T, i_, g_, w.topk, y, ws)

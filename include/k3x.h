@@ -149,6 +149,19 @@ k3x_status k3x_moe_forward(const k3x_pool *p, const void *x_bf16, int32_t T, con
                            const float *gates, int32_t topk, float *y, void *ws,
                            size_t ws_bytes, void *stream);
 
+/* Router and experts in one call (README Part II section 9: route, then the experts of the
+ * picks): the same idx_out, gates_out and y, bit for bit, as k3x_route_topk followed by
+ * k3x_moe_forward on them.  Requires r->n_experts == p->E, r->hidden == p->H, topk <= 64
+ * (K3X_E_INVALID_ARG / K3X_E_UNSUPPORTED otherwise); one workspace serves both steps.
+ * x_bf16 bf16 [T][hidden]; idx_out int32 [T][topk], gates_out fp32
+ * [T][topk], y fp32 [T][hidden] (all written); ws: at least k3x_route_moe_workspace_size
+ * bytes, 256-byte aligned, its start is the experts' workspace (k3x_fetch_drops(ws) reads
+ * the drop count).  T = 0 enqueues nothing. */
+size_t k3x_route_moe_workspace_size(const k3x_router_desc *r, const k3x_pool *p, int32_t T);
+k3x_status k3x_route_moe_forward(const k3x_router_desc *r, const k3x_pool *p, const void *x_bf16,
+                                 int32_t T, int32_t *idx_out, float *gates_out, float *y,
+                                 void *ws, size_t ws_bytes, void *stream);
+
 /* Waits for stream, then stores in *n the number of dropped slots of the latest
  * k3x_moe_forward that used ws.  Returns K3X_E_DROPS when *n > 0 (the run must be treated
  * as invalid), K3X_OK when 0.  n is a host pointer. */

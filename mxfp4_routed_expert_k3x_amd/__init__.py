@@ -90,6 +90,7 @@ EXPORTS = (
     "k3x_route_workspace_size", "k3x_route_topk", "k3x_moe_workspace_size", "k3x_moe_forward",
     "k3x_fetch_drops", "k3x_rmsnorm_bf16", "k3x_residual_add_bf16", "k3x_residual_add_rmsnorm_bf16",
     "k3x_latent_workspace_size", "k3x_latent_forward", "k3x_latent_ws_layout",
+    "k3x_route_moe_workspace_size", "k3x_route_moe_forward",
     "k3x_profiler_create", "k3x_profiler_destroy", "k3x_profiler_attach", "k3x_profiler_reset",
     "k3x_profiler_count", "k3x_profiler_read",
 )
@@ -132,6 +133,10 @@ def load_library(path: str = LIB_PATH):
     L.k3x_residual_add_rmsnorm_bf16.argtypes = [P, P, I32, I32, ctypes.c_float, P, P]
     L.k3x_profiler_create.restype = ctypes.c_int
     LD, RD = ctypes.POINTER(k3x_latent_desc), ctypes.POINTER(k3x_router_desc)
+    L.k3x_route_moe_workspace_size.restype = SZ
+    L.k3x_route_moe_workspace_size.argtypes = [RD, P, I32]
+    L.k3x_route_moe_forward.restype = ctypes.c_int
+    L.k3x_route_moe_forward.argtypes = [RD, P, P, I32, P, P, P, P, SZ, P]
     L.k3x_latent_workspace_size.restype = SZ
     L.k3x_latent_workspace_size.argtypes = [LD, P, RD, I32]
     L.k3x_latent_ws_layout.restype = ctypes.c_int
@@ -272,6 +277,18 @@ def k3x_moe_forward(pool: Pool, x, T: int, idx, gates, topk: int, y, ws, ws_byte
     nbytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
     _check(lib().k3x_moe_forward(pool.handle, _ptr(x), int(T), _ptr(idx), _ptr(gates),
                                  int(topk), _ptr(y), _ptr(ws), int(nbytes), _stream(stream)))
+
+
+def k3x_route_moe_workspace_size(r: k3x_router_desc, pool: Pool, T: int) -> int:
+    return int(lib().k3x_route_moe_workspace_size(ctypes.byref(r), pool.handle, int(T)))
+
+
+def k3x_route_moe_forward(r: k3x_router_desc, pool: Pool, x, T: int, idx_out, gates_out, y, ws,
+                          ws_bytes=None, stream=None):
+    nbytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    _check(lib().k3x_route_moe_forward(ctypes.byref(r), pool.handle, _ptr(x), int(T),
+                                       _ptr(idx_out), _ptr(gates_out), _ptr(y), _ptr(ws),
+                                       int(nbytes), _stream(stream)))
 
 
 def k3x_fetch_drops(ws, stream=None) -> int:

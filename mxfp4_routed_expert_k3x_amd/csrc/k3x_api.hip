@@ -273,6 +273,62 @@ k3x_status k3x_latent_forward(const k3x_latent_desc* d, const k3x_pool* p,
   return K3X_OK;
 }
 
+static k3x_status check_route_moe(const k3x_router_desc* r, const k3x_pool* p, int32_t T) {
+  k3x_status st = check_router(r);
+  if (st != K3X_OK) return st;
+  if (!p) return fail(K3X_E_INVALID_ARG, "route_moe: NULL pool");
+  if (r->n_experts != p->E)
+    return fail(K3X_E_INVALID_ARG, "route_moe: router experts %d != pool experts %d",
+                r->n_experts, p->E);
+  if (r->hidden != p->H)
+    return fail(K3X_E_INVALID_ARG, "route_moe: router hidden %d != pool hidden %d", r->hidden,
+                p->H);
+  if (r->topk > 64) return fail(K3X_E_UNSUPPORTED, "route_moe: topk %d above 64", r->topk);
+  if (T < 0) return fail(K3X_E_INVALID_ARG, "route_moe: T %d < 0", T);
+  if ((int64_t)T * r->topk > (int64_t)1 << 26)
+    return fail(K3X_E_UNSUPPORTED, "route_moe: T * topk above 2^26");
+  return K3X_OK;
+}
+
+// Workspace of k3x_route_moe_forward: the experts' workspace first (its drop counter at 0),
+// then the router's scores.
+static size_t route_moe_scores_offset(const k3x_router_desc* r, const k3x_pool* p, int32_t T) {
+  const size_t moe = k3x_moe_workspace_size(p, T, r->topk);
+  return (moe + 255) & ~(size_t)255;
+}
+
+size_t k3x_route_moe_workspace_size(const k3x_router_desc* r, const k3x_pool* p, int32_t T) {
+  if (check_route_moe(r, p, T) != K3X_OK) return 0;
+  return route_moe_scores_offset(r, p, T) + k3x_route_workspace_size(r, T);
+}
+
+k3x_status k3x_route_moe_forward(const k3x_router_desc* r, const k3x_pool* p, const void* x_bf16,
+                                 int32_t T, int32_t* idx_out, float* gates_out, float* y,
+                                 void* ws, size_t ws_bytes, void* stream) {
+  k3x_status st = check_route_moe(r, p, T);
+  if (st != K3X_OK) return st;
+  const size_t need = k3x_route_moe_workspace_size(r, p, T);
+  if (!ws || ws_bytes < need || !aligned(ws, 256))
+    return fail(K3X_E_WORKSPACE, "route_moe_forward: workspace %zu bytes, need %zu (256-byte aligned)",
+                ws_bytes, need);
+  if (T == 0) return K3X_OK;
+  if (!x_bf16 || !idx_out || !gates_out || !y)
+    return fail(K3X_E_INVALID_ARG, "route_moe_forward: NULL x, idx, gates or y");
+  if (!aligned(x_bf16, 16) || !aligned(y, 16))
+    return fail(K3X_E_UNSUPPORTED, "route_moe_forward: x and y must be 16-byte aligned");
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  float* scores = reinterpret_cast<float*>(w + route_moe_scores_offset(r, p, T));
+  const uint16_t* x = static_cast<const uint16_t*>(x_bf16);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = k3x::launch_route(*r, x, T, idx_out, gates_out, scores, s);
+  if (e == hipSuccess) {
+    const k3x::MoeLayout L = k3x::moe_layout(p->E, p->H, p->I, T, r->topk);
+    e = k3x::launch_moe(*p, x, T, idx_out, gates_out, r->topk, y, w, L, s);
+  }
+  if (e != hipSuccess) return hip_fail(e, "route_moe_forward");
+  return K3X_OK;
+}
+
 k3x_status k3x_fetch_drops(const void* ws, int64_t* n, void* stream) {
   if (!ws || !n) return fail(K3X_E_INVALID_ARG, "fetch_drops: NULL ws or n");
   int64_t v = 0;

@@ -135,7 +135,10 @@ namespace k3x {
 // ---------------------------------------------------------------------------------------
 hipError_t launch_route(const k3x_router_desc& r, const uint16_t* x, int32_t T, int32_t* idx,
                         float* gates, float* scores, hipStream_t s);
-// The selection alone, on scores fp32 [T][E] already computed (the latent block's own pass).
+// The sigmoid scores alone (fp32 [T][E]).
+hipError_t launch_route_scores(const k3x_router_desc& r, const uint16_t* x, int32_t T,
+                               float* scores, hipStream_t s);
+// The selection alone, on scores fp32 [T][E] already computed.
 hipError_t launch_route_select(const k3x_router_desc& r, int32_t T, const float* scores,
                                int32_t* idx, float* gates, hipStream_t s);
 
@@ -149,7 +152,6 @@ size_t decode_exact_ws(const k3x_pool& p, int32_t topk, size_t* off_h);
 hipError_t launch_decode_exact(const k3x_pool& p, const uint16_t* x, const int32_t* idx,
                                const float* gates, int32_t topk, float* y, uint8_t* ws,
                                hipStream_t s);
-
 // Latent MoE block (k3x_dense.hip): workspace layout and launcher.
 struct LatentLayout {
   size_t scores;  // router scores fp32 [T][E]

@@ -18,6 +18,7 @@
 // ties go to the lower expert and -0 equals +0 as in an IEEE compare; the chosen experts
 // are then put in selection order by their rank.
 #include "k3x_internal.h"
+#include "k3x_select.h"
 
 namespace k3x {
 namespace {
@@ -160,32 +161,7 @@ ScoresKernel staged_kernel(int nch, int nt) {
   return (nt == 1 ? k1 : k4)[nch - 1];
 }
 
-// (c, index) total order: true when candidate b beats a.  Index -1 means "no candidate".
-__device__ __forceinline__ bool beats(float cb, int ib, float ca, int ia) {
-  if (ib < 0) return false;
-  if (ia < 0) return true;
-  return cb > ca || (cb == ca && ib < ia);
-}
-
-// Order-preserving 32-bit key of a selection score: a larger float gives a larger key, and
-// -0 is first made +0 so that the two compare equal, as in an IEEE compare.
-__device__ __forceinline__ uint32_t score_key(float c) {
-  const uint32_t b = c == 0.0f ? 0u : __float_as_uint(c);
-  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-}
-
-constexpr int kSelThreads = 256;
-constexpr int kMaxEqual = 256;  // experts sharing the threshold key handled at once
-
-// One workgroup of 256 threads per token; thread i owns experts i + 256 m (m < M).
-//  1. The key of the topk-th largest selection score is found by a radix select: four
-//     passes over 8-bit digits, each building a 256-bin LDS histogram of the keys that
-//     match the digits fixed so far and walking it from the top.
-//  2. The chosen set is every expert whose key is larger, plus, among the experts whose key
-//     equals it, the ones of lowest index until topk are taken -- exactly the experts the
-//     repeated argmax (larger score first, lower index on ties) would pick.
-//  3. Each chosen expert's slot is its rank in that total order; the gates are the unbiased
-//     scores in slot order, renormalised by their float sum (added in slot order).
+// Kernel 2: one workgroup of kSelThreads per token (select_topk, k3x_select.h).
 template <int M>
 __global__ __launch_bounds__(kSelThreads) void route_select(const float* __restrict__ scores,
                                                             const float* __restrict__ bias,
@@ -193,142 +169,10 @@ __global__ __launch_bounds__(kSelThreads) void route_select(const float* __restr
                                                             int32_t renorm, float rscale,
                                                             int32_t* __restrict__ idx_out,
                                                             float* __restrict__ gates_out) {
-  extern __shared__ float dyn[];  // [topk] c, [topk] s, [topk] e (as int), [topk] ranked s
-  float* sel_c = dyn;
-  float* sel_s = dyn + topk;
-  int* sel_e = reinterpret_cast<int*>(dyn + 2 * topk);
-  float* ranked = dyn + 3 * topk;
-  __shared__ uint32_t hist[256];
-  __shared__ int eq_e[kMaxEqual];
-  __shared__ uint32_t s_prefix, s_rem;
-  __shared__ int s_nsel, s_neq;
-  __shared__ float s_sum;
-  const int tid = threadIdx.x;
-  const int t = blockIdx.x;
-  const float* s_t = scores + (size_t)t * E;
-
-  float sc[M], c[M];
-  uint32_t key[M];
-#pragma unroll
-  for (int m = 0; m < M; ++m) {
-    const int e = tid + kSelThreads * m;
-    sc[m] = e < E ? s_t[e] : 0.0f;
-    c[m] = e < E ? sc[m] + (bias ? bias[e] : 0.0f) : 0.0f;
-    key[m] = score_key(c[m]);
-  }
-
-  uint32_t prefix = 0, mask = 0, rem = (uint32_t)topk;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    hist[tid] = 0;
-    __syncthreads();
-#pragma unroll
-    for (int m = 0; m < M; ++m)
-      if (tid + kSelThreads * m < E && (key[m] & mask) == prefix)
-        atomicAdd(&hist[(key[m] >> shift) & 255u], 1u);
-    __syncthreads();
-    if (tid < kWave) {
-      // lane l sums bins 255-4l .. 252-4l (descending); an inclusive scan over lanes gives
-      // the number of keys in all bins from 255 down to the lane's lowest bin
-      uint32_t hb[4], local = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        hb[i] = hist[255 - 4 * tid - i];
-        local += hb[i];
-      }
-      uint32_t incl = local;
-#pragma unroll
-      for (int d = 1; d < kWave; d <<= 1) {
-        const uint32_t o = __shfl_up(incl, d, kWave);
-        if (tid >= d) incl += o;
-      }
-      const uint32_t excl = incl - local;
-      if (excl < rem && rem <= incl) {  // exactly one lane
-        uint32_t above = excl;
-        int bin = 255 - 4 * tid - 3;
-        uint32_t left = rem - above;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if (above < rem && rem <= above + hb[i]) {
-            bin = 255 - 4 * tid - i;
-            left = rem - above;
-            break;
-          }
-          above += hb[i];
-        }
-        s_prefix = prefix | ((uint32_t)bin << shift);
-        s_rem = left;
-      }
-    }
-    __syncthreads();
-    prefix = s_prefix;
-    rem = s_rem;
-    mask |= 255u << shift;
-    __syncthreads();
-  }
-
-  // prefix is now the key of the topk-th expert; rem of the experts with that key are
-  // taken, those of lowest index
-  if (tid == 0) {
-    s_nsel = 0;
-    s_neq = 0;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int m = 0; m < M; ++m) {
-    const int e = tid + kSelThreads * m;
-    if (e < E && key[m] == prefix) {
-      const int pos = atomicAdd(&s_neq, 1);
-      if (pos < kMaxEqual) eq_e[pos] = e;
-    }
-  }
-  __syncthreads();
-  const int neq = s_neq < kMaxEqual ? s_neq : kMaxEqual;
-#pragma unroll
-  for (int m = 0; m < M; ++m) {
-    const int e = tid + kSelThreads * m;
-    if (e >= E) continue;
-    bool take = key[m] > prefix;
-    if (key[m] == prefix) {
-      uint32_t below = 0;
-      if (s_neq <= kMaxEqual) {
-        for (int i = 0; i < neq; ++i) below += eq_e[i] < e ? 1u : 0u;
-      } else {  // very many equal scores: count them from the inputs
-        for (int e2 = 0; e2 < e; ++e2)
-          below += score_key(s_t[e2] + (bias ? bias[e2] : 0.0f)) == prefix ? 1u : 0u;
-      }
-      take = below < rem;
-    }
-    if (take) {
-      const int pos = atomicAdd(&s_nsel, 1);
-      sel_c[pos] = c[m];
-      sel_s[pos] = sc[m];
-      sel_e[pos] = e;
-    }
-  }
-  __syncthreads();
-  // slot of each chosen expert = its rank under (larger c, then lower index)
-  for (int i = tid; i < topk; i += kSelThreads) {
-    const float ci = sel_c[i];
-    const int ei = sel_e[i];
-    int r = 0;
-    for (int j = 0; j < topk; ++j) r += beats(sel_c[j], sel_e[j], ci, ei) ? 1 : 0;
-    idx_out[(size_t)t * topk + r] = ei;
-    ranked[r] = sel_s[i];
-  }
-  __syncthreads();
-  if (tid == 0) {
-    float sum = 0.0f;
-    if (renorm)
-      for (int j = 0; j < topk; ++j) sum = sum + ranked[j];
-    s_sum = sum;
-  }
-  __syncthreads();
-  const float sum = s_sum;
-  for (int j = tid; j < topk; j += kSelThreads) {
-    float w = ranked[j];
-    if (renorm && sum > 0.0f) w = w / sum;
-    gates_out[(size_t)t * topk + j] = w * rscale;
-  }
+  extern __shared__ float dyn[];  // [4][topk]
+  const size_t t = blockIdx.x;
+  select_topk<M>(scores + t * E, bias, E, topk, renorm, rscale, dyn, idx_out + t * topk,
+                 gates_out + t * topk);
 }
 
 }  // namespace
@@ -347,6 +191,13 @@ hipError_t launch_route_select(const k3x_router_desc& r, int32_t T, const float*
 
 hipError_t launch_route(const k3x_router_desc& r, const uint16_t* x, int32_t T, int32_t* idx,
                         float* gates, float* scores, hipStream_t s) {
+  hipError_t err = launch_route_scores(r, x, T, scores, s);
+  if (err != hipSuccess) return err;
+  return launch_route_select(r, T, scores, idx, gates, s);
+}
+
+hipError_t launch_route_scores(const k3x_router_desc& r, const uint16_t* x, int32_t T,
+                               float* scores, hipStream_t s) {
   if (T == 0) return hipSuccess;
   const int E = r.n_experts, H = r.hidden;
   const uint16_t* W = static_cast<const uint16_t*>(r.weight);
@@ -365,8 +216,7 @@ hipError_t launch_route(const k3x_router_desc& r, const uint16_t* x, int32_t T, 
     else
       err = launch("route_scores", route_scores<32>, g1, dim3(256), 0, s, x, W, T, H, E, scores);
   }
-  if (err != hipSuccess) return err;
-  return launch_route_select(r, T, scores, idx, gates, s);
+  return err;
 }
 
 }  // namespace k3x

@@ -254,6 +254,50 @@ def test_latent_block_host_validation(k3x):
         lib.k3x_expert_pool_destroy(h)
 
 
+def test_route_moe_host_validation(k3x):
+    lib = k3x.lib()
+    fake = 1 << 40
+    st, h = _create(k3x, _desc(k3x))  # E 8, hidden 256
+    assert st == 0
+    try:
+        def router(**kw):
+            r = k3x.k3x_router_desc()
+            r.weight, r.bias, r.n_experts, r.hidden, r.topk, r.renorm, r.routed_scale = \
+                fake, None, 8, 256, 2, 1, 1.0
+            for k, v in kw.items():
+                setattr(r, k, v)
+            return r
+
+        R = ctypes.byref
+        need = lib.k3x_route_moe_workspace_size(R(router()), h, 3)
+        assert need >= lib.k3x_moe_workspace_size(h, 3, 2) + 3 * 8 * 4
+        fwd = lambda r, T=3, x=fake, ws=fake, n=need: lib.k3x_route_moe_forward(
+            R(r), h, x, T, fake, fake, fake, ws, n, None)
+        assert fwd(router(), T=0) == 0
+        assert fwd(router(n_experts=9)) == k3x.K3X_E_INVALID_ARG
+        assert fwd(router(hidden=512)) == k3x.K3X_E_INVALID_ARG
+        assert fwd(router(topk=9)) == k3x.K3X_E_INVALID_ARG
+        assert fwd(router(), T=-1) == k3x.K3X_E_INVALID_ARG
+        assert fwd(router(), n=need - 1) == k3x.K3X_E_WORKSPACE
+        assert fwd(router(), ws=fake + 64) == k3x.K3X_E_WORKSPACE
+        assert fwd(router(), x=None) == k3x.K3X_E_INVALID_ARG
+        assert fwd(router(), x=fake + 2) == k3x.K3X_E_UNSUPPORTED
+        assert lib.k3x_route_moe_workspace_size(R(router(n_experts=9)), h, 3) == 0
+        assert lib.k3x_route_moe_forward(R(router()), None, fake, 3, fake, fake, fake, fake,
+                                         need, None) == k3x.K3X_E_INVALID_ARG
+    finally:
+        lib.k3x_expert_pool_destroy(h)
+    st, h = _create(k3x, _desc(k3x, n_experts=100))
+    try:
+        r = k3x.k3x_router_desc()
+        r.weight, r.bias, r.n_experts, r.hidden, r.topk, r.renorm, r.routed_scale = \
+            fake, None, 100, 256, 65, 1, 1.0
+        assert lib.k3x_route_moe_forward(ctypes.byref(r), h, fake, 1, fake, fake, fake, fake,
+                                         1 << 30, None) == k3x.K3X_E_UNSUPPORTED
+    finally:
+        lib.k3x_expert_pool_destroy(h)
+
+
 def test_status_strings(k3x):
     for s in (0, -1, -2, -3, -4, -5):
         assert k3x.k3x_status_str(s)

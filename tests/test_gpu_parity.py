@@ -401,6 +401,67 @@ def test_router_shared_key_digits(dev, orc):
                 assert list(i_ref[0]) == list(range(k))
 
 
+def _route_moe_both(torch, k3x, pool, Wd, bd, xd, T, k, renorm=1, scale=1.0):
+    """k3x_route_moe_forward against k3x_route_topk + k3x_moe_forward on the same inputs."""
+    r = k3x.router_desc(Wd, bd, k, renorm, scale)
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    gates = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    y = torch.empty((T, pool.H), dtype=torch.float32, device="cuda")
+    ws = k3x.alloc_workspace(k3x.k3x_route_moe_workspace_size(r, pool, T))
+    k3x.k3x_route_moe_forward(r, pool, xd, T, idx, gates, y, ws)
+    torch.cuda.synchronize()
+    assert k3x.k3x_fetch_drops(ws) == 0
+    i2, g2, _ = k3x.route_topk(Wd, bd, xd, k, renorm, scale)
+    y2, _ = k3x.moe_forward(pool, xd, i2, g2)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, i2) and torch.equal(gates.view(torch.int32), g2.view(torch.int32))
+    assert torch.equal(y.view(torch.int32), y2.view(torch.int32))
+    return _np(idx), _np(gates), _np(y)
+
+
+def test_route_moe_forward_equals_separate_calls(dev, orc):
+    """Router and experts in one call: idx, gates and y equal the two separate calls bit for
+    bit, and the oracle's router and forward; also more than 1024 experts (16 keys per
+    selection thread), no bias, no renormalisation with a routed scale, SiTU-GLU, batches."""
+    torch, k3x = dev
+    w = S.WORKLOADS[2]
+    _log("case: route_moe one token, K3 shape")
+    pool = _pool(torch, k3x, S.device_pool(w.seed, 0, w.E, w.H, w.I), w.E, w.H, w.I)
+    W, b = S.router_inputs(w)
+    Wd, bd = _t(torch, W), _t(torch, b)
+    cache = {}
+    for t in range(3):
+        x = S.normal_bf16(w.seed + 100 + t, S.P_X, 0, (1, w.H))
+        idx, gates, y = _route_moe_both(torch, k3x, pool, Wd, bd, _t(torch, x), 1, w.topk)
+        i_ref, g_ref = orc.route(x, W, b, w.topk)
+        assert np.array_equal(idx, i_ref)
+        assert np.array_equal(gates.view(np.uint32), g_ref.view(np.uint32))
+        y_ref = oracle_forward_sampled(orc, w.seed, 0, w.H, w.I, x, i_ref, g_ref, [0], cache=cache)
+        assert np.array_equal(y, y_ref)
+    _log("case: route_moe options (no bias; renorm 0 with routed scale 2.5; T = 5)")
+    x = S.normal_bf16(w.seed + 200, S.P_X, 0, (5, w.H))
+    _route_moe_both(torch, k3x, pool, Wd, None, _t(torch, x[:1]), 1, w.topk)
+    _route_moe_both(torch, k3x, pool, Wd, bd, _t(torch, x[:1]), 1, w.topk, renorm=0, scale=2.5)
+    _route_moe_both(torch, k3x, pool, Wd, bd, _t(torch, x), 5, w.topk)
+    del pool
+    _log("case: route_moe SiTU one token")
+    pool = _pool(torch, k3x, S.device_pool(w.seed, 0, w.E, w.H, w.I), w.E, w.H, w.I, act=SITU)
+    _route_moe_both(torch, k3x, pool, Wd, bd, _t(torch, x[:1]), 1, w.topk)
+    del pool
+    for E, H, I, k in ((2048, 512, 384, 16), (1025, 256, 256, 64), (64, 512, 512, 8)):
+        _log(f"case: route_moe E={E} H={H} I={I} k={k}")
+        pool = _pool(torch, k3x, S.device_pool(E, 0, E, H, I), E, H, I)
+        W = S.normal_bf16(E, S.P_WR, 0, (E, H), std=0.05)
+        b = S.normal_f32(E, S.P_BIAS, 0, (E,), std=0.01)
+        x = S.normal_bf16(E, S.P_X, 0, (1, H))
+        idx, gates, y = _route_moe_both(torch, k3x, pool, _t(torch, W), _t(torch, b),
+                                        _t(torch, x), 1, k)
+        i_ref, g_ref = orc.route(x, W, b, k)
+        assert np.array_equal(idx, i_ref)
+        assert np.array_equal(gates.view(np.uint32), g_ref.view(np.uint32))
+        del pool
+
+
 # ------------------------------------------------------------------------------------------
 # the five workloads at full size (sampled tokens where the oracle would take minutes)
 # ------------------------------------------------------------------------------------------
