@@ -57,11 +57,30 @@ struct DenseArgs {
   float* out;              // fp32 [T][D]
 };
 
-// The fixed 64-way fold of the lane partials; the sum is read from lane 0 (uniform).
+// A double from lane + n of the same row of 16 lanes (DPP row_shl:n; 0 past the row).
+template <int N>
+__device__ __forceinline__ double row_shl(double v) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, 0x100 + N, 0xF, 0xF, true);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), 0x100 + N, 0xF, 0xF, true);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// The fixed 64-way fold of the lane partials, p[L] += p[L + s] for s = 32 .. 1, exact for
+// lane 0 (the steps inside a row of 16 lanes read their partner with DPP); the sum is read
+// from lane 0 (uniform).
+__device__ __forceinline__ double fold64_d(double p) {
+  p = p + __shfl_down(p, 32, kWave);
+  p = p + __shfl_down(p, 16, kWave);
+  p = p + row_shl<8>(p);
+  p = p + row_shl<4>(p);
+  p = p + row_shl<2>(p);
+  p = p + row_shl<1>(p);
+  return p;
+}
+
 __device__ __forceinline__ float fold64(double p) {
-#pragma unroll
-  for (int s = 32; s >= 1; s >>= 1) p = p + __shfl_down(p, s, kWave);
-  const float f = (float)p;
+  const float f = (float)fold64_d(p);
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, f), 0));
 }
 
@@ -245,8 +264,7 @@ __device__ void stage_out(const DenseArgs& a, uint4* xs, int cpr) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) ss = ss + (double)v[j] * (double)v[j];
     }
-#pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) ss = ss + __shfl_down(ss, s, kWave);
+    ss = fold64_d(ss);
     if (lane == 0) s_inv[wave] = (float)(1.0 / sqrt(ss / (double)L + (double)a.eps));
   }
   __syncthreads();
