@@ -247,6 +247,88 @@ k3x_status k3x_latent_ws_layout(const k3x_latent_desc *d, const k3x_pool *p,
                                 const k3x_router_desc *r, int32_t T, size_t offs[6]);
 
 /* ------------------------------------------------------------------------------------------
+ * Expert arena: pools larger than HBM (README Part II section 12 "An LRU cache for the
+ * experts", section 13 "How big should that cache be? Ask the trace").  n_slots experts are
+ * resident in an HBM arena; the rest stay in a backing store in pinned host memory and are
+ * copied in on demand.  A slot holds an expert, or is EMPTY, or INFLIGHT; a miss takes the
+ * lowest EMPTY slot, else the least recently used slot that is not in flight, pinned or held
+ * by the same batch (recency: one tick per request).  A batch reserves serially, copies its
+ * misses in the backing store's offset order, then publishes them.  Host-side state; use an
+ * arena from one host thread and one stream.
+ * ---------------------------------------------------------------------------------------- */
+typedef struct k3x_arena k3x_arena;
+
+typedef struct k3x_arena_desc {
+  int32_t n_slots;            /* experts resident at once, 1..8192                          */
+  int32_t n_layers;           /* the backing store holds n_layers * n_experts experts       */
+  int32_t n_experts;          /* per layer                                                  */
+  int32_t hidden, inter, group; /* as k3x_pool_desc (group 32)                              */
+  const void *host[6];        /* backing store, PINNED host memory (hipHostMalloc): tensor k
+                                 (w1_packed, w1_scale, w3_packed, w3_scale, w2_packed,
+                                 w2_scale) of expert (l, e) at host[k] + (l * n_experts + e)
+                                 * host_stride[k]; when the six are back to back with one
+                                 stride, an expert is one copy, else six                    */
+  int64_t host_stride[6];     /* bytes, 0 = the tensor's dense size                         */
+  int32_t max_slots_per_call; /* T * topk bound of k3x_arena_moe_forward                    */
+  int32_t activation;         /* as k3x_pool_desc                                           */
+  float situ_b1, situ_b2;
+} k3x_arena_desc;
+
+/* Bytes of one expert's six tensors (17,547,264 at hidden 3584, inter 3072); 0 if invalid. */
+size_t k3x_expert_bytes(int32_t hidden, int32_t inter);
+
+/* Allocates the arena: n_slots * (k3x_expert_bytes rounded up to 256) bytes of device memory,
+ * pinned host and device buffers of max_slots_per_call ids, and a pool over the slots.
+ * Refuses NULL backing pointers, strides below the dense sizes or sizes out of range
+ * (K3X_E_INVALID_ARG), shapes a pool refuses (K3X_E_UNSUPPORTED); K3X_E_HIP when the device
+ * allocation fails (k3x_arena_last_error says why).  The backing store is borrowed. */
+k3x_status k3x_arena_create(const k3x_arena_desc *d, k3x_arena **out);
+void k3x_arena_destroy(k3x_arena *a);
+const char *k3x_arena_last_error(void);
+
+/* The pool whose experts are the arena's slots (owned by the arena). */
+const k3x_pool *k3x_arena_pool(const k3x_arena *a);
+
+/* Makes experts[0..n) of one layer resident (host int32 ids; ids outside [0, n_experts) are
+ * skipped) and writes slots_out[j] (host int32): the slot of experts[j], or -1 when none
+ * could be given (every slot in flight, pinned or held by this batch).  An id repeated in
+ * the batch shares its first request's slot.  The copies are enqueued on stream (ordered
+ * before any later work on it); *hits and *misses (host, may be NULL) count this call. */
+k3x_status k3x_arena_getmany(k3x_arena *a, int32_t layer, const int32_t *experts, int32_t n,
+                             int32_t *slots_out, int32_t *hits, int32_t *misses, void *stream);
+
+/* Pins a resident expert: its slot is never evicted (K3X_E_INVALID_ARG if not resident). */
+k3x_status k3x_arena_pin(k3x_arena *a, int32_t layer, int32_t expert);
+
+/* Totals since creation: requests that hit, requests that missed, bytes copied in. */
+k3x_status k3x_arena_stats(const k3x_arena *a, int64_t *hits, int64_t *misses, int64_t *bytes);
+
+/* The expert forward of one layer through the arena: copies idx (device int32 [T][topk]) to
+ * the host (this waits for the stream), makes the call's distinct experts resident in slot
+ * order (token-major), writes the slot ids to the device and runs k3x_moe_forward on the
+ * arena's pool.  The result equals k3x_moe_forward on a pool holding the layer's experts,
+ * bit for bit.  Experts that got no slot are dropped (k3x_fetch_drops on ws counts them).
+ * T * topk <= max_slots_per_call (else K3X_E_UNSUPPORTED); ws as k3x_moe_forward on
+ * k3x_arena_pool.  Waits for the stream again before returning. */
+k3x_status k3x_arena_moe_forward(k3x_arena *a, int32_t layer, const void *x_bf16, int32_t T,
+                                 const int32_t *idx, const float *gates, int32_t topk, float *y,
+                                 void *ws, size_t ws_bytes, int32_t *hits, int32_t *misses,
+                                 void *stream);
+
+/* Trace replay (host only): the hits of a replacement rule with cap slots over trace[0..n)
+ * (keys, one request each).  K3X_CACHE_LRU is the arena's own policy; K3X_CACHE_BELADY evicts
+ * the key needed furthest ahead (a ceiling, not a policy); K3X_CACHE_PIN_LRU is LRU with the
+ * keys pinned[0..n_pinned) never evicted once resident. */
+typedef enum { K3X_CACHE_LRU = 0, K3X_CACHE_BELADY = 1, K3X_CACHE_PIN_LRU = 2 } k3x_cache_policy;
+k3x_status k3x_cache_replay(const int64_t *trace, int64_t n, int32_t cap, int32_t policy,
+                            const int64_t *pinned, int32_t n_pinned, int64_t *hits);
+
+/* The arena's policy over batches without a device: batch b is keys[batch_start[b] ..
+ * batch_start[b + 1]); slots_out[j] is the slot given to keys[j] (-1: none). */
+k3x_status k3x_cache_replay_batches(const int64_t *keys, const int64_t *batch_start,
+                                    int64_t n_batches, int32_t cap, int32_t *slots_out);
+
+/* ------------------------------------------------------------------------------------------
  * Kernel timing (instrumentation only; the work done is unchanged).  While a profiler is
  * attached to the calling thread, every kernel the library enqueues from that thread is
  * bracketed by two HIP events recorded on the same stream, up to the profiler's capacity.

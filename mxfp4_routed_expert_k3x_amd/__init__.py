@@ -85,12 +85,34 @@ class k3x_latent_desc(ctypes.Structure):
     ]
 
 
+class k3x_arena_desc(ctypes.Structure):
+    _fields_ = [
+        ("n_slots", ctypes.c_int32),
+        ("n_layers", ctypes.c_int32),
+        ("n_experts", ctypes.c_int32),
+        ("hidden", ctypes.c_int32),
+        ("inter", ctypes.c_int32),
+        ("group", ctypes.c_int32),
+        ("host", ctypes.c_void_p * 6),
+        ("host_stride", ctypes.c_int64 * 6),
+        ("max_slots_per_call", ctypes.c_int32),
+        ("activation", ctypes.c_int32),
+        ("situ_b1", ctypes.c_float),
+        ("situ_b2", ctypes.c_float),
+    ]
+
+
+K3X_CACHE_LRU, K3X_CACHE_BELADY, K3X_CACHE_PIN_LRU = 0, 1, 2
+
 EXPORTS = (
     "k3x_status_str", "k3x_last_error", "k3x_expert_pool_create", "k3x_expert_pool_destroy",
     "k3x_route_workspace_size", "k3x_route_topk", "k3x_moe_workspace_size", "k3x_moe_forward",
     "k3x_fetch_drops", "k3x_rmsnorm_bf16", "k3x_residual_add_bf16", "k3x_residual_add_rmsnorm_bf16",
     "k3x_latent_workspace_size", "k3x_latent_forward", "k3x_latent_ws_layout",
     "k3x_route_moe_workspace_size", "k3x_route_moe_forward",
+    "k3x_expert_bytes", "k3x_arena_create", "k3x_arena_destroy", "k3x_arena_last_error",
+    "k3x_arena_pool", "k3x_arena_getmany", "k3x_arena_pin", "k3x_arena_stats",
+    "k3x_arena_moe_forward", "k3x_cache_replay", "k3x_cache_replay_batches",
     "k3x_profiler_create", "k3x_profiler_destroy", "k3x_profiler_attach", "k3x_profiler_reset",
     "k3x_profiler_count", "k3x_profiler_read",
 )
@@ -143,6 +165,30 @@ def load_library(path: str = LIB_PATH):
     L.k3x_latent_ws_layout.argtypes = [LD, P, RD, I32, ctypes.POINTER(SZ)]
     L.k3x_latent_forward.restype = ctypes.c_int
     L.k3x_latent_forward.argtypes = [LD, P, RD, P, I32, P, P, SZ, P]
+    I64 = ctypes.c_int64
+    AD = ctypes.POINTER(k3x_arena_desc)
+    L.k3x_expert_bytes.restype = SZ
+    L.k3x_expert_bytes.argtypes = [I32, I32]
+    L.k3x_arena_create.restype = ctypes.c_int
+    L.k3x_arena_create.argtypes = [AD, ctypes.POINTER(P)]
+    L.k3x_arena_destroy.restype = None
+    L.k3x_arena_destroy.argtypes = [P]
+    L.k3x_arena_last_error.restype = ctypes.c_char_p
+    L.k3x_arena_last_error.argtypes = []
+    L.k3x_arena_pool.restype = P
+    L.k3x_arena_pool.argtypes = [P]
+    L.k3x_arena_getmany.restype = ctypes.c_int
+    L.k3x_arena_getmany.argtypes = [P, I32, P, I32, P, P, P, P]
+    L.k3x_arena_pin.restype = ctypes.c_int
+    L.k3x_arena_pin.argtypes = [P, I32, I32]
+    L.k3x_arena_stats.restype = ctypes.c_int
+    L.k3x_arena_stats.argtypes = [P, P, P, P]
+    L.k3x_arena_moe_forward.restype = ctypes.c_int
+    L.k3x_arena_moe_forward.argtypes = [P, I32, P, I32, P, P, I32, P, P, SZ, P, P, P]
+    L.k3x_cache_replay.restype = ctypes.c_int
+    L.k3x_cache_replay.argtypes = [P, I64, I32, I32, P, I32, ctypes.POINTER(I64)]
+    L.k3x_cache_replay_batches.restype = ctypes.c_int
+    L.k3x_cache_replay_batches.argtypes = [P, P, I64, I32, P]
     L.k3x_profiler_create.argtypes = [I32, ctypes.POINTER(P)]
     L.k3x_profiler_destroy.restype = None
     L.k3x_profiler_destroy.argtypes = [P]
@@ -350,6 +396,129 @@ def k3x_latent_forward(d: k3x_latent_desc, pool: Pool, r: k3x_router_desc, x, T:
     nbytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
     _check(lib().k3x_latent_forward(ctypes.byref(d), pool.handle, ctypes.byref(r), _ptr(x),
                                     int(T), _ptr(out), _ptr(ws), int(nbytes), _stream(stream)))
+
+
+# ------------------------------------------------------------------------------------------
+# Expert arena (pools larger than HBM) and trace replay
+# ------------------------------------------------------------------------------------------
+class Arena:
+    """Owns a k3x_arena handle; keeps the borrowed pinned backing tensors alive.  .pool is a
+    Pool view of the slots (owned by the arena)."""
+
+    def __init__(self, handle, backing, n_slots, H, I):
+        self.handle = handle
+        self.backing = backing
+        self.pool = Pool(0, {}, n_slots, H, I)
+        self.pool.handle = lib().k3x_arena_pool(handle)
+        self.pool.close = lambda: None  # the arena owns it
+
+    def close(self):
+        if self.handle:
+            lib().k3x_arena_destroy(self.handle)
+            self.handle = 0
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def k3x_expert_bytes(hidden: int, inter: int) -> int:
+    return int(lib().k3x_expert_bytes(int(hidden), int(inter)))
+
+
+def k3x_arena_create(host: dict, n_slots: int, n_layers: int, n_experts: int, hidden: int,
+                     inter: int, max_slots_per_call: int = 1024, host_strides=None,
+                     activation: str = "swiglu", situ_b1: float = 4.0, situ_b2: float = 25.0,
+                     group: int = 32) -> Arena:
+    """host: the six pinned host tensors (or integer addresses) by name, expert (l, e) at
+    index l * n_experts + e of each (stride = host_strides[k] bytes, None = dense)."""
+    d = k3x_arena_desc()
+    d.n_slots, d.n_layers, d.n_experts = n_slots, n_layers, n_experts
+    d.hidden, d.inter, d.group = hidden, inter, group
+    for k, name in enumerate(TENSOR_ORDER):
+        d.host[k] = _ptr(host[name])
+        d.host_stride[k] = 0 if host_strides is None else int(host_strides[k])
+    d.max_slots_per_call = max_slots_per_call
+    d.activation = {"swiglu": K3X_ACT_SWIGLU, "situ": K3X_ACT_SITU}[activation]
+    d.situ_b1, d.situ_b2 = situ_b1, situ_b2
+    h = ctypes.c_void_p()
+    st = lib().k3x_arena_create(ctypes.byref(d), ctypes.byref(h))
+    if st != K3X_OK:
+        raise K3xError(st, f"{k3x_status_str(st)}: {lib().k3x_arena_last_error().decode()} "
+                           f"{k3x_last_error()}")
+    return Arena(h.value, dict(host), n_slots, hidden, inter)
+
+
+def k3x_arena_destroy(arena: Arena):
+    arena.close()
+
+
+def k3x_arena_last_error() -> str:
+    return lib().k3x_arena_last_error().decode()
+
+
+def k3x_arena_pool(arena: Arena) -> Pool:
+    return arena.pool
+
+
+def k3x_arena_getmany(arena: Arena, layer: int, experts, stream=None):
+    """experts: host int sequence.  Returns (slots list, hits, misses)."""
+    import numpy as np
+    e = np.ascontiguousarray(np.asarray(experts, dtype=np.int32))
+    out = np.empty(len(e), dtype=np.int32)
+    h, m = ctypes.c_int32(0), ctypes.c_int32(0)
+    _check(lib().k3x_arena_getmany(arena.handle, int(layer), e.ctypes.data, len(e),
+                                   out.ctypes.data, ctypes.byref(h), ctypes.byref(m),
+                                   _stream(stream)))
+    return out.tolist(), h.value, m.value
+
+
+def k3x_arena_pin(arena: Arena, layer: int, expert: int):
+    _check(lib().k3x_arena_pin(arena.handle, int(layer), int(expert)))
+
+
+def k3x_arena_stats(arena: Arena):
+    h, m, b = ctypes.c_int64(0), ctypes.c_int64(0), ctypes.c_int64(0)
+    _check(lib().k3x_arena_stats(arena.handle, ctypes.byref(h), ctypes.byref(m), ctypes.byref(b)))
+    return h.value, m.value, b.value
+
+
+def k3x_arena_moe_forward(arena: Arena, layer: int, x, T: int, idx, gates, topk: int, y, ws,
+                          ws_bytes=None, stream=None):
+    """Returns (hits, misses) of the call."""
+    nbytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    h, m = ctypes.c_int32(0), ctypes.c_int32(0)
+    _check(lib().k3x_arena_moe_forward(arena.handle, int(layer), _ptr(x), int(T), _ptr(idx),
+                                       _ptr(gates), int(topk), _ptr(y), _ptr(ws), int(nbytes),
+                                       ctypes.byref(h), ctypes.byref(m), _stream(stream)))
+    return h.value, m.value
+
+
+def k3x_cache_replay(trace, cap: int, policy: int = K3X_CACHE_LRU, pinned=()) -> int:
+    import numpy as np
+    t = np.ascontiguousarray(np.asarray(trace, dtype=np.int64))
+    p = np.ascontiguousarray(np.asarray(list(pinned), dtype=np.int64))
+    hits = ctypes.c_int64(0)
+    _check(lib().k3x_cache_replay(t.ctypes.data, len(t), int(cap), int(policy),
+                                  p.ctypes.data if len(p) else None, len(p), ctypes.byref(hits)))
+    return hits.value
+
+
+def k3x_cache_replay_batches(batches, cap: int):
+    """batches: list of key lists.  Returns the slot given to every key, batch by batch."""
+    import numpy as np
+    keys = np.ascontiguousarray(np.asarray([k for b in batches for k in b], dtype=np.int64))
+    starts = np.ascontiguousarray(np.cumsum([0] + [len(b) for b in batches]).astype(np.int64))
+    out = np.empty(len(keys), dtype=np.int32)
+    _check(lib().k3x_cache_replay_batches(keys.ctypes.data, starts.ctypes.data, len(batches),
+                                          int(cap), out.ctypes.data))
+    res, j = [], 0
+    for b in batches:
+        res.append(out[j:j + len(b)].tolist())
+        j += len(b)
+    return res
 
 
 # ------------------------------------------------------------------------------------------
