@@ -335,6 +335,149 @@ def bench_chain(w, args, torch, S, k3x):
 
 
 LATENT_WORKLOADS = {"latent_t1_e896": 1, "latent_t8_e896": 8}
+# expert arena: (layers, slots) -- one decode token through the chained layers, the experts in
+# pinned host memory (about 36 GB can be pinned here: two layers, 31.4 GB), n slots in HBM
+ARENA_WORKLOADS = {"arena_chain2_t1_e896_s512": (2, 512)}
+PCIE_PEAK_GBS = 64.0  # PCIe 5.0 x16, one direction
+
+
+def bench_arena(args, torch, S, k3x):
+    """Decode tokens through L chained layers of 896 experts whose bytes live in pinned host
+    memory (L * 15.7 GB), with an HBM arena of n slots: RMSNorm -> router -> arena expert
+    forward (misses copied in from the host) -> residual per layer.  Every step is a fresh
+    token (steady-state decode, no graph: the arena waits for each layer's routing)."""
+    L, n_slots = ARENA_WORKLOADS[args.workload]
+    w = S.WORKLOADS[5]  # the chained workload's shape, router and Zipf bias per layer
+    H, I, E, k = w.H, w.I, w.E, w.topk
+    steps = args.steps if args.steps is not None else 100
+    warmup = args.warmup if args.warmup is not None else 50
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    log(f"backing store: {L} layers x {E} experts in pinned host memory "
+        f"({L * E * S.expert_bytes_per_expert(H, I) / 1e9:.1f} GB); arena {n_slots} slots")
+    host = {}
+    for t, n in enumerate(S.TENSOR_NAMES):
+        rows, cols = S.tensor_shape(t, H, I)
+        host[n] = torch.empty((L * E, rows, cols), dtype=torch.uint8, pin_memory=True)
+    layers = []
+    for l in range(L):  # generated on the device, one layer at a time, then copied out
+        pool_dev = S.device_pool(w.seed, l, E, H, I)
+        for n in S.TENSOR_NAMES:
+            host[n][l * E:(l + 1) * E].copy_(pool_dev[n])
+        del pool_dev
+        W, b = S.router_inputs(w, l)
+        Wd = torch.from_numpy(W.view(np.int16)).to(dev)
+        bd = torch.from_numpy(b).to(dev)
+        layers.append({"W": W, "b": b, "rdesc": k3x.router_desc(Wd, bd, k), "keep": (Wd, bd)})
+        log(f"layer {l} in the backing store")
+    torch.cuda.synchronize()
+    arena = k3x.k3x_arena_create(host, n_slots, L, E, H, I, max_slots_per_call=64)
+    n_tok = warmup + steps
+    x = S.normal_bf16(w.seed, S.P_X, 0, (n_tok, H))
+    xb = torch.empty((1, H), dtype=torch.int16, device=dev)
+    xn = torch.empty_like(xb)
+    idx = torch.empty((1, k), dtype=torch.int32, device=dev)
+    gates = torch.empty((1, k), dtype=torch.float32, device=dev)
+    y = torch.empty((1, H), dtype=torch.float32, device=dev)
+    ws = k3x.alloc_workspace(k3x.k3x_moe_workspace_size(arena.pool, 1, k), dev)
+    rws = k3x.alloc_workspace(k3x.k3x_route_workspace_size(layers[0]["rdesc"], 1), dev)
+    xs = torch.from_numpy(x.view(np.int16)).to(dev)
+    idx_log = torch.empty((n_tok, L, k), dtype=torch.int32, device=dev)  # the routing trace
+
+    def step(i):
+        xb.copy_(xs[i:i + 1])
+        k3x.k3x_rmsnorm_bf16(xb, 1, H, 1e-6, xn)
+        for li, lay in enumerate(layers):
+            k3x.k3x_route_topk(lay["rdesc"], xn, 1, idx, gates, rws)
+            k3x.k3x_arena_moe_forward(arena, li, xn, 1, idx, gates, k, y, ws)
+            idx_log[i, li].copy_(idx[0])
+            if li + 1 < L:
+                k3x.k3x_residual_add_rmsnorm_bf16(xb, y, 1, H, 1e-6, xn)
+            else:
+                k3x.k3x_residual_add_bf16(xb, y, 1, H)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    h0, m0, b0 = k3x.k3x_arena_stats(arena)
+    t0 = time.perf_counter()
+    for i in range(warmup, n_tok):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    h1, m1, b1 = k3x.k3x_arena_stats(arena)
+    if k3x.k3x_fetch_drops(ws):
+        sys.exit("run invalid: dropped slots")
+
+    # kernel times of a few more steps, event-timed
+    prof = k3x.k3x_profiler_create(20 * L * 8 + 16)
+    k3x.k3x_profiler_attach(prof)
+    for i in range(min(20, n_tok)):
+        step(i)
+    torch.cuda.synchronize()
+    k3x.k3x_profiler_attach(None)
+    durs = k3x.profiler_durations(prof)
+    k3x.k3x_profiler_destroy(prof)
+    kernels = {}
+    for name, ms in durs.items():
+        nbytes, flops = per_kernel_work(name, H, I, E, 1, k, k)
+        avg_s = float(np.mean(ms)) * 1e-3
+        kernels[name] = {"launches": len(ms), "avg_us": round(avg_s * 1e6, 3),
+                         "alg_bytes": int(nbytes), "gbps": round(nbytes / avg_s / 1e9, 1)}
+    dk = kernels["w13_decode"]
+    traffic = traffic_for("decode_t1_e896_router", "w13_decode")
+    roof = {"bound": "hbm", "achieved": dk["gbps"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(dk["gbps"] / PEAK_HBM_GBS, 4),
+            "traffic": int(traffic) if traffic is not None else None, "kernel": "w13_decode",
+            "alg_bytes": dk["alg_bytes"]}
+    # sizing by trace replay: the recorded routing of the timed steps, keys layer * E + expert
+    log_np = idx_log.cpu().numpy()[warmup:warmup + steps]
+    tr = [int(li * E + e) for row in log_np for li in range(L) for e in row[li]]
+    counts = np.bincount(np.asarray(tr, dtype=np.int64), minlength=L * E)
+    by_count = np.lexsort((np.arange(L * E), -counts))  # most requested first, ties by key
+    sizes = sorted({128, 256, n_slots, 1024, 1536})
+    replay = {}
+    for cap in sizes:
+        pins = [int(v) for v in by_count[:cap // 2] if counts[v] > 0]
+        replay[str(cap)] = {
+            "lru": round(k3x.k3x_cache_replay(tr, cap, k3x.K3X_CACHE_LRU) / len(tr), 4),
+            "belady": round(k3x.k3x_cache_replay(tr, cap, k3x.K3X_CACHE_BELADY) / len(tr), 4),
+            "pin_lru": round(k3x.k3x_cache_replay(tr, cap, k3x.K3X_CACHE_PIN_LRU, pins) / len(tr), 4)}
+    dh, dm, db = h1 - h0, m1 - m0, b1 - b0
+    res = {
+        "metric": METRIC,
+        "value": round(steps / wall, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(wall / steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "tokens": 1, "layers": L, "experts": E,
+                   "hidden": H, "inter": I, "topk": k, "router": True, "zipf_bias": True,
+                   "arena_slots": n_slots, "arena_gb": round(n_slots * k3x.k3x_expert_bytes(H, I) / 1e9, 1),
+                   "backing_gb_pinned_host": round(L * E * k3x.k3x_expert_bytes(H, I) / 1e9, 1),
+                   "timed_region": "eager: every layer waits for its routing on the host"},
+        "roofline": roof,
+        "arena": {"hit_rate": round(dh / max(dh + dm, 1), 4), "hits": dh, "misses": dm,
+                  "h2d_bytes_per_token": int(db / steps),
+                  "h2d_gbps": round(db / wall / 1e9, 2), "h2d_peak_gbps": PCIE_PEAK_GBS,
+                  "replay_hit_rate_by_slots": replay,
+                  "distinct_in_trace": len(set(tr)), "requests_in_trace": len(tr)},
+        "kernels": kernels,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the oracle on the host (bounded sample)")
+        pools = [{n: host[n][l * E:(l + 1) * E] for n in S.TENSOR_NAMES} for l in range(L)]
+        res["cpu_baseline"] = chain_cpu_baseline(
+            w, x, [{"W": lay["W"], "b": lay["b"], "pool": pools[l]} for l, lay in enumerate(layers)])
+    arena.close()
+    print(json.dumps(res), flush=True)
 
 
 def latent_cpu_baseline(sh, x, w, pool_dev, topk, budget_s=12.0):
@@ -606,9 +749,12 @@ def main():
     k3x.load_library()
     if args.workload in LATENT_WORKLOADS:
         return bench_latent(args, torch, S, k3x)
+    if args.workload in ARENA_WORKLOADS:
+        return bench_arena(args, torch, S, k3x)
     wl = {w.name: w for w in S.WORKLOADS.values()}
     if args.workload not in wl:
-        sys.exit(f"unknown workload {args.workload}; one of {sorted(wl) + sorted(LATENT_WORKLOADS)}")
+        sys.exit(f"unknown workload {args.workload}; one of "
+                 f"{sorted(wl) + sorted(LATENT_WORKLOADS) + sorted(ARENA_WORKLOADS)}")
     w = wl[args.workload]
     if w.layers != 1:
         return bench_chain(w, args, torch, S, k3x)
