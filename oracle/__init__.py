@@ -76,6 +76,11 @@ def lib():
         L.oracle_residual_add_bf16.argtypes = [P, P, ci, ci]
         L.oracle_rmsnorm_w_f32.restype = ci
         L.oracle_rmsnorm_w_f32.argtypes = [P, ci, ci, P, ctypes.c_float, P]
+        L.oracle_mxfp4_matvec_contract.restype = None
+        L.oracle_mxfp4_matvec_contract.argtypes = [P, P, P, i64, i64, P]
+        L.oracle_expert_forward_contract.restype = ci
+        L.oracle_expert_forward_contract.argtypes = [P, i64, i64, P, P, P, P, P, P, ci,
+                                                     ctypes.c_float, ctypes.c_float, P, P]
         L.oracle_dense64_bf16.restype = ci
         L.oracle_dense64_bf16.argtypes = [P, P, i64, i64, P]
         L.oracle_glu.restype = ci
@@ -295,6 +300,36 @@ def rmsnorm_w_f32(x, w, eps):
     if lib().oracle_rmsnorm_w_f32(_p(x), T, n, _p(wp), eps, _p(out)) != 0:
         raise ValueError("oracle_rmsnorm_w_f32: bad arguments")
     return out
+
+
+def mxfp4_matvec_contract(x_f32, packed, scales):
+    """The contract's MXFP4 matmul in the listing's order (double, groups in sequence, one
+    rounding to float).  x fp32 [K]; packed u8 [rows][K/2]; scales u8 [rows][K/32]."""
+    x = _c(x_f32, np.float32)
+    p = _c(packed, np.uint8)
+    sc = _c(scales, np.uint8)
+    rows, K = p.shape[0], x.shape[0]
+    assert p.shape == (rows, K // 2) and sc.shape == (rows, K // 32)
+    y = np.empty(rows, dtype=np.float32)
+    lib().oracle_mxfp4_matvec_contract(_p(x), _p(p), _p(sc), rows, K, _p(y))
+    return y
+
+
+def expert_forward_contract(x_bf16, ex, act="swiglu", want_hidden=False):
+    """One expert in the contract's arithmetic (h kept in fp32).  Returns d fp32 [H] (and
+    h fp32 [I] with want_hidden)."""
+    x = _c(x_bf16, np.uint16)
+    H = x.shape[0]
+    t = [_c(getattr(ex, n), np.uint8) for n in ("w1_packed", "w1_scale", "w3_packed",
+                                                  "w3_scale", "w2_packed", "w2_scale")]
+    I = t[0].shape[0]
+    a, b1, b2 = _act(act)
+    d = np.empty(H, dtype=np.float32)
+    h = np.empty(I, dtype=np.float32)
+    if lib().oracle_expert_forward_contract(_p(x), H, I, *[_p(v) for v in t], a, b1, b2, _p(h),
+                                            _p(d)) != 0:
+        raise ValueError("oracle_expert_forward_contract: bad arguments")
+    return (d, h) if want_hidden else d
 
 
 def dense64_bf16(W, v):

@@ -74,6 +74,7 @@ typedef ORACLE_ACC acc_t;
 
 int oracle_rmsnorm_w_f32(const float *x, int T, int n, const float *w, float eps, uint16_t *out);
 int oracle_dense64_bf16(const uint16_t *W, const uint16_t *v, int64_t rows, int64_t K, float *y);
+static float glu_one(float g, float u, int act, float b1, float b2);
 int oracle_route(const uint16_t *x, int T, int H, const uint16_t *Wr, const float *bias, int E,
                  int topk, int renorm, float routed_scale, int32_t *idx, float *gates,
                  float *logits_out, float *scores_out);
@@ -142,6 +143,55 @@ void oracle_f32_to_bf16_n(const float *x, int64_t n, uint16_t *out) {
 }
 
 double oracle_sum64(const double *a, const double *b, int64_t n) { return sum64_products(a, b, n); }
+
+/* The contract's MXFP4 matmul in the listing's own order (README Part II section 4, the
+ * MXFP4 matmul; section 5, "double, always"): per row, acc = 0 in double; groups in order; a
+ * scale byte of 255 (NaN) skips its group; else part = the sequential double sum of the
+ * group's products (exact in double) and acc += part * scale; y = (float)acc.
+ * x fp32 [K]; packed u8 [rows][K/2] (low nibble = even element); scales u8 [rows][K/32]. */
+void oracle_mxfp4_matvec_contract(const float *x, const uint8_t *packed, const uint8_t *scales,
+                                  int64_t rows, int64_t K, float *y) {
+  const int64_t ngroup = K / 32, rowbytes = K / 2;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r) {
+    const uint8_t *prow = packed + r * rowbytes;
+    const uint8_t *srow = scales + r * ngroup;
+    double acc = 0.0;
+    for (int64_t g = 0; g < ngroup; ++g) {
+      if (srow[g] == 255u) continue;
+      double part = 0.0;
+      for (int64_t c = 32 * g; c < 32 * g + 32; ++c)
+        part += (double)x[c] * (double)e2m1_value(nibble_at(prow, c));
+      acc += part * (double)e8m0_value(srow[g]);
+    }
+    y[r] = (float)acc;
+  }
+}
+
+/* One routed expert in the contract's arithmetic: g, u by the matmul above on x (bf16 widened
+ * exactly), h = act(g, u) kept in fp32 (not rounded to bf16), d = W2 . h by the same matmul.
+ * h_out fp32 [I] may be NULL; d_out fp32 [H].  Returns -1 on bad arguments. */
+int oracle_expert_forward_contract(const uint16_t *x, int64_t H, int64_t I, const uint8_t *w1p,
+                                   const uint8_t *w1s, const uint8_t *w3p, const uint8_t *w3s,
+                                   const uint8_t *w2p, const uint8_t *w2s, int act, float b1,
+                                   float b2, float *h_out, float *d_out) {
+  if (H <= 0 || I <= 0 || H % 32 || I % 32 || (act != 0 && act != 1)) return -1;
+  float *xf = (float *)malloc(sizeof(float) * (size_t)H);
+  float *g = (float *)malloc(sizeof(float) * (size_t)I);
+  float *u = (float *)malloc(sizeof(float) * (size_t)I);
+  float *h = (float *)malloc(sizeof(float) * (size_t)I);
+  for (int64_t i = 0; i < H; ++i) xf[i] = bf16_to_float(x[i]);
+  oracle_mxfp4_matvec_contract(xf, w1p, w1s, I, H, g);
+  oracle_mxfp4_matvec_contract(xf, w3p, w3s, I, H, u);
+  for (int64_t r = 0; r < I; ++r) h[r] = glu_one(g[r], u[r], act, b1, b2);
+  oracle_mxfp4_matvec_contract(h, w2p, w2s, H, I, d_out);
+  if (h_out) memcpy(h_out, h, sizeof(float) * (size_t)I);
+  free(xf);
+  free(g);
+  free(u);
+  free(h);
+  return 0;
+}
 
 /* The contract's bf16 matmul (README Part II section 5) in the fixed 64-way order:
  * y[r] = (float) sum64(W[r][k] * v[k]), W bf16 [rows][K], v bf16 [K], K % 8 == 0.  The

@@ -598,6 +598,67 @@ def _bf16_round64(v):
     return bf16_rne_from64(v)
 
 
+def _mx_row(codes, scale_bytes):
+    """Packed nibbles (low nibble = even element) and scale bytes of one row."""
+    c = np.asarray(codes, dtype=np.uint8)
+    return (c[0::2] | (c[1::2] << 4)).astype(np.uint8)[None], np.asarray(scale_bytes, np.uint8)[None]
+
+
+def test_contract_matvec_exact_on_integers(orc):
+    """The contract's MXFP4 matmul on integer-valued data is exact whatever the order: every row
+    equals its integer dot product (a transposed, dropped or misplaced term changes it)."""
+    rng = np.random.default_rng(8)
+    rows, K = 5, 256
+    codes = rng.integers(0, 16, (rows, K)).astype(np.uint8)
+    vals = np.array([orc.e2m1(int(c)) for c in range(16)])
+    W = vals[codes]
+    x = rng.integers(-4, 5, K).astype(np.float32)
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    scales = np.full((rows, K // 32), 128, dtype=np.uint8)  # 2.0
+    y = orc.mxfp4_matvec_contract(x, packed, scales)
+    assert np.array_equal(y, (2.0 * (W @ x.astype(np.float64))).astype(np.float32))
+
+
+def test_contract_matvec_skips_nan_scales_and_sums_groups_in_order(orc):
+    # a scale byte of 255 drops its group, whatever its nibbles
+    codes = [2] * 64  # 1.0 everywhere
+    x = np.ones(64, dtype=np.float32)
+    p, sc = _mx_row(codes, [127, 255])
+    assert orc.mxfp4_matvec_contract(x, p, sc)[0] == 32.0
+    # group terms 1, 2^60, -2^60, 1: the listing adds them in sequence, ((1 + 2^60) - 2^60) + 1
+    # = 1 (the first 1 is lost to rounding), where a pairwise tree gives (1 + 2^60) +
+    # (-2^60 + 1) = 0
+    K = 128
+    codes = np.zeros(K, dtype=np.uint8)
+    codes[[0, 32, 64, 96]] = [2, 2, 10, 2]  # 1.0, 1.0, -1.0, 1.0
+    p, sc = _mx_row(codes, [127, 187, 187, 127])  # scales 1, 2^60, 2^60, 1
+    x = np.ones(K, dtype=np.float32)
+    assert orc.mxfp4_matvec_contract(x, p, sc)[0] == 1.0
+    assert orc.mxfp4_matvec(x, p, sc, acc="f64")[0] == 0.0
+
+
+def test_contract_expert_against_float64_algebra(orc):
+    """The contract's expert forward (h kept in fp32) against numpy float64 algebra on the
+    dequantised weights, rounding g, u and h to fp32 at the same points."""
+    H, I = 256, 384
+    ex = S.expert_bytes(3, 0, 1, H, I)
+    x = S.normal_bf16(3, S.P_X, 0, (H,))
+    for act in ("swiglu", ("situ", 4.0, 25.0)):
+        d, h = orc.expert_forward_contract(x, ex, act=act, want_hidden=True)
+        xf = bits_to_f(x)
+        W1 = dequant64(ex.w1_packed, ex.w1_scale)
+        W3 = dequant64(ex.w3_packed, ex.w3_scale)
+        W2 = dequant64(ex.w2_packed, ex.w2_scale)
+        g, u = (W1 @ xf).astype(np.float32), (W3 @ xf).astype(np.float32)
+        h_ref = orc.glu(g, u, act)
+        assert np.max(np.abs(h - h_ref)) <= 1e-6 * np.max(np.abs(h_ref))
+        d_ref = W2 @ h.astype(np.float64)
+        assert np.linalg.norm(d - d_ref) / np.linalg.norm(d_ref) < 1e-6
+        # the bf16 rounding of h is what separates it from the routed path's arithmetic
+        d_bf16 = orc.expert_forward(x, ex, acc="f64", act=act)
+        assert not np.array_equal(d, d_bf16)
+
+
 def test_dense64_exact_on_integers(orc):
     """The contract's bf16 matmul on small integers: every product and partial sum is exact,
     so each row must equal its integer dot product whatever the order (a dropped term, a
