@@ -55,7 +55,8 @@ KERNEL_SYMBOLS = {"w13_decode": "decode_w13", "w2_combine_decode": "decode_w2_co
                   "w13_prefill": "gemm_prefill<true>", "w2_prefill": "gemm_prefill<false>",
                   "w13_grouped": "gemm_decode<true>", "w2_grouped": "gemm_decode<false>",
                   "route_scores": "route_scores", "route_select": "route_select",
-                  "latent_in": "latent_in", "latent_out": "latent_out"}
+                  "latent_in": "latent_in", "latent_out": "latent_out",
+                  "w13_contract": "contract_rows<true>", "w2_contract": "contract_rows<false>"}
 
 
 def log(*a):
@@ -74,6 +75,12 @@ def per_kernel_work(name, H, I, E, T, topk, U):
     slots = T * topk
     if name in ("w13_decode", "w13_grouped", "w13_prefill"):
         return U * w13 + T * H * 2 + slots * I * 2, slots * 4.0 * I * H
+    if name == "w13_contract":  # h kept in fp32
+        return U * w13 + T * H * 2 + slots * I * 4, slots * 4.0 * I * H
+    if name == "w2_contract":
+        return U * w2 + slots * I * 4 + slots * H * 4, slots * 2.0 * H * I
+    if name == "combine_contract":
+        return slots * H * 4 + T * H * 4 + slots * 8, 2.0 * slots * H
     if name in ("w2_grouped", "w2_prefill"):
         return U * w2 + slots * I * 2 + slots * H * 4, slots * 2.0 * H * I
     if name == "w2_combine_decode":
@@ -729,6 +736,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--activation", choices=("swiglu", "situ"), default="swiglu",
                     help="gated activation of the expert pool (situ: SiTU-GLU, caps 4 and 25)")
+    ap.add_argument("--contract", action="store_true",
+                    help="the floating point contract's arithmetic (double sums in the listing's "
+                         "order, h in fp32); one token per call")
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"))
     args = ap.parse_args()
@@ -766,8 +776,10 @@ def main():
 
     log(f"generating pool: E={w.E} H={w.H} I={w.I}")
     pool_dev = S.device_pool(w.seed, 0, w.E, w.H, w.I)
+    if args.contract and w.T != 1:
+        sys.exit("--contract runs one token per call: use a decode workload")
     pool = k3x.k3x_expert_pool_create(pool_dev, hidden=w.H, inter=w.I, n_experts=w.E,
-                                      activation=args.activation)
+                                      activation=args.activation, contract=args.contract)
     R = 1 if prefill else ROTATE
     x = S.normal_bf16(w.seed, S.P_X, 0, (R * w.T, w.H))
     xs = [torch.from_numpy(x[r * w.T:(r + 1) * w.T].view(np.int16)).to(dev) for r in range(R)]
@@ -899,6 +911,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "activation": args.activation, "tokens": w.T,
+                   "arithmetic": "contract (fp64 sums, h fp32)" if args.contract else "routed (fp32 sums, h bf16)",
                    "experts": w.E, "hidden": w.H,
                    "inter": w.I, "topk": w.topk, "router": w.router, "zipf_bias": w.zipf,
                    "weights": "mxfp4 (e2m1 + e8m0 per 32)", "rotated_batches": R,

@@ -87,6 +87,11 @@ typedef struct k3x_pool_desc {
   int32_t activation; /* k3x_activation; 0 (a zeroed desc) is SwiGLU               */
   float situ_b1;      /* K3X_ACT_SITU: gate cap, finite and > 0 (4.0 in the checkpoint) */
   float situ_b2;      /* K3X_ACT_SITU: up cap, finite and > 0 (25.0 in the checkpoint)  */
+  int32_t contract;   /* 0: the routed path's arithmetic (per-group fp32 sums, h in bf16);
+                         1: the floating point contract of README Part II sections 4 and 5
+                         (per row, groups summed in sequence in double, each the sequential
+                         double sum of its products times its scale, one rounding to float;
+                         h kept in fp32) -- one token per call only                       */
 } k3x_pool_desc;
 
 typedef struct k3x_pool k3x_pool;

@@ -48,6 +48,7 @@ class k3x_pool_desc(ctypes.Structure):
         ("activation", ctypes.c_int32),
         ("situ_b1", ctypes.c_float),
         ("situ_b2", ctypes.c_float),
+        ("contract", ctypes.c_int32),
     ]
 
 
@@ -265,14 +266,18 @@ TENSOR_ORDER = ("w1_packed", "w1_scale", "w3_packed", "w3_scale", "w2_packed", "
 
 def k3x_expert_pool_create(tensors: dict, hidden: int, inter: int, n_experts: int,
                            group: int = 32, strides=None, activation: str = "swiglu",
-                           situ_b1: float = 4.0, situ_b2: float = 25.0) -> Pool:
+                           situ_b1: float = 4.0, situ_b2: float = 25.0,
+                           contract: bool = False) -> Pool:
     """tensors: the six uint8 device tensors by name (each [E][rows][cols] or any layout that
     matches the strides).  strides: per-expert byte strides (None / 0 = dense).
-    activation: "swiglu" or "situ" (SiTU-GLU with caps situ_b1, situ_b2)."""
+    activation: "swiglu" or "situ" (SiTU-GLU with caps situ_b1, situ_b2).  contract: the
+    floating point contract's arithmetic (double sums in the listing's order, h in fp32; one
+    token per call)."""
     d = k3x_pool_desc()
     d.n_experts, d.hidden, d.inter, d.group = n_experts, hidden, inter, group
     d.activation = {"swiglu": K3X_ACT_SWIGLU, "situ": K3X_ACT_SITU}[activation]
     d.situ_b1, d.situ_b2 = situ_b1, situ_b2
+    d.contract = 1 if contract else 0
     for name in TENSOR_ORDER:
         t = tensors.get(name)
         setattr(d, name, None if t is None else _ptr(t))

@@ -79,6 +79,10 @@ k3x_status k3x_expert_pool_create(const k3x_pool_desc* d, k3x_pool** out) {
         d->situ_b2 > 0.0f))
     return fail(K3X_E_INVALID_ARG, "pool_create: SiTU caps %g, %g must be finite and > 0",
                 (double)d->situ_b1, (double)d->situ_b2);
+  if (d->contract != 0 && d->contract != 1)
+    return fail(K3X_E_INVALID_ARG, "pool_create: contract %d is neither 0 nor 1", d->contract);
+  if (d->contract && (d->hidden > 4096 || d->inter > 4096))
+    return fail(K3X_E_UNSUPPORTED, "pool_create: the contract arithmetic takes hidden and inter <= 4096");
   const void* ptrs[6] = {d->w1_packed, d->w1_scale, d->w3_packed, d->w3_scale, d->w2_packed, d->w2_scale};
   const int64_t H = d->hidden, I = d->inter;
   const int64_t dense[6] = {I * H / 2, I * H / 32, I * H / 2, I * H / 32, H * I / 2, H * I / 32};
@@ -90,6 +94,7 @@ k3x_status k3x_expert_pool_create(const k3x_pool_desc* d, k3x_pool** out) {
   p->act = d->activation;
   p->b1 = d->activation == K3X_ACT_SITU ? d->situ_b1 : 0.0f;
   p->b2 = d->activation == K3X_ACT_SITU ? d->situ_b2 : 0.0f;
+  p->contract = d->contract;
   for (int k = 0; k < 6; ++k) {
     if (!ptrs[k]) {
       delete p;
@@ -159,9 +164,14 @@ size_t k3x_moe_workspace_size(const k3x_pool* p, int32_t T, int32_t topk) {
   if (!p || T < 0 || topk < 1 || topk > 64) return 0;
   if ((int64_t)T * topk > (int64_t)1 << 26) return 0;
   const size_t general = k3x::moe_layout(p->E, p->H, p->I, T, topk).total;
-  size_t off_h;
+  size_t off_h, off_d;
   const size_t exact = k3x::decode_exact_ws(*p, topk, &off_h);
-  return general > exact ? general : exact;
+  size_t need = general > exact ? general : exact;
+  if (p->contract) {
+    const size_t c = k3x::contract_ws(*p, topk, &off_h, &off_d);
+    need = need > c ? need : c;
+  }
+  return need;
 }
 
 k3x_status k3x_moe_forward(const k3x_pool* p, const void* x_bf16, int32_t T, const int32_t* idx,
@@ -172,6 +182,8 @@ k3x_status k3x_moe_forward(const k3x_pool* p, const void* x_bf16, int32_t T, con
   if (topk < 1 || topk > 64) return fail(K3X_E_INVALID_ARG, "moe_forward: topk %d not in 1..64", topk);
   if ((int64_t)T * topk > (int64_t)1 << 26)
     return fail(K3X_E_UNSUPPORTED, "moe_forward: T * topk above 2^26");
+  if (p->contract && T > 1)
+    return fail(K3X_E_UNSUPPORTED, "moe_forward: the contract arithmetic runs one token per call");
   const size_t need = k3x_moe_workspace_size(p, T, topk);
   if (!ws || ws_bytes < need || !aligned(ws, 256))
     return fail(K3X_E_WORKSPACE, "moe_forward: workspace %zu bytes, need %zu (256-byte aligned)",
@@ -230,6 +242,8 @@ static k3x_status check_latent(const k3x_latent_desc* d, const k3x_pool* p,
     return fail(K3X_E_UNSUPPORTED, "latent: norm weight not 16-byte aligned");
   if ((int64_t)T * r->topk > (int64_t)1 << 26)
     return fail(K3X_E_UNSUPPORTED, "latent: T * topk above 2^26");
+  if (p->contract && T > 1)
+    return fail(K3X_E_UNSUPPORTED, "latent: the contract arithmetic runs one token per call");
   return K3X_OK;
 }
 
@@ -285,6 +299,8 @@ static k3x_status check_route_moe(const k3x_router_desc* r, const k3x_pool* p, i
                 p->H);
   if (r->topk > 64) return fail(K3X_E_UNSUPPORTED, "route_moe: topk %d above 64", r->topk);
   if (T < 0) return fail(K3X_E_INVALID_ARG, "route_moe: T %d < 0", T);
+  if (p->contract && T > 1)
+    return fail(K3X_E_UNSUPPORTED, "route_moe: the contract arithmetic runs one token per call");
   if ((int64_t)T * r->topk > (int64_t)1 << 26)
     return fail(K3X_E_UNSUPPORTED, "route_moe: T * topk above 2^26");
   return K3X_OK;

@@ -126,6 +126,7 @@ struct k3x_pool {
   int64_t stride[6];
   int32_t act;   // k3x_activation
   float b1, b2;  // SiTU-GLU caps
+  int32_t contract;  // 1: the floating point contract's arithmetic (k3x_contract.hip)
 };
 
 namespace k3x {
@@ -145,6 +146,13 @@ hipError_t launch_route_select(const k3x_router_desc& r, int32_t T, const float*
 hipError_t launch_moe(const k3x_pool& p, const uint16_t* x, int32_t T, const int32_t* idx,
                       const float* gates, int32_t topk, float* y, uint8_t* ws,
                       const MoeLayout& L, hipStream_t s);
+
+// One token in the floating point contract's arithmetic (k3x_contract.hip).
+bool contract_supported(const k3x_pool& p, int32_t T, int32_t topk);
+size_t contract_ws(const k3x_pool& p, int32_t topk, size_t* off_h, size_t* off_d);
+hipError_t launch_contract(const k3x_pool& p, const uint16_t* x, const int32_t* idx,
+                           const float* gates, int32_t topk, float* y, uint8_t* ws,
+                           hipStream_t s);
 
 // Single-token decode in the reference arithmetic order (k3x_decode.hip).
 bool decode_exact_supported(const k3x_pool& p, int32_t T, int32_t topk);

@@ -545,6 +545,7 @@ __global__ __launch_bounds__(256) void moe_combine(const float* __restrict__ d,
 hipError_t launch_moe(const k3x_pool& p, const uint16_t* x, int32_t T, const int32_t* idx,
                       const float* gates, int32_t topk, float* y, uint8_t* ws,
                       const MoeLayout& L, hipStream_t s) {
+  if (p.contract && T > 0) return launch_contract(p, x, idx, gates, topk, y, ws, s);
   if (decode_exact_supported(p, T, topk))
     return launch_decode_exact(p, x, idx, gates, topk, y, ws, s);
   hipError_t err;

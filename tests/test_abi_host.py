@@ -298,6 +298,25 @@ def test_route_moe_host_validation(k3x):
         lib.k3x_expert_pool_destroy(h)
 
 
+def test_contract_pool_checks(k3x):
+    lib = k3x.lib()
+    assert _create(k3x, _desc(k3x, contract=2))[0] == k3x.K3X_E_INVALID_ARG
+    assert _create(k3x, _desc(k3x, contract=1, hidden=8192))[0] == k3x.K3X_E_UNSUPPORTED
+    st, h = _create(k3x, _desc(k3x, contract=1))
+    assert st == 0
+    try:
+        fake = 1 << 40
+        # one token per call in the contract arithmetic; more is refused before any launch
+        assert lib.k3x_moe_forward(h, fake, 2, fake, fake, 4, fake, fake, 1 << 30, None) == \
+            k3x.K3X_E_UNSUPPORTED
+        n1 = lib.k3x_moe_workspace_size(h, 1, 4)
+        st0, h0 = _create(k3x, _desc(k3x))
+        assert n1 >= lib.k3x_moe_workspace_size(h0, 1, 4) and n1 >= 256 + 4 * 4 * (384 + 256)
+        lib.k3x_expert_pool_destroy(h0)
+    finally:
+        lib.k3x_expert_pool_destroy(h)
+
+
 def test_status_strings(k3x):
     for s in (0, -1, -2, -3, -4, -5):
         assert k3x.k3x_status_str(s)
