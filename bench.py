@@ -23,9 +23,11 @@ The copy's readings give the scale of each counter (bytes moved / bytes counted)
 summary records the hash of the kernel sources, and a normal run reports the traffic only
 while those sources are unchanged.
 
-Prints ONE JSON line.  The timed region replays one HIP graph per rotated batch (captured
-once, each replay checked bit for bit against the eager result first), so `value` and
-`ms_per_step` are the path's throughput without host launch gaps.  Kernel durations for the
+Prints ONE JSON line.  The timed region replays a HIP graph that runs the rotated batches one
+after another (captured once, every replay checked bit for bit against the eager results
+first), so `value` and `ms_per_step` are the path's throughput without host launch gaps, as
+when the layers of a model run inside one graph; `path.ms_per_step_one_graph_per_step` is the
+same steps with one graph per step (each graph launch adds a gap of several microseconds).  Kernel durations for the
 roofline come from HIP events the library records around each of its launches
 (k3x_profiler_*) in a second timed pass over the same steps, launched eagerly.
 """
@@ -46,6 +48,8 @@ METRIC = "MoE-layer tokens/s + achieved HBM GB/s (decode), TFLOP/s (prefill)"
 PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
 ROTATE = 64
+TIMED_REGION = ("HIP graph replay: one graph runs the rotated batches in order, as a model's "
+                "layers run inside one graph (single-batch graphs for any remainder)")
 ORACLE_ACT = {"swiglu": "swiglu", "situ": ("situ", 4.0, 25.0)}
 COPY_PROBE_BYTES = 1 << 30
 KERNEL_SOURCES = ("k3x_decode.hip", "k3x_moe.hip", "k3x_prefill.hip", "k3x_router.hip")
@@ -119,6 +123,75 @@ def latent_kernel_work(name, sh, T):
         return (D * (L + Sx) * 2 + T * (L * 4 + Sx * 2) + L * 4 + T * D * 4,
                 2.0 * T * D * (L + Sx))
     return per_kernel_work(name, L, sh.I, sh.E, T, sh.topk, min(sh.E, T * sh.topk))
+
+
+def graph_timing(torch, step, R, outs, eager, steps, warmup):
+    """Captures one HIP graph per rotated batch and one graph of all R batches in order (the
+    way a model's layers run back to back inside one graph), checks every replay bit for bit
+    against the eager outputs (each output overwritten first, eager steps between replays),
+    and times `steps` steps both ways after `warmup` untimed ones: the sequence graph for
+    steps // R replays and single graphs for the rest, then single graphs only.  outs(r) gives
+    the output tensors of batch r, eager[r] their eager values.  Returns the wall seconds of
+    the two timed passes (sequence graph, one graph per step)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(0)
+    torch.cuda.current_stream().wait_stream(side)
+    singles = []
+    for r in range(R):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(r)
+        singles.append(g)
+    seq = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(seq):
+        for r in range(R):
+            step(r)
+
+    def spoil(r):
+        for o in outs(r):
+            o.fill_(-1)
+
+    def check(what, r):
+        if not all(torch.equal(o, e) for o, e in zip(outs(r), eager[r])):
+            sys.exit(f"{what} differs from the eager result at batch {r}")
+
+    for r in range(R):
+        spoil(r)
+        singles[r].replay()
+        torch.cuda.synchronize()
+        check("graph replay", r)
+        step((r + 1) % R)
+        torch.cuda.synchronize()
+    for rep_ in range(2):
+        for r in range(R):
+            spoil(r)
+        seq.replay()
+        torch.cuda.synchronize()
+        for r in range(R):
+            check(f"sequence graph replay {rep_}", r)
+        step(rep_ % R)
+        torch.cuda.synchronize()
+
+    def run(n, use_seq):
+        rem = n
+        if use_seq:
+            for _ in range(n // R):
+                seq.replay()
+            rem = n % R
+        for j in range(rem):
+            singles[j % R].replay()
+
+    walls = []
+    for use_seq in (True, False):
+        run(warmup, use_seq)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        run(steps, use_seq)
+        torch.cuda.synchronize()
+        walls.append(time.perf_counter() - t0)
+    return walls[0], walls[1]
 
 
 def cpu_baseline(w, x, W, b, dev_idx, dev_gates, pool_dev, budget_s=12.0, act="swiglu"):
@@ -528,8 +601,8 @@ def bench_latent(args, torch, S, k3x):
     tokens, one HIP graph per rotated batch."""
     T = LATENT_WORKLOADS[args.workload]
     sh = S.LATENT_K3
-    steps = args.steps if args.steps is not None else 200
-    warmup = args.warmup if args.warmup is not None else 20
+    steps = args.steps if args.steps is not None else 4 * ROTATE
+    warmup = args.warmup if args.warmup is not None else ROTATE
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
     seed = S.LATENT_SEED
@@ -545,47 +618,21 @@ def bench_latent(args, torch, S, k3x):
     R = ROTATE
     x = S.normal_bf16(seed, S.P_X, 0, (R * T, sh.D))
     xs = [torch.from_numpy(x[i * T:(i + 1) * T].view(np.int16)).to(dev) for i in range(R)]
-    out = torch.empty((T, sh.D), dtype=torch.float32, device=dev)
+    outs_ = [torch.empty((T, sh.D), dtype=torch.float32, device=dev) for _ in range(R)]
     ws = k3x.alloc_workspace(k3x.k3x_latent_workspace_size(d, pool, r, T), dev)
     moe_off = k3x.k3x_latent_ws_layout(d, pool, r, T)["moe"]
 
     def step(i):
-        k3x.k3x_latent_forward(d, pool, r, xs[i], T, out, ws)
+        k3x.k3x_latent_forward(d, pool, r, xs[i], T, outs_[i], ws)
 
-    out_eager = []
+    eager = []
     for i in range(R):
         step(i)
         torch.cuda.synchronize()
-        out_eager.append(out.clone())
+        eager.append([outs_[i].clone()])
     if k3x.k3x_fetch_drops(ws[moe_off:]):
         sys.exit("run invalid: dropped slots")
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        step(0)
-    torch.cuda.current_stream().wait_stream(side)
-    graphs = []
-    for i in range(R):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            step(i)
-        graphs.append(g)
-    for i in range(R):
-        graphs[i].replay()
-        torch.cuda.synchronize()
-        if not torch.equal(out, out_eager[i]):
-            sys.exit(f"graph replay of batch {i} differs from the eager result")
-        step((i + 1) % R)
-        torch.cuda.synchronize()
-
-    for i in range(warmup):
-        graphs[i % R].replay()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        graphs[i % R].replay()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    wall, wall_single = graph_timing(torch, step, R, lambda i: (outs_[i],), eager, steps, warmup)
 
     prof = k3x.k3x_profiler_create(steps * 16 + 16)
     torch.cuda.synchronize()
@@ -640,7 +687,8 @@ def bench_latent(args, torch, S, k3x):
                  "hbm_gbps_kernel_sum": round(path_bytes / ksum / 1e9, 1),
                  "hbm_frac_kernel_sum": round(path_bytes / ksum / 1e9 / PEAK_HBM_GBS, 4),
                  "hbm_gbps_wall": round(path_bytes / (wall / steps) / 1e9, 1),
-                 "timed_region": "HIP graph replay, one graph per rotated batch"},
+                 "timed_region": TIMED_REGION,
+                 "ms_per_step_one_graph_per_step": round(wall_single / steps * 1e3, 5)},
         "kernels": kernels,
         "cpu_baseline": None,
     }
@@ -769,8 +817,8 @@ def main():
     if w.layers != 1:
         return bench_chain(w, args, torch, S, k3x)
     prefill = w.T > 64
-    steps = args.steps if args.steps is not None else (20 if prefill else 200)
-    warmup = args.warmup if args.warmup is not None else (3 if prefill else 20)
+    steps = args.steps if args.steps is not None else (20 if prefill else 4 * ROTATE)
+    warmup = args.warmup if args.warmup is not None else (3 if prefill else ROTATE)
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
 
@@ -794,9 +842,10 @@ def main():
             i_, g_ = S.uniform_routing(w.seed + r, w.T, w.E, w.topk)
             routes_np.append((i_, g_))
             routes.append((torch.from_numpy(i_).to(dev), torch.from_numpy(g_).to(dev)))
-    idx = torch.empty((w.T, w.topk), dtype=torch.int32, device=dev)
-    gates = torch.empty((w.T, w.topk), dtype=torch.float32, device=dev)
-    y = torch.empty((w.T, w.H), dtype=torch.float32, device=dev)
+    # outputs of each rotated batch
+    idxs = [torch.empty((w.T, w.topk), dtype=torch.int32, device=dev) for _ in range(R)]
+    gatess = [torch.empty((w.T, w.topk), dtype=torch.float32, device=dev) for _ in range(R)]
+    ys = [torch.empty((w.T, w.H), dtype=torch.float32, device=dev) for _ in range(R)]
     rdesc = k3x.router_desc(Wd, bd, w.topk) if w.router else None
     # with a router: router + experts in one call
     ws = k3x.alloc_workspace(k3x.k3x_route_moe_workspace_size(rdesc, pool, w.T) if w.router
@@ -804,52 +853,27 @@ def main():
 
     def step(r):
         if w.router:
-            k3x.k3x_route_moe_forward(rdesc, pool, xs[r], w.T, idx, gates, y, ws)
+            k3x.k3x_route_moe_forward(rdesc, pool, xs[r], w.T, idxs[r], gatess[r], ys[r], ws)
         else:
             i_, g_ = routes[r]
-            k3x.k3x_moe_forward(pool, xs[r], w.T, i_, g_, w.topk, y, ws)
+            k3x.k3x_moe_forward(pool, xs[r], w.T, i_, g_, w.topk, ys[r], ws)
+
+    def outs(r):
+        return (idxs[r], gatess[r], ys[r]) if w.router else (ys[r],)
 
     # distinct experts per rotated batch (from the GPU's own routing), eager results kept
-    U, y_eager = [], []
+    U, eager = [], []
     for r in range(R):
         step(r)
         torch.cuda.synchronize()
-        ids = (idx if w.router else routes[r][0]).cpu().numpy()
+        ids = (idxs[r] if w.router else routes[r][0]).cpu().numpy()
         U.append(len(np.unique(ids)))
-        y_eager.append(y.clone())
+        eager.append([o.clone() for o in outs(r)])
     drops = k3x.k3x_fetch_drops(ws)
     if drops:
         sys.exit(f"run invalid: {drops} dropped slots")
 
-    # one graph per rotated batch; every graph is replayed and checked against the eager
-    # result, with eager steps in between
-    graphs = []
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        step(0)
-    torch.cuda.current_stream().wait_stream(side)
-    for r in range(R):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            step(r)
-        graphs.append(g)
-    for r in range(R):
-        graphs[r].replay()
-        torch.cuda.synchronize()
-        if not torch.equal(y, y_eager[r]):
-            sys.exit(f"graph replay of batch {r} differs from the eager result")
-        step((r + 1) % R)
-        torch.cuda.synchronize()
-
-    for i in range(warmup):
-        graphs[i % R].replay()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        graphs[i % R].replay()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    wall, wall_single = graph_timing(torch, step, R, outs, eager, steps, warmup)
 
     # kernel durations: the same steps launched eagerly, HIP events around each launch
     kernels_per_step = 6 if w.router else 4
@@ -923,7 +947,8 @@ def main():
                  "hbm_frac_kernel_sum": round(path_bytes / ksum / 1e9 / PEAK_HBM_GBS, 4),
                  "tflops_kernel_sum": round(path_flops / ksum / 1e12, 2),
                  "hbm_gbps_wall": round(path_bytes / (wall / steps) / 1e9, 1),
-                 "timed_region": "HIP graph replay, one graph per rotated batch",
+                 "timed_region": TIMED_REGION,
+                 "ms_per_step_one_graph_per_step": round(wall_single / steps * 1e3, 5),
                  "eager_ms_per_step": round(wall_eager / steps * 1e3, 5)},
         "kernels": kernels,
         "cpu_baseline": None,

@@ -90,24 +90,38 @@ __device__ __forceinline__ float group_sum(const uint4& q, const float (&x)[32])
   return p;
 }
 
-// bf16 activations of this lane's groups L (x0) and 64 + L (x1) -> floats; zero past the
-// last group.
-__device__ __forceinline__ void load_act(const uint16_t* __restrict__ row, int lane, int ngroups,
-                                         float (&x0)[32], float (&x1)[32]) {
+// The bf16 activations of this lane's groups L and 64 + L, as loaded: raw[4 h + c] holds
+// elements 8c .. 8c + 7 of group L + 64 h.  Lanes past the last group read the last group
+// (act_to_f32 zeroes them), so the loads are unconditional and can be issued early, their
+// conversion waiting until the first weight rows are in flight.
+__device__ __forceinline__ void load_act_raw(const uint16_t* __restrict__ row, int lane,
+                                             int ngroups, uint4 (&raw)[8]) {
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const int g = lane + 64 * h;
-    const bool ok = g < ngroups;
+    const int g = min(lane + 64 * h, ngroups - 1);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) raw[4 * h + c] = *reinterpret_cast<const uint4*>(row + 32 * g + 8 * c);
+  }
+}
+
+// raw -> floats of groups L (x0) and 64 + L (x1); zero past the last group.  The raw words
+// pass through an empty asm, so the conversion stays where it is called (after the first
+// weight rows are requested) instead of being hoisted next to the loads.
+__device__ __forceinline__ void act_to_f32(const uint4 (&raw)[8], int lane, int ngroups,
+                                           float (&x0)[32], float (&x1)[32]) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const bool ok = lane + 64 * h < ngroups;
     float* dst = h ? x1 : x0;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const uint4 v =
-          ok ? *reinterpret_cast<const uint4*>(row + 32 * g + 8 * c) : make_uint4(0, 0, 0, 0);
+      uint4 v = raw[4 * h + c];
+      asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
       const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        dst[8 * c + 2 * j] = bf16_bits_to_f32(w[j] & 0xFFFFu);
-        dst[8 * c + 2 * j + 1] = bf16_bits_to_f32(w[j] >> 16);
+        dst[8 * c + 2 * j] = ok ? bf16_bits_to_f32(w[j] & 0xFFFFu) : 0.0f;
+        dst[8 * c + 2 * j + 1] = ok ? bf16_bits_to_f32(w[j] >> 16) : 0.0f;
       }
     }
   }
@@ -131,10 +145,11 @@ __device__ __forceinline__ void row_leaves(const RowBits& r, const float (&x0)[3
 // takes a contiguous, balanced share of it, and each wave of the die a contiguous, balanced
 // run of that share, so every wave streams nearly the same number of rows and the expert
 // (and, for W2, the slot's activations) changes at most a few times along a run.
+template <int kThreads>
 __device__ __forceinline__ void wave_rows(int total, int& g0, int& g1) {
   int die, rank, per_die;
   xcd_rank(die, rank, per_die);
-  const int wpb = blockDim.x / kWave;
+  constexpr int wpb = kThreads / kWave;
   const int W = per_die * wpb;
   const int w = rank * wpb + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lo = (int)((int64_t)total * die / kNumXcd);
@@ -207,16 +222,18 @@ __device__ __forceinline__ LaneOffsets lane_offsets(int lane, int ngroups, uint3
 
 // Streams rows r0 .. rlast of one expert (one matrix, or W1 and W3 side by side when kW13)
 // against the activations x0/x1: rows are loaded three ahead of the arithmetic and finished
-// four at a time.  After each group of four rows r .. r + 3 every lane calls
+// four at a time.  prep() runs once the first three rows are requested (it fills x0/x1 from
+// activations already in flight).  After each group of four rows r .. r + 3 every lane calls
 // emit(r + lane, sum_a, sum_b, valid, n): lanes 0..3 with valid set hold the full dot
 // products of row r + lane (sum_b only when kW13), and n (the same on every lane) is the
 // number of valid rows in the group.
-template <bool kW13, typename Emit>
+template <bool kW13, typename Prep, typename Emit>
 __device__ __forceinline__ void stream_rows(const uint8_t* wa, const uint8_t* sa,
                                             const uint8_t* wb, const uint8_t* sb, int r0,
                                             int rlast, uint32_t wrow, uint32_t srow,
                                             const LaneOffsets& lo, const float (&x0)[32],
-                                            const float (&x1)[32], int lane, Emit emit) {
+                                            const float (&x1)[32], int lane, Prep prep,
+                                            Emit emit) {
   RowBits A[4] = {}, C[4] = {};
   // row r into buffer i (rows past the segment re-read rlast); the scheduling barriers keep
   // the loads where they stand, three rows ahead of the arithmetic
@@ -230,6 +247,7 @@ __device__ __forceinline__ void stream_rows(const uint8_t* wa, const uint8_t* sa
   load(0, r0);
   load(1, r0 + 1);
   load(2, r0 + 2);
+  prep();
 #pragma unroll 1
   for (int r = r0; r <= rlast; r += 4) {
     float v[kW13 ? 2 : 1][8];
@@ -252,21 +270,24 @@ __device__ __forceinline__ void stream_rows(const uint8_t* wa, const uint8_t* sa
 // and their activations evaluated up to 64 at a time, one per lane, so the double-precision
 // exponentials and tanh do not hold up the row loop.  Workgroup 0 also writes the number of
 // dropped slots.
-__global__ __launch_bounds__(256) void decode_w13(DecodeArgs a) {
+constexpr int kW13Threads = 256;
+
+__global__ __launch_bounds__(kW13Threads) void decode_w13(DecodeArgs a) {
   const int lane = threadIdx.x % kWave;
   const int my_idx = lane < a.topk ? a.idx[lane] : -1;
+  const int ngroups = a.K / kGroup;
+  uint4 xr[8];
+  load_act_raw(a.act, lane, ngroups, xr);
   if (blockIdx.x == 0 && threadIdx.x < kWave) {
     const unsigned long long bad = __ballot(lane < a.topk && !expert_ok(my_idx, a.E));
     if (lane == 0) *reinterpret_cast<int64_t*>(a.ws) = __popcll(bad);
   }
-  const int ngroups = a.K / kGroup;
   const uint32_t wrow = (uint32_t)a.K / 2, srow = (uint32_t)ngroups;
   const LaneOffsets lo = lane_offsets(lane, ngroups, wrow, srow);
   int g0, g1;
-  wave_rows(a.topk * a.rows, g0, g1);
+  wave_rows<kW13Threads>(a.topk * a.rows, g0, g1);
 
   float x0[32], x1[32];
-  load_act(a.act, lane, ngroups, x0, x1);
 
   __shared__ float s_g[4][kWave], s_u[4][kWave];
   __shared__ int32_t s_o[4][kWave];
@@ -305,6 +326,7 @@ __global__ __launch_bounds__(256) void decode_w13(DecodeArgs a) {
     stream_rows<true>(a.wa + (size_t)e * a.st_wa, a.sa + (size_t)e * a.st_sa,
                       a.wb + (size_t)e * a.st_wb, a.sb + (size_t)e * a.st_sb, r0, r0 + n - 1,
                       wrow, srow, lo, x0, x1, lane,
+                      [&]() { act_to_f32(xr, lane, ngroups, x0, x1); },
                       [&](int r, float gv, float uv, bool valid, int nv) {
                         if (valid) {
                           s_g[wv][nbuf + lane] = gv;
@@ -346,10 +368,12 @@ __global__ __launch_bounds__(kW2Waves * kWave) void decode_w2_combine(DecodeArgs
   for (int slot = wave; slot < a.topk; slot += kW2Waves) {
     const int e = __builtin_amdgcn_readlane(my_idx, slot);
     if (!expert_ok(e, a.E)) continue;
-    load_act(a.act + (size_t)slot * a.K, lane, ngroups, x0, x1);
+    uint4 hr[8];
+    load_act_raw(a.act + (size_t)slot * a.K, lane, ngroups, hr);
     float* d = dsh + slot * R - rb0;
     stream_rows<false>(a.wa + (size_t)e * a.st_wa, a.sa + (size_t)e * a.st_sa, nullptr, nullptr,
                        rb0, rlast, wrow, srow, lo, x0, x1, lane,
+                       [&]() { act_to_f32(hr, lane, ngroups, x0, x1); },
                        [&](int r, float dv, float, bool valid, int) {
                          if (valid) d[r] = dv;
                        });
@@ -370,7 +394,7 @@ int decode_w13_grid() {
   static int per_cu = 0;
   if (!per_cu) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_w13, 256, 0) != hipSuccess || n < 1)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_w13, kW13Threads, 0) != hipSuccess || n < 1)
       n = 2;
     per_cu = n;
   }
@@ -416,7 +440,7 @@ hipError_t launch_decode_exact(const k3x_pool& p, const uint16_t* x, const int32
   a.gact = p.act;
   a.b1 = p.b1;
   a.b2 = p.b2;
-  hipError_t err = launch("w13_decode", decode_w13, dim3(decode_w13_grid()), dim3(256), 0, s, a);
+  hipError_t err = launch("w13_decode", decode_w13, dim3(decode_w13_grid()), dim3(kW13Threads), 0, s, a);
   if (err != hipSuccess) return err;
   DecodeArgs b = a;
   b.wa = p.base[4];
