@@ -98,9 +98,10 @@ typedef struct k3x_pool k3x_pool;
 
 /* Validates d and creates a host-side handle in *out.  Refuses (K3X_E_UNSUPPORTED)
  * group != 32, hidden or inter not a multiple of 128, packed pointers or strides not
- * 16-byte aligned; refuses (K3X_E_INVALID_ARG) NULL pointers, n_experts out of range,
- * strides smaller than the dense tensor size, an unknown activation and, for SiTU-GLU,
- * caps that are not finite and positive.  Allocates host memory only; the device
+ * 16-byte aligned, and a contract pool with hidden or inter above 4096; refuses
+ * (K3X_E_INVALID_ARG) NULL pointers, n_experts out of range, strides smaller than the dense
+ * tensor size, an unknown activation, contract not 0 or 1 and, for SiTU-GLU, caps that are
+ * not finite and positive.  Allocates host memory only; the device
  * tensors are borrowed and must outlive the pool.  Scale bytes are read as given: bytes
  * 2..253 give normal weights; 255 zeroes a group; 0, 1 and 254 are outside the range this
  * build promises to reproduce exactly. */
@@ -149,7 +150,9 @@ size_t k3x_moe_workspace_size(const k3x_pool *p, int32_t T, int32_t topk);
  * y fp32 [T][hidden], overwritten (not accumulated).  topk in 1..64.  Duplicate experts
  * within a token are allowed (slots are independent).  A slot whose expert id lies outside
  * [0, n_experts) contributes 0 and is counted in the workspace's drop counter, which each
- * call resets; read it with k3x_fetch_drops.  T = 0 only resets the counter. */
+ * call resets; read it with k3x_fetch_drops.  T = 0 only resets the counter.  A contract pool
+ * (k3x_pool_desc.contract = 1) takes T <= 1 and returns K3X_E_UNSUPPORTED for more; its y
+ * follows the contract's arithmetic, with h in fp32 instead of bf16. */
 k3x_status k3x_moe_forward(const k3x_pool *p, const void *x_bf16, int32_t T, const int32_t *idx,
                            const float *gates, int32_t topk, float *y, void *ws,
                            size_t ws_bytes, void *stream);
