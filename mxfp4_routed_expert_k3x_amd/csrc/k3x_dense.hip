@@ -22,6 +22,8 @@
 // activations sit in LDS once per launch; each wave streams whole weight rows (lane L reads
 // the 16-byte chunks L, L + 64, ...: one load instruction covers 1 KB of a row), one row ahead
 // of the arithmetic.
+#include <type_traits>
+
 #include "k3x_internal.h"
 
 namespace k3x {
@@ -104,15 +106,16 @@ __device__ __forceinline__ void wave_range(int rows, int pair0, int& r0, int& r1
 // of pa for i < na, then L, L + 64, ... of pb).  Each part is summed on its own (kSplit; else
 // na == NCH) and emit(r, t, A, B) receives the two sums of token t, the same on every lane.
 // stage() (run by every thread of the block, with its barriers) fills xs; the wave's first
-// row is requested before it, so the row's latency overlaps the staging.
+// row is requested before it, so the row's latency overlaps the staging.  The last row is
+// summed by a second copy of the loop body that requests nothing after it (a wave has only a
+// few rows, and a re-read of its last row would often miss the cache).
 template <int NCH, int NT, bool kSplit, class Base, class Stage, class Emit>
 __device__ __forceinline__ void stream_dense(int r0, int r1, int na, const uint4* xs, int lane,
                                              Base base, Stage stage, Emit emit) {
   uint4 cur[NCH], nxt[NCH];  // the next row is loaded while this one is summed
   auto load = [&](uint4 (&b)[NCH], int r) {
-    const int rr = r < r1 ? r : r1 - 1;  // past the end: the last row again (no branch)
     const uint4 *pa, *pb;  // uniform row bases; the lane's chunks are added at the load
-    base(rr, pa, pb);
+    base(r, pa, pb);
     pb = pb - kWave * na;
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -121,9 +124,10 @@ __device__ __forceinline__ void stream_dense(int r0, int r1, int na, const uint4
   };
   if (r0 < r1) load(cur, r0);
   stage();
-#pragma unroll 1
-  for (int r = r0; r < r1; ++r) {
-    load(nxt, r + 1);
+  // row r; kNext: the next row is requested first and becomes the current one after
+  auto row = [&](int r, auto next) {
+    constexpr bool kNext = decltype(next)::value;
+    if constexpr (kNext) load(nxt, r + 1);
     // the activations are read again for every row (kept out of registers)
     int xo = lane;
     asm volatile("" : "+v"(xo));
@@ -171,9 +175,14 @@ __device__ __forceinline__ void stream_dense(int r0, int r1, int na, const uint4
       const float A = kSplit ? fold64(accA[t]) : B;
       emit(r, t, A, B);
     }
+    if constexpr (kNext) {
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) cur[i] = nxt[i];
-  }
+      for (int i = 0; i < NCH; ++i) cur[i] = nxt[i];
+    }
+  };
+#pragma unroll 1
+  for (int r = r0; r < r1 - 1; ++r) row(r, std::true_type{});
+  if (r0 < r1) row(r1 - 1, std::false_type{});
 }
 
 // Zero-fills the staged slots of tokens nt .. NT - 1 (their sums are computed and dropped).
