@@ -29,6 +29,8 @@
 // combine in its epilogue (each workgroup owns a block of output rows of every slot, so the
 // slot-order sum happens in LDS and the per-slot W2 outputs never reach memory).  Loads run
 // three rows ahead of the arithmetic.
+#include <atomic>
+
 #include "k3x_internal.h"
 
 // Products and sums below are rounded one at a time unless written as an explicit fma.
@@ -390,15 +392,17 @@ __global__ __launch_bounds__(kW2Waves * kWave) void decode_w2_combine(DecodeArgs
   }
 }
 
+// Workgroups per CU is a property of the kernel and the architecture, so one cached value
+// serves every device; concurrent first calls store the same value.
 int decode_w13_grid() {
-  static int per_cu = 0;
-  if (!per_cu) {
-    int n = 0;
+  static std::atomic<int> per_cu{0};
+  int n = per_cu.load(std::memory_order_relaxed);
+  if (!n) {
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_w13, kW13Threads, 0) != hipSuccess || n < 1)
       n = 2;
-    per_cu = n;
+    per_cu.store(n, std::memory_order_relaxed);
   }
-  return device_cu_count() * per_cu;
+  return device_cu_count() * n;
 }
 
 }  // namespace

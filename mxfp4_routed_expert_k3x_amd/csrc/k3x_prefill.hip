@@ -33,6 +33,8 @@
 // workgroups take (tile, chunk) items in turn.  Items are pipelined: the next item's routing
 // rows are fetched during the current item's K loop, and its first activation and weight
 // blocks are in flight while the current item's epilogue runs.
+#include <atomic>
+
 #include "k3x_internal.h"
 
 namespace k3x {
@@ -48,7 +50,6 @@ constexpr int kXPass = (kTT + kXRowsPerPass - 1) / kXRowsPerPass;  // staged pie
 constexpr int kXRows = kXPass * kXRowsPerPass;  // staged rows (>= kTT)
 constexpr int kMaxScaleRow = 128;               // scale bytes per weight row (K <= 4096)
 constexpr int kScaleRows = kWaves * 16 * kRB;   // weight rows of one item (W1 + W3, or W2)
-constexpr int kScaleSlots = kScaleRows * kMaxScaleRow / 16 / kThreads;  // 16-byte copies per thread
 
 struct PrefillArgs {
   const uint8_t* wa;  // W1 (W1/W3 mode) or W2, packed, expert 0
@@ -79,9 +80,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
 __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
   return make_uint4(v[0], v[1], v[2], v[3]);
-}
-__device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
 }
 
 __device__ __forceinline__ uint32_t dword_of(const uint4& v, int s) {
@@ -119,7 +117,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_prefill(PrefillArgs a, const
   const int nk = a.K / kKBlock;
   const uint32_t wrow = (uint32_t)a.K / 2, srow = (uint32_t)a.K / kGroup;
   const __amdgpu_buffer_rsrc_t xrs = make_rsrc(a.act, a.act_bytes);
-  const uint32_t wbytes = (uint32_t)a.rows * wrow, sbytes = (uint32_t)a.rows * srow;
+  const uint32_t wbytes = (uint32_t)a.rows * wrow;
   // per-lane part of the weight addresses; the row block's base is uniform
   const uint32_t wl = (uint32_t)n * wrow + 16u * (uint32_t)q;
   // this lane's scale bytes in LDS: row block rb at sbase + rb_off(rb), group 4 kb + q
@@ -135,7 +133,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_prefill(PrefillArgs a, const
   // ---- item state: expert, first position, slot count, first output row of this wave ----
   int e, start, m, r0;
   uint32_t xoff[kXPass];  // byte offset of this thread's staged activation rows
-  __amdgpu_buffer_rsrc_t wlo, whi, slo, shi;
+  __amdgpu_buffer_rsrc_t wlo, whi;
   // tile and routing rows of the next item, fetched one item ahead (W1/W3 mode: slot ids)
   int ne = 0, nstart = 0, nm = 1, nchunk = 0;
   int32_t nslot[kXPass];
@@ -166,9 +164,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_prefill(PrefillArgs a, const
       xoff[p] = 2u * (r * (uint32_t)a.K) + 16u * (uint32_t)xc;
     }
     wlo = make_rsrc(a.wa + (size_t)e * a.st_wa, wbytes);
-    slo = make_rsrc(a.sa + (size_t)e * a.st_sa, sbytes);  // whole scale tensor of expert e
     whi = kW13 ? make_rsrc(a.wb + (size_t)e * a.st_wb, wbytes) : wlo;
-    shi = kW13 ? make_rsrc(a.sb + (size_t)e * a.st_sb, sbytes) : slo;
   };
 
   // ---- operand staging ----
@@ -403,16 +399,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_prefill(PrefillArgs a, const
   }
 }
 
+// Workgroups per CU of each mode, cached once for every device (a property of the kernel and
+// the architecture); concurrent first calls store the same value.
 int prefill_grid(const void* fn) {
-  static int cached[2] = {0, 0};
+  static std::atomic<int> cached[2] = {{0}, {0}};
   const int which = fn == reinterpret_cast<const void*>(&gemm_prefill<true>) ? 0 : 1;
-  if (!cached[which]) {
-    int per_cu = 0;
+  int per_cu = cached[which].load(std::memory_order_relaxed);
+  if (!per_cu) {
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, 0) != hipSuccess || per_cu < 1)
       per_cu = 1;
-    cached[which] = per_cu;
+    cached[which].store(per_cu, std::memory_order_relaxed);
   }
-  return device_cu_count() * cached[which];
+  return device_cu_count() * per_cu;
 }
 
 }  // namespace
