@@ -52,7 +52,9 @@ TIMED_REGION = ("HIP graph replay: one graph runs the rotated batches in order, 
                 "layers run inside one graph (single-batch graphs for any remainder)")
 ORACLE_ACT = {"swiglu": "swiglu", "situ": ("situ", 4.0, 25.0)}
 COPY_PROBE_BYTES = 1 << 30
-KERNEL_SOURCES = ("k3x_decode.hip", "k3x_moe.hip", "k3x_prefill.hip", "k3x_router.hip")
+# the kernel sources of the routed path, with the headers they include
+KERNEL_SOURCES = ("k3x_internal.h", "k3x_select.h", "k3x_decode.hip", "k3x_moe.hip", "k3x_prefill.hip",
+                  "k3x_router.hip")
 LATENT_SOURCES = KERNEL_SOURCES + ("k3x_dense.hip",)
 # rocprofv3 kernel names of the library's launch names
 KERNEL_SYMBOLS = {"w13_decode": "decode_w13", "w2_combine_decode": "decode_w2_combine",
