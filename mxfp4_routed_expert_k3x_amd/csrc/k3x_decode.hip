@@ -273,6 +273,11 @@ __device__ __forceinline__ void stream_rows(const uint8_t* wa, const uint8_t* sa
 // exponentials and tanh do not hold up the row loop.  Workgroup 0 also writes the number of
 // dropped slots.
 constexpr int kW13Threads = 256;
+// Dynamic LDS the launch reserves (and the kernel leaves unused) so that one 4-wave workgroup
+// runs per CU: with one wave per SIMD the launch streams its rows faster than with two (fewer
+// concurrent streams; the bytes in flight still suffice), and much faster than with half a
+// wave per SIMD.
+constexpr uint32_t kW13LdsLimiter = 96 * 1024;
 
 __global__ __launch_bounds__(kW13Threads) void decode_w13(DecodeArgs a) {
   const int lane = threadIdx.x % kWave;
@@ -398,8 +403,10 @@ int decode_w13_grid() {
   static std::atomic<int> per_cu{0};
   int n = per_cu.load(std::memory_order_relaxed);
   if (!n) {
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_w13, kW13Threads, 0) != hipSuccess || n < 1)
-      n = 2;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_w13, kW13Threads, kW13LdsLimiter) !=
+            hipSuccess ||
+        n < 1)
+      n = 1;
     per_cu.store(n, std::memory_order_relaxed);
   }
   return device_cu_count() * n;
@@ -444,7 +451,8 @@ hipError_t launch_decode_exact(const k3x_pool& p, const uint16_t* x, const int32
   a.gact = p.act;
   a.b1 = p.b1;
   a.b2 = p.b2;
-  hipError_t err = launch("w13_decode", decode_w13, dim3(decode_w13_grid()), dim3(kW13Threads), 0, s, a);
+  hipError_t err = launch("w13_decode", decode_w13, dim3(decode_w13_grid()), dim3(kW13Threads),
+                          kW13LdsLimiter, s, a);
   if (err != hipSuccess) return err;
   DecodeArgs b = a;
   b.wa = p.base[4];
