@@ -28,7 +28,8 @@
 // streams a contiguous run of rows over all slots and writes h), then W2 with the weighted
 // combine in its epilogue (each workgroup owns a block of output rows of every slot, so the
 // slot-order sum happens in LDS and the per-slot W2 outputs never reach memory).  Loads run
-// three rows ahead of the arithmetic.
+// two rows ahead of the arithmetic (three or more measured slower: the launch streams best
+// with few requests in flight per CU).
 #include <atomic>
 
 #include "k3x_internal.h"
@@ -223,8 +224,8 @@ __device__ __forceinline__ LaneOffsets lane_offsets(int lane, int ngroups, uint3
 }
 
 // Streams rows r0 .. rlast of one expert (one matrix, or W1 and W3 side by side when kW13)
-// against the activations x0/x1: rows are loaded three ahead of the arithmetic and finished
-// four at a time.  prep() runs once the first three rows are requested (it fills x0/x1 from
+// against the activations x0/x1: rows are loaded two ahead of the arithmetic and finished
+// four at a time.  prep() runs once the first two rows are requested (it fills x0/x1 from
 // activations already in flight).  After each group of four rows r .. r + 3 every lane calls
 // emit(r + lane, sum_a, sum_b, valid, n): lanes 0..3 with valid set hold the full dot
 // products of row r + lane (sum_b only when kW13), and n (the same on every lane) is the
@@ -238,7 +239,7 @@ __device__ __forceinline__ void stream_rows(const uint8_t* wa, const uint8_t* sa
                                             Emit emit) {
   RowBits A[4] = {}, C[4] = {};
   // row r into buffer i (rows past the segment re-read rlast); the scheduling barriers keep
-  // the loads where they stand, three rows ahead of the arithmetic
+  // the loads where they stand, two rows ahead of the arithmetic
   auto load = [&](int i, int r) {
     const int rr = r <= rlast ? r : rlast;
     __builtin_amdgcn_sched_barrier(0);
@@ -248,14 +249,13 @@ __device__ __forceinline__ void stream_rows(const uint8_t* wa, const uint8_t* sa
   };
   load(0, r0);
   load(1, r0 + 1);
-  load(2, r0 + 2);
   prep();
 #pragma unroll 1
   for (int r = r0; r <= rlast; r += 4) {
     float v[kW13 ? 2 : 1][8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      load((i + 3) % 4, r + i + 3);
+      load((i + 2) % 4, r + i + 2);
       row_leaves(A[i], x0, x1, v[0][i], v[0][4 + i]);
       if (kW13) row_leaves(C[i], x0, x1, v[kW13 ? 1 : 0][i], v[kW13 ? 1 : 0][4 + i]);
     }
