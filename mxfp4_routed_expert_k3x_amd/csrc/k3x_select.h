@@ -23,6 +23,9 @@ __device__ __forceinline__ uint32_t score_key(float c) {
 
 constexpr int kSelThreads = 256;
 constexpr int kSelWaves = kSelThreads / kWave;
+// Thread t clears histogram bin t (one thread per 8-bit digit value), so the workgroup has
+// exactly as many threads as bins.
+static_assert(kSelThreads == 256, "one thread per histogram bin");
 
 // Wave-wide scans with DPP row shifts inside each row of 16 lanes and lane reads across
 // rows (no LDS round trips).
