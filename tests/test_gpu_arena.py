@@ -115,3 +115,41 @@ def test_arena_forward_and_policy(dev, orc, whole):
     torch.cuda.synchronize()
     arena.close()
     del keep
+
+
+def test_arena_drops_experts_without_a_slot(dev):
+    """More distinct experts in a call than the arena has slots: the experts that get no slot
+    (the cache oracle says which) are dropped and counted, and y equals the full pool's
+    forward with those slots' ids out of range, bit for bit."""
+    torch, k3x = dev
+    seed, E, H, I, slots, k = 78, 16, 256, 384, 4, 6
+    _log(f"case: arena smaller than a call, E={E} slots={slots} topk={k}")
+    host, strides, keep = _backing(torch, k3x, seed, 1, E, H, I, True)
+    arena = k3x.k3x_arena_create(host, slots, 1, E, H, I, max_slots_per_call=64,
+                                 host_strides=strides)
+    pool = k3x.k3x_expert_pool_create(S.device_pool(seed, 0, E, H, I), hidden=H, inter=I,
+                                      n_experts=E)
+    ref = C.SlotCache(slots)
+    rng = np.random.default_rng(seed)
+    for step in range(8):
+        idx = rng.choice(E, k, replace=False).astype(np.int32)[None]
+        gates = rng.random((1, k)).astype(np.float32)
+        gates /= gates.sum(axis=1, keepdims=True)
+        x = S.normal_bf16(seed + step, S.P_X, 0, (1, H))
+        xd = torch.from_numpy(x.view(np.int16)).cuda()
+        gd = torch.from_numpy(gates).cuda()
+        y = torch.empty((1, H), dtype=torch.float32, device="cuda")
+        ws = k3x.alloc_workspace(k3x.k3x_moe_workspace_size(arena.pool, 1, k))
+        k3x.k3x_arena_moe_forward(arena, 0, xd, 1, torch.from_numpy(idx).cuda(), gd, k, y, ws)
+        keys = [int(e) for e in idx[0]]
+        got, _ = ref.serve(keys)
+        idx_ref = np.array([[e if s >= 0 else -1 for e, s in zip(keys, got)]], dtype=np.int32)
+        n_drop = int((idx_ref < 0).sum())
+        assert n_drop >= k - slots, step
+        y_ref, _ = k3x.moe_forward(pool, xd, torch.from_numpy(idx_ref).cuda(), gd)
+        torch.cuda.synchronize()
+        assert k3x.k3x_fetch_drops(ws) == n_drop, step
+        assert torch.equal(y.view(torch.int32), y_ref.view(torch.int32)), step
+    _log(f"  {step + 1} calls, drops checked")
+    arena.close()
+    del keep
