@@ -92,3 +92,23 @@ def test_contract_k3_shape(dev, orc):
     rel = float(np.linalg.norm(y.cpu().numpy() - got) / np.linalg.norm(got))
     _log(f"  routed path vs contract: rel {rel:.2e}")
     assert 0 < rel < 1e-2
+
+
+def test_contract_empty_call_resets_the_drop_counter(dev, orc):
+    """T = 0 on a contract pool enqueues only the reset of the workspace's drop counter."""
+    torch, k3x = dev
+    E, H, I, k = 6, 256, 384, 3
+    _log("case: contract T = 0 after a call with a dropped slot")
+    pool = k3x.k3x_expert_pool_create(S.device_pool(7, 0, E, H, I), hidden=H, inter=I,
+                                      n_experts=E, contract=True)
+    x = torch.from_numpy(S.normal_bf16(7, S.P_X, 0, (1, H)).view(np.int16)).cuda()
+    idx = torch.tensor([[0, E + 1, 2]], dtype=torch.int32, device="cuda")
+    gates = torch.full((1, k), 1.0 / k, dtype=torch.float32, device="cuda")
+    y, ws = k3x.moe_forward(pool, x, idx, gates)
+    torch.cuda.synchronize()
+    assert k3x.k3x_fetch_drops(ws) == 1
+    y0 = y.clone()
+    k3x.k3x_moe_forward(pool, x, 0, idx, gates, k, y, ws)
+    torch.cuda.synchronize()
+    assert k3x.k3x_fetch_drops(ws) == 0
+    assert torch.equal(y, y0)  # nothing else was written
