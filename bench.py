@@ -23,13 +23,21 @@ The copy's readings give the scale of each counter (bytes moved / bytes counted)
 summary records the hash of the kernel sources, and a normal run reports the traffic only
 while those sources are unchanged.
 
-Prints ONE JSON line.  The timed region replays a HIP graph that runs the rotated batches one
-after another (captured once, every replay checked bit for bit against the eager results
-first), so `value` and `ms_per_step` are the path's throughput without host launch gaps, as
-when the layers of a model run inside one graph; `path.ms_per_step_one_graph_per_step` is the
-same steps with one graph per step (each graph launch adds a gap of several microseconds).  Kernel durations for the
+Prints ONE JSON line.  The timed region replays HIP graphs that run the rotated batches one
+after another (a graph of min(steps, 64) batches, replayed steps // that many times, then a
+graph of the remainder; every replay checked bit for bit against the eager results first),
+so `value` and `ms_per_step` are the path's throughput without host launch gaps, as when the
+layers of a model run inside one graph, for any --steps; `path.timed_mode` says how the steps
+were split, and `path.ms_per_step_one_graph_per_step` is the same steps with one graph per
+step (each graph launch adds a gap of several microseconds).  Kernel durations for the
 roofline come from HIP events the library records around each of its launches
 (k3x_profiler_*) in a second timed pass over the same steps, launched eagerly.
+
+The default run (decode_t1_e896_router) also measures the 4096-token prefill
+(prefill_t4096_e896: 896 experts, uniform routing, no router) and reports it in the same line
+under "prefill", with its TFLOP/s against the bf16 MFMA peak (--no-prefill skips it).
+`cpu_baseline` is the oracle on this host: the median of 3 runs on all of its threads
+(`value`, `cores`) and of 3 on one thread (`value_1core`), with the CPU model.
 """
 from __future__ import annotations
 
@@ -49,7 +57,9 @@ PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
 ROTATE = 64
 TIMED_REGION = ("HIP graph replay: one graph runs the rotated batches in order, as a model's "
-                "layers run inside one graph (single-batch graphs for any remainder)")
+                "layers run inside one graph")
+DEFAULT_WORKLOAD = "decode_t1_e896_router"
+PREFILL_WORKLOAD = "prefill_t4096_e896"
 ORACLE_ACT = {"swiglu": "swiglu", "situ": ("situ", 4.0, 25.0)}
 COPY_PROBE_BYTES = 1 << 30
 # the kernel sources of the routed path, with the headers they include
@@ -128,13 +138,17 @@ def latent_kernel_work(name, sh, T):
 
 
 def graph_timing(torch, step, R, outs, eager, steps, warmup):
-    """Captures one HIP graph per rotated batch and one graph of all R batches in order (the
-    way a model's layers run back to back inside one graph), checks every replay bit for bit
-    against the eager outputs (each output overwritten first, eager steps between replays),
-    and times `steps` steps both ways after `warmup` untimed ones: the sequence graph for
-    steps // R replays and single graphs for the rest, then single graphs only.  outs(r) gives
-    the output tensors of batch r, eager[r] their eager values.  Returns the wall seconds of
-    the two timed passes (sequence graph, one graph per step)."""
+    """Times `steps` steps inside HIP graphs, the way a model's layers run back to back inside
+    one graph.  The sequence graph runs Rs = min(steps, R) rotated batches in order; the timed
+    region replays it steps // Rs times, then a graph of the first steps % Rs batches, so
+    every timed step runs inside a multi-step graph whatever `steps` is.  Also captures one
+    graph per batch and times the same steps with one graph launch per step.  Every replay
+    is first checked bit for bit against the eager outputs (each output overwritten before,
+    eager steps between replays).  outs(r) gives the output tensors of batch r, eager[r]
+    their eager values.  Returns (wall seconds in the sequence mode, wall seconds with one
+    graph per step, a description of the sequence mode)."""
+    Rs = max(1, min(steps, R))
+    rem = steps % Rs
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -146,10 +160,16 @@ def graph_timing(torch, step, R, outs, eager, steps, warmup):
         with torch.cuda.graph(g):
             step(r)
         singles.append(g)
-    seq = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(seq):
-        for r in range(R):
-            step(r)
+
+    def capture(n):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for r in range(n):
+                step(r)
+        return g
+
+    seq = capture(Rs)
+    tail = capture(rem) if rem else None
 
     def spoil(r):
         for o in outs(r):
@@ -166,24 +186,33 @@ def graph_timing(torch, step, R, outs, eager, steps, warmup):
         check("graph replay", r)
         step((r + 1) % R)
         torch.cuda.synchronize()
-    for rep_ in range(2):
-        for r in range(R):
-            spoil(r)
-        seq.replay()
-        torch.cuda.synchronize()
-        for r in range(R):
-            check(f"sequence graph replay {rep_}", r)
-        step(rep_ % R)
-        torch.cuda.synchronize()
+    for what, g, n in (("sequence graph", seq, Rs), ("tail graph", tail, rem)):
+        if g is None:
+            continue
+        for rep_ in range(2):
+            for r in range(n):
+                spoil(r)
+            g.replay()
+            torch.cuda.synchronize()
+            for r in range(n):
+                check(f"{what} replay {rep_}", r)
+            step((rep_ + 1) % R)
+            torch.cuda.synchronize()
 
     def run(n, use_seq):
-        rem = n
         if use_seq:
-            for _ in range(n // R):
+            for _ in range(n // Rs):
                 seq.replay()
-            rem = n % R
-        for j in range(rem):
-            singles[j % R].replay()
+            if n % Rs:
+                # the timed run ends with the tail graph; a warm-up remainder replays singles
+                if n % Rs == rem and tail is not None:
+                    tail.replay()
+                else:
+                    for j in range(n % Rs):
+                        singles[j].replay()
+        else:
+            for j in range(n):
+                singles[j % R].replay()
 
     walls = []
     for use_seq in (True, False):
@@ -193,46 +222,143 @@ def graph_timing(torch, step, R, outs, eager, steps, warmup):
         run(steps, use_seq)
         torch.cuda.synchronize()
         walls.append(time.perf_counter() - t0)
-    return walls[0], walls[1]
+    mode = f"{steps // Rs} replay(s) of one graph of {Rs} rotated batch(es) in order"
+    if rem:
+        mode += f", then one graph of the first {rem}"
+    return walls[0], walls[1], mode
 
 
-def cpu_baseline(w, x, W, b, dev_idx, dev_gates, pool_dev, budget_s=12.0, act="swiglu"):
+def host_cpu():
+    """The host's CPU model (from /proc/cpuinfo) and its CPU counts."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "host_cpus": os.cpu_count(),
+            "affinity_cpus": len(os.sched_getaffinity(0))}
+
+
+def timed_oracle(run, n_all, n_one, units, unit, runs=3):
+    """Times run(n) -> oracle seconds for the first n items of a sample: the median of `runs`
+    runs over n_all items on all of the oracle's threads, then over n_one items on one
+    thread.  units(n) is the work of n items in the unit of the rate."""
+    import oracle
+
+    threads = oracle.threads()
+    all_t = [run(n_all) for _ in range(runs)]
+    oracle.set_threads(1)
+    try:
+        one_t = [run(n_one) for _ in range(runs)]
+    finally:
+        oracle.set_threads(threads)
+    med_all, med_one = float(np.median(all_t)), float(np.median(one_t))
+    return {"value": units(n_all) / med_all, "unit": unit, "cores": threads,
+            "value_1core": units(n_one) / med_one, "runs": runs,
+            "seconds_all_cores": [round(v, 3) for v in all_t],
+            "seconds_1core": [round(v, 3) for v in one_t],
+            **host_cpu()}
+
+
+def cpu_baseline(w, x, W, b, dev_idx, dev_gates, pool_dev, act="swiglu", seconds=3.0):
     """The oracle as it stands, on this host's cores, over a bounded sample of the same
-    workload's tokens, repeated until about budget_s seconds of oracle time.  Each token's
-    expert bytes are copied from the generator's device pool (k3x_synth writes the same
-    bytes on the device and the host) outside the timing."""
+    workload's tokens (each: the router when the workload has one, the token's experts, the
+    slot-order combine).  Each token's expert bytes are copied from the generator's device
+    pool (k3x_synth writes the same bytes on the device and the host) outside the timing.
+    Median of three runs on all of the oracle's threads and three on one thread, each about
+    `seconds` of oracle time."""
     import k3x_synth as S
     import oracle
 
-    n_tok, t_used, i = 0, 0.0, 0
-    while t_used < budget_s:
-        t = i % len(x)
-        i += 1
-        xt = x[t:t + 1]
-        if w.router:
+    toks = []
+
+    def token(i):
+        while len(toks) <= i:
+            t = len(toks) % len(x)
+            xt = x[t:t + 1]
+            if w.router:
+                idx, gates = oracle.route(xt, W, b, w.topk)
+            else:
+                idx, gates = dev_idx[t:t + 1], dev_gates[t:t + 1]
+            exps = [S.ExpertBytes(*[pool_dev[nm][int(e)].cpu().numpy() for nm in S.TENSOR_NAMES])
+                    for e in idx[0]]
+            toks.append((xt, gates, exps))
+        return toks[i]
+
+    def run(n):
+        used = 0.0
+        for i in range(n):
+            xt, gates, exps = token(i)
             t0 = time.perf_counter()
-            idx, gates = oracle.route(xt, W, b, w.topk)
-            t_used += time.perf_counter() - t0
-        else:
-            idx, gates = dev_idx[t:t + 1], dev_gates[t:t + 1]
-        exps = []
-        for e in idx[0]:
-            e = int(e)
-            exps.append(S.ExpertBytes(*[pool_dev[nm][e].cpu().numpy() for nm in S.TENSOR_NAMES]))
-        t0 = time.perf_counter()
-        d = np.stack([oracle.expert_forward(xt[0], ex, act=act) for ex in exps])[None]
-        oracle.combine(gates, d)
-        t_used += time.perf_counter() - t0
-        n_tok += 1
-    return {
-        "value": n_tok / t_used,
-        "unit": "tokens/s",
-        "cores": oracle.threads(),
-        "kind": "oracle",
-        "sample": f"{n_tok} token(s) of the same workload ({'router + ' if w.router else ''}"
-                  f"{w.topk} experts each + combine), {t_used:.1f} s of oracle time; expert bytes "
-                  f"copied to the host outside the timing",
-    }
+            if w.router:
+                _, gates = oracle.route(xt, W, b, w.topk)
+            d = np.stack([oracle.expert_forward(xt[0], ex, act=act) for ex in exps])[None]
+            oracle.combine(gates, d)
+            used += time.perf_counter() - t0
+        return used
+
+    one = run(1)  # calibration (also fetches the first token's experts)
+    n_all = max(1, int(round(seconds / one)))
+    n_one = max(1, int(round(seconds / (one * oracle.threads()))))
+    res = timed_oracle(run, n_all, n_one, lambda n: n, "tokens/s")
+    res["kind"] = "oracle"
+    res["sample"] = (f"the first {n_all} token(s) of the workload on all threads, {n_one} on one "
+                     f"({'router + ' if w.router else ''}{w.topk} experts each + combine), median "
+                     f"of 3 runs each; expert bytes copied to the host outside the timing")
+    return res
+
+
+def prefill_cpu_baseline(w, x, idx, gates, pool_dev, act="swiglu", seconds=3.0):
+    """The oracle on a prefill batch, walking the experts one by one as a prefill does (each
+    expert applied to every slot routed to it, oracle.expert_forward_many): a bounded sample
+    of the experts in ascending order, timed as tokens/s = slots / topk per second (the
+    slot-order combine, about 0.01 % of the work, is not in the sample).  Expert bytes are
+    copied from the device pool outside the timing.  Median of three runs on all threads
+    and three on one thread."""
+    import k3x_synth as S
+    import oracle
+
+    k = idx.shape[1]
+    flat = idx.reshape(-1).astype(np.int64)
+    order = np.argsort(flat, kind="stable")
+    experts, starts = np.unique(flat[order], return_index=True)
+    bounds = list(starts) + [len(order)]
+    cache = {}
+
+    def expert(i):
+        if i not in cache:
+            e = int(experts[i])
+            cache[i] = S.ExpertBytes(*[pool_dev[nm][e].cpu().numpy() for nm in S.TENSOR_NAMES])
+        return cache[i]
+
+    def run(n):
+        used = 0.0
+        for i in range(n):
+            ex = expert(i)
+            sl = order[bounds[i]:bounds[i + 1]]
+            xs_ = x[sl // k]
+            t0 = time.perf_counter()
+            oracle.expert_forward_many(xs_, ex, act=act)
+            used += time.perf_counter() - t0
+        return used
+
+    def tokens(n):
+        return (bounds[n] - bounds[0]) / k
+
+    one = run(1)
+    n_all = max(1, min(len(experts), int(round(seconds / one))))
+    n_one = max(1, min(len(experts), int(round(seconds / (one * oracle.threads())))))
+    res = timed_oracle(run, n_all, n_one, tokens, "tokens/s")
+    res["kind"] = "oracle"
+    res["sample"] = (f"the first {n_all} of the batch's {len(experts)} experts with all their "
+                     f"slots ({bounds[n_all]} slots = {tokens(n_all):.1f} tokens' worth) on all "
+                     f"threads, {n_one} expert(s) on one, expert-major, median of 3 runs each; "
+                     f"expert bytes copied to the host outside the timing")
+    return res
 
 
 def chain_cpu_baseline(w, x, layers, budget_s=12.0, act="swiglu"):
@@ -634,7 +760,8 @@ def bench_latent(args, torch, S, k3x):
         eager.append([outs_[i].clone()])
     if k3x.k3x_fetch_drops(ws[moe_off:]):
         sys.exit("run invalid: dropped slots")
-    wall, wall_single = graph_timing(torch, step, R, lambda i: (outs_[i],), eager, steps, warmup)
+    wall, wall_single, mode = graph_timing(torch, step, R, lambda i: (outs_[i],), eager, steps,
+                                           warmup)
 
     prof = k3x.k3x_profiler_create(steps * 16 + 16)
     torch.cuda.synchronize()
@@ -689,7 +816,7 @@ def bench_latent(args, torch, S, k3x):
                  "hbm_gbps_kernel_sum": round(path_bytes / ksum / 1e9, 1),
                  "hbm_frac_kernel_sum": round(path_bytes / ksum / 1e9 / PEAK_HBM_GBS, 4),
                  "hbm_gbps_wall": round(path_bytes / (wall / steps) / 1e9, 1),
-                 "timed_region": TIMED_REGION,
+                 "timed_region": TIMED_REGION, "timed_mode": mode,
                  "ms_per_step_one_graph_per_step": round(wall_single / steps * 1e3, 5)},
         "kernels": kernels,
         "cpu_baseline": None,
@@ -782,7 +909,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", default="decode_t1_e896_router")
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="the default run skips its prefill leg (prefill_t4096_e896)")
+    ap.add_argument("--prefill-steps", type=int, default=None,
+                    help="timed steps of the default run's prefill leg (default 20)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--activation", choices=("swiglu", "situ"), default="swiglu",
                     help="gated activation of the expert pool (situ: SiTU-GLU, caps 4 and 25)")
@@ -818,13 +949,31 @@ def main():
     w = wl[args.workload]
     if w.layers != 1:
         return bench_chain(w, args, torch, S, k3x)
+    out = bench_single(w, args, torch, S, k3x, args.steps, args.warmup)
+    if args.workload == DEFAULT_WORKLOAD and not args.no_prefill and not args.contract:
+        # the prefill half of the metric, in the same line
+        torch.cuda.empty_cache()
+        pw = wl[PREFILL_WORKLOAD]
+        pre = bench_single(pw, args, torch, S, k3x, args.prefill_steps, None)
+        out["prefill"] = {k_: pre[k_] for k_ in ("value", "unit", "steps", "warmup", "ms_per_step",
+                                                 "config", "roofline", "path", "kernels",
+                                                 "cpu_baseline")}
+        out["prefill"]["tflops"] = pre["path"]["tflops_wall"]
+    print(json.dumps(out), flush=True)
+
+
+def bench_single(w, args, torch, S, k3x, steps, warmup):
+    """One layer of w.E experts, w.T tokens per step (decode rotates over ROTATE batches;
+    prefill repeats one batch of 4096 tokens).  Returns the result record."""
     prefill = w.T > 64
-    steps = args.steps if args.steps is not None else (20 if prefill else 4 * ROTATE)
-    warmup = args.warmup if args.warmup is not None else (3 if prefill else ROTATE)
+    if steps is None:
+        steps = 20 if prefill else 4 * ROTATE
+    if warmup is None:
+        warmup = 3 if prefill else ROTATE
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
 
-    log(f"generating pool: E={w.E} H={w.H} I={w.I}")
+    log(f"{w.name}: generating pool E={w.E} H={w.H} I={w.I}")
     pool_dev = S.device_pool(w.seed, 0, w.E, w.H, w.I)
     if args.contract and w.T != 1:
         sys.exit("--contract runs one token per call: use a decode workload")
@@ -875,7 +1024,7 @@ def main():
     if drops:
         sys.exit(f"run invalid: {drops} dropped slots")
 
-    wall, wall_single = graph_timing(torch, step, R, outs, eager, steps, warmup)
+    wall, wall_single, mode = graph_timing(torch, step, R, outs, eager, steps, warmup)
 
     # kernel durations: the same steps launched eagerly, HIP events around each launch
     kernels_per_step = 6 if w.router else 4
@@ -945,22 +1094,30 @@ def main():
         "roofline": roof,
         "path": {"kernel_sum_us": round(ksum * 1e6, 3),
                  "alg_bytes_per_step": int(path_bytes),
+                 "alg_flops_per_step": path_flops,
                  "hbm_gbps_kernel_sum": round(path_bytes / ksum / 1e9, 1),
                  "hbm_frac_kernel_sum": round(path_bytes / ksum / 1e9 / PEAK_HBM_GBS, 4),
                  "tflops_kernel_sum": round(path_flops / ksum / 1e12, 2),
                  "hbm_gbps_wall": round(path_bytes / (wall / steps) / 1e9, 1),
-                 "timed_region": TIMED_REGION,
+                 "tflops_wall": round(path_flops / (wall / steps) / 1e12, 2),
+                 "timed_region": TIMED_REGION, "timed_mode": mode,
                  "ms_per_step_one_graph_per_step": round(wall_single / steps * 1e3, 5),
                  "eager_ms_per_step": round(wall_eager / steps * 1e3, 5)},
         "kernels": kernels,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        log("timing the oracle on the host (bounded sample)")
-        di = np.concatenate([r_[0] for r_ in routes_np]) if routes_np else None
-        dg = np.concatenate([r_[1] for r_ in routes_np]) if routes_np else None
-        out["cpu_baseline"] = cpu_baseline(w, x, W, b, di, dg, pool_dev, act=ORACLE_ACT[args.activation])
-    print(json.dumps(out), flush=True)
+        log(f"{w.name}: timing the oracle on the host (bounded sample)")
+        act = ORACLE_ACT[args.activation]
+        if prefill:
+            i_, g_ = routes_np[0]
+            out["cpu_baseline"] = prefill_cpu_baseline(w, x, i_, g_, pool_dev, act=act)
+        else:
+            di = np.concatenate([r_[0] for r_ in routes_np]) if routes_np else None
+            dg = np.concatenate([r_[1] for r_ in routes_np]) if routes_np else None
+            out["cpu_baseline"] = cpu_baseline(w, x, W, b, di, dg, pool_dev, act=act)
+    del pool, pool_dev, ws, ys
+    return out
 
 
 if __name__ == "__main__":

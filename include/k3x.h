@@ -103,8 +103,9 @@ typedef struct k3x_pool k3x_pool;
  * tensor size, an unknown activation, contract not 0 or 1 and, for SiTU-GLU, caps that are
  * not finite and positive.  Allocates host memory only; the device
  * tensors are borrowed and must outlive the pool.  Scale bytes are read as given: bytes
- * 2..253 give normal weights; 255 zeroes a group; 0, 1 and 254 are outside the range this
- * build promises to reproduce exactly. */
+ * 2..252 give finite, normal weights for every E2M1 code (6 * 2^125 is the largest); 255
+ * zeroes a group; 0, 1, 253 and 254 are outside the range this build promises to reproduce
+ * exactly (253 and 254 overflow float for the larger codes, 0 and 1 give subnormal weights). */
 k3x_status k3x_expert_pool_create(const k3x_pool_desc *d, k3x_pool **out);
 
 /* Frees the handle only (never the borrowed tensors).  NULL is a no-op. */
@@ -164,7 +165,8 @@ k3x_status k3x_moe_forward(const k3x_pool *p, const void *x_bf16, int32_t T, con
  * x_bf16 bf16 [T][hidden]; idx_out int32 [T][topk], gates_out fp32
  * [T][topk], y fp32 [T][hidden] (all written); ws: at least k3x_route_moe_workspace_size
  * bytes, 256-byte aligned, its start is the experts' workspace (k3x_fetch_drops(ws) reads
- * the drop count).  T = 0 enqueues nothing. */
+ * the drop count).  T = 0 routes nothing and only resets the drop counter (x, idx_out,
+ * gates_out and y may then be NULL). */
 size_t k3x_route_moe_workspace_size(const k3x_router_desc *r, const k3x_pool *p, int32_t T);
 k3x_status k3x_route_moe_forward(const k3x_router_desc *r, const k3x_pool *p, const void *x_bf16,
                                  int32_t T, int32_t *idx_out, float *gates_out, float *y,
@@ -212,8 +214,9 @@ k3x_status k3x_residual_add_rmsnorm_bf16(void *x, const float *y, int32_t T, int
  *   5. out = up . a;
  *   6. out += sh2 . s, s = bf16(act(sh1 . x, sh3 . x)): the shared experts on the ORIGINAL x,
  *      added unweighted (act = shared_activation with the caps).
- * Dense products are bf16 x bf16 summed in fp32; the path is sized for decode batches (larger
- * ones read the dense weights once per 8 tokens).
+ * Dense products are bf16 x bf16, exact in double and summed in double in a fixed order, then
+ * rounded once to float (the floating point contract's bf16 matmul, README Part II section 5);
+ * the path is sized for decode batches (larger ones read the dense weights once per 8 tokens).
  * ---------------------------------------------------------------------------------------- */
 typedef struct k3x_latent_desc {
   int32_t hidden;           /* D: multiple of 512, <= 8192 (7168 in the checkpoint)        */
@@ -239,7 +242,7 @@ size_t k3x_latent_workspace_size(const k3x_latent_desc *d, const k3x_pool *p,
  * hidden != L) and (K3X_E_UNSUPPORTED) D, L or S not multiples of 512 or above 8192, or
  * L + S above 9728 (the K3 block: 3584 + 6144), or topk above 64.  Dropped
  * routed slots are counted in the workspace as for k3x_moe_forward (k3x_fetch_drops on
- * ws + offs[5] of k3x_latent_ws_layout). */
+ * ws + offs[5] of k3x_latent_ws_layout).  T = 0 only resets that counter. */
 k3x_status k3x_latent_forward(const k3x_latent_desc *d, const k3x_pool *p,
                               const k3x_router_desc *r, const void *x_bf16, int32_t T,
                               float *out, void *ws, size_t ws_bytes, void *stream);

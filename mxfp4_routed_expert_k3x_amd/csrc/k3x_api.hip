@@ -275,7 +275,14 @@ k3x_status k3x_latent_forward(const k3x_latent_desc* d, const k3x_pool* p,
   if (!ws || ws_bytes < need || !aligned(ws, 256))
     return fail(K3X_E_WORKSPACE, "latent_forward: workspace %zu bytes, need %zu (256-byte aligned)",
                 ws_bytes, need);
-  if (T == 0) return K3X_OK;
+  if (T == 0) {
+    // the routed experts' empty call resets their drop counter, as k3x_moe_forward does
+    const k3x::LatentLayout L = k3x::latent_layout(*d, *p, r->n_experts, 0, r->topk);
+    const k3x::MoeLayout ML = k3x::moe_layout(p->E, p->H, p->I, 0, r->topk);
+    hipError_t e = k3x::launch_moe(*p, nullptr, 0, nullptr, nullptr, r->topk, nullptr,
+                                   static_cast<uint8_t*>(ws) + L.moe, ML, (hipStream_t)stream);
+    return e == hipSuccess ? K3X_OK : hip_fail(e, "latent_forward");
+  }
   if (!x_bf16 || !out) return fail(K3X_E_INVALID_ARG, "latent_forward: NULL x or out");
   if (!aligned(x_bf16, 16) || !aligned(out, 16))
     return fail(K3X_E_UNSUPPORTED, "latent_forward: x and out must be 16-byte aligned");
@@ -327,7 +334,13 @@ k3x_status k3x_route_moe_forward(const k3x_router_desc* r, const k3x_pool* p, co
   if (!ws || ws_bytes < need || !aligned(ws, 256))
     return fail(K3X_E_WORKSPACE, "route_moe_forward: workspace %zu bytes, need %zu (256-byte aligned)",
                 ws_bytes, need);
-  if (T == 0) return K3X_OK;
+  if (T == 0) {
+    // nothing to route; the experts' empty call resets the drop counter, as k3x_moe_forward does
+    const k3x::MoeLayout L = k3x::moe_layout(p->E, p->H, p->I, 0, r->topk);
+    hipError_t e = k3x::launch_moe(*p, nullptr, 0, nullptr, nullptr, r->topk, nullptr,
+                                   static_cast<uint8_t*>(ws), L, (hipStream_t)stream);
+    return e == hipSuccess ? K3X_OK : hip_fail(e, "route_moe_forward");
+  }
   if (!x_bf16 || !idx_out || !gates_out || !y)
     return fail(K3X_E_INVALID_ARG, "route_moe_forward: NULL x, idx, gates or y");
   if (!aligned(x_bf16, 16) || !aligned(y, 16))

@@ -49,8 +49,8 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
 }
 
 // Eight consecutive E2M1 elements (the four bytes of one dword, low nibble = even element)
-// times a power-of-two scale, as eight bf16 in element order.  The products are exact for
-// scale bytes 2..253.
+// times a power-of-two scale, as eight bf16 in element order.  The products are exact and
+// normal for scale bytes 2..252 (0.5 * 2^-125 = 2^-126 is the smallest, 6 * 2^125 the largest).
 __device__ __forceinline__ bf16x8 dequant8(uint32_t dw, float scale) {
   const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, scale, 0);
   const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, scale, 1);

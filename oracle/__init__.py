@@ -66,6 +66,10 @@ def lib():
         L.oracle_f32_to_bf16.argtypes = [ctypes.c_float]
         L.oracle_f32_to_bf16_n.restype = None
         L.oracle_f32_to_bf16_n.argtypes = [P, i64, P]
+        L.oracle_set_threads.restype = None
+        L.oracle_set_threads.argtypes = [ci]
+        L.oracle_max_threads.restype = ci
+        L.oracle_max_threads.argtypes = []
         L.oracle_sum64.restype = ctypes.c_double
         L.oracle_sum64.argtypes = [P, P, i64]
         L.oracle_route.restype = ci
@@ -107,6 +111,10 @@ def lib():
             f.argtypes = [i64] * 7 + [P, P, P, ci, ctypes.c_float, P, P, P, P, P, P,
                                       ctypes.c_float, P, P, P, P, P, P, ci, ctypes.c_float,
                                       ctypes.c_float, ci, P]
+            f = getattr(L, f"oracle_expert_forward_many_{sfx}")
+            f.restype = None
+            f.argtypes = [P, i64, i64, i64, P, P, P, P, P, P, ci, ctypes.c_float,
+                          ctypes.c_float, P]
             f = getattr(L, f"oracle_moe_forward_act_{sfx}")
             f.restype = i64
             f.argtypes = [i64, i64, i64, P, P, P, P, P, P, P, ci, ctypes.c_float, ctypes.c_float,
@@ -216,6 +224,21 @@ def expert_forward(x_bf16, ex, acc="f32", want_hidden=False, act="swiglu"):
     return (h, g, u, d) if want_hidden else d
 
 
+def expert_forward_many(x_bf16, ex, acc="f32", act="swiglu"):
+    """One expert on n activations, expert-major (oracle_expert_forward_many): row t of the
+    result equals expert_forward(x_bf16[t], ex) bit for bit.  x bf16 [n][H] -> d fp32 [n][H]."""
+    x = _c(x_bf16, np.uint16)
+    n, H = x.shape
+    I = ex.w1_packed.shape[0]
+    t = [_c(a, np.uint8) for a in ex.tensors()]
+    assert t[0].shape == (I, H // 2) and t[4].shape == (H, I // 2)
+    d = np.empty((n, H), dtype=np.float32)
+    a_, b1, b2 = _act(act)
+    getattr(lib(), f"oracle_expert_forward_many_{_sfx(acc)}")(
+        _p(x), n, H, I, *[_p(a) for a in t], a_, b1, b2, _p(d))
+    return d
+
+
 def combine(gates, d, valid=None, acc="f32"):
     """y[t] = sum_j gates[t][j] * d[t][j] in slot order.  gates [T][k], d [T][k][H]."""
     gates = _c(gates, np.float32)
@@ -287,8 +310,12 @@ def residual_add_bf16(x_bf16, y):
 
 def threads() -> int:
     """OpenMP threads the oracle's parallel loops use."""
-    n = os.environ.get("OMP_NUM_THREADS")
-    return int(n) if n and n.isdigit() else (os.cpu_count() or 1)
+    return int(lib().oracle_max_threads())
+
+
+def set_threads(n: int) -> None:
+    """Sets the threads of the oracle's parallel loops (the results do not depend on it)."""
+    lib().oracle_set_threads(int(n))
 
 
 def rmsnorm_w_f32(x, w, eps):

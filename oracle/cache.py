@@ -23,7 +23,8 @@ few hundred thousand requests.
 """
 from __future__ import annotations
 
-from collections import defaultdict, deque
+import heapq
+from collections import defaultdict
 
 EMPTY = -1
 INFLIGHT = -2
@@ -54,24 +55,34 @@ def lru_hits(trace, cap, pinned=()):
 
 def belady_hits(trace, cap):
     """Hits of Belady's rule: on a miss with every slot taken, evict the resident key whose
-    next request lies furthest ahead (never again counts as infinitely far)."""
-    uses = defaultdict(deque)
-    for i, k in enumerate(trace):
-        uses[k].append(i)
-    never = len(trace) + 1
-    resident = set()
+    next request lies furthest ahead (a key never requested again is furthest of all).
+
+    One backward pass finds, for every request, the position of the same key's next request.
+    Resident keys are kept with that position, and a max-heap orders them by it; a heap entry
+    whose key has been requested again (or evicted) since it was pushed no longer matches the
+    key's recorded position and is discarded when it reaches the top."""
+    n = len(trace)
+    later = [n] * n  # n: never requested again
+    upcoming = {}
+    for i in range(n - 1, -1, -1):
+        later[i] = upcoming.get(trace[i], n)
+        upcoming[trace[i]] = i
+    due = {}   # resident key -> position of its next request
+    heap = []  # (-next request, push order, key): the push order keeps keys from being compared
     hits = 0
-    for k in trace:
-        uses[k].popleft()
-        if k in resident:
+    for i, k in enumerate(trace):
+        if k in due:
             hits += 1
+        elif cap <= 0:
             continue
-        if cap <= 0:
-            continue
-        if len(resident) >= cap:
-            victim = max(resident, key=lambda r: uses[r][0] if uses[r] else never)
-            resident.discard(victim)
-        resident.add(k)
+        elif len(due) >= cap:
+            while True:
+                neg_next, _, v = heapq.heappop(heap)
+                if due.get(v) == -neg_next:
+                    break
+            del due[v]
+        due[k] = later[i]
+        heapq.heappush(heap, (-later[i], i, k))
     return hits
 
 

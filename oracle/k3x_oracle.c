@@ -56,6 +56,7 @@
  * -DORACLE_ACC=double -DORACLE_SFX=f64.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -143,6 +144,11 @@ void oracle_f32_to_bf16_n(const float *x, int64_t n, uint16_t *out) {
 }
 
 double oracle_sum64(const double *a, const double *b, int64_t n) { return sum64_products(a, b, n); }
+
+/* Threads of the oracle's OpenMP loops (the CPU baseline times one core and all of them);
+ * the arithmetic of every output is the same for any count. */
+void oracle_set_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
+int oracle_max_threads(void) { return omp_get_max_threads(); }
 
 /* The contract's MXFP4 matmul in the listing's own order (README Part II section 4, the
  * MXFP4 matmul; section 5, "double, always"): per row, acc = 0 in double; groups in order; a
@@ -407,6 +413,73 @@ void ORC(oracle_expert_forward_act)(const uint16_t *x, int64_t H, int64_t I, con
   free(g);
   free(u);
   free(hf);
+}
+
+/* The MXFP4 product of the matvec above for n vectors at once: xt fp32 [K][n] (vector t in
+ * column t), yt fp32 [rows][n].  Output (r, t) is computed with exactly the operations
+ * oracle_mxfp4_matvec performs for vector t alone (the same products, the same sequential
+ * sum inside each group, the same scale, the same pairwise tree); the vectors only run side
+ * by side in the innermost loops, so every weight is decoded once for all of them. */
+static void ORC(mxfp4_matmat)(const float *xt, int64_t n, const uint8_t *packed,
+                              const uint8_t *scales, int64_t rows, int64_t K, float *yt) {
+  const int64_t ngroup = K / 32;
+  const int64_t rowbytes = K / 2;
+  int64_t npad = 1;
+  while (npad < ngroup) npad <<= 1;
+#pragma omp parallel
+  {
+    acc_t *part = (acc_t *)malloc(sizeof(acc_t) * (size_t)(npad * n)); /* [npad][n] */
+#pragma omp for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+      const uint8_t *prow = packed + r * rowbytes;
+      const uint8_t *srow = scales + r * ngroup;
+      for (int64_t g = 0; g < npad; ++g) {
+        acc_t *pg = part + g * n;
+        for (int64_t t = 0; t < n; ++t) pg[t] = 0;
+        if (g >= ngroup || srow[g] == 255u) continue; /* padding; a NaN scale zeroes the group */
+        for (int64_t c = 32 * g; c < 32 * g + 32; ++c) {
+          const acc_t w = (acc_t)e2m1_value(nibble_at(prow, c));
+          const float *xc = xt + c * n;
+#pragma omp simd
+          for (int64_t t = 0; t < n; ++t) pg[t] += (acc_t)xc[t] * w;
+        }
+        const acc_t s = (acc_t)e8m0_value(srow[g]); /* exact power of two */
+        for (int64_t t = 0; t < n; ++t) pg[t] = pg[t] * s;
+      }
+      for (int64_t m = npad; m > 1; m >>= 1)
+        for (int64_t i = 0; i < m / 2; ++i)
+          for (int64_t t = 0; t < n; ++t) part[i * n + t] = part[2 * i * n + t] + part[(2 * i + 1) * n + t];
+      for (int64_t t = 0; t < n; ++t) yt[r * n + t] = (float)part[t];
+    }
+    free(part);
+  }
+}
+
+/* One routed expert on n activations (an expert-major pass, as a prefill walks the experts
+ * one by one): d_out[t] equals what oracle_expert_forward_act gives for x[t] alone, bit for
+ * bit.  x bf16 [n][H]; d_out fp32 [n][H]. */
+void ORC(oracle_expert_forward_many)(const uint16_t *x, int64_t n, int64_t H, int64_t I,
+                                     const uint8_t *w1p, const uint8_t *w1s, const uint8_t *w3p,
+                                     const uint8_t *w3s, const uint8_t *w2p, const uint8_t *w2s,
+                                     int act, float b1, float b2, float *d_out) {
+  if (n <= 0) return;
+  float *xt = (float *)malloc(sizeof(float) * (size_t)(H * n));
+  float *gt = (float *)malloc(sizeof(float) * (size_t)(I * n));
+  float *ut = (float *)malloc(sizeof(float) * (size_t)(I * n));
+  float *dt = (float *)malloc(sizeof(float) * (size_t)(H * n));
+  for (int64_t t = 0; t < n; ++t)
+    for (int64_t c = 0; c < H; ++c) xt[c * n + t] = bf16_to_float(x[t * H + c]);
+  ORC(mxfp4_matmat)(xt, n, w1p, w1s, I, H, gt);
+  ORC(mxfp4_matmat)(xt, n, w3p, w3s, I, H, ut);
+  /* h = bf16(act(g, u)), widened back to fp32 for W2 (kept in gt) */
+  for (int64_t i = 0; i < I * n; ++i) gt[i] = bf16_to_float(float_to_bf16(glu_one(gt[i], ut[i], act, b1, b2)));
+  ORC(mxfp4_matmat)(gt, n, w2p, w2s, H, I, dt);
+  for (int64_t t = 0; t < n; ++t)
+    for (int64_t r = 0; r < H; ++r) d_out[t * H + r] = dt[r * n + t];
+  free(xt);
+  free(gt);
+  free(ut);
+  free(dt);
 }
 
 /* The SwiGLU expert (act 0). */

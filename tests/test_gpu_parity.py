@@ -10,7 +10,8 @@ import numpy as np
 import pytest
 
 import k3x_synth as S
-from cases import assert_y_close, assert_y_close_oracle, oracle_forward_sampled, y_errors
+from cases import (assert_y_close, assert_y_close_oracle, oracle_forward_all, oracle_forward_sampled,
+                   token_errors, y_errors)
 
 pytestmark = pytest.mark.gpu
 
@@ -277,6 +278,28 @@ def test_moe_zero_tokens(dev):
     assert k3x.k3x_fetch_drops(ws) == 0
 
 
+def test_route_moe_zero_tokens_resets_the_drop_counter(dev):
+    """An empty router + experts call leaves the workspace's drop counter at 0, as an empty
+    k3x_moe_forward does, also after a call that dropped a slot on the same workspace."""
+    torch, k3x = dev
+    _log("case: route_moe T=0 after a call with a dropped slot")
+    E, H, I, k = 8, 256, 256, 4
+    pool = _pool(torch, k3x, S.device_pool(5, 0, E, H, I), E, H, I)
+    W = S.normal_bf16(5, S.P_WR, 0, (E, H), std=0.05)
+    r = k3x.router_desc(_t(torch, W), None, k, 1, 1.0)
+    ws = k3x.alloc_workspace(max(k3x.k3x_route_moe_workspace_size(r, pool, 2),
+                                 k3x.k3x_moe_workspace_size(pool, 2, k)))
+    x = _t(torch, S.normal_bf16(5, S.P_X, 0, (2, H)))
+    idx = torch.tensor([[0, 1, 2, E + 3], [4, 5, 6, 7]], dtype=torch.int32, device="cuda")
+    g = torch.full((2, k), 0.25, dtype=torch.float32, device="cuda")
+    y = torch.empty((2, H), dtype=torch.float32, device="cuda")
+    k3x.k3x_moe_forward(pool, x, 2, idx, g, k, y, ws)
+    assert k3x.k3x_fetch_drops(ws) == 1
+    e0 = torch.empty((0,), dtype=torch.int32, device="cuda")
+    k3x.k3x_route_moe_forward(r, pool, e0, 0, e0, e0, e0, ws)
+    assert k3x.k3x_fetch_drops(ws) == 0
+
+
 # ------------------------------------------------------------------------------------------
 # router
 # ------------------------------------------------------------------------------------------
@@ -463,7 +486,7 @@ def test_route_moe_forward_equals_separate_calls(dev, orc):
 
 
 # ------------------------------------------------------------------------------------------
-# the five workloads at full size (sampled tokens where the oracle would take minutes)
+# the five workloads at full size, every output checked
 # ------------------------------------------------------------------------------------------
 def test_workload1_decode_e64(dev, orc):
     torch, k3x = dev
@@ -526,6 +549,20 @@ def test_decode_single_token_equals_oracle_many(dev, orc):
     _log(f"  worst rel_l2 over 24 tokens: {worst:.3e}")
 
 
+def _whole_tensor_verdict(torch, orc, w, y, x, idx, gates, what, act="swiglu"):
+    """The y verdict over the whole [T][H] output of a full-size run (every token), against
+    the oracle walking the experts one by one; the fp64 oracle is computed only if the
+    fallback needs it.  Logs the whole-tensor errors and the worst single token."""
+    y_ref = oracle_forward_all(orc, w.seed, 0, w.H, w.I, x, idx, gates, act=act, log=_log)
+    r = assert_y_close_oracle(
+        y, y_ref, lambda: oracle_forward_all(orc, w.seed, 0, w.H, w.I, x, idx, gates, acc="f64",
+                                             act=act, log=_log), what)
+    rel, t_rel, mx, t_mx = token_errors(y, y_ref)
+    _log(f"  {what}: whole tensor rel_l2={r[0]:.3e} max_abs={r[1]:.3e}; worst token rel_l2="
+         f"{rel:.3e} (token {t_rel}), worst token max_abs={mx:.3e} (token {t_mx})")
+    return r
+
+
 def test_workload3_decode_t32_zipf(dev, orc):
     torch, k3x = dev
     w = S.WORKLOADS[3]
@@ -537,16 +574,15 @@ def test_workload3_decode_t32_zipf(dev, orc):
     idx, gates, _ = k3x.route_topk(_t(torch, W), _t(torch, b), xd, w.topk)
     y, ws = k3x.moe_forward(pool, xd, idx, gates)
     torch.cuda.synchronize()
+    assert k3x.k3x_fetch_drops(ws) == 0
     i_ref, g_ref = orc.route(x, W, b, w.topk)
     assert np.array_equal(_np(idx), i_ref)
     assert np.array_equal(_np(gates).view(np.uint32), g_ref.view(np.uint32))
-    U = len(np.unique(i_ref))
-    tokens = [0, 13, 31]
-    y_ref = oracle_forward_sampled(orc, w.seed, 0, w.H, w.I, x, i_ref, g_ref, tokens)
-    r = assert_y_close(_np(y)[tokens], y_ref, w.name)
-    _log(f"  distinct experts U={U} rel_l2={r[0]:.3e} max_abs={r[1]:.3e}")
-    del pool
+    _log(f"  distinct experts U={len(np.unique(i_ref))}")
+    yv = _np(y)
+    del pool, ws, y
     torch.cuda.empty_cache()
+    _whole_tensor_verdict(torch, orc, w, yv, x, i_ref, g_ref, w.name)
 
 
 def test_workload4_prefill_t4096(dev, orc):
@@ -559,12 +595,90 @@ def test_workload4_prefill_t4096(dev, orc):
     y, ws = k3x.moe_forward(pool, _t(torch, x), _t(torch, idx), _t(torch, gates))
     torch.cuda.synchronize()
     assert k3x.k3x_fetch_drops(ws) == 0
-    tokens = [0, 1, 2047, 4095]
-    y_ref = oracle_forward_sampled(orc, w.seed, 0, w.H, w.I, x, idx, gates, tokens)
-    r = assert_y_close(_np(y)[tokens], y_ref, w.name)
-    _log(f"  rel_l2={r[0]:.3e} max_abs={r[1]:.3e}")
-    del pool, ws
+    yv = _np(y)
+    del pool, ws, y
     torch.cuda.empty_cache()
+    _whole_tensor_verdict(torch, orc, w, yv, x, idx, gates, w.name)
+
+
+# ------------------------------------------------------------------------------------------
+# the format's edge cases on every path
+# ------------------------------------------------------------------------------------------
+EDGE_C0 = 5  # the x element that meets the scale-2 weights (kept at |x| = 1.5)
+
+
+def _edge_pool(seed, E, H, I):
+    """A host pool with the edge cases of the MXFP4 format (kimi-k3-in-c README, Part II
+    section 4: the E2M1 table with its -0 code 8; the E8M0 scale 2^(s - 127), byte 255 zeroing
+    its group), arranged so every output stays finite and of normal size:
+      - NaN scale bytes (255) in about 4 % of the groups of W1, W3 and W2;
+      - row 1 of every matrix all code 8 (-0), and about 5 % of the low nibbles set to 8;
+      - scale byte 2: W3 rows 32..63 hold a single 6.0 (code 7) at element EDGE_C0 in a group
+        of scale byte 2, so u = x[EDGE_C0] * 6 * 2^-125 there and h is up to about 1e-34 (a
+        normal bf16); W2 row 7 has scale byte 2 in every group (a normal fp32 output near
+        1e-31);
+      - scale byte 252: W2 group 1 (the columns of those tiny h) has scale byte 252 in every
+        row, which brings their products back to ordinary magnitudes (2^125 * 6 * 1e-34)."""
+    pool = S.host_pool(seed, 0, E, H, I)
+    rng = np.random.default_rng(seed)
+    for name in ("w1", "w3", "w2"):
+        p = pool[name + "_packed"]
+        sc = pool[name + "_scale"]
+        sc[rng.random(sc.shape) < 0.04] = 255
+        p[:, 1, :] = 0x88
+        m = rng.random(p.shape) < 0.05
+        p[m] = (p[m] & 0xF0) | 0x08
+    p3, s3 = pool["w3_packed"], pool["w3_scale"]
+    p3[:, 32:64, :] = 0
+    p3[:, 32:64, EDGE_C0 // 2] = 0x70 if EDGE_C0 % 2 else 0x07
+    s3[:, 32:64, EDGE_C0 // 32] = 2
+    s2 = pool["w2_scale"]
+    s2[:, :, 1] = 252
+    s2[:, 7, :] = 2
+    return pool
+
+
+@pytest.mark.parametrize("path,E,H,I,T,k", [("decode", 4, 512, 512, 1, 4),
+                                            ("grouped", 4, 384, 256, 3, 3),
+                                            ("prefill", 4, 512, 1024, 40, 2)])
+def test_format_edge_cases(dev, orc, path, E, H, I, T, k):
+    """Scale byte 255, code 8 (-0) and the extreme scale bytes 2 and 252 reach the kernels of
+    each path: the exact single-token decode equals the fp32 oracle bit for bit; the grouped
+    and sorted-tile paths meet the y verdict, and so does output element 7 (W2's all-scale-2
+    row) on its own."""
+    torch, k3x = dev
+    _log(f"case: format edge cases, {path} path E={E} H={H} I={I} T={T} k={k}")
+    seed = 4000 + H + I + T
+    host = _edge_pool(seed, E, H, I)
+    devp = {n: _t(torch, host[n]) for n in S.TENSOR_NAMES}
+    pool = _pool(torch, k3x, devp, E, H, I)
+    x = S.normal_bf16(seed, S.P_X, 0, (T, H))
+    x[:, EDGE_C0] = np.where(np.arange(T) % 2 == 0, 0x3FC0, 0xBFC0)  # +-1.5
+    x[0, 9] = 0x8000  # -0
+    rng = np.random.default_rng(seed)
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    _, gates = S.uniform_routing(seed, T, k, k)
+    y, ws = k3x.moe_forward(pool, _t(torch, x), _t(torch, idx), _t(torch, gates))
+    torch.cuda.synchronize()
+    assert k3x.k3x_fetch_drops(ws) == 0
+    yv = _np(y)
+    y_ref, drops = orc.moe_forward(host, x, idx, gates)
+    assert drops == 0 and np.all(np.isfinite(y_ref))
+    # the tiny h rows really reach W2 through the scale-252 group: without them y changes
+    flat = {n: a.copy() for n, a in host.items()}
+    flat["w2_scale"][:, :, 1] = 255
+    y_wo, _ = orc.moe_forward(flat, x, idx, gates)
+    assert y_errors(y_wo, y_ref)[0] > 1e-3
+    col = np.abs(y_ref[:, 7])
+    assert np.all(col < 1e-25) and np.all(col[col > 0] > 1e-37)
+    assert np.all(np.isfinite(yv)), "non-finite output"
+    if path == "decode":
+        assert np.array_equal(yv, y_ref), "single-token decode differs from the fp32 oracle"
+        return
+    r = assert_y_close_oracle(yv, y_ref, lambda: orc.moe_forward(host, x, idx, gates, acc="f64")[0],
+                              f"edge {path}")
+    rc = assert_y_close(yv[:, 7:8], y_ref[:, 7:8], f"edge {path}, the all-scale-2 row")
+    _log(f"  rel_l2={r[0]:.3e} max_abs={r[1]:.3e}; scale-2 row rel_l2={rc[0]:.3e}")
 
 
 # ------------------------------------------------------------------------------------------
@@ -614,7 +728,7 @@ def test_situ_grouped_and_prefill_paths(dev, orc, E, H, I, T, k):
 
 def test_situ_workload2_and_prefill_full_size(dev, orc):
     """Full shapes with SiTU-GLU: one routed decode token over 896 experts (bit-exact) and
-    the 4096-token prefill (sampled tokens, tolerance)."""
+    the 4096-token prefill (every token, tolerance)."""
     torch, k3x = dev
     w = S.WORKLOADS[2]
     _log("case: SiTU workload decode_t1_e896_router")
@@ -636,12 +750,10 @@ def test_situ_workload2_and_prefill_full_size(dev, orc):
     idx, gates = S.uniform_routing(w.seed, w.T, w.E, w.topk)
     y, ws = k3x.moe_forward(pool, _t(torch, x), _t(torch, idx), _t(torch, gates))
     torch.cuda.synchronize()
-    tokens = [0, 1, 2047, 4095]
-    y_ref = oracle_forward_sampled(orc, w.seed, 0, w.H, w.I, x, idx, gates, tokens, act=SITU)
-    r = assert_y_close(_np(y)[tokens], y_ref, "SiTU prefill")
-    _log(f"  rel_l2={r[0]:.3e} max_abs={r[1]:.3e}")
-    del pool, ws
+    yv = _np(y)
+    del pool, ws, y
     torch.cuda.empty_cache()
+    _whole_tensor_verdict(torch, orc, w, yv, x, idx, gates, "SiTU prefill", act=SITU)
 
 
 # ------------------------------------------------------------------------------------------

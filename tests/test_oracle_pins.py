@@ -345,6 +345,53 @@ def test_dropped_slots_are_counted_and_contribute_nothing(orc):
     assert d0 == 0 and np.array_equal(y, y_ref)
 
 
+def _edge_expert(seed, H, I):
+    """An expert with the format's edge cases: NaN scale bytes (255), rows and scattered
+    nibbles of code 8 (-0), and the extreme scale bytes 2 and 252 over groups of zero codes
+    (so nothing overflows)."""
+    ex = S.expert_bytes(seed, 0, 0, H, I)
+    rng = np.random.default_rng(seed)
+    for name in ("w1", "w3", "w2"):
+        p = getattr(ex, name + "_packed")
+        sc = getattr(ex, name + "_scale")
+        sc[rng.random(sc.shape) < 0.05] = 255
+        sc[rng.random(sc.shape) < 0.03] = 2
+        p[1, :] = 0x88
+        m = rng.random(p.shape) < 0.05
+        p[m] = (p[m] & 0xF0) | 0x08
+        r, g = 2, 1
+        p[r, 16 * g:16 * g + 16] = 0x80
+        sc[r, g] = 252
+    return ex
+
+
+@pytest.mark.parametrize("acc", ["f32", "f64"])
+@pytest.mark.parametrize("act", ["swiglu", ("situ", 4.0, 25.0)])
+@pytest.mark.parametrize("n", [1, 7, 33])
+def test_expert_forward_many_equals_per_token(orc, acc, act, n):
+    """The expert-major oracle (one expert on n activations, the tokens side by side in the
+    innermost loops) gives every token exactly what the per-token oracle gives it."""
+    H, I = 96, 128
+    ex = _edge_expert(40 + n, H, I)
+    x = S.normal_bf16(41 + n, S.P_X, 0, (n, H))
+    x[0, 3] = 0x8000  # -0
+    x[n - 1, 5] = 0x0000
+    d = orc.expert_forward_many(x, ex, acc=acc, act=act)
+    assert np.all(np.isfinite(d))
+    for t in range(n):
+        want = orc.expert_forward(x[t], ex, acc=acc, act=act)
+        assert np.array_equal(d[t].view(np.uint32), want.view(np.uint32)), t
+
+
+def test_expert_forward_many_full_shape(orc):
+    H, I = S.H_K3, S.I_K3
+    ex = S.expert_bytes(91, 0, 5, H, I)
+    x = S.normal_bf16(91, S.P_X, 0, (5, H))
+    d = orc.expert_forward_many(x, ex)
+    for t in range(5):
+        assert np.array_equal(d[t].view(np.uint32), orc.expert_forward(x[t], ex).view(np.uint32)), t
+
+
 def test_fp32_oracle_noise_floor_full_size(orc):
     """The verdict (fp32) oracle against its fp64 self-check at the real expert shape."""
     H, I, E, k = S.H_K3, S.I_K3, 4, 4

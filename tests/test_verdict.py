@@ -4,7 +4,9 @@ itself lies beyond the tolerance from the fp64 oracle."""
 import numpy as np
 import pytest
 
-from cases import MAX_ABS_TOL, REL_L2_TOL, assert_y_close, assert_y_close_oracle, y_errors
+import k3x_synth as S
+from cases import (FALLBACKS, MAX_ABS_TOL, REL_L2_TOL, assert_y_close, assert_y_close_oracle,
+                   oracle_forward_all, oracle_forward_sampled, token_errors, y_errors)
 
 
 def _ref(seed=0, shape=(6, 64)):
@@ -49,5 +51,52 @@ def test_oracle_fallback_only_when_fp32_oracle_is_off():
     # when the fp32 oracle agrees with the fp64 one, no fallback: a miss of the fp32 oracle fails
     with pytest.raises(AssertionError):
         assert_y_close_oracle(noisy32, r64, lambda: r64)
+    # a result within tolerance of the fp64 oracle but farther from it than the fp32 oracle
+    # is fails: the fallback never accepts a worse result
+    big64 = _ref(2, (400, 64))
+    scaled32 = big64 * (1 + 3 * REL_L2_TOL)  # fp32 oracle off in rel L2 only (max-abs 3e-4)
+    worse = big64.copy()
+    worse[0, 0] += 0.8 * MAX_ABS_TOL * np.abs(big64).max()  # within tolerance, past the floor
+    assert y_errors(worse, big64)[0] <= REL_L2_TOL and y_errors(worse, big64)[1] <= MAX_ABS_TOL
+    with pytest.raises(AssertionError, match="farther than the fp32 oracle"):
+        assert_y_close_oracle(worse, scaled32, lambda: big64)
+    # every fallback is recorded
+    n = len(FALLBACKS)
+    assert_y_close_oracle(r64, noisy32, lambda: r64)
+    assert len(FALLBACKS) == n + 1 and FALLBACKS[-1][1][1] > MAX_ABS_TOL
     # results within tolerance of the fp32 oracle never consult the fp64 one
     assert_y_close_oracle(r64, r64, lambda: (_ for _ in ()).throw(RuntimeError("not needed")))
+
+
+def test_token_errors_name_the_worst_token():
+    r = _ref(3, (5, 32))
+    y = r.copy()
+    y[3] *= 1 + 1e-3
+    y[1, 7] += 0.25
+    rel, t_rel, mx, t_mx = token_errors(y, r)
+    assert t_rel == 1 or t_rel == 3
+    assert rel == pytest.approx(max(np.linalg.norm(y[t] - r[t]) / np.linalg.norm(r[t]) for t in range(5)))
+    assert t_mx == int(np.argmax([np.abs(y[t] - r[t]).max() / np.abs(r[t]).max() for t in range(5)]))
+    assert mx == pytest.approx(np.abs(y[t_mx] - r[t_mx]).max() / np.abs(r[t_mx]).max())
+
+
+@pytest.mark.parametrize("act", ["swiglu", ("situ", 4.0, 25.0)])
+def test_expert_major_reference_equals_per_token_oracle(orc, act):
+    """The whole-tensor reference of the full-size parity tests (experts walked one by one,
+    per-slot outputs kept, slot-order combine) equals the oracle's per-token forward, with
+    duplicates and dropped slots."""
+    E, H, I, T, k, seed = 7, 64, 96, 23, 4, 515
+    pool = S.host_pool(seed, 0, E, H, I)
+    x = S.normal_bf16(seed, S.P_X, 0, (T, H))
+    rng = np.random.default_rng(seed)
+    idx = rng.integers(0, E, (T, k)).astype(np.int32)
+    idx[3, 1] = E + 2
+    idx[5, 0] = -1
+    _, gates = S.uniform_routing(seed, T, k, k)
+    for acc in ("f32", "f64"):
+        want, drops = orc.moe_forward(pool, x, idx, gates, acc=acc, act=act)
+        assert drops == 2
+        got = oracle_forward_all(orc, seed, 0, H, I, x, idx, gates, E=E, acc=acc, act=act)
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), acc
+        some = oracle_forward_sampled(orc, seed, 0, H, I, x, idx, gates, [0, 3, 22], E=E, acc=acc, act=act)
+        assert np.array_equal(some.view(np.uint32), want[[0, 3, 22]].view(np.uint32)), acc
