@@ -43,6 +43,12 @@ def test_python_binding_has_the_c_names(k3x):
         assert hasattr(k3x, n), n
 
 
+def _gpu_present():
+    import torch
+
+    return torch.cuda.is_available()
+
+
 def _desc(k3x, **kw):
     d = k3x.k3x_pool_desc()
     d.n_experts, d.hidden, d.inter, d.group = 8, 256, 384, 32
@@ -217,7 +223,10 @@ def test_latent_block_host_validation(k3x):
         assert lib.k3x_latent_ws_layout(ctypes.byref(desc()), h, ctypes.byref(router()), 3,
                                         None) == k3x.K3X_E_INVALID_ARG
         assert need - off >= lib.k3x_moe_workspace_size(h, 3, 2)
-        assert fwd(desc(), router(), T=0) == 0  # nothing to do, nothing launched
+        if not _gpu_present():
+            # an empty call still enqueues the reset of the routed experts' drop counter; with no
+            # device that launch fails (on a GPU the fake workspace must not be touched)
+            assert fwd(desc(), router(), T=0) == k3x.K3X_E_HIP
         E_ARG, E_UNS, E_WS = k3x.K3X_E_INVALID_ARG, k3x.K3X_E_UNSUPPORTED, k3x.K3X_E_WORKSPACE
         cases = [
             (desc(hidden=1536), router(), E_ARG),           # router width != block width
@@ -273,7 +282,9 @@ def test_route_moe_host_validation(k3x):
         assert need >= lib.k3x_moe_workspace_size(h, 3, 2) + 3 * 8 * 4
         fwd = lambda r, T=3, x=fake, ws=fake, n=need: lib.k3x_route_moe_forward(
             R(r), h, x, T, fake, fake, fake, ws, n, None)
-        assert fwd(router(), T=0) == 0
+        if not _gpu_present():
+            # an empty call enqueues only the reset of the drop counter: no device, a HIP error
+            assert fwd(router(), T=0) == k3x.K3X_E_HIP
         assert fwd(router(n_experts=9)) == k3x.K3X_E_INVALID_ARG
         assert fwd(router(hidden=512)) == k3x.K3X_E_INVALID_ARG
         assert fwd(router(topk=9)) == k3x.K3X_E_INVALID_ARG
