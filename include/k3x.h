@@ -172,6 +172,23 @@ k3x_status k3x_route_moe_forward(const k3x_router_desc *r, const k3x_pool *p, co
                                  int32_t T, int32_t *idx_out, float *gates_out, float *y,
                                  void *ws, size_t ws_bytes, void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation): k3x_moe_forward with its workspace in a
+ * scratch array built into the library instead of a caller's buffer.  Each GPU the library
+ * runs on holds its own K3X_NOALLOC_SCRATCH_BYTES (32 MiB) of it from module load until the
+ * process ends; the call itself allocates nothing, host or device.  Arguments as
+ * k3x_moe_forward (the calling thread's current device must be that of the stream and the
+ * pointers).  drops_out: NULL, or a DEVICE int64 that receives this call's drop count
+ * (copied on the stream after the forward).  Refuses (K3X_E_UNSUPPORTED) a call whose
+ * workspace, k3x_moe_workspace_size(p, T, topk), exceeds the scratch (at the K3 shape, hidden
+ * 3584 and inter 3072, up to T = 102 at topk 16), and enqueues nothing then.  Every call on one GPU
+ * uses that GPU's one scratch, which keeps the last call's contents: calls that overlap in
+ * time on one GPU (other streams or threads) race and must be serialised by the caller. */
+#define K3X_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+k3x_status k3x_moe_forward_noalloc(const k3x_pool *p, const void *x_bf16, int32_t T,
+                                   const int32_t *idx, const float *gates, int32_t topk, float *y,
+                                   int64_t *drops_out, void *stream);
+
 /* Waits for stream, then stores in *n the number of dropped slots of the latest
  * k3x_moe_forward that used ws.  Returns K3X_E_DROPS when *n > 0 (the run must be treated
  * as invalid), K3X_OK when 0.  n is a host pointer. */

@@ -108,6 +108,7 @@ K3X_CACHE_LRU, K3X_CACHE_BELADY, K3X_CACHE_PIN_LRU = 0, 1, 2
 EXPORTS = (
     "k3x_status_str", "k3x_last_error", "k3x_expert_pool_create", "k3x_expert_pool_destroy",
     "k3x_route_workspace_size", "k3x_route_topk", "k3x_moe_workspace_size", "k3x_moe_forward",
+    "k3x_moe_forward_noalloc",
     "k3x_fetch_drops", "k3x_rmsnorm_bf16", "k3x_residual_add_bf16", "k3x_residual_add_rmsnorm_bf16",
     "k3x_latent_workspace_size", "k3x_latent_forward", "k3x_latent_ws_layout",
     "k3x_route_moe_workspace_size", "k3x_route_moe_forward",
@@ -146,6 +147,8 @@ def load_library(path: str = LIB_PATH):
     L.k3x_moe_workspace_size.argtypes = [P, I32, I32]
     L.k3x_moe_forward.restype = ctypes.c_int
     L.k3x_moe_forward.argtypes = [P, P, I32, P, P, I32, P, P, SZ, P]
+    L.k3x_moe_forward_noalloc.restype = ctypes.c_int
+    L.k3x_moe_forward_noalloc.argtypes = [P, P, I32, P, P, I32, P, P, P]
     L.k3x_fetch_drops.restype = ctypes.c_int
     L.k3x_fetch_drops.argtypes = [P, ctypes.POINTER(ctypes.c_int64), P]
     L.k3x_rmsnorm_bf16.restype = ctypes.c_int
@@ -340,6 +343,17 @@ def k3x_route_moe_forward(r: k3x_router_desc, pool: Pool, x, T: int, idx_out, ga
     _check(lib().k3x_route_moe_forward(ctypes.byref(r), pool.handle, _ptr(x), int(T),
                                        _ptr(idx_out), _ptr(gates_out), _ptr(y), _ptr(ws),
                                        int(nbytes), _stream(stream)))
+
+
+K3X_NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def k3x_moe_forward_noalloc(pool: Pool, x, T: int, idx, gates, topk: int, y, drops_out=None,
+                            stream=None):
+    """k3x_moe_forward with the library's built-in scratch as its workspace (allocates
+    nothing); drops_out: None or a device int64 tensor of one element."""
+    _check(lib().k3x_moe_forward_noalloc(pool.handle, _ptr(x), int(T), _ptr(idx), _ptr(gates),
+                                         int(topk), _ptr(y), _ptr(drops_out), _stream(stream)))
 
 
 def k3x_fetch_drops(ws, stream=None) -> int:

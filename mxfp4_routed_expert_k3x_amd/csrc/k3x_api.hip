@@ -32,6 +32,16 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 namespace k3x {
 
+k3x_status fail_status(k3x_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+k3x_status hip_status(hipError_t e, const char* where) { return hip_fail(e, where); }
+
 int device_cu_count() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 256;

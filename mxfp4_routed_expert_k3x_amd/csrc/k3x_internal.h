@@ -204,6 +204,11 @@ hipError_t launch_residual_rmsnorm(uint16_t* x, const float* y, int32_t T, int32
 
 int device_cu_count();
 
+// Records a message as the calling thread's last error (k3x_last_error) and returns st.
+k3x_status fail_status(k3x_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+// The same for a HIP error: "where: <HIP error string>", K3X_E_HIP.
+k3x_status hip_status(hipError_t e, const char* where);
+
 // When a profiler is attached to the calling thread and has room, reserves the next record
 // for kernel `name` and returns its start/stop events.
 bool profiler_events(const char* name, hipEvent_t* start, hipEvent_t* stop);

@@ -332,3 +332,27 @@ def test_status_strings(k3x):
     for s in (0, -1, -2, -3, -4, -5):
         assert k3x.k3x_status_str(s)
     assert k3x.k3x_status_str(7) == "unknown status"
+
+
+def test_noalloc_host_refusals(k3x):
+    """k3x_moe_forward_noalloc refuses on the host, before touching any device: a NULL pool,
+    topk out of range, and a call whose workspace exceeds the built-in scratch."""
+    lib = k3x.lib()
+    fake = 1 << 40
+    d = _desc(k3x, hidden=3584, inter=3072)
+    d.n_experts = 896
+    st, h = _create(k3x, d)
+    assert st == 0
+    try:
+        f = lambda pool, T, k, drops=None: lib.k3x_moe_forward_noalloc(
+            pool, fake, T, fake, fake, k, fake, drops, None)
+        assert f(None, 4, 16) == k3x.K3X_E_INVALID_ARG
+        assert f(h, 4, 0) == k3x.K3X_E_INVALID_ARG
+        assert f(h, -1, 16) == k3x.K3X_E_INVALID_ARG
+        assert lib.k3x_moe_workspace_size(h, 102, 16) <= k3x.K3X_NOALLOC_SCRATCH_BYTES
+        assert lib.k3x_moe_workspace_size(h, 103, 16) > k3x.K3X_NOALLOC_SCRATCH_BYTES
+        assert f(h, 103, 16) == k3x.K3X_E_UNSUPPORTED
+        assert b"scratch" in lib.k3x_last_error()
+        assert f(h, 4, 16, drops=fake + 4) == k3x.K3X_E_INVALID_ARG
+    finally:
+        lib.k3x_expert_pool_destroy(h)
