@@ -98,8 +98,12 @@ __device__ __forceinline__ void xcd_rank(int& die, int& rank, int& per_die) {
 // ---------------------------------------------------------------------------------------
 // Workspace layout of k3x_moe_forward (byte offsets; every region 256-byte aligned)
 // ---------------------------------------------------------------------------------------
+// Tile classes of the sort: class k holds the tiles of 16 k + 1 .. 16 k + 16 slots.
+constexpr int kMaxTileClasses = 6;
+
 struct MoeLayout {
-  size_t drops;       // int64 drop counter (+ int32 n_tiles at +8)
+  size_t drops;       // int64 drop counter, int32 n_tiles at +8, int32 end of each tile class
+                      // [kMaxTileClasses] at +12 (64 bytes)
   size_t offsets;     // int32 [E + 1] start of each expert's slots in perm
   size_t tiles;       // int32 [max_tiles][4] = expert, first slot in perm, count, pad
   size_t perm;        // int32 [T * topk] slot ids (t * topk + j) grouped by expert

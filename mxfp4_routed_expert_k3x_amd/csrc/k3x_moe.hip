@@ -40,7 +40,7 @@ MoeLayout moe_layout(int32_t E, int32_t H, int32_t I, int32_t T, int32_t topk) {
   L.max_tiles = (int32_t)(nonempty + (slots + L.tile_tokens - 1) / L.tile_tokens + 1);
   size_t off = 0;
   L.drops = off;
-  off = up(off + 16);
+  off = up(off + 64);  // drop count, tile count, the tile classes' ends
   L.offsets = off;
   off = up(off + sizeof(int32_t) * ((size_t)E + 1));
   L.tiles = off;
@@ -69,6 +69,80 @@ namespace {
 // ---------------------------------------------------------------------------------------
 constexpr int kSortThreads = 1024;
 
+// Tiles are written class by class: class k holds the tiles of 16 k + 1 .. 16 k + 16 slots
+// (the number of 16-column MFMA blocks they need, minus one), each class in expert order.  The
+// header of the workspace gives the tile count at byte 8 and, from byte 12, the end of each
+// class in the tile array (kTileClasses ints), so the sorted-tile kernels can run every class
+// with a loop compiled for its width.
+constexpr int kTileClasses = kMaxTileClasses;
+
+__device__ __forceinline__ int tile_class(int size) { return min((size + 15) / 16, kTileClasses) - 1; }
+
+// Workgroup-wide inclusive scans (kSortThreads threads) of the slot count csum and the
+// per-class tile counts kc[] of each thread's experts; returns, in csum and kc[], the
+// exclusive prefixes, in tot[] the workgroup totals (tot[0] slots, tot[1 + k] tiles of class k).
+__device__ void scan_tiles(int32_t (&sc)[1 + kTileClasses][kSortThreads], int& csum,
+                           int (&kc)[kTileClasses], int (&tot)[1 + kTileClasses]) {
+  const int tid = threadIdx.x;
+  sc[0][tid] = csum;
+#pragma unroll
+  for (int k = 0; k < kTileClasses; ++k) sc[1 + k][tid] = kc[k];
+  __syncthreads();
+  for (int o = 1; o < kSortThreads; o <<= 1) {
+    int v[1 + kTileClasses];
+#pragma unroll
+    for (int k = 0; k <= kTileClasses; ++k) v[k] = tid >= o ? sc[k][tid - o] : 0;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k <= kTileClasses; ++k) sc[k][tid] += v[k];
+    __syncthreads();
+  }
+  csum = sc[0][tid] - csum;
+#pragma unroll
+  for (int k = 0; k < kTileClasses; ++k) kc[k] = sc[1 + k][tid] - kc[k];
+#pragma unroll
+  for (int k = 0; k <= kTileClasses; ++k) tot[k] = sc[k][kSortThreads - 1];
+}
+
+// The tiles of one expert (c slots from position bc) at the cursors of their classes.
+__device__ __forceinline__ void emit_expert_tiles(int4* tiles, int e, int bc, int c, int tt,
+                                                  int (&cur)[kTileClasses]) {
+  const int nt = (c + tt - 1) / tt;
+  for (int i = 0; i < nt; ++i) {
+    int4 tv;
+    tv.x = e;
+    tv.y = bc + i * tt;
+    tv.z = min(tt, c - i * tt);
+    tv.w = 0;
+    const int k = tile_class(tv.z);
+#pragma unroll
+    for (int j = 0; j < kTileClasses; ++j)
+      if (j == k) tiles[cur[j]++] = tv;
+  }
+}
+
+// Per-thread tile counts by class of experts with the given slot count.
+__device__ __forceinline__ void count_expert_tiles(int c, int tt, int (&kc)[kTileClasses]) {
+  const int nt = (c + tt - 1) / tt;
+  for (int i = 0; i < nt; ++i) {
+    const int k = tile_class(min(tt, c - i * tt));
+#pragma unroll
+    for (int j = 0; j < kTileClasses; ++j) kc[j] += j == k;
+  }
+}
+
+// Writes the header's tile count and class ends (thread 0).
+__device__ __forceinline__ void write_tile_header(uint8_t* ws, const int (&tot)[1 + kTileClasses]) {
+  int32_t* h = reinterpret_cast<int32_t*>(ws + 8);
+  int end = 0;
+#pragma unroll
+  for (int k = 0; k < kTileClasses; ++k) {
+    end += tot[1 + k];
+    h[1 + k] = end;
+  }
+  h[0] = end;
+}
+
 struct SortArgs {
   const int32_t* idx;
   int32_t T, topk, E, tile_tokens;
@@ -78,8 +152,7 @@ struct SortArgs {
 
 __global__ __launch_bounds__(kSortThreads) void moe_sort(SortArgs a) {
   extern __shared__ int32_t counts[];  // [E]
-  __shared__ int32_t scan_c[kSortThreads];
-  __shared__ int32_t scan_t[kSortThreads];
+  __shared__ int32_t scan[1 + kTileClasses][kSortThreads];
   __shared__ int32_t drop_cnt;
   const int tid = threadIdx.x;
   const int n_slots = a.T * a.topk;
@@ -103,45 +176,35 @@ __global__ __launch_bounds__(kSortThreads) void moe_sort(SortArgs a) {
 
   const int per = (E + kSortThreads - 1) / kSortThreads;
   const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
-  int csum = 0, tsum = 0;
+  int csum = 0;
+  int kc[kTileClasses] = {};
   for (int e = e0; e < e1; ++e) {
     const int c = counts[e];
     csum += c;
-    tsum += (c + a.tile_tokens - 1) / a.tile_tokens;
+    count_expert_tiles(c, a.tile_tokens, kc);
   }
-  scan_c[tid] = csum;
-  scan_t[tid] = tsum;
-  __syncthreads();
-  for (int o = 1; o < kSortThreads; o <<= 1) {
-    const int vc = tid >= o ? scan_c[tid - o] : 0;
-    const int vt = tid >= o ? scan_t[tid - o] : 0;
-    __syncthreads();
-    scan_c[tid] += vc;
-    scan_t[tid] += vt;
-    __syncthreads();
+  int tot[1 + kTileClasses];
+  scan_tiles(scan, csum, kc, tot);
+  // class k's tiles start after all tiles of the classes before it
+  int cur[kTileClasses];
+  int base = 0;
+#pragma unroll
+  for (int k = 0; k < kTileClasses; ++k) {
+    cur[k] = base + kc[k];
+    base += tot[1 + k];
   }
-  int bc = scan_c[tid] - csum;
-  int bt = scan_t[tid] - tsum;
+  int bc = csum;
   for (int e = e0; e < e1; ++e) {
     const int c = counts[e];
     offsets[e] = bc;
-    const int nt = (c + a.tile_tokens - 1) / a.tile_tokens;
-    for (int i = 0; i < nt; ++i) {
-      int4 tv;
-      tv.x = e;
-      tv.y = bc + i * a.tile_tokens;
-      tv.z = min(a.tile_tokens, c - i * a.tile_tokens);
-      tv.w = 0;
-      reinterpret_cast<int4*>(tiles)[bt + i] = tv;
-    }
+    emit_expert_tiles(reinterpret_cast<int4*>(tiles), e, bc, c, a.tile_tokens, cur);
     counts[e] = bc;  // becomes the scatter cursor
     bc += c;
-    bt += nt;
   }
   if (tid == kSortThreads - 1) {
-    offsets[E] = scan_c[kSortThreads - 1];
+    offsets[E] = tot[0];
     *reinterpret_cast<int64_t*>(a.ws) = (int64_t)drop_cnt;
-    *reinterpret_cast<int32_t*>(a.ws + 8) = scan_t[kSortThreads - 1];
+    write_tile_header(a.ws, tot);
   }
   __syncthreads();
   for (int p = tid; p < n_slots; p += kSortThreads) {
@@ -197,8 +260,7 @@ __global__ __launch_bounds__(kSplitThreads) void sort_count(SplitArgs a) {
 }
 
 __global__ __launch_bounds__(kSortThreads) void sort_scan(SplitArgs a) {
-  __shared__ int32_t scan_c[kSortThreads];
-  __shared__ int32_t scan_t[kSortThreads];
+  __shared__ int32_t scan[1 + kTileClasses][kSortThreads];
   const int tid = threadIdx.x;
   const int E = a.E;
   int32_t* offsets = reinterpret_cast<int32_t*>(a.ws + a.off_offsets);
@@ -212,25 +274,23 @@ __global__ __launch_bounds__(kSortThreads) void sort_scan(SplitArgs a) {
     for (int g = 0; g < kSortParts; ++g) c += parts[(size_t)g * E + e];
     return c;
   };
-  int csum = 0, tsum = 0;
+  int csum = 0;
+  int kc[kTileClasses] = {};
   for (int e = e0; e < e1; ++e) {
     const int c = total_of(e);
     csum += c;
-    tsum += (c + a.tile_tokens - 1) / a.tile_tokens;
+    count_expert_tiles(c, a.tile_tokens, kc);
   }
-  scan_c[tid] = csum;
-  scan_t[tid] = tsum;
-  __syncthreads();
-  for (int o = 1; o < kSortThreads; o <<= 1) {
-    const int vc = tid >= o ? scan_c[tid - o] : 0;
-    const int vt = tid >= o ? scan_t[tid - o] : 0;
-    __syncthreads();
-    scan_c[tid] += vc;
-    scan_t[tid] += vt;
-    __syncthreads();
+  int tot[1 + kTileClasses];
+  scan_tiles(scan, csum, kc, tot);
+  int cur[kTileClasses];
+  int base = 0;
+#pragma unroll
+  for (int k = 0; k < kTileClasses; ++k) {
+    cur[k] = base + kc[k];
+    base += tot[1 + k];
   }
-  int bc = scan_c[tid] - csum;
-  int bt = scan_t[tid] - tsum;
+  int bc = csum;
   for (int e = e0; e < e1; ++e) {
     offsets[e] = bc;
     int run = bc;
@@ -241,24 +301,15 @@ __global__ __launch_bounds__(kSortThreads) void sort_scan(SplitArgs a) {
       run += c;
     }
     const int c = run - bc;
-    const int nt = (c + a.tile_tokens - 1) / a.tile_tokens;
-    for (int i = 0; i < nt; ++i) {
-      int4 tv;
-      tv.x = e;
-      tv.y = bc + i * a.tile_tokens;
-      tv.z = min(a.tile_tokens, c - i * a.tile_tokens);
-      tv.w = 0;
-      reinterpret_cast<int4*>(tiles)[bt + i] = tv;
-    }
+    emit_expert_tiles(reinterpret_cast<int4*>(tiles), e, bc, c, a.tile_tokens, cur);
     bc += c;
-    bt += nt;
   }
   if (tid == kSortThreads - 1) {
-    offsets[E] = scan_c[kSortThreads - 1];
+    offsets[E] = tot[0];
     int64_t dr = 0;
     for (int g = 0; g < kSortParts; ++g) dr += parts[(size_t)kSortParts * E + g];
     *reinterpret_cast<int64_t*>(a.ws) = dr;
-    *reinterpret_cast<int32_t*>(a.ws + 8) = scan_t[kSortThreads - 1];
+    write_tile_header(a.ws, tot);
   }
 }
 
