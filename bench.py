@@ -21,7 +21,12 @@ Two helper modes support `roofline.traffic` (HBM bytes from rocprofv3 counters):
                                                  # the copy (CF, CW) -> profiles/traffic_<workload>.txt
 The copy's readings give the scale of each counter (bytes moved / bytes counted); the
 summary records the hash of the kernel sources, and a normal run reports the traffic only
-while those sources are unchanged.
+while those sources are unchanged.  Two more turn profiler output into the summaries kept
+with the code:
+    python bench.py --workload W --stats-from STATS_CSV --profile-cmd "..."
+        # rocprofv3 --kernel-trace --stats -> profiles/kernel_trace_<W>.md
+    python bench.py --workload W --counters-from PASS1_CSV PASS2_CSV ... --profile-cmd "..."
+        # rocprofv3 --pmc passes -> profiles/counters_<W>.txt (MFMA use, LDS conflicts, waits)
 
 Prints ONE JSON line.  The timed region replays HIP graphs that run the rotated batches one
 after another (a graph of min(steps, 64) batches, replayed steps // that many times, then a
@@ -68,6 +73,7 @@ KERNEL_SOURCES = ("k3x_internal.h", "k3x_select.h", "k3x_decode.hip", "k3x_moe.h
 LATENT_SOURCES = KERNEL_SOURCES + ("k3x_dense.hip",)
 # rocprofv3 kernel names of the library's launch names
 KERNEL_SYMBOLS = {"w13_decode": "decode_w13", "w2_combine_decode": "decode_w2_combine",
+                  "moe_combine": "moe_combine",
                   "w13_prefill": "gemm_prefill<true>", "w2_prefill": "gemm_prefill<false>",
                   "w13_grouped": "gemm_decode<true>", "w2_grouped": "gemm_decode<false>",
                   "route_scores": "route_scores", "route_select": "route_select",
@@ -889,6 +895,104 @@ def traffic_from(f_csv, w_csv, cf_csv, cw_csv, workload):
     print("\n".join(lines))
 
 
+def _kernel_label(name):
+    """The library's launch name of a kernel symbol (or the symbol, shortened)."""
+    for label, sym in KERNEL_SYMBOLS.items():
+        if sym in name:
+            return label
+    for sym in ("moe_combine", "moe_sort", "sort_count", "sort_scan", "sort_scatter", "rmsnorm",
+                "residual", "fill_packed", "fill_scale", "combine_contract"):
+        if sym in name:
+            return sym
+    return name[:60]
+
+
+def stats_from(path, workload, command, steps):
+    """profiles/kernel_trace_<workload>.md from a rocprofv3 --stats kernel CSV, with the
+    per-dispatch trace beside it (run_kernel_trace.csv): the average of the last `steps`
+    dispatches of each kernel is that of bench.py's event-timed eager pass, the figure the
+    bench line's roofline uses; the trace also gives each kernel's registers and LDS."""
+    import csv
+    rows = list(csv.DictReader(open(path)))
+    trace = os.path.join(os.path.dirname(path), "run_kernel_trace.csv")
+    per = {}
+    res = {}
+    if os.path.exists(trace):
+        for r in csv.DictReader(open(trace)):
+            lab = _kernel_label(r["Kernel_Name"])
+            per.setdefault(lab, []).append((int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+            res[lab] = (r["VGPR_Count"], r["Accum_VGPR_Count"], r["SGPR_Count"], r["LDS_Block_Size"],
+                        r["Scratch_Size"], r["Workgroup_Size_X"], r["Grid_Size_X"])
+    out = [f"# rocprofv3 kernel trace: {workload}", "",
+           "Command (from /tmp with TMPDIR=/tmp, repository at $R):", "", f"    {command}", "",
+           "Calls include the warm-up, graph-check and eager passes of bench.py; `last N avg` is",
+           f"the mean of each kernel's last N = {steps} dispatches, bench.py's event-timed eager pass.", "",
+           "| kernel | calls | avg us | last N avg us | min us | max us | % of GPU time | VGPR | AGPR | SGPR | LDS B | scratch B | WG | grid |",
+           "|---|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    for r in rows:
+        lab = _kernel_label(r["Name"])
+        d = sorted(per.get(lab, []))[-steps:]
+        last = f"{np.mean([(b - a) for a, b in d]) / 1e3:.2f}" if d else "-"
+        rs = res.get(lab, ("-",) * 7)
+        out.append(f"| {lab} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {last} | "
+                   f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                   f"{float(r['Percentage']):.2f} | " + " | ".join(rs) + " |")
+    dst = os.path.join(ROOT, "profiles", f"kernel_trace_{workload}.md")
+    with open(dst, "w") as f:
+        f.write("\n".join(out) + "\n")
+    print("\n".join(out))
+
+
+def counters_from(paths, workload, command, n_xcd=8, n_simd=1024):
+    """profiles/counters_<workload>.txt from rocprofv3 --pmc CSVs (one per counter pass):
+    per library kernel the average of each counter per dispatch and the figures derived
+    from them.  SQ counters are summed over the chip; GRBM_GUI_ACTIVE is summed over the
+    n_xcd dies, so the kernel's clock cycles are GRBM_GUI_ACTIVE / n_xcd."""
+    import csv
+    acc = {}
+    for path in paths:
+        for r in csv.DictReader(open(path)):
+            lab = _kernel_label(r["Kernel_Name"])
+            if lab not in KERNEL_SYMBOLS and lab not in ("moe_combine",):
+                continue
+            d = acc.setdefault(lab, {"dur": []})
+            d.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+            d["dur"].append((float(r["End_Timestamp"]) - float(r["Start_Timestamp"])) * 1e-9)
+    lines = [f"# rocprofv3 counters of {workload} (averages per dispatch)", "",
+             "Commands (from /tmp with TMPDIR=/tmp, repository at $R), one pass per counter set:", "",
+             f"    {command}", "",
+             f"Derived: mfma_util = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / {n_xcd} * {n_simd} SIMDs);",
+             "mfma_tflops = SQ_INSTS_VALU_MFMA_MOPS_BF16 * 512 / duration; lds_conflict = SQ_LDS_BANK_CONFLICT /",
+             "SQ_LDS_IDX_ACTIVE; valu_per_mfma = (SQ_INSTS_VALU - SQ_INSTS_MFMA) / SQ_INSTS_MFMA; wait_frac =",
+             "SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES; clock_ghz = GRBM_GUI_ACTIVE / n_xcd / duration.", ""]
+    for lab in sorted(acc):
+        d = {k: float(np.mean(v)) for k, v in acc[lab].items()}
+        dur = d.pop("dur")
+        lines.append(f"kernel {lab} duration_us={dur * 1e6:.1f}")
+        for k in sorted(d):
+            lines.append(f"  {k} {d[k]:.6g}")
+        der = []
+        g = d.get("GRBM_GUI_ACTIVE")
+        if g:
+            der.append(f"clock_ghz={g / n_xcd / dur / 1e9:.3f}")
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in d:
+                der.append(f"mfma_util={d['SQ_VALU_MFMA_BUSY_CYCLES'] / (g / n_xcd * n_simd):.3f}")
+        if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in d:
+            der.append(f"mfma_tflops={d['SQ_INSTS_VALU_MFMA_MOPS_BF16'] * 512 / dur / 1e12:.1f}")
+        if d.get("SQ_LDS_IDX_ACTIVE"):
+            der.append(f"lds_conflict={d.get('SQ_LDS_BANK_CONFLICT', 0) / d['SQ_LDS_IDX_ACTIVE']:.3f}")
+        if d.get("SQ_INSTS_MFMA"):
+            der.append(f"valu_per_mfma={(d.get('SQ_INSTS_VALU', 0) - d['SQ_INSTS_MFMA']) / d['SQ_INSTS_MFMA']:.2f}")
+        if d.get("SQ_WAVE_CYCLES") and "SQ_WAIT_INST_ANY" in d:
+            der.append(f"wait_frac={d['SQ_WAIT_INST_ANY'] / d['SQ_WAVE_CYCLES']:.3f}")
+        if der:
+            lines.append("  derived " + " ".join(der))
+    dst = os.path.join(ROOT, "profiles", f"counters_{workload}.txt")
+    with open(dst, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def traffic_for(workload, kernel):
     """Calibrated HBM bytes per launch of `kernel`, or None (no summary, or kernels changed)."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
@@ -922,11 +1026,22 @@ def main():
                          "order, h in fp32); one token per call")
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"))
+    ap.add_argument("--stats-from", metavar="KERNEL_STATS_CSV",
+                    help="write profiles/kernel_trace_<workload>.md from a rocprofv3 --stats CSV")
+    ap.add_argument("--counters-from", nargs="+", metavar="COUNTER_CSV",
+                    help="write profiles/counters_<workload>.txt from rocprofv3 --pmc CSVs")
+    ap.add_argument("--profile-cmd", default="",
+                    help="the profiling command, recorded in the summary")
     args = ap.parse_args()
     if args.copy_probe:
         return copy_probe()
     if args.traffic_from:
         return traffic_from(*args.traffic_from, args.workload)
+    if args.stats_from:
+        steps = args.steps or (20 if args.workload.startswith("prefill") else 4 * ROTATE)
+        return stats_from(args.stats_from, args.workload, args.profile_cmd, steps)
+    if args.counters_from:
+        return counters_from(args.counters_from, args.workload, args.profile_cmd)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path is "
               f"built and measured for a single MI355X", file=sys.stderr)
@@ -1027,8 +1142,7 @@ def bench_single(w, args, torch, S, k3x, steps, warmup):
     wall, wall_single, mode = graph_timing(torch, step, R, outs, eager, steps, warmup)
 
     # kernel durations: the same steps launched eagerly, HIP events around each launch
-    kernels_per_step = 6 if w.router else 4
-    prof = k3x.k3x_profiler_create(steps * kernels_per_step + 16)
+    prof = k3x.k3x_profiler_create(steps * 16 + 16)
     torch.cuda.synchronize()
     k3x.k3x_profiler_attach(prof)
     t1 = time.perf_counter()
@@ -1043,6 +1157,8 @@ def bench_single(w, args, torch, S, k3x, steps, warmup):
     mean_U = float(np.mean([U[i % R] for i in range(steps)]))
     kernels = {}
     for name, ms in durs.items():
+        if len(ms) != steps:
+            sys.exit(f"profiler recorded {len(ms)} launches of {name} over {steps} steps")
         nbytes, flops = per_kernel_work(name, w.H, w.I, w.E, w.T, w.topk, mean_U)
         avg_s = float(np.mean(ms)) * 1e-3
         kernels[name] = {
