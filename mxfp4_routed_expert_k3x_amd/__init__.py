@@ -299,7 +299,9 @@ def k3x_expert_pool_destroy(pool: Pool):
 # Router
 # ------------------------------------------------------------------------------------------
 def router_desc(weight, bias, topk, renorm=1, routed_scale=1.0) -> k3x_router_desc:
+    """The descriptor holds raw device pointers; it also keeps `weight` and `bias` alive."""
     r = k3x_router_desc()
+    r._keep = (weight, bias)
     r.weight = _ptr(weight)
     r.bias = _ptr(bias)
     r.n_experts = int(weight.shape[0])

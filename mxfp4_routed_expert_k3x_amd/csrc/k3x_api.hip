@@ -359,7 +359,13 @@ k3x_status k3x_route_moe_forward(const k3x_router_desc* r, const k3x_pool* p, co
   float* scores = reinterpret_cast<float*>(w + route_moe_scores_offset(r, p, T));
   const uint16_t* x = static_cast<const uint16_t*>(x_bf16);
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = k3x::launch_route(*r, x, T, idx_out, gates_out, scores, s);
+  hipError_t e;
+  if (!p->contract && k3x::decode_routed_supported(*r, *p, T)) {
+    e = k3x::launch_decode_routed(*r, *p, x, scores, idx_out, gates_out, y, w, s);
+    if (e != hipSuccess) return hip_fail(e, "route_moe_forward");
+    return K3X_OK;
+  }
+  e = k3x::launch_route(*r, x, T, idx_out, gates_out, scores, s);
   if (e == hipSuccess) {
     const k3x::MoeLayout L = k3x::moe_layout(p->E, p->H, p->I, T, r->topk);
     e = k3x::launch_moe(*p, x, T, idx_out, gates_out, r->topk, y, w, L, s);

@@ -33,6 +33,7 @@
 #include <atomic>
 
 #include "k3x_internal.h"
+#include "k3x_select.h"
 
 // Products and sums below are rounded one at a time unless written as an explicit fma.
 #pragma clang fp contract(off)
@@ -162,23 +163,31 @@ __device__ __forceinline__ void wave_rows(int total, int& g0, int& g1) {
   g1 = lo + (int)((int64_t)n * (w + 1) / W);
 }
 
-// Loads row r of one matrix of expert e: wave-uniform row addresses plus per-lane offsets.
-// Lanes past the last group re-read the row's last 16 bytes (and last scale byte); their
-// activations are zero, so their leaves are zero.  The load is unconditional (callers clamp
-// r to a real row), so the loop body has no branches and loads stay in flight across rows.
+// Loads row r of one matrix of expert e through buffer descriptors whose range is the row
+// (the row's bytes, the row's scale bytes): wave-uniform row addresses plus per-lane offsets.
+// Lanes past the last group get an offset beyond the range, so the buffer unit returns zeros
+// for them without a memory request; their activations are zero as well, so their leaves are
+// zero.  The load is unconditional (callers clamp r to a real row), so the loop body has no
+// branches and loads stay in flight across rows.
 struct LaneOffsets {
   uint32_t wa, wb, sa, sb;  // weight bytes and scale bytes of groups L and 64 + L
 };
 
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const uint8_t* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p), 0, bytes, 0x00020000);
+}
+
 __device__ __forceinline__ void load_row(RowBits& b, const uint8_t* wexp, const uint8_t* sexp,
                                          int r, uint32_t wrow, uint32_t srow,
                                          const LaneOffsets& o) {
-  const uint8_t* w = wexp + (size_t)r * wrow;
-  const uint8_t* sc = sexp + (size_t)r * srow;
-  b.q0 = *reinterpret_cast<const uint4*>(w + o.wa);
-  b.q1 = *reinterpret_cast<const uint4*>(w + o.wb);
-  b.s0 = sc[o.sa];
-  b.s1 = sc[o.sb];
+  const __amdgpu_buffer_rsrc_t rw = row_rsrc(wexp + (size_t)r * wrow, wrow);
+  const __amdgpu_buffer_rsrc_t rs = row_rsrc(sexp + (size_t)r * srow, srow);
+  const auto v0 = __builtin_amdgcn_raw_buffer_load_b128(rw, o.wa, 0, 0);
+  const auto v1 = __builtin_amdgcn_raw_buffer_load_b128(rw, o.wb, 0, 0);
+  b.q0 = make_uint4(v0[0], v0[1], v0[2], v0[3]);
+  b.q1 = make_uint4(v1[0], v1[1], v1[2], v1[3]);
+  b.s0 = __builtin_amdgcn_raw_buffer_load_b8(rs, o.sa, 0, 0);
+  b.s1 = __builtin_amdgcn_raw_buffer_load_b8(rs, o.sb, 0, 0);
 }
 
 // Reduce-scatter of eight leaves per vector (rows 0..3 of half A, then rows 0..3 of half B)
@@ -211,15 +220,15 @@ __device__ __forceinline__ void reduce8(float (&v)[NV][8], int lane) {
   }
 }
 
-// Per-lane load offsets of a row of K/32 groups (lanes past the last group point at the
-// row's last 16 bytes and last scale byte).
-__device__ __forceinline__ LaneOffsets lane_offsets(int lane, int ngroups, uint32_t wrow,
-                                                    uint32_t srow) {
+// Per-lane load offsets of a row of K/32 groups (lanes past the last group get an offset
+// outside the row's descriptor range).
+__device__ __forceinline__ LaneOffsets lane_offsets(int lane, int ngroups) {
+  constexpr uint32_t kOutside = 0x40000000u;
   LaneOffsets lo;
-  lo.wa = lane < ngroups ? 16u * lane : wrow - 16u;
-  lo.wb = lane + 64 < ngroups ? 16u * (lane + 64) : wrow - 16u;
-  lo.sa = lane < ngroups ? (uint32_t)lane : srow - 1u;
-  lo.sb = lane + 64 < ngroups ? (uint32_t)lane + 64u : srow - 1u;
+  lo.wa = lane < ngroups ? 16u * lane : kOutside;
+  lo.wb = lane + 64 < ngroups ? 16u * (lane + 64) : kOutside;
+  lo.sa = lane < ngroups ? (uint32_t)lane : kOutside;
+  lo.sb = lane + 64 < ngroups ? (uint32_t)lane + 64u : kOutside;
   return lo;
 }
 
@@ -279,18 +288,45 @@ constexpr int kW13Threads = 256;
 // wave per SIMD.
 constexpr uint32_t kW13LdsLimiter = 96 * 1024;
 
-__global__ __launch_bounds__(kW13Threads) void decode_w13(DecodeArgs a) {
+// With kSel the launch also picks the token's experts: every workgroup runs the router's
+// selection (select_topk_bitonic) on the scores of route_scores while its activations load, and
+// workgroup 0 writes the picks and gates for the W2 launch and the caller.
+struct SelArgs {
+  const float* scores;  // [E] sigmoid scores of the token
+  const float* bias;    // [E] correction bias or NULL
+  int32_t E, renorm;
+  float rscale;
+  int32_t* idx_out;     // [topk]
+  float* gates_out;     // [topk]
+};
+
+template <bool kSel>
+__global__ __launch_bounds__(kW13Threads) void decode_w13(DecodeArgs a, SelArgs sel) {
   const int lane = threadIdx.x % kWave;
-  const int my_idx = lane < a.topk ? a.idx[lane] : -1;
   const int ngroups = a.K / kGroup;
   uint4 xr[8];
   load_act_raw(a.act, lane, ngroups, xr);
+  int my_idx;
+  if constexpr (kSel) {
+    __shared__ int32_t s_idx[kWave];
+    __shared__ float s_gate[kWave];
+    select_topk_bitonic(sel.scores, sel.bias, sel.E, a.topk, sel.renorm, sel.rscale, s_idx,
+                        s_gate);
+    __syncthreads();
+    my_idx = lane < a.topk ? s_idx[lane] : -1;
+    if (blockIdx.x == 0 && threadIdx.x < a.topk) {
+      sel.idx_out[threadIdx.x] = s_idx[threadIdx.x];
+      sel.gates_out[threadIdx.x] = s_gate[threadIdx.x];
+    }
+  } else {
+    my_idx = lane < a.topk ? a.idx[lane] : -1;
+  }
   if (blockIdx.x == 0 && threadIdx.x < kWave) {
     const unsigned long long bad = __ballot(lane < a.topk && !expert_ok(my_idx, a.E));
     if (lane == 0) *reinterpret_cast<int64_t*>(a.ws) = __popcll(bad);
   }
   const uint32_t wrow = (uint32_t)a.K / 2, srow = (uint32_t)ngroups;
-  const LaneOffsets lo = lane_offsets(lane, ngroups, wrow, srow);
+  const LaneOffsets lo = lane_offsets(lane, ngroups);
   int g0, g1;
   wave_rows<kW13Threads>(a.topk * a.rows, g0, g1);
 
@@ -369,7 +405,7 @@ __global__ __launch_bounds__(kW2Waves * kWave) void decode_w2_combine(DecodeArgs
   const int nr = rlast - rb0 + 1;
   const int ngroups = a.K / kGroup;
   const uint32_t wrow = (uint32_t)a.K / 2, srow = (uint32_t)ngroups;
-  const LaneOffsets lo = lane_offsets(lane, ngroups, wrow, srow);
+  const LaneOffsets lo = lane_offsets(lane, ngroups);
 
   float x0[32], x1[32];
   for (int slot = wave; slot < a.topk; slot += kW2Waves) {
@@ -403,7 +439,7 @@ int decode_w13_grid() {
   static std::atomic<int> per_cu{0};
   int n = per_cu.load(std::memory_order_relaxed);
   if (!n) {
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_w13, kW13Threads, kW13LdsLimiter) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_w13<true>, kW13Threads, kW13LdsLimiter) !=
             hipSuccess ||
         n < 1)
       n = 1;
@@ -426,9 +462,13 @@ size_t decode_exact_ws(const k3x_pool& p, int32_t topk, size_t* off_h) {
   return off;
 }
 
-hipError_t launch_decode_exact(const k3x_pool& p, const uint16_t* x, const int32_t* idx,
-                               const float* gates, int32_t topk, float* y, uint8_t* ws,
-                               hipStream_t s) {
+namespace {
+
+// The two launches of the single-token decode; sel.scores set means the W1/W3 launch also
+// selects the experts (a.idx then names where the picks go).
+hipError_t launch_decode(const k3x_pool& p, const uint16_t* x, const int32_t* idx,
+                         const float* gates, int32_t topk, float* y, uint8_t* ws,
+                         const SelArgs& sel, hipStream_t s) {
   size_t off_h;
   decode_exact_ws(p, topk, &off_h);
   DecodeArgs a{};
@@ -451,8 +491,10 @@ hipError_t launch_decode_exact(const k3x_pool& p, const uint16_t* x, const int32
   a.gact = p.act;
   a.b1 = p.b1;
   a.b2 = p.b2;
-  hipError_t err = launch("w13_decode", decode_w13, dim3(decode_w13_grid()), dim3(kW13Threads),
-                          kW13LdsLimiter, s, a);
+  hipError_t err = sel.scores ? launch("w13_decode", decode_w13<true>, dim3(decode_w13_grid()),
+                                       dim3(kW13Threads), kW13LdsLimiter, s, a, sel)
+                              : launch("w13_decode", decode_w13<false>, dim3(decode_w13_grid()),
+                                       dim3(kW13Threads), kW13LdsLimiter, s, a, sel);
   if (err != hipSuccess) return err;
   DecodeArgs b = a;
   b.wa = p.base[4];
@@ -471,6 +513,27 @@ hipError_t launch_decode_exact(const k3x_pool& p, const uint16_t* x, const int32
   const int nblk = (p.H + R - 1) / R;
   return launch("w2_combine_decode", decode_w2_combine, dim3(nblk), dim3(kW2Waves * kWave),
                 (uint32_t)(sizeof(float) * topk * R), s, b, gates, y, R);
+}
+
+}  // namespace
+
+hipError_t launch_decode_exact(const k3x_pool& p, const uint16_t* x, const int32_t* idx,
+                               const float* gates, int32_t topk, float* y, uint8_t* ws,
+                               hipStream_t s) {
+  return launch_decode(p, x, idx, gates, topk, y, ws, SelArgs{}, s);
+}
+
+bool decode_routed_supported(const k3x_router_desc& r, const k3x_pool& p, int32_t T) {
+  return decode_exact_supported(p, T, r.topk) && select_bitonic_supported(r.n_experts, r.topk);
+}
+
+hipError_t launch_decode_routed(const k3x_router_desc& r, const k3x_pool& p, const uint16_t* x,
+                                float* scores, int32_t* idx, float* gates, float* y, uint8_t* ws,
+                                hipStream_t s) {
+  hipError_t err = launch_route_scores(r, x, 1, scores, s);
+  if (err != hipSuccess) return err;
+  const SelArgs sel{scores, r.bias, r.n_experts, r.renorm, r.routed_scale, idx, gates};
+  return launch_decode(p, x, idx, gates, r.topk, y, ws, sel, s);
 }
 
 }  // namespace k3x

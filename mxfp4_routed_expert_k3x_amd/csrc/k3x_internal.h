@@ -164,6 +164,13 @@ size_t decode_exact_ws(const k3x_pool& p, int32_t topk, size_t* off_h);
 hipError_t launch_decode_exact(const k3x_pool& p, const uint16_t* x, const int32_t* idx,
                                const float* gates, int32_t topk, float* y, uint8_t* ws,
                                hipStream_t s);
+// Router and single-token decode in three launches: route_scores, then W1/W3 with the
+// selection run by every workgroup (no separate selection launch), then W2 + combine.  Its
+// picks, gates and y equal launch_route followed by launch_decode_exact, bit for bit.
+bool decode_routed_supported(const k3x_router_desc& r, const k3x_pool& p, int32_t T);
+hipError_t launch_decode_routed(const k3x_router_desc& r, const k3x_pool& p, const uint16_t* x,
+                                float* scores, int32_t* idx, float* gates, float* y, uint8_t* ws,
+                                hipStream_t s);
 // Latent MoE block (k3x_dense.hip): workspace layout and launcher.
 struct LatentLayout {
   size_t scores;  // router scores fp32 [T][E]

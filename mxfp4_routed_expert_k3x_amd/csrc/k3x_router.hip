@@ -13,10 +13,13 @@
 // fixed number of 16-byte chunks per lane) and the block's tokens are staged in LDS while the
 // row is in flight; other widths take a guarded loop that reads the tokens from memory.
 //
-// Kernel 2 (route_select): one workgroup per token.  A radix select finds the selection
-// score of the topk-th expert under the total order (larger c first, then lower index), so
-// ties go to the lower expert and -0 equals +0 as in an IEEE compare; the chosen experts
-// are then put in selection order by their rank.
+// Kernel 2 (route_select): one workgroup per token.  Up to 1024 experts and 16 picks the
+// experts are ranked by sorting networks over (selection key, index) words
+// (select_topk_bitonic, which the fused single-token decode also runs); beyond that a radix
+// select (select_topk) finds the selection score of the topk-th expert under the total order
+// (larger c first, then lower index) on order-preserving integer keys, so ties go to the lower
+// expert and -0 equals +0 as in an IEEE compare, and puts the chosen experts in selection
+// order by their rank.
 #include "k3x_internal.h"
 #include "k3x_select.h"
 
@@ -175,12 +178,27 @@ __global__ __launch_bounds__(kSelThreads) void route_select(const float* __restr
                  gates_out + t * topk);
 }
 
+// The same for up to 1024 experts and 16 picks (select_topk_bitonic, k3x_select.h).
+__global__ __launch_bounds__(kSelThreads) void route_select_bitonic(const float* __restrict__ scores,
+                                                                    const float* __restrict__ bias,
+                                                                    int32_t E, int32_t topk,
+                                                                    int32_t renorm, float rscale,
+                                                                    int32_t* __restrict__ idx_out,
+                                                                    float* __restrict__ gates_out) {
+  const size_t t = blockIdx.x;
+  select_topk_bitonic(scores + t * E, bias, E, topk, renorm, rscale, idx_out + t * topk,
+                      gates_out + t * topk);
+}
+
 }  // namespace
 
 hipError_t launch_route_select(const k3x_router_desc& r, int32_t T, const float* scores,
                                int32_t* idx, float* gates, hipStream_t s) {
   if (T == 0) return hipSuccess;
   const int E = r.n_experts;
+  if (select_bitonic_supported(E, r.topk))
+    return launch("route_select", route_select_bitonic, dim3(T), dim3(kSelThreads), 0, s,
+                  scores, r.bias, E, r.topk, r.renorm, r.routed_scale, idx, gates);
   const uint32_t lds = (uint32_t)(sizeof(float) * 4 * (size_t)r.topk);
   if (E <= kSelThreads * 4)
     return launch("route_select", route_select<4>, dim3(T), dim3(kSelThreads), lds, s, scores,

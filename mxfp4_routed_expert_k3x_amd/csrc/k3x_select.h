@@ -70,6 +70,27 @@ __device__ __forceinline__ void wave_and_or(uint32_t& a, uint32_t& o) {
   o = o_all;
 }
 
+// Thread tid's experts e = tid + 256 m (m < M): the unbiased score sc, the selection score
+// c = sc + bias (zero past E) and whether e < E.  Every load is issued before any is used
+// (indices past E read expert E - 1), so the workgroup waits for memory once.
+template <int M>
+__device__ __forceinline__ void load_scores(const float* __restrict__ s_t,
+                                            const float* __restrict__ bias, int32_t E,
+                                            float (&sc)[M], float (&c)[M], bool (&ok)[M]) {
+  const int tid = threadIdx.x;
+  float sv[M], bv[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) sv[m] = s_t[min(tid + kSelThreads * m, E - 1)];
+#pragma unroll
+  for (int m = 0; m < M; ++m) bv[m] = bias ? bias[min(tid + kSelThreads * m, E - 1)] : 0.0f;
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    ok[m] = tid + kSelThreads * m < E;
+    sc[m] = ok[m] ? sv[m] : 0.0f;
+    c[m] = ok[m] ? sc[m] + bv[m] : 0.0f;
+  }
+}
+
 // One workgroup of 256 threads per token; thread i owns experts i + 256 m (m < M).
 //  1. The key of the topk-th largest selection score is found by a radix select over 8-bit
 //     digits, each pass building a 256-bin LDS histogram of the keys that match the digits
@@ -104,13 +125,10 @@ __device__ __forceinline__ void select_topk(const float* __restrict__ s_t,
 
   float sc[M], c[M];
   uint32_t key[M];
+  bool ok[M];
+  load_scores<M>(s_t, bias, E, sc, c, ok);
 #pragma unroll
-  for (int m = 0; m < M; ++m) {
-    const int e = tid + kSelThreads * m;
-    sc[m] = e < E ? s_t[e] : 0.0f;
-    c[m] = e < E ? sc[m] + (bias ? bias[e] : 0.0f) : 0.0f;
-    key[m] = score_key(c[m]);
-  }
+  for (int m = 0; m < M; ++m) key[m] = score_key(c[m]);
 
   // bits every key shares: their AND equals their OR there
   uint32_t kand = ~0u, kor = 0u;
@@ -283,5 +301,169 @@ __device__ __forceinline__ void select_topk(const float* __restrict__ s_t,
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// The same selection for topk <= 16 and E <= 1024 as sorting networks over registers, with
+// no histogram, atomic or scalar round trip on the way.  Each expert is one 64-bit word:
+// its selection key above, the complement of its index below (0 when absent), so the words
+// order exactly as the picks do (larger selection score first, lower index on ties).
+//  1. Thread tid holds experts tid + 256 m (m < 4); every four lanes hold 16 words and sort
+//     them, largest first, with a bitonic network (element r + 4 (lane & 3) is register r of
+//     that lane; partners two or four elements away sit in the same lane, eight or sixteen
+//     away in the neighbouring lanes of the quad).
+//  2. Two sorted lists of 16 give the 16 largest of their union when each element takes the
+//     larger of itself and the other list's element at the mirrored position (the result is
+//     bitonic), followed by a descending clean-up network.  Merging the quads of a wave in
+//     four such rounds leaves the wave's 16 largest in every quad.
+//  3. Wave 0 merges the four waves' lists the same way; its first topk elements are the
+//     picks in slot order.  The gates follow from the unbiased scores as above.
+// ---------------------------------------------------------------------------------------
+namespace bitonic {
+
+__device__ __forceinline__ uint64_t hi_of(uint64_t a, uint64_t b) { return a > b ? a : b; }
+__device__ __forceinline__ uint64_t lo_of(uint64_t a, uint64_t b) { return a > b ? b : a; }
+
+// Word of the lane whose index is lane ^ X (X < 4: within the quad, by DPP).
+template <int X>
+__device__ __forceinline__ uint64_t quad_xor(uint64_t v) {
+  constexpr int ctrl = X == 1 ? 0xB1 : X == 2 ? 0x4E : 0x1B;  // quad_perm [1032] [2301] [3210]
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)v, ctrl, 0xF, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), ctrl, 0xF, 0xF, false);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Word of lane ^ x for any x < 64 (through the LDS crossbar; no LDS memory is used).
+__device__ __forceinline__ uint64_t lane_xor(uint64_t v, int x) {
+  const int src = ((int)(threadIdx.x % kWave) ^ x) * 4;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)(uint32_t)v);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)(uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// One compare-exchange stage at element distance J within blocks of K (descending where
+// element i has bit K clear; K = 32 means every block descends).  q = lane & 3.
+template <int K, int J>
+__device__ __forceinline__ void stage(uint64_t (&v)[4], int q) {
+  if constexpr (J < 4) {  // partners in the same lane: registers r and r + J
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if (r & J) continue;
+      const int i = r + 4 * q;
+      const bool desc = K >= 32 || (i & K) == 0;
+      const uint64_t a = v[r], b = v[r + J];
+      v[r] = desc ? hi_of(a, b) : lo_of(a, b);
+      v[r + J] = desc ? lo_of(a, b) : hi_of(a, b);
+    }
+  } else {  // partners in lane ^ (J / 4), the same register
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = r + 4 * q;
+      const bool desc = K >= 32 || (i & K) == 0;
+      const bool lower = (i & J) == 0;
+      const uint64_t o = quad_xor<J / 4>(v[r]);
+      v[r] = (lower == desc) ? hi_of(v[r], o) : lo_of(v[r], o);
+    }
+  }
+}
+
+// Sorts the quad's 16 words, largest first.
+__device__ __forceinline__ void sort16(uint64_t (&v)[4], int q) {
+  stage<2, 1>(v, q);
+  stage<4, 2>(v, q);
+  stage<4, 1>(v, q);
+  stage<8, 4>(v, q);
+  stage<8, 2>(v, q);
+  stage<8, 1>(v, q);
+  stage<16, 8>(v, q);
+  stage<16, 4>(v, q);
+  stage<16, 2>(v, q);
+  stage<16, 1>(v, q);
+}
+
+// The 16 largest of this quad's sorted list and that of the quad `dq` quads away (lane
+// distance 4 dq), sorted, in both quads.
+__device__ __forceinline__ void merge16(uint64_t (&v)[4], int q, int dq) {
+  // element i meets element 15 - i of the other list: lane (lane ^ 4 dq) ^ 3, register 3 - r
+  const int x = 4 * dq ^ 3;
+  uint64_t o[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) o[r] = lane_xor(v[3 - r], x);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) v[r] = hi_of(v[r], o[r]);
+  stage<32, 8>(v, q);
+  stage<32, 4>(v, q);
+  stage<32, 2>(v, q);
+  stage<32, 1>(v, q);
+}
+
+}  // namespace bitonic
+
+__host__ __device__ inline bool select_bitonic_supported(int32_t E, int32_t topk) {
+  return E >= 1 && E <= 4 * kSelThreads && topk >= 1 && topk <= 16;
+}
+
+// One 256-thread workgroup, topk <= 16, E <= 1024.  idx_out and gates_out may be global or
+// LDS addresses; every thread of the workgroup must call it.
+__device__ __forceinline__ void select_topk_bitonic(const float* __restrict__ s_t,
+                                                    const float* __restrict__ bias, int32_t E,
+                                                    int32_t topk, int32_t renorm, float rscale,
+                                                    int32_t* idx_out, float* gates_out) {
+  using namespace bitonic;
+  __shared__ float sc_of[4 * kSelThreads];       // unbiased score by expert
+  __shared__ uint64_t best[kSelWaves][16];        // each wave's 16 largest words
+  __shared__ float ranked[16];
+  const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave, q = lane & 3;
+
+  float sc[4], c[4];
+  bool ok[4];
+  load_scores<4>(s_t, bias, E, sc, c, ok);
+  uint64_t v[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int e = tid + kSelThreads * m;
+    if (ok[m]) sc_of[e] = sc[m];
+    v[m] = ok[m] ? ((uint64_t)score_key(c[m]) << 32) | (uint32_t)~(uint32_t)e : 0ull;
+  }
+  sort16(v, q);
+  merge16(v, q, 1);
+  merge16(v, q, 2);
+  merge16(v, q, 4);
+  merge16(v, q, 8);
+  if (lane < 4) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) best[wv][r + 4 * q] = v[r];
+  }
+  __syncthreads();
+  if (wv != 0) return;
+  // quads 0..3 take the lists of waves 0..3 (the other quads empty lists)
+  const int quad = lane >> 2;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) v[r] = quad < kSelWaves ? best[quad][r + 4 * q] : 0ull;
+  merge16(v, q, 1);
+  merge16(v, q, 2);
+  // slot i = element i of quad 0: lane i / 4, register i % 4
+  if (lane < 4) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = r + 4 * q;
+      if (i < topk) {
+        const int e = (int)~(uint32_t)v[r];
+        idx_out[i] = e;
+        ranked[i] = sc_of[e];
+      }
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+  const bool mine = lane < topk;
+  const float rs = mine ? ranked[lane] : 0.0f;
+  float sum = 0.0f;
+  if (renorm)
+    for (int j = 0; j < topk; ++j)
+      sum = sum + __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, rs), j));
+  if (mine) {
+    float w = rs;
+    if (renorm && sum > 0.0f) w = w / sum;
+    gates_out[lane] = w * rscale;
+  }
+}
 
 }  // namespace k3x

@@ -445,7 +445,9 @@ def _route_moe_both(torch, k3x, pool, Wd, bd, xd, T, k, renorm=1, scale=1.0):
 def test_route_moe_forward_equals_separate_calls(dev, orc):
     """Router and experts in one call: idx, gates and y equal the two separate calls bit for
     bit, and the oracle's router and forward; also more than 1024 experts (16 keys per
-    selection thread), no bias, no renormalisation with a routed scale, SiTU-GLU, batches."""
+    selection thread), no bias, no renormalisation with a routed scale, SiTU-GLU, batches,
+    and, for the single-token path that selects inside its W1/W3 launch, 64 picks of 1024
+    and 300 tied selection scores."""
     torch, k3x = dev
     w = S.WORKLOADS[2]
     _log("case: route_moe one token, K3 shape")
@@ -471,11 +473,15 @@ def test_route_moe_forward_equals_separate_calls(dev, orc):
     pool = _pool(torch, k3x, S.device_pool(w.seed, 0, w.E, w.H, w.I), w.E, w.H, w.I, act=SITU)
     _route_moe_both(torch, k3x, pool, Wd, bd, _t(torch, x[:1]), 1, w.topk)
     del pool
-    for E, H, I, k in ((2048, 512, 384, 16), (1025, 256, 256, 64), (64, 512, 512, 8)):
+    for E, H, I, k in ((2048, 512, 384, 16), (1025, 256, 256, 64), (64, 512, 512, 8),
+                       (1024, 512, 256, 64), (700, 256, 256, 16), (700, 256, 256, 64)):
         _log(f"case: route_moe E={E} H={H} I={I} k={k}")
         pool = _pool(torch, k3x, S.device_pool(E, 0, E, H, I), E, H, I)
         W = S.normal_bf16(E, S.P_WR, 0, (E, H), std=0.05)
         b = S.normal_f32(E, S.P_BIAS, 0, (E,), std=0.01)
+        if E == 700:  # 300 equal selection scores: ties go to the lower index
+            W[100:400] = W[100]
+            b[100:400] = 3.0
         x = S.normal_bf16(E, S.P_X, 0, (1, H))
         idx, gates, y = _route_moe_both(torch, k3x, pool, _t(torch, W), _t(torch, b),
                                         _t(torch, x), 1, k)
