@@ -23,13 +23,16 @@
 //
 // Decode is bound by HBM: lane L reads group L of a weight row, then group 64 + L, so each
 // load instruction of a wave covers up to 1 KB of the row contiguously (whole cache lines);
-// dequantization is in registers (gfx950 FP4 -> f32 conversion, two weights per
-// instruction) and nothing dequantized is ever written.  Two launches: W1/W3 (each wave
-// streams a contiguous run of rows over all slots and writes h), then W2 with the weighted
-// combine in its epilogue (each workgroup owns a block of output rows of every slot, so the
-// slot-order sum happens in LDS and the per-slot W2 outputs never reach memory).  Loads run
-// two rows ahead of the arithmetic (three or more measured slower: the launch streams best
-// with few requests in flight per CU).
+// loads go through buffer descriptors whose range is the row, so lanes past its last group
+// issue no request.  Dequantization is in registers (gfx950 FP4 -> f32 conversion, two
+// weights per instruction) and nothing dequantized is ever written.  Two launches: W1/W3
+// (each wave streams a contiguous run of rows over all slots and writes h; called from the
+// router path it first selects the experts itself), then W2 with the weighted combine in its
+// epilogue (each workgroup owns a block of output rows of every slot, so the slot-order sum
+// happens in LDS and the per-slot W2 outputs never reach memory; rows of 65..96 groups share
+// the load of their second halves two rows at a time).  Loads run two rows ahead of the
+// arithmetic (three or more measured slower: the launch streams best with few requests in
+// flight per CU).
 #include <atomic>
 
 #include "k3x_internal.h"
@@ -274,6 +277,154 @@ __device__ __forceinline__ void stream_rows(const uint8_t* wa, const uint8_t* sa
   }
 }
 
+// Rows of 64 < G <= 96 groups (W2 at I = 3072): the second half of a row (groups 64 .. G - 1)
+// has at most 32 groups, so two rows share one load there: lanes 0..31 take groups 64 + L of
+// the even row, lanes 32..63 groups 64 + (L - 32) of the odd row, and every lane's arithmetic
+// is used.  The sums keep the same tree: each row's second half is the subtree of groups
+// 64..95 (lanes of one half-wave, distances 1..16) joined to the zero subtree of groups
+// 96..127 by an explicit + 0, and the root adds the two halves.
+struct PairLanes {
+  uint32_t wa, wb, sa, sb;  // group L of a row; group 64 + (L & 31) of the even / odd row
+};
+
+__device__ __forceinline__ PairLanes pair_lanes(int lane, int ngroups, uint32_t wrow,
+                                                uint32_t srow) {
+  constexpr uint32_t kOutside = 0x40000000u;
+  const int g = 64 + (lane & 31);
+  const bool odd = lane >= 32;
+  PairLanes o;
+  o.wa = 16u * lane;
+  o.sa = (uint32_t)lane;
+  o.wb = g < ngroups ? (odd ? wrow : 0u) + 16u * g : kOutside;
+  o.sb = g < ngroups ? (odd ? srow : 0u) + (uint32_t)g : kOutside;
+  return o;
+}
+
+struct PairBits {
+  uint4 a0, a1, b;        // first halves of the even and odd rows, shared second half
+  uint32_t s0, s1, sb;
+};
+
+// Rows r and r + 1 (r + 1 past rlast: the odd row is absent, its loads return zeros).
+__device__ __forceinline__ void load_pair(PairBits& p, const uint8_t* wexp, const uint8_t* sexp,
+                                          int r, int rlast, uint32_t wrow, uint32_t srow,
+                                          const PairLanes& o) {
+  const int r1 = r + 1 <= rlast ? r + 1 : r;
+  const uint32_t nrows = r1 > r ? 2u : 1u;
+  const __amdgpu_buffer_rsrc_t w0 = row_rsrc(wexp + (size_t)r * wrow, wrow);
+  const __amdgpu_buffer_rsrc_t w1 = row_rsrc(wexp + (size_t)r1 * wrow, wrow);
+  const __amdgpu_buffer_rsrc_t wb = row_rsrc(wexp + (size_t)r * wrow, nrows * wrow);
+  const __amdgpu_buffer_rsrc_t s0 = row_rsrc(sexp + (size_t)r * srow, srow);
+  const __amdgpu_buffer_rsrc_t s1 = row_rsrc(sexp + (size_t)r1 * srow, srow);
+  const __amdgpu_buffer_rsrc_t sb = row_rsrc(sexp + (size_t)r * srow, nrows * srow);
+  const auto v0 = __builtin_amdgcn_raw_buffer_load_b128(w0, o.wa, 0, 0);
+  const auto v1 = __builtin_amdgcn_raw_buffer_load_b128(w1, o.wa, 0, 0);
+  const auto vb = __builtin_amdgcn_raw_buffer_load_b128(wb, o.wb, 0, 0);
+  p.a0 = make_uint4(v0[0], v0[1], v0[2], v0[3]);
+  p.a1 = make_uint4(v1[0], v1[1], v1[2], v1[3]);
+  p.b = make_uint4(vb[0], vb[1], vb[2], vb[3]);
+  p.s0 = __builtin_amdgcn_raw_buffer_load_b8(s0, o.sa, 0, 0);
+  p.s1 = __builtin_amdgcn_raw_buffer_load_b8(s1, o.sa, 0, 0);
+  p.sb = __builtin_amdgcn_raw_buffer_load_b8(sb, o.sb, 0, 0);
+}
+
+// Activations of the paired layout: x0 = group L, x1 = group 64 + (L & 31) (zero past G).
+__device__ __forceinline__ void load_act_raw_pair(const uint16_t* __restrict__ row, int lane,
+                                                  int ngroups, uint4 (&raw)[8]) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int g = min(h ? 64 + (lane & 31) : lane, ngroups - 1);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) raw[4 * h + c] = *reinterpret_cast<const uint4*>(row + 32 * g + 8 * c);
+  }
+}
+
+__device__ __forceinline__ void act_to_f32_pair(const uint4 (&raw)[8], int lane, int ngroups,
+                                                float (&x0)[32], float (&x1)[32]) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const bool ok = (h ? 64 + (lane & 31) : lane) < ngroups;
+    float* dst = h ? x1 : x0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      uint4 v = raw[4 * h + c];
+      asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        dst[8 * c + 2 * j] = ok ? bf16_bits_to_f32(w[j] & 0xFFFFu) : 0.0f;
+        dst[8 * c + 2 * j + 1] = ok ? bf16_bits_to_f32(w[j] >> 16) : 0.0f;
+      }
+    }
+  }
+}
+
+// Four rows from two pairs: A[r] = first-half leaves of row r, B[0] = second halves of rows 0
+// (lanes 0..31) and 1 (lanes 32..63), B[1] the same for rows 2 and 3.  Returns, in lane L < 4,
+// the full sum of row L.
+__device__ __forceinline__ float reduce_pairs(const float (&A)[4], const float (&B)[2], int lane) {
+  const bool b0 = lane & 1, b1 = (lane >> 1) & 1;
+  float a[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {  // rows 2j, 2j + 1 -> row 2j + b0
+    const float k = b0 ? A[2 * j + 1] : A[2 * j];
+    const float s = b0 ? A[2 * j] : A[2 * j + 1];
+    a[j] = k + __shfl_xor(s, 1, kWave);
+  }
+  float t;
+  {
+    const float k = b1 ? a[1] : a[0], s = b1 ? a[0] : a[1];
+    t = k + __shfl_xor(s, 2, kWave);  // row L & 3
+  }
+#pragma unroll
+  for (int d = 4; d < kWave; d <<= 1) t = t + __shfl_xor(t, d, kWave);  // first half, row L & 3
+  float u;
+  {
+    const float k = b0 ? B[1] : B[0], s = b0 ? B[0] : B[1];
+    u = k + __shfl_xor(s, 1, kWave);
+  }
+#pragma unroll
+  for (int d = 2; d < 32; d <<= 1) u = u + __shfl_xor(u, d, kWave);  // groups 64..95
+  u = u + 0.0f;  // joined to the zero subtree of groups 96..127
+  // second half of row r sits in lane (r >> 1) + 32 (r & 1)
+  const int r = lane & 3;
+  const float ub = __shfl(u, (r >> 1) + 32 * (r & 1), kWave);
+  return t + ub;
+}
+
+// Streams rows r0 .. rlast of one W2 matrix in the paired layout, one pair loaded ahead of the
+// arithmetic; emit as in stream_rows (sum_b unused).
+template <typename Prep, typename Emit>
+__device__ __forceinline__ void stream_pairs(const uint8_t* wa, const uint8_t* sa, int r0,
+                                             int rlast, uint32_t wrow, uint32_t srow,
+                                             const PairLanes& po, const float (&x0)[32],
+                                             const float (&x1)[32], int lane, Prep prep,
+                                             Emit emit) {
+  PairBits P[2] = {};
+  auto load = [&](int i, int r) {
+    const int rr = r <= rlast ? r : rlast;
+    __builtin_amdgcn_sched_barrier(0);
+    load_pair(P[i], wa, sa, rr, rlast, wrow, srow, po);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  load(0, r0);
+  prep();
+#pragma unroll 1
+  for (int r = r0; r <= rlast; r += 4) {
+    float A[4], B[2];
+    load(1, r + 2);
+    A[0] = group_sum(P[0].a0, x0) * e8m0_to_f32(P[0].s0);
+    A[1] = group_sum(P[0].a1, x0) * e8m0_to_f32(P[0].s1);
+    B[0] = group_sum(P[0].b, x1) * e8m0_to_f32(P[0].sb);
+    load(0, r + 4);
+    A[2] = group_sum(P[1].a0, x0) * e8m0_to_f32(P[1].s0);
+    A[3] = group_sum(P[1].a1, x0) * e8m0_to_f32(P[1].s1);
+    B[1] = group_sum(P[1].b, x1) * e8m0_to_f32(P[1].sb);
+    const float v = reduce_pairs(A, B, lane);
+    emit(r + lane, v, 0.0f, lane < 4 && r + lane <= rlast, min(4, rlast - r + 1));
+  }
+}
+
 // g = W1 x, u = W3 x, h = bf16(silu(g) * u) (or of SiTU-GLU, with each tanh the float nearest
 // to its double value, products and quotients in fp32 left to right) for every (slot, row)
 // of this wave's run.  A run is cut at slot boundaries into segments of one expert; a dropped
@@ -406,20 +557,29 @@ __global__ __launch_bounds__(kW2Waves * kWave) void decode_w2_combine(DecodeArgs
   const int ngroups = a.K / kGroup;
   const uint32_t wrow = (uint32_t)a.K / 2, srow = (uint32_t)ngroups;
   const LaneOffsets lo = lane_offsets(lane, ngroups);
+  const bool paired = ngroups > kWave && ngroups <= kWave + 32;
+  const PairLanes po = pair_lanes(lane, ngroups, wrow, srow);
 
   float x0[32], x1[32];
   for (int slot = wave; slot < a.topk; slot += kW2Waves) {
     const int e = __builtin_amdgcn_readlane(my_idx, slot);
     if (!expert_ok(e, a.E)) continue;
     uint4 hr[8];
-    load_act_raw(a.act + (size_t)slot * a.K, lane, ngroups, hr);
     float* d = dsh + slot * R - rb0;
-    stream_rows<false>(a.wa + (size_t)e * a.st_wa, a.sa + (size_t)e * a.st_sa, nullptr, nullptr,
-                       rb0, rlast, wrow, srow, lo, x0, x1, lane,
-                       [&]() { act_to_f32(hr, lane, ngroups, x0, x1); },
-                       [&](int r, float dv, float, bool valid, int) {
-                         if (valid) d[r] = dv;
-                       });
+    auto park = [&](int r, float dv, float, bool valid, int) {
+      if (valid) d[r] = dv;
+    };
+    if (paired) {
+      load_act_raw_pair(a.act + (size_t)slot * a.K, lane, ngroups, hr);
+      stream_pairs(a.wa + (size_t)e * a.st_wa, a.sa + (size_t)e * a.st_sa, rb0, rlast, wrow,
+                   srow, po, x0, x1, lane,
+                   [&]() { act_to_f32_pair(hr, lane, ngroups, x0, x1); }, park);
+    } else {
+      load_act_raw(a.act + (size_t)slot * a.K, lane, ngroups, hr);
+      stream_rows<false>(a.wa + (size_t)e * a.st_wa, a.sa + (size_t)e * a.st_sa, nullptr,
+                         nullptr, rb0, rlast, wrow, srow, lo, x0, x1, lane,
+                         [&]() { act_to_f32(hr, lane, ngroups, x0, x1); }, park);
+    }
   }
   __syncthreads();
   if (threadIdx.x < nr) {

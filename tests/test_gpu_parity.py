@@ -156,11 +156,14 @@ def test_moe_duplicates_and_drops(dev, orc):
 
 
 @pytest.mark.parametrize("H,I,E,k", [(512, 384, 12, 1), (512, 384, 12, 9), (2560, 2304, 12, 17),
-                                       (2560, 2304, 12, 40), (512, 384, 12, 64)])
+                                       (2560, 2304, 12, 40), (512, 384, 12, 64),
+                                       (768, 2176, 6, 5), (512, 3072, 6, 16)])
 def test_decode_exact_slot_counts(dev, orc, H, I, E, k):
     """Single-token decode with 1 to 64 slots (duplicates and one dropped slot when k > 1):
     every workgroup of the W2 + combine launch takes several slots per wave, and the
-    result equals the fp32 oracle's bit for bit."""
+    result equals the fp32 oracle's bit for bit.  W2 rows of 65 to 96 groups (I = 2176,
+    2304, 3072) share the load of their second halves two rows at a time, including an odd
+    number of rows per workgroup (H = 768: three)."""
     torch, k3x = dev
     _log(f"case: exact decode H={H} I={I} E={E} k={k}")
     host = S.host_pool(11, 0, E, H, I)
