@@ -40,7 +40,9 @@ roofline come from HIP events the library records around each of its launches
 
 The default run (decode_t1_e896_router) also measures the 4096-token prefill
 (prefill_t4096_e896: 896 experts, uniform routing, no router) and reports it in the same line
-under "prefill", with its TFLOP/s against the bf16 MFMA peak (--no-prefill skips it).
+under "prefill", with its TFLOP/s against the bf16 MFMA peak (--no-prefill skips it), and a
+decode batch of 32 tokens through the router with Zipf-skewed expert popularity
+(decode_t32_e896_zipf) under "decode_batch" (--no-batch skips it).
 `cpu_baseline` is the oracle on this host: the median of 3 runs on all of its threads
 (`value`, `cores`) and of 3 on one thread (`value_1core`), with the CPU model.
 """
@@ -65,6 +67,7 @@ TIMED_REGION = ("HIP graph replay: one graph runs the rotated batches in order, 
                 "layers run inside one graph")
 DEFAULT_WORKLOAD = "decode_t1_e896_router"
 PREFILL_WORKLOAD = "prefill_t4096_e896"
+BATCH_WORKLOAD = "decode_t32_e896_zipf"
 ORACLE_ACT = {"swiglu": "swiglu", "situ": ("situ", 4.0, 25.0)}
 COPY_PROBE_BYTES = 1 << 30
 # the kernel sources of the routed path, with the headers they include
@@ -1014,6 +1017,8 @@ def main():
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-batch", action="store_true",
+                    help="skip the 32-token decode batch leg of the default run")
     ap.add_argument("--no-prefill", action="store_true",
                     help="the default run skips its prefill leg (prefill_t4096_e896)")
     ap.add_argument("--prefill-steps", type=int, default=None,
@@ -1074,6 +1079,13 @@ def main():
                                                  "config", "roofline", "path", "kernels",
                                                  "cpu_baseline")}
         out["prefill"]["tflops"] = pre["path"]["tflops_wall"]
+    if args.workload == DEFAULT_WORKLOAD and not args.no_batch and not args.contract:
+        # a decode batch of 32 tokens through the router, experts shared Zipf-fashion
+        torch.cuda.empty_cache()
+        bt = bench_single(wl[BATCH_WORKLOAD], args, torch, S, k3x, None, None)
+        out["decode_batch"] = {k_: bt[k_] for k_ in ("value", "unit", "steps", "warmup",
+                                                     "ms_per_step", "config", "roofline", "path",
+                                                     "kernels", "cpu_baseline")}
     print(json.dumps(out), flush=True)
 
 

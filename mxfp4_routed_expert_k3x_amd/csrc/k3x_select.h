@@ -306,93 +306,101 @@ __device__ __forceinline__ void select_topk(const float* __restrict__ s_t,
 // no histogram, atomic or scalar round trip on the way.  Each expert is one 64-bit word:
 // its selection key above, the complement of its index below (0 when absent), so the words
 // order exactly as the picks do (larger selection score first, lower index on ties).
-//  1. Thread tid holds experts tid + 256 m (m < 4); every four lanes hold 16 words and sort
-//     them, largest first, with a bitonic network (element r + 4 (lane & 3) is register r of
-//     that lane; partners two or four elements away sit in the same lane, eight or sixteen
-//     away in the neighbouring lanes of the quad).
-//  2. Two sorted lists of 16 give the 16 largest of their union when each element takes the
-//     larger of itself and the other list's element at the mirrored position (the result is
-//     bitonic), followed by a descending clean-up network.  Merging the quads of a wave in
-//     four such rounds leaves the wave's 16 largest in every quad.
-//  3. Wave 0 merges the four waves' lists the same way; its first topk elements are the
-//     picks in slot order.  The gates follow from the unbiased scores as above.
+//  1. Thread tid holds experts tid + 256 m (m < 4); every four lanes (a quad) hold 16 words
+//     and sort them with a bitonic network (element r + 4 (lane & 3) is register r of that
+//     lane; partners one or two elements away sit in the same lane, four or eight away in
+//     the neighbouring lanes of the quad).  Quads sort in alternating directions.
+//  2. Two sorted lists of 16 in opposite directions give the 16 largest of their union as
+//     the element-wise larger of the two (a bitonic sequence), sorted by a clean-up network.
+//     Four such rounds, the partner quad 1, 2, 4, 8 quads away and each round's result in the
+//     direction its next partner needs, leave the wave's 16 largest in every quad.
+//  3. Wave 0 merges the four waves' lists the same way (every other list read reversed); its
+//     first topk elements are the picks in slot order.  The gates follow from the unbiased
+//     scores as above.
 // ---------------------------------------------------------------------------------------
 namespace bitonic {
 
-__device__ __forceinline__ uint64_t hi_of(uint64_t a, uint64_t b) { return a > b ? a : b; }
-__device__ __forceinline__ uint64_t lo_of(uint64_t a, uint64_t b) { return a > b ? b : a; }
+__device__ __forceinline__ uint64_t join(uint32_t lo, uint32_t hi) {
+  return ((uint64_t)hi << 32) | lo;
+}
 
-// Word of the lane whose index is lane ^ X (X < 4: within the quad, by DPP).
+// Word of lane ^ X by DPP: X < 4 within the quad (quad_perm), X = 4 or 8 within the row of 16.
 template <int X>
-__device__ __forceinline__ uint64_t quad_xor(uint64_t v) {
-  constexpr int ctrl = X == 1 ? 0xB1 : X == 2 ? 0x4E : 0x1B;  // quad_perm [1032] [2301] [3210]
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)v, ctrl, 0xF, 0xF, false);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), ctrl, 0xF, 0xF, false);
-  return ((uint64_t)hi << 32) | lo;
+__device__ __forceinline__ uint32_t dpp_xor32(uint32_t v) {
+  if constexpr (X == 1 || X == 2 || X == 3) {
+    constexpr int ctrl = X == 1 ? 0xB1 : X == 2 ? 0x4E : 0x1B;  // [1032] [2301] [3210]
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, ctrl, 0xF, 0xF, false);
+  } else if constexpr (X == 8) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false);  // row_ror:8
+  } else {
+    static_assert(X == 4, "lane distance");
+    const uint32_t up = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x104, 0xF, 0xF, false);  // row_shl:4
+    const uint32_t dn = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x114, 0xF, 0xF, false);  // row_shr:4
+    return (threadIdx.x & 4) ? dn : up;
+  }
 }
 
-// Word of lane ^ x for any x < 64 (through the LDS crossbar; no LDS memory is used).
-__device__ __forceinline__ uint64_t lane_xor(uint64_t v, int x) {
-  const int src = ((int)(threadIdx.x % kWave) ^ x) * 4;
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)(uint32_t)v);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)(uint32_t)(v >> 32));
-  return ((uint64_t)hi << 32) | lo;
+template <int X>
+__device__ __forceinline__ uint64_t lane_xor(uint64_t v) {
+  if constexpr (X <= 8) {
+    return join(dpp_xor32<X>((uint32_t)v), dpp_xor32<X>((uint32_t)(v >> 32)));
+  } else {  // across rows: through the LDS crossbar (no LDS memory is used)
+    const int src = ((int)(threadIdx.x % kWave) ^ X) * 4;
+    return join((uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)(uint32_t)v),
+                (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)(uint32_t)(v >> 32)));
+  }
 }
 
-// One compare-exchange stage at element distance J within blocks of K (descending where
-// element i has bit K clear; K = 32 means every block descends).  q = lane & 3.
+// One compare-exchange stage at element distance J within blocks of K; a block descends when
+// element i + 16 flip has bit K clear (K = 32: the whole list descends unless flip).  One
+// compare per pair: equal words are only absent ones (0), for which either order is right.
 template <int K, int J>
-__device__ __forceinline__ void stage(uint64_t (&v)[4], int q) {
-  if constexpr (J < 4) {  // partners in the same lane: registers r and r + J
+__device__ __forceinline__ void stage(uint64_t (&v)[4], int q, int flip) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
+  for (int r = 0; r < 4; ++r) {
+    const int i = r + 4 * q;
+    const bool desc = K >= 32 ? !flip : ((i + 16 * flip) & K) == 0;
+    if constexpr (J < 4) {  // partners in the same lane: registers r and r + J
       if (r & J) continue;
-      const int i = r + 4 * q;
-      const bool desc = K >= 32 || (i & K) == 0;
       const uint64_t a = v[r], b = v[r + J];
-      v[r] = desc ? hi_of(a, b) : lo_of(a, b);
-      v[r + J] = desc ? lo_of(a, b) : hi_of(a, b);
-    }
-  } else {  // partners in lane ^ (J / 4), the same register
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = r + 4 * q;
-      const bool desc = K >= 32 || (i & K) == 0;
-      const bool lower = (i & J) == 0;
-      const uint64_t o = quad_xor<J / 4>(v[r]);
-      v[r] = (lower == desc) ? hi_of(v[r], o) : lo_of(v[r], o);
+      const bool swap = (a < b) == desc;  // descending wants a >= b, ascending a <= b
+      v[r] = swap ? b : a;
+      v[r + J] = swap ? a : b;
+    } else {  // partners in lane ^ (J / 4), the same register
+      const bool want_hi = ((i & J) == 0) == desc;
+      const uint64_t o = lane_xor<J / 4>(v[r]);
+      v[r] = ((v[r] < o) == want_hi) ? o : v[r];
     }
   }
 }
 
-// Sorts the quad's 16 words, largest first.
-__device__ __forceinline__ void sort16(uint64_t (&v)[4], int q) {
-  stage<2, 1>(v, q);
-  stage<4, 2>(v, q);
-  stage<4, 1>(v, q);
-  stage<8, 4>(v, q);
-  stage<8, 2>(v, q);
-  stage<8, 1>(v, q);
-  stage<16, 8>(v, q);
-  stage<16, 4>(v, q);
-  stage<16, 2>(v, q);
-  stage<16, 1>(v, q);
+// Sorts the quad's 16 words, largest first (smallest first when flip).
+__device__ __forceinline__ void sort16(uint64_t (&v)[4], int q, int flip) {
+  stage<2, 1>(v, q, flip);
+  stage<4, 2>(v, q, flip);
+  stage<4, 1>(v, q, flip);
+  stage<8, 4>(v, q, flip);
+  stage<8, 2>(v, q, flip);
+  stage<8, 1>(v, q, flip);
+  stage<16, 8>(v, q, flip);
+  stage<16, 4>(v, q, flip);
+  stage<16, 2>(v, q, flip);
+  stage<16, 1>(v, q, flip);
 }
 
-// The 16 largest of this quad's sorted list and that of the quad `dq` quads away (lane
-// distance 4 dq), sorted, in both quads.
-__device__ __forceinline__ void merge16(uint64_t (&v)[4], int q, int dq) {
-  // element i meets element 15 - i of the other list: lane (lane ^ 4 dq) ^ 3, register 3 - r
-  const int x = 4 * dq ^ 3;
-  uint64_t o[4];
+// The 16 largest of this quad's list and that of the quad DQ quads away (sorted in opposite
+// directions), sorted ascending when flip, in both quads.
+template <int DQ>
+__device__ __forceinline__ void merge16(uint64_t (&v)[4], int q, int flip) {
 #pragma unroll
-  for (int r = 0; r < 4; ++r) o[r] = lane_xor(v[3 - r], x);
-#pragma unroll
-  for (int r = 0; r < 4; ++r) v[r] = hi_of(v[r], o[r]);
-  stage<32, 8>(v, q);
-  stage<32, 4>(v, q);
-  stage<32, 2>(v, q);
-  stage<32, 1>(v, q);
+  for (int r = 0; r < 4; ++r) {
+    const uint64_t o = lane_xor<4 * DQ>(v[r]);
+    v[r] = v[r] < o ? o : v[r];
+  }
+  stage<32, 8>(v, q, flip);
+  stage<32, 4>(v, q, flip);
+  stage<32, 2>(v, q, flip);
+  stage<32, 1>(v, q, flip);
 }
 
 }  // namespace bitonic
@@ -409,9 +417,10 @@ __device__ __forceinline__ void select_topk_bitonic(const float* __restrict__ s_
                                                     int32_t* idx_out, float* gates_out) {
   using namespace bitonic;
   __shared__ float sc_of[4 * kSelThreads];       // unbiased score by expert
-  __shared__ uint64_t best[kSelWaves][16];        // each wave's 16 largest words
+  __shared__ uint64_t best[kSelWaves][16];        // each wave's 16 largest words, descending
   __shared__ float ranked[16];
   const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave, q = lane & 3;
+  const int quad = lane >> 2;
 
   float sc[4], c[4];
   bool ok[4];
@@ -421,25 +430,29 @@ __device__ __forceinline__ void select_topk_bitonic(const float* __restrict__ s_
   for (int m = 0; m < 4; ++m) {
     const int e = tid + kSelThreads * m;
     if (ok[m]) sc_of[e] = sc[m];
-    v[m] = ok[m] ? ((uint64_t)score_key(c[m]) << 32) | (uint32_t)~(uint32_t)e : 0ull;
+    v[m] = ok[m] ? join(~(uint32_t)e, score_key(c[m])) : 0ull;
   }
-  sort16(v, q);
-  merge16(v, q, 1);
-  merge16(v, q, 2);
-  merge16(v, q, 4);
-  merge16(v, q, 8);
+  // a quad's list runs in the direction its next partner needs: bit l of the quad index
+  // before the round with partner 2^l quads away
+  sort16(v, q, quad & 1);
+  merge16<1>(v, q, (quad >> 1) & 1);
+  merge16<2>(v, q, (quad >> 2) & 1);
+  merge16<4>(v, q, (quad >> 3) & 1);
+  merge16<8>(v, q, 0);
   if (lane < 4) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) best[wv][r + 4 * q] = v[r];
   }
   __syncthreads();
   if (wv != 0) return;
-  // quads 0..3 take the lists of waves 0..3 (the other quads empty lists)
-  const int quad = lane >> 2;
+  // quads 0..3 take the lists of waves 0..3, odd ones reversed (ascending); other quads empty
 #pragma unroll
-  for (int r = 0; r < 4; ++r) v[r] = quad < kSelWaves ? best[quad][r + 4 * q] : 0ull;
-  merge16(v, q, 1);
-  merge16(v, q, 2);
+  for (int r = 0; r < 4; ++r) {
+    const int i = r + 4 * q;
+    v[r] = quad < kSelWaves ? best[quad][(quad & 1) ? 15 - i : i] : 0ull;
+  }
+  merge16<1>(v, q, (quad >> 1) & 1);
+  merge16<2>(v, q, 0);
   // slot i = element i of quad 0: lane i / 4, register i % 4
   if (lane < 4) {
 #pragma unroll
@@ -453,14 +466,19 @@ __device__ __forceinline__ void select_topk_bitonic(const float* __restrict__ s_
     }
   }
   __builtin_amdgcn_wave_barrier();
-  const bool mine = lane < topk;
-  const float rs = mine ? ranked[lane] : 0.0f;
+  // every lane forms the slot-order sum from its own copy of the picks' scores (one LDS read
+  // of all sixteen, then the additions in order)
+  float rk[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) rk[j] = ranked[j];  // entries past topk are not used
   float sum = 0.0f;
-  if (renorm)
-    for (int j = 0; j < topk; ++j)
-      sum = sum + __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, rs), j));
-  if (mine) {
-    float w = rs;
+  if (renorm) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (j < topk) sum = sum + rk[j];
+  }
+  if (lane < topk) {
+    float w = ranked[lane];
     if (renorm && sum > 0.0f) w = w / sum;
     gates_out[lane] = w * rscale;
   }
