@@ -192,14 +192,13 @@ int prefill_tile_tokens();
 hipError_t launch_prefill_gemms(const k3x_pool& p, const uint16_t* x, int32_t T, int32_t topk, uint8_t* ws,
                                 const MoeLayout& L, hipStream_t s);
 
-// True when a batch has enough slots per expert (16 on average) for the prefill kernels and
-// the shapes fit their tiling (hidden a multiple of 256).
+// True when the sorted-tile kernels take the batch: two or more tokens, hidden and inter
+// multiples of 512, K <= 4096 and 32-bit row offsets.
 inline bool use_prefill(int32_t E, int32_t H, int32_t I, int32_t T, int32_t topk) {
-  // Every batch of two or more tokens whose shapes the sorted-tile kernels take: tiles of 96
-  // slots; items of 256 h rows (W1/W3) or 512 d rows (W2); the item's scale rows (K / 32
-  // bytes each, K <= 4096) fit in LDS; 32-bit row offsets.  (They also stream the weights of
-  // lightly shared experts faster than the 16-slot tiles.)  A single token takes the exact
-  // decode path before this is asked.
+  // Tiles of 96 slots; items of 128 h rows (W1/W3) or 256 d rows (W2); the item's scale rows
+  // (K / 32 bytes each, K <= 4096) fit in LDS.  (They also stream the weights of lightly
+  // shared experts faster than the 16-slot tiles.)  A single token takes the exact decode
+  // path before this is asked.
   (void)E;
   const int64_t slots = (int64_t)T * topk;
   return T >= 2 && H % 512 == 0 && I % 512 == 0 && H <= 4096 && I <= 4096 &&
