@@ -376,10 +376,13 @@ def test_router_many_equal_scores(dev, orc):
 
 def test_router_selection_paths(dev, orc):
     """Selection at the boundaries of its register layouts (E up to 1024 and beyond, topk up
-    to 64 and beyond), ragged token counts, and biases that make +0 and -0 selection
-    scores compare equal."""
+    to 64 and beyond; the sorting-network selection's limits E <= 1024, topk <= 16, with
+    fewer experts than one quad's 16 words, one wave's 256 and the workgroup's 1024), ragged
+    token counts, and biases that make +0 and -0 selection scores compare equal."""
     torch, k3x = dev
-    for E, k, T in ((1024, 64, 7), (1024, 65, 3), (1025, 16, 5), (64, 64, 6), (2048, 16, 9)):
+    for E, k, T in ((1024, 64, 7), (1024, 65, 3), (1025, 16, 5), (64, 64, 6), (2048, 16, 9),
+                    (1024, 16, 4), (1, 1, 2), (5, 5, 3), (16, 16, 2), (17, 16, 2), (256, 16, 3),
+                    (257, 1, 2), (300, 17, 2)):
         _log(f"case: router selection E={E} topk={k} T={T}")
         H = 256
         W = S.normal_bf16(E + k, S.P_WR, 0, (E, H), std=0.05)
