@@ -967,7 +967,9 @@ def counters_from(paths, workload, command, n_xcd=8, n_simd=1024):
              f"Derived: mfma_util = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / {n_xcd} * {n_simd} SIMDs);",
              "mfma_tflops = SQ_INSTS_VALU_MFMA_MOPS_BF16 * 512 / duration; lds_conflict = SQ_LDS_BANK_CONFLICT /",
              "SQ_LDS_IDX_ACTIVE; valu_per_mfma = (SQ_INSTS_VALU - SQ_INSTS_MFMA) / SQ_INSTS_MFMA; wait_frac =",
-             "SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES; clock_ghz = GRBM_GUI_ACTIVE / n_xcd / duration.", ""]
+             "SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES; clock_ghz = GRBM_GUI_ACTIVE / n_xcd / duration (clock and",
+             "MFMA use only for dispatches of 100 us or more: GRBM_GUI_ACTIVE spans the counter window, a few",
+             "microseconds more than the dispatch).  duration = the counter run's own dispatch times.", ""]
     for lab in sorted(acc):
         d = {k: float(np.mean(v)) for k, v in acc[lab].items()}
         dur = d.pop("dur")
@@ -976,7 +978,9 @@ def counters_from(paths, workload, command, n_xcd=8, n_simd=1024):
             lines.append(f"  {k} {d[k]:.6g}")
         der = []
         g = d.get("GRBM_GUI_ACTIVE")
-        if g:
+        # GRBM_GUI_ACTIVE spans the counter window, a few microseconds more than a dispatch, so
+        # the clock and the MFMA use are derived only for dispatches of 100 us or more
+        if g and dur >= 100e-6:
             der.append(f"clock_ghz={g / n_xcd / dur / 1e9:.3f}")
             if "SQ_VALU_MFMA_BUSY_CYCLES" in d:
                 der.append(f"mfma_util={d['SQ_VALU_MFMA_BUSY_CYCLES'] / (g / n_xcd * n_simd):.3f}")
