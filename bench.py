@@ -903,8 +903,9 @@ def _kernel_label(name):
     for label, sym in KERNEL_SYMBOLS.items():
         if sym in name:
             return label
-    for sym in ("moe_combine", "moe_sort", "sort_count", "sort_scan", "sort_scatter", "rmsnorm",
-                "residual", "fill_packed", "fill_scale", "combine_contract"):
+    for sym in ("moe_combine", "moe_sort", "sort_count", "sort_scan", "sort_scatter",
+                "residual_rmsnorm", "rmsnorm", "residual", "latent_in", "latent_out", "w13_contract",
+                "w2_contract", "fill_packed", "fill_scale", "combine_contract"):
         if sym in name:
             return sym
     return name[:60]
