@@ -407,7 +407,9 @@ def chain_cpu_baseline(w, x, layers, budget_s=12.0, act="swiglu"):
 
 def bench_chain(w, args, torch, S, k3x):
     """One decode token through w.layers MoE layers, every layer's experts resident in HBM:
-    RMSNorm -> router -> experts -> residual add per layer, one HIP graph per starting token."""
+    RMSNorm -> router -> experts -> residual add per layer, one HIP graph per starting token.
+    Each layer is one k3x_residual_route_moe_forward call (the previous layer's residual
+    update and this layer's RMSNorm run inside the router's scores launch)."""
     steps = args.steps if args.steps is not None else 50
     warmup = args.warmup if args.warmup is not None else 5
     torch.cuda.set_device(0)
@@ -432,29 +434,31 @@ def bench_chain(w, args, torch, S, k3x):
     R = ROTATE
     x = S.normal_bf16(w.seed, S.P_X, 0, (R, w.H))
     xs = [torch.from_numpy(x[r:r + 1].view(np.int16)).to(dev) for r in range(R)]
-    xb = torch.empty((1, w.H), dtype=torch.int16, device=dev)   # residual stream
-    xn = torch.empty_like(xb)
+    # the residual stream takes turns between two buffers (a layer's update must not write
+    # the x it reads); y is both the previous layer's output and this layer's
+    xbuf = [torch.empty((1, w.H), dtype=torch.int16, device=dev) for _ in range(2)]
+    xn = torch.empty_like(xbuf[0])
     idx = torch.empty((1, w.topk), dtype=torch.int32, device=dev)
     gates = torch.empty((1, w.topk), dtype=torch.float32, device=dev)
     y = torch.empty((1, w.H), dtype=torch.float32, device=dev)
-    # router + experts in one call per layer
     ws = k3x.alloc_workspace(
         k3x.k3x_route_moe_workspace_size(layers[0]["rdesc"], layers[0]["pool"], 1), dev)
 
     def step(r):
-        # layer l's residual update and layer l + 1's RMSNorm are one fused launch
-        xb.copy_(xs[r])
-        k3x.k3x_rmsnorm_bf16(xb, 1, w.H, 1e-6, xn)
+        x_cur = xs[r]
         for li, lay in enumerate(layers):
-            k3x.k3x_route_moe_forward(lay["rdesc"], lay["pool"], xn, 1, idx, gates, y, ws)
-            if li + 1 < len(layers):
-                k3x.k3x_residual_add_rmsnorm_bf16(xb, y, 1, w.H, 1e-6, xn)
-            else:
-                k3x.k3x_residual_add_bf16(xb, y, 1, w.H)
+            x_next = xbuf[0] if x_cur is not xbuf[0] else xbuf[1]
+            k3x.k3x_residual_route_moe_forward(lay["rdesc"], lay["pool"], x_cur,
+                                               y if li else None, 1e-6,
+                                               x_next if li else None, xn, 1, idx, gates, y, ws)
+            if li:
+                x_cur = x_next
+        k3x.k3x_residual_add_bf16(x_cur, y, 1, w.H)
+        return x_cur
 
     out_eager = []
     for r in range(R):
-        step(r)
+        xb = step(r)
         torch.cuda.synchronize()
         out_eager.append(xb.clone())
     if k3x.k3x_fetch_drops(ws):

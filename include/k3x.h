@@ -172,6 +172,30 @@ k3x_status k3x_route_moe_forward(const k3x_router_desc *r, const k3x_pool *p, co
                                  int32_t T, int32_t *idx_out, float *gates_out, float *y,
                                  void *ws, size_t ws_bytes, void *stream);
 
+/* The previous layer's residual update and this layer's RMSNorm (README section 5, "Kernels
+ * with a floating point contract"), then the router and the experts (README Part II section
+ * 9), in one call:
+ *   x_next = bf16_rne(float(x) + y_prev)       (when y_prev != NULL; else x_next = x, unwritten)
+ *   xn     = RMSNorm(x_next), unit weight, eps (as k3x_rmsnorm_bf16)
+ *   idx_out, gates_out, y = k3x_route_moe_forward on xn.
+ * All four outputs equal those of k3x_residual_add_rmsnorm_bf16 (or k3x_rmsnorm_bf16 when
+ * y_prev is NULL) followed by k3x_route_moe_forward, bit for bit.  At one token, when the
+ * single-token decode applies, the update and the norm run inside the router's scores launch
+ * (three launches per layer instead of four).
+ * x bf16 [T][hidden] (read only); y_prev fp32 [T][hidden] or NULL (the first layer);
+ * x_next bf16 [T][hidden] (written when y_prev != NULL, may be NULL otherwise); xn bf16
+ * [T][hidden] (written: the router's and experts' input, for a caller that also needs it);
+ * idx_out, gates_out, y, ws, ws_bytes as k3x_route_moe_forward (same workspace size).  y may
+ * be y_prev: a chain of layers can pass one y buffer and swap two x buffers.  x_next must not
+ * overlap x, y_prev or xn, and xn must not overlap x, y_prev or y (K3X_E_INVALID_ARG); all
+ * pointers 16-byte aligned, hidden a multiple of 8 and <= 16384 (K3X_E_UNSUPPORTED).  Other
+ * errors as k3x_route_moe_forward; T = 0 only resets the drop counter. */
+k3x_status k3x_residual_route_moe_forward(const k3x_router_desc *r, const k3x_pool *p,
+                                          const void *x_bf16, const float *y_prev, float eps,
+                                          void *x_next_bf16, void *xn_bf16, int32_t T,
+                                          int32_t *idx_out, float *gates_out, float *y, void *ws,
+                                          size_t ws_bytes, void *stream);
+
 /* For callers that cannot allocate device memory (code under HIP graph capture, tight
  * serving loops, harnesses that forbid allocation): k3x_moe_forward with its workspace in a
  * scratch array built into the library instead of a caller's buffer.  Each GPU the library

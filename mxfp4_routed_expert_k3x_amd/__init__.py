@@ -111,7 +111,7 @@ EXPORTS = (
     "k3x_moe_forward_noalloc",
     "k3x_fetch_drops", "k3x_rmsnorm_bf16", "k3x_residual_add_bf16", "k3x_residual_add_rmsnorm_bf16",
     "k3x_latent_workspace_size", "k3x_latent_forward", "k3x_latent_ws_layout",
-    "k3x_route_moe_workspace_size", "k3x_route_moe_forward",
+    "k3x_route_moe_workspace_size", "k3x_route_moe_forward", "k3x_residual_route_moe_forward",
     "k3x_expert_bytes", "k3x_arena_create", "k3x_arena_destroy", "k3x_arena_last_error",
     "k3x_arena_pool", "k3x_arena_getmany", "k3x_arena_pin", "k3x_arena_stats",
     "k3x_arena_moe_forward", "k3x_cache_replay", "k3x_cache_replay_batches",
@@ -163,6 +163,9 @@ def load_library(path: str = LIB_PATH):
     L.k3x_route_moe_workspace_size.argtypes = [RD, P, I32]
     L.k3x_route_moe_forward.restype = ctypes.c_int
     L.k3x_route_moe_forward.argtypes = [RD, P, P, I32, P, P, P, P, SZ, P]
+    L.k3x_residual_route_moe_forward.restype = ctypes.c_int
+    L.k3x_residual_route_moe_forward.argtypes = [RD, P, P, P, ctypes.c_float, P, P, I32, P, P, P,
+                                                 P, SZ, P]
     L.k3x_latent_workspace_size.restype = SZ
     L.k3x_latent_workspace_size.argtypes = [LD, P, RD, I32]
     L.k3x_latent_ws_layout.restype = ctypes.c_int
@@ -345,6 +348,17 @@ def k3x_route_moe_forward(r: k3x_router_desc, pool: Pool, x, T: int, idx_out, ga
     _check(lib().k3x_route_moe_forward(ctypes.byref(r), pool.handle, _ptr(x), int(T),
                                        _ptr(idx_out), _ptr(gates_out), _ptr(y), _ptr(ws),
                                        int(nbytes), _stream(stream)))
+
+
+def k3x_residual_route_moe_forward(r: k3x_router_desc, pool: Pool, x, y_prev, eps: float, x_next,
+                                   xn, T: int, idx_out, gates_out, y, ws, ws_bytes=None,
+                                   stream=None):
+    """y_prev and x_next may be None (the first layer: RMSNorm of x alone)."""
+    nbytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    _check(lib().k3x_residual_route_moe_forward(
+        ctypes.byref(r), pool.handle, _ptr(x), _ptr(y_prev), float(eps), _ptr(x_next), _ptr(xn),
+        int(T), _ptr(idx_out), _ptr(gates_out), _ptr(y), _ptr(ws), int(nbytes),
+        _stream(stream)))
 
 
 K3X_NOALLOC_SCRATCH_BYTES = 32 << 20

@@ -335,6 +335,20 @@ size_t k3x_route_moe_workspace_size(const k3x_router_desc* r, const k3x_pool* p,
   return route_moe_scores_offset(r, p, T) + k3x_route_workspace_size(r, T);
 }
 
+// Router and experts after the checks: the fused single-token decode when it applies, else
+// the router's two launches and the experts' path for T tokens.
+static hipError_t route_moe_run(const k3x_router_desc* r, const k3x_pool* p, const uint16_t* x,
+                                int32_t T, int32_t* idx_out, float* gates_out, float* y,
+                                uint8_t* w, hipStream_t s) {
+  float* scores = reinterpret_cast<float*>(w + route_moe_scores_offset(r, p, T));
+  if (!p->contract && k3x::decode_routed_supported(*r, *p, T))
+    return k3x::launch_decode_routed(*r, *p, x, scores, idx_out, gates_out, y, w, s);
+  hipError_t e = k3x::launch_route(*r, x, T, idx_out, gates_out, scores, s);
+  if (e != hipSuccess) return e;
+  const k3x::MoeLayout L = k3x::moe_layout(p->E, p->H, p->I, T, r->topk);
+  return k3x::launch_moe(*p, x, T, idx_out, gates_out, r->topk, y, w, L, s);
+}
+
 k3x_status k3x_route_moe_forward(const k3x_router_desc* r, const k3x_pool* p, const void* x_bf16,
                                  int32_t T, int32_t* idx_out, float* gates_out, float* y,
                                  void* ws, size_t ws_bytes, void* stream) {
@@ -355,22 +369,62 @@ k3x_status k3x_route_moe_forward(const k3x_router_desc* r, const k3x_pool* p, co
     return fail(K3X_E_INVALID_ARG, "route_moe_forward: NULL x, idx, gates or y");
   if (!aligned(x_bf16, 16) || !aligned(y, 16))
     return fail(K3X_E_UNSUPPORTED, "route_moe_forward: x and y must be 16-byte aligned");
-  uint8_t* w = static_cast<uint8_t*>(ws);
-  float* scores = reinterpret_cast<float*>(w + route_moe_scores_offset(r, p, T));
+  hipError_t e = route_moe_run(r, p, static_cast<const uint16_t*>(x_bf16), T, idx_out, gates_out,
+                               y, static_cast<uint8_t*>(ws), (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "route_moe_forward");
+  return K3X_OK;
+}
+
+static bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
+  const uintptr_t ao = (uintptr_t)a, bo = (uintptr_t)b;
+  return a && b && ao < bo + bn && bo < ao + an;
+}
+
+k3x_status k3x_residual_route_moe_forward(const k3x_router_desc* r, const k3x_pool* p,
+                                          const void* x_bf16, const float* y_prev, float eps,
+                                          void* x_next_bf16, void* xn_bf16, int32_t T,
+                                          int32_t* idx_out, float* gates_out, float* y, void* ws,
+                                          size_t ws_bytes, void* stream) {
+  k3x_status st = check_route_moe(r, p, T);
+  if (st != K3X_OK) return st;
+  const int32_t H = p->H;
+  if (H % 8 || H > 16384)
+    return fail(K3X_E_UNSUPPORTED, "residual_route_moe: H %d must be a multiple of 8, <= 16384", H);
+  const size_t need = k3x_route_moe_workspace_size(r, p, T);
+  if (!ws || ws_bytes < need || !aligned(ws, 256))
+    return fail(K3X_E_WORKSPACE,
+                "residual_route_moe: workspace %zu bytes, need %zu (256-byte aligned)", ws_bytes,
+                need);
+  if (T == 0) return k3x_route_moe_forward(r, p, nullptr, 0, nullptr, nullptr, nullptr, ws,
+                                           ws_bytes, stream);
+  if (!x_bf16 || !xn_bf16 || !idx_out || !gates_out || !y || (y_prev && !x_next_bf16))
+    return fail(K3X_E_INVALID_ARG, "residual_route_moe: NULL x, x_next, xn, idx, gates or y");
+  if (!aligned(x_bf16, 16) || !aligned(y_prev, 16) || !aligned(x_next_bf16, 16) ||
+      !aligned(xn_bf16, 16) || !aligned(y, 16))
+    return fail(K3X_E_UNSUPPORTED, "residual_route_moe: 16-byte alignment");
+  const size_t xb = (size_t)T * H * 2, yb = (size_t)T * H * 4;
+  void* x_next = y_prev ? x_next_bf16 : nullptr;
+  if (overlaps(x_next, xb, x_bf16, xb) || overlaps(x_next, xb, y_prev, yb) ||
+      overlaps(x_next, xb, xn_bf16, xb) || overlaps(xn_bf16, xb, x_bf16, xb) ||
+      overlaps(xn_bf16, xb, y_prev, yb) || overlaps(xn_bf16, xb, y, yb))
+    return fail(K3X_E_INVALID_ARG, "residual_route_moe: x_next or xn overlaps another operand");
   const uint16_t* x = static_cast<const uint16_t*>(x_bf16);
+  uint16_t* xn = static_cast<uint16_t*>(xn_bf16);
+  uint8_t* w = static_cast<uint8_t*>(ws);
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
-  if (!p->contract && k3x::decode_routed_supported(*r, *p, T)) {
-    e = k3x::launch_decode_routed(*r, *p, x, scores, idx_out, gates_out, y, w, s);
-    if (e != hipSuccess) return hip_fail(e, "route_moe_forward");
-    return K3X_OK;
+  if (!p->contract && k3x::decode_routed_residual_supported(*r, *p, T)) {
+    float* scores = reinterpret_cast<float*>(w + route_moe_scores_offset(r, p, T));
+    e = k3x::launch_decode_routed_residual(*r, *p, x, y_prev, eps,
+                                           static_cast<uint16_t*>(x_next), xn, scores, idx_out,
+                                           gates_out, y, w, s);
+  } else {
+    e = y_prev ? k3x::launch_residual_rmsnorm(x, y_prev, T, H, eps,
+                                              static_cast<uint16_t*>(x_next), xn, s)
+               : k3x::launch_rmsnorm(x, T, H, eps, xn, s);
+    if (e == hipSuccess) e = route_moe_run(r, p, xn, T, idx_out, gates_out, y, w, s);
   }
-  e = k3x::launch_route(*r, x, T, idx_out, gates_out, scores, s);
-  if (e == hipSuccess) {
-    const k3x::MoeLayout L = k3x::moe_layout(p->E, p->H, p->I, T, r->topk);
-    e = k3x::launch_moe(*p, x, T, idx_out, gates_out, r->topk, y, w, L, s);
-  }
-  if (e != hipSuccess) return hip_fail(e, "route_moe_forward");
+  if (e != hipSuccess) return hip_fail(e, "residual_route_moe");
   return K3X_OK;
 }
 
@@ -421,7 +475,8 @@ k3x_status k3x_residual_add_rmsnorm_bf16(void* x, const float* y, int32_t T, int
   const uintptr_t xo = (uintptr_t)x, yo = (uintptr_t)y, oo = (uintptr_t)out;
   if ((oo < xo + xb && xo < oo + xb) || (oo < yo + yb && yo < oo + xb))
     return fail(K3X_E_INVALID_ARG, "residual_add_rmsnorm: out overlaps x or y");
-  hipError_t e = k3x::launch_residual_rmsnorm(static_cast<uint16_t*>(x), y, T, H, eps,
+  hipError_t e = k3x::launch_residual_rmsnorm(static_cast<const uint16_t*>(x), y, T, H, eps,
+                                              static_cast<uint16_t*>(x),
                                               static_cast<uint16_t*>(out), (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "residual_add_rmsnorm");
   return K3X_OK;

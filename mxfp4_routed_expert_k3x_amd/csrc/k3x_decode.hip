@@ -696,4 +696,19 @@ hipError_t launch_decode_routed(const k3x_router_desc& r, const k3x_pool& p, con
   return launch_decode(p, x, idx, gates, r.topk, y, ws, sel, s);
 }
 
+bool decode_routed_residual_supported(const k3x_router_desc& r, const k3x_pool& p, int32_t T) {
+  return decode_routed_supported(r, p, T) && route_scores_residual_supported(r, T);
+}
+
+hipError_t launch_decode_routed_residual(const k3x_router_desc& r, const k3x_pool& p,
+                                         const uint16_t* x, const float* y_prev, float eps,
+                                         uint16_t* x_next, uint16_t* xn, float* scores,
+                                         int32_t* idx, float* gates, float* y, uint8_t* ws,
+                                         hipStream_t s) {
+  hipError_t err = launch_route_scores_residual(r, x, y_prev, eps, x_next, xn, scores, s);
+  if (err != hipSuccess) return err;
+  const SelArgs sel{scores, r.bias, r.n_experts, r.renorm, r.routed_scale, idx, gates};
+  return launch_decode(p, xn, idx, gates, r.topk, y, ws, sel, s);
+}
+
 }  // namespace k3x

@@ -143,6 +143,15 @@ hipError_t launch_route(const k3x_router_desc& r, const uint16_t* x, int32_t T, 
 // The sigmoid scores alone (fp32 [T][E]).
 hipError_t launch_route_scores(const k3x_router_desc& r, const uint16_t* x, int32_t T,
                                float* scores, hipStream_t s);
+// One token's scores with the hidden-state update and RMSNorm before the router folded in:
+// x_next = bf16(x + y_prev) (skipped when y_prev is NULL; x_next may then be NULL too), xn =
+// the RMSNorm of that (unit weight, eps), scores = the router's scores of xn; all three equal
+// those of launch_residual_rmsnorm (or launch_rmsnorm) followed by launch_route_scores, bit for
+// bit.  x_next must not overlap x (other workgroups still read x while workgroup 0 writes it).
+bool route_scores_residual_supported(const k3x_router_desc& r, int32_t T);
+hipError_t launch_route_scores_residual(const k3x_router_desc& r, const uint16_t* x,
+                                        const float* y_prev, float eps, uint16_t* x_next,
+                                        uint16_t* xn, float* scores, hipStream_t s);
 // The selection alone, on scores fp32 [T][E] already computed.
 hipError_t launch_route_select(const k3x_router_desc& r, int32_t T, const float* scores,
                                int32_t* idx, float* gates, hipStream_t s);
@@ -171,6 +180,14 @@ bool decode_routed_supported(const k3x_router_desc& r, const k3x_pool& p, int32_
 hipError_t launch_decode_routed(const k3x_router_desc& r, const k3x_pool& p, const uint16_t* x,
                                 float* scores, int32_t* idx, float* gates, float* y, uint8_t* ws,
                                 hipStream_t s);
+// The same with the residual update and RMSNorm folded into the scores launch
+// (launch_route_scores_residual); the experts read xn.
+bool decode_routed_residual_supported(const k3x_router_desc& r, const k3x_pool& p, int32_t T);
+hipError_t launch_decode_routed_residual(const k3x_router_desc& r, const k3x_pool& p,
+                                         const uint16_t* x, const float* y_prev, float eps,
+                                         uint16_t* x_next, uint16_t* xn, float* scores,
+                                         int32_t* idx, float* gates, float* y, uint8_t* ws,
+                                         hipStream_t s);
 // Latent MoE block (k3x_dense.hip): workspace layout and launcher.
 struct LatentLayout {
   size_t scores;  // router scores fp32 [T][E]
@@ -209,8 +226,9 @@ hipError_t launch_rmsnorm(const uint16_t* x, int32_t T, int32_t H, float eps, ui
                           hipStream_t s);
 
 hipError_t launch_residual(uint16_t* x, const float* y, int32_t T, int32_t H, hipStream_t s);
-hipError_t launch_residual_rmsnorm(uint16_t* x, const float* y, int32_t T, int32_t H, float eps,
-                                   uint16_t* out, hipStream_t s);
+// x_out <- bf16(x + y) and out <- rmsnorm(x_out); x_out may be x, out overlaps neither.
+hipError_t launch_residual_rmsnorm(const uint16_t* x, const float* y, int32_t T, int32_t H,
+                                   float eps, uint16_t* x_out, uint16_t* out, hipStream_t s);
 
 int device_cu_count();
 

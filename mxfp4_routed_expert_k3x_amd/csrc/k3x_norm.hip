@@ -68,19 +68,22 @@ __global__ __launch_bounds__(256) void residual_add_bf16(uint16_t* __restrict__ 
   reinterpret_cast<uint4*>(x)[i] = make_uint4(w[0], w[1], w[2], w[3]);
 }
 
-// Residual update of one layer fused with the RMSNorm that starts the next: x[t] <- bf16(x[t]
-// + y[t]) and out[t] <- rmsnorm(x[t]), one wave per token.  The updated chunks stay in
-// registers (NC per lane) for the norm; the squares are summed in the same order as
-// rmsnorm_bf16, so both outputs equal those of the two separate launches bit for bit.
+// Residual update of one layer fused with the RMSNorm that starts the next: x_out[t] <-
+// bf16(x[t] + y[t]) and out[t] <- rmsnorm(x_out[t]), one wave per token.  The updated chunks
+// stay in registers (NC per lane) for the norm; the squares are summed in the same order as
+// rmsnorm_bf16, so both outputs equal those of the two separate launches bit for bit.  x_out
+// may be x (each lane rewrites only the chunks it has read).
 template <int NC>
-__global__ __launch_bounds__(256) void residual_rmsnorm_bf16(uint16_t* __restrict__ x,
+__global__ __launch_bounds__(256) void residual_rmsnorm_bf16(const uint16_t* x,
                                                              const float* __restrict__ y,
                                                              int32_t T, int32_t H, float eps,
+                                                             uint16_t* x_out,
                                                              uint16_t* __restrict__ out) {
   const int lane = threadIdx.x % kWave;
   const int t = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
   if (t >= T) return;
-  uint4* xr = reinterpret_cast<uint4*>(x + (size_t)t * H);
+  const uint4* xr = reinterpret_cast<const uint4*>(x + (size_t)t * H);
+  uint4* xw = reinterpret_cast<uint4*>(x_out + (size_t)t * H);
   const float4* yr = reinterpret_cast<const float4*>(y + (size_t)t * H);
   const int chunks = H / 8;
   uint4 nv[NC];
@@ -105,7 +108,7 @@ __global__ __launch_bounds__(256) void residual_rmsnorm_bf16(uint16_t* __restric
         ss = ss + dh * dh;
       }
       nv[i] = make_uint4(o[0], o[1], o[2], o[3]);
-      xr[c] = nv[i];
+      xw[c] = nv[i];
     }
   }
 #pragma unroll
@@ -132,14 +135,14 @@ __global__ __launch_bounds__(256) void residual_rmsnorm_bf16(uint16_t* __restric
 
 }  // namespace
 
-hipError_t launch_residual_rmsnorm(uint16_t* x, const float* y, int32_t T, int32_t H, float eps,
-                                   uint16_t* out, hipStream_t s) {
+hipError_t launch_residual_rmsnorm(const uint16_t* x, const float* y, int32_t T, int32_t H,
+                                   float eps, uint16_t* x_out, uint16_t* out, hipStream_t s) {
   if (T == 0) return hipSuccess;
   if (H <= 64 * 8 * 8)
     return launch("residual_rmsnorm_bf16", residual_rmsnorm_bf16<8>, dim3((T + 3) / 4),
-                  dim3(256), 0, s, x, y, T, H, eps, out);
+                  dim3(256), 0, s, x, y, T, H, eps, x_out, out);
   return launch("residual_rmsnorm_bf16", residual_rmsnorm_bf16<32>, dim3((T + 3) / 4), dim3(256),
-                0, s, x, y, T, H, eps, out);
+                0, s, x, y, T, H, eps, x_out, out);
 }
 
 hipError_t launch_rmsnorm(const uint16_t* x, int32_t T, int32_t H, float eps, uint16_t* out,

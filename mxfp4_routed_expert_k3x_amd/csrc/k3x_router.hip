@@ -155,6 +155,102 @@ __global__ __launch_bounds__(256) void route_scores_staged(const uint16_t* __res
   }
 }
 
+// Single-token scores with the hidden-state update and the RMSNorm that precede the router
+// folded in (README Part II section 5): xr = bf16(x + y_prev) (x itself when y_prev is NULL),
+// xn = bf16(xr * inv), inv = (float)(1 / sqrt(sum of squares / H + eps)) with the squares of
+// xr summed in double in the order of the standalone RMSNorm (lane L's chunks L + 64 i
+// ascending, the low then the high half of each pair, then the fold s = 32 .. 1), and the
+// scores of xn in route_scores_staged's order.  The workgroup builds xr in LDS once; each wave
+// then sums the squares itself, so no second barrier is needed, and scores its expert.
+// Workgroup 0 stores xr (when x_next is given) and xn.  H = 512 * NCH.
+template <int NCH>
+__global__ __launch_bounds__(256) void route_scores_residual(
+    const uint16_t* __restrict__ x, const float* __restrict__ y_prev, float eps,
+    const uint16_t* __restrict__ W, int32_t H, int32_t E, float* __restrict__ scores,
+    uint16_t* __restrict__ x_next, uint16_t* __restrict__ xn) {
+  constexpr int cpr = NCH * kWave;
+  __shared__ uint4 xs[cpr];
+  const int lane = threadIdx.x % kWave;
+  const int e = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  uint4 wv[NCH];
+  const uint4* wrow = reinterpret_cast<const uint4*>(W + (size_t)(e < E ? e : E - 1) * H);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) wv[i] = wrow[lane + kWave * i];
+  __builtin_amdgcn_sched_barrier(0);
+  for (int c = threadIdx.x; c < cpr; c += blockDim.x) {
+    uint4 v = reinterpret_cast<const uint4*>(x)[c];
+    if (y_prev) {
+      const float4 y0 = reinterpret_cast<const float4*>(y_prev)[2 * c];
+      const float4 y1 = reinterpret_cast<const float4*>(y_prev)[2 * c + 1];
+      const float ys[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
+      uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        w[j] = f32_to_bf16_bits(bf16_bits_to_f32(w[j] & 0xFFFFu) + ys[2 * j]) |
+               (f32_to_bf16_bits(bf16_bits_to_f32(w[j] >> 16) + ys[2 * j + 1]) << 16);
+      v = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+    xs[c] = v;
+  }
+  __syncthreads();
+  if (e >= E) return;
+  uint4 xv[NCH];
+  double ss = 0.0;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    xv[i] = xs[lane + kWave * i];
+    const uint32_t w[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const double lo = (double)bf16_bits_to_f32(w[j] & 0xFFFFu);
+      const double hi = (double)bf16_bits_to_f32(w[j] >> 16);
+      ss = ss + lo * lo;
+      ss = ss + hi * hi;
+    }
+  }
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) ss = ss + __shfl_down(ss, s, kWave);
+  ss = __shfl(ss, 0, kWave);
+  const float inv = (float)(1.0 / sqrt(ss / (double)H + (double)eps));
+  const bool store = blockIdx.x == 0 && threadIdx.x < kWave;
+  double acc = 0.0;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const uint32_t xw[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
+    const uint32_t ws[4] = {wv[i].x, wv[i].y, wv[i].z, wv[i].w};
+    uint32_t o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t lo = f32_to_bf16_bits(bf16_bits_to_f32(xw[j] & 0xFFFFu) * inv);
+      const uint32_t hi = f32_to_bf16_bits(bf16_bits_to_f32(xw[j] >> 16) * inv);
+      o[j] = lo | (hi << 16);
+      acc = acc + (double)bf16_bits_to_f32(lo) * (double)bf16_bits_to_f32(ws[j] & 0xFFFFu);
+      acc = acc + (double)bf16_bits_to_f32(hi) * (double)bf16_bits_to_f32(ws[j] >> 16);
+    }
+    if (store) {
+      const int c = lane + kWave * i;
+      reinterpret_cast<uint4*>(xn)[c] = make_uint4(o[0], o[1], o[2], o[3]);
+      if (x_next) reinterpret_cast<uint4*>(x_next)[c] = xv[i];
+    }
+  }
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) acc = acc + __shfl_down(acc, s, kWave);
+  if (lane == 0) {
+    const float l = (float)acc;
+    scores[e] = (float)(1.0 / (1.0 + exp(-(double)l)));
+  }
+}
+
+typedef void (*ResidualScoresKernel)(const uint16_t*, const float*, float, const uint16_t*,
+                                     int32_t, int32_t, float*, uint16_t*, uint16_t*);
+
+template <int... N>
+ResidualScoresKernel residual_kernel(int nch) {
+  constexpr ResidualScoresKernel k[] = {route_scores_residual<N>...};
+  return k[nch - 1];
+}
+
 typedef void (*ScoresKernel)(const uint16_t*, const uint16_t*, int32_t, int32_t, int32_t, float*);
 
 template <int... N>
@@ -235,6 +331,20 @@ hipError_t launch_route_scores(const k3x_router_desc& r, const uint16_t* x, int3
       err = launch("route_scores", route_scores<32>, g1, dim3(256), 0, s, x, W, T, H, E, scores);
   }
   return err;
+}
+
+bool route_scores_residual_supported(const k3x_router_desc& r, int32_t T) {
+  return T == 1 && r.hidden % 512 == 0 && r.hidden <= 8192;
+}
+
+hipError_t launch_route_scores_residual(const k3x_router_desc& r, const uint16_t* x,
+                                        const float* y_prev, float eps, uint16_t* x_next,
+                                        uint16_t* xn, float* scores, hipStream_t s) {
+  const int E = r.n_experts, H = r.hidden;
+  return launch("route_scores",
+                residual_kernel<1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16>(H / 512),
+                dim3((E + 3) / 4), dim3(256), 0, s, x, y_prev, eps,
+                static_cast<const uint16_t*>(r.weight), H, E, scores, x_next, xn);
 }
 
 }  // namespace k3x

@@ -497,6 +497,102 @@ def test_route_moe_forward_equals_separate_calls(dev, orc):
         del pool
 
 
+def _residual_route_moe_both(torch, k3x, orc, pool, Wd, bd, x, y_prev, T, k, alias_y=False):
+    """k3x_residual_route_moe_forward against k3x_residual_add_rmsnorm_bf16 (k3x_rmsnorm_bf16
+    without y_prev) followed by k3x_route_moe_forward: x_next, xn, idx, gates and y equal bit
+    for bit, x is left as it was, and x_next and xn equal the oracle's residual update and
+    RMSNorm."""
+    H = pool.H
+    r = k3x.router_desc(Wd, bd, k)
+    xd = _t(torch, x)
+    yp = _t(torch, y_prev) if y_prev is not None else None
+    x_next = torch.full_like(xd, 0x7F7F) if y_prev is not None else None
+    xn = torch.full_like(xd, 0x7F7F)
+    idx = torch.full((T, k), -7, dtype=torch.int32, device="cuda")
+    gates = torch.full((T, k), float("nan"), dtype=torch.float32, device="cuda")
+    y = yp.clone() if alias_y else torch.full((T, H), float("nan"), device="cuda")
+    ws = k3x.alloc_workspace(k3x.k3x_route_moe_workspace_size(r, pool, T))
+    k3x.k3x_residual_route_moe_forward(r, pool, xd, y if alias_y else yp, 1e-6, x_next, xn, T,
+                                       idx, gates, y, ws)
+    torch.cuda.synchronize()
+    assert k3x.k3x_fetch_drops(ws) == 0
+    xr, xn2 = xd.clone(), torch.empty_like(xd)
+    if y_prev is not None:
+        k3x.k3x_residual_add_rmsnorm_bf16(xr, yp, T, H, 1e-6, xn2)
+    else:
+        k3x.k3x_rmsnorm_bf16(xd, T, H, 1e-6, xn2)
+    idx2, gates2 = torch.empty_like(idx), torch.empty_like(gates)
+    y2 = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    ws2 = k3x.alloc_workspace(k3x.k3x_route_moe_workspace_size(r, pool, T))
+    k3x.k3x_route_moe_forward(r, pool, xn2, T, idx2, gates2, y2, ws2)
+    torch.cuda.synchronize()
+    assert np.array_equal(_np(xd, np.uint16), x)
+    x_ref = x if y_prev is None else orc.residual_add_bf16(x, y_prev)
+    if y_prev is not None:
+        assert torch.equal(x_next, xr)
+        assert np.array_equal(_np(x_next, np.uint16), x_ref)
+    assert torch.equal(xn, xn2)
+    assert np.array_equal(_np(xn, np.uint16), orc.rmsnorm_bf16(x_ref, 1e-6))
+    assert torch.equal(idx, idx2)
+    assert torch.equal(gates.view(torch.int32), gates2.view(torch.int32))
+    assert torch.equal(y.view(torch.int32), y2.view(torch.int32))
+
+
+def test_residual_route_moe_equals_separate_calls(dev, orc):
+    """The residual update and RMSNorm in front of the router in one call: at one token the
+    router's scores launch does both (K3 shape; 1022 experts of width 1024, whose last
+    workgroup has idle waves); at several tokens or widths that are not multiples of 512 the
+    separate norm launch runs first.  Also the first layer (no y_prev), y passed as y_prev, a
+    contract pool, and the overlap checks."""
+    torch, k3x = dev
+    w = S.WORKLOADS[2]
+    pool = _pool(torch, k3x, S.device_pool(w.seed, 0, w.E, w.H, w.I), w.E, w.H, w.I)
+    W, b = S.router_inputs(w)
+    Wd, bd = _t(torch, W), _t(torch, b)
+    rng = np.random.default_rng(11)
+    x = S.normal_bf16(w.seed + 300, S.P_X, 0, (3, w.H))
+    yp = (rng.standard_normal((3, w.H)) * 0.5).astype(np.float32)
+    for T, y_prev, alias in ((1, None, False), (1, yp[:1], False), (1, yp[:1], True),
+                             (3, yp, False), (3, None, False)):
+        _log(f"case: residual_route_moe K3 shape T={T} y_prev={y_prev is not None} "
+             f"y_is_y_prev={alias}")
+        _residual_route_moe_both(torch, k3x, orc, pool, Wd, bd, x[:T], y_prev, T, w.topk,
+                                 alias_y=alias)
+    _log("case: residual_route_moe overlap checks")
+    r = k3x.router_desc(Wd, bd, w.topk)
+    xd = _t(torch, x[:1])
+    buf = torch.empty((4, w.H), dtype=torch.int16, device="cuda")
+    ypd = _t(torch, yp[:1])
+    idx = torch.empty((1, w.topk), dtype=torch.int32, device="cuda")
+    gates = torch.empty((1, w.topk), dtype=torch.float32, device="cuda")
+    y = torch.empty((1, w.H), dtype=torch.float32, device="cuda")
+    ws = k3x.alloc_workspace(k3x.k3x_route_moe_workspace_size(r, pool, 1))
+    for x_arg, x_next, xn in ((xd, xd, buf[0]), (xd, buf[0], buf[0]), (xd, buf[1], xd),
+                              (buf[1], buf[0], buf[1])):
+        with pytest.raises(k3x.K3xError) as err:
+            k3x.k3x_residual_route_moe_forward(r, pool, x_arg, ypd, 1e-6, x_next, xn, 1, idx,
+                                               gates, y, ws)
+        assert err.value.status == k3x.K3X_E_INVALID_ARG
+    with pytest.raises(k3x.K3xError) as err:  # xn inside y
+        k3x.k3x_residual_route_moe_forward(r, pool, xd, ypd, 1e-6, buf[0], y, 1, idx, gates, y,
+                                           ws)
+    assert err.value.status == k3x.K3X_E_INVALID_ARG
+    del pool
+    for E, H, I, k, contract in ((1022, 1024, 256, 16, False), (64, 256, 256, 8, False),
+                                 (64, 512, 512, 8, True)):
+        _log(f"case: residual_route_moe E={E} H={H} I={I} k={k} contract={contract}")
+        pool = k3x.k3x_expert_pool_create(S.device_pool(E, 0, E, H, I), hidden=H, inter=I,
+                                          n_experts=E, contract=contract)
+        W = S.normal_bf16(E, S.P_WR, 0, (E, H), std=0.05)
+        b = S.normal_f32(E, S.P_BIAS, 0, (E,), std=0.01)
+        x = S.normal_bf16(E + 1, S.P_X, 0, (2, H))
+        yp = (rng.standard_normal((2, H)) * 0.5).astype(np.float32)
+        for T in ((1,) if contract else (1, 2)):
+            _residual_route_moe_both(torch, k3x, orc, pool, _t(torch, W), _t(torch, b), x[:T],
+                                     yp[:T], T, k)
+        del pool
+
+
 # ------------------------------------------------------------------------------------------
 # the five workloads at full size, every output checked
 # ------------------------------------------------------------------------------------------
@@ -840,19 +936,77 @@ def _chain(torch, k3x, orc, L, E, log_every=True):
     return worst
 
 
+def _chain_fused(torch, k3x, orc, L, E, log_every=True):
+    """The chain as the benchmark runs it: one k3x_residual_route_moe_forward per layer (the
+    previous layer's residual update, this layer's RMSNorm, router and experts), two x
+    buffers taking turns, one y buffer that is both y_prev and y, and a last residual add."""
+    w = S.WORKLOADS[5]
+    H, I, k = w.H, w.I, w.topk
+    x = S.activations(w)
+    bufs = [_t(torch, x), torch.empty((1, H), dtype=torch.int16, device="cuda"),
+            torch.empty((1, H), dtype=torch.int16, device="cuda")]
+    x_cur = bufs[0]
+    xn = torch.empty_like(x_cur)
+    idx = torch.empty((1, k), dtype=torch.int32, device="cuda")
+    gates = torch.empty((1, k), dtype=torch.float32, device="cuda")
+    y = torch.empty((1, H), dtype=torch.float32, device="cuda")
+    worst, ws = 0.0, None
+    for layer in range(L):
+        pool = _pool(torch, k3x, S.device_pool(w.seed, layer, E, H, I), E, H, I)
+        W = S.normal_bf16(w.seed, S.P_WR, layer, (E, H), std=0.02)
+        b = S.zipf_bias(w.seed, E, layer)
+        r = k3x.router_desc(_t(torch, W), _t(torch, b), k)
+        if ws is None:
+            ws = k3x.alloc_workspace(k3x.k3x_route_moe_workspace_size(r, pool, 1))
+        x_in = _np(x_cur, np.uint16).copy()
+        y_in = _np(y).copy() if layer else None
+        x_next = bufs[1] if x_cur is not bufs[1] else bufs[2]
+        k3x.k3x_residual_route_moe_forward(r, pool, x_cur, y if layer else None, 1e-6,
+                                           x_next if layer else None, xn, 1, idx, gates, y, ws)
+        torch.cuda.synchronize()
+        assert k3x.k3x_fetch_drops(ws) == 0
+        # teacher forcing: the oracle takes this layer's GPU inputs
+        x_ref = orc.residual_add_bf16(x_in, y_in) if layer else x_in
+        if layer:
+            assert np.array_equal(_np(x_next, np.uint16), x_ref), layer
+            x_cur = x_next
+        xn_ref = orc.rmsnorm_bf16(x_ref, 1e-6)
+        assert np.array_equal(_np(xn, np.uint16), xn_ref), layer
+        i_ref, g_ref = orc.route(xn_ref, W, b, k)
+        assert np.array_equal(_np(idx), i_ref), layer
+        assert np.array_equal(_np(gates).view(np.uint32), g_ref.view(np.uint32)), layer
+        y_ref = oracle_forward_sampled(orc, w.seed, layer, H, I, xn_ref, i_ref, g_ref, [0])
+        rel, mx = assert_y_close(_np(y), y_ref, f"layer {layer}")
+        assert np.array_equal(_np(y), y_ref), f"layer {layer}: differs from the fp32 oracle"
+        worst = max(worst, rel)
+        if log_every:
+            _log(f"  layer {layer}: rel_l2={rel:.3e} max_abs={mx:.3e}")
+        del pool
+    x_in = _np(x_cur, np.uint16).copy()
+    k3x.k3x_residual_add_bf16(x_cur, y, 1, H)
+    torch.cuda.synchronize()
+    assert np.array_equal(_np(x_cur, np.uint16), orc.residual_add_bf16(x_in, _np(y)))
+    return worst
+
+
 def test_chain12_reduced_pool(dev, orc):
     """Twelve chained layers (RMSNorm -> router -> experts -> residual) with 64 experts per
-    layer; every layer is checked against the oracle on the GPU's own layer input."""
+    layer, as separate calls and as one fused call per layer; every layer is checked against
+    the oracle on the GPU's own layer input."""
     torch, k3x = dev
-    _log("case: chain of 12 layers, E=64")
+    _log("case: chain of 12 layers, E=64, separate calls")
     _chain(torch, k3x, orc, 12, 64)
+    _log("case: chain of 12 layers, E=64, fused calls")
+    _chain_fused(torch, k3x, orc, 12, 64)
 
 
 def test_chain12_full_size(dev, orc):
-    """The chained workload at its full size: 12 layers of 896 experts with per-layer router
-    weights and Zipf-skewed bias.  Layers are generated one after another (one 15.7 GB pool
-    on the device at a time); each is checked against the oracle on the GPU's own input:
-    RMSNorm bitwise, routing bit-exact, y equal to the fp32 oracle bit for bit."""
+    """The chained workload at its full size, run as the benchmark runs it: 12 layers of 896
+    experts with per-layer router weights and Zipf-skewed bias, one fused residual + RMSNorm
+    + router + experts call per layer.  Layers are generated one after another (one 15.7 GB
+    pool on the device at a time); each is checked against the oracle on the GPU's own input:
+    residual update and RMSNorm bitwise, routing bit-exact, y equal to the fp32 oracle bit
+    for bit."""
     torch, k3x = dev
-    _log("case: chain of 12 layers, E=896 (full size)")
-    _chain(torch, k3x, orc, 12, 896)
+    _log("case: chain of 12 layers, E=896 (full size), fused calls")
+    _chain_fused(torch, k3x, orc, 12, 896)
