@@ -392,37 +392,84 @@ __device__ __forceinline__ float reduce_pairs(const float (&A)[4], const float (
   return t + ub;
 }
 
-// Streams rows r0 .. rlast of one W2 matrix in the paired layout, one pair loaded ahead of the
-// arithmetic; emit as in stream_rows (sum_b unused).
-template <typename Prep, typename Emit>
-__device__ __forceinline__ void stream_pairs(const uint8_t* wa, const uint8_t* sa, int r0,
-                                             int rlast, uint32_t wrow, uint32_t srow,
-                                             const PairLanes& po, const float (&x0)[32],
-                                             const float (&x1)[32], int lane, Prep prep,
-                                             Emit emit) {
+// The three leaves of one pair (first halves of the even and odd rows, the shared second half).
+__device__ __forceinline__ void pair_leaves(const PairBits& p, const float (&x0)[32],
+                                            const float (&x1)[32], float& a0, float& a1,
+                                            float& b) {
+  a0 = group_sum(p.a0, x0) * e8m0_to_f32(p.s0);
+  a1 = group_sum(p.a1, x0) * e8m0_to_f32(p.s1);
+  b = group_sum(p.b, x1) * e8m0_to_f32(p.sb);
+}
+
+// Rows r0 .. rlast of W2 for one or two slots in the paired layout, as one stream: the pairs
+// of the first slot, then those of the second (s1 < 0: none), one pair loaded ahead of the
+// arithmetic also across the change of slot, so the loads never drain in between (a wave
+// whose two slots ran as separate streams waited a full memory latency at the change).  Both
+// slots' activations are requested up front; the second's are widened when its first pair
+// comes up.  Rows are finished four at a time (two pairs); with an odd number of pairs per
+// slot one group of four holds the last pair of the first slot and the first of the second.
+// Every lane calls emit(s, r, sum, valid) after each group: lane L < 4 with valid set holds
+// the full sum of row r of slot s.
+template <typename Emit>
+__device__ __forceinline__ void stream_pairs2(const DecodeArgs& a, int s0, int e0, int s1,
+                                              int e1, int r0, int rlast, uint32_t wrow,
+                                              uint32_t srow, const PairLanes& po, int lane,
+                                              int ngroups, Emit emit) {
+  const int np = (rlast - r0 + 2) / 2;  // pairs per slot
+  const bool two = s1 >= 0;
+  const int Q = two ? 2 * np : np;
+  const int sl1 = two ? s1 : s0, ex1 = two ? e1 : e0;
+  const uint8_t* w0 = a.wa + (size_t)e0 * a.st_wa;
+  const uint8_t* c0 = a.sa + (size_t)e0 * a.st_sa;
+  const uint8_t* w1 = a.wa + (size_t)ex1 * a.st_wa;
+  const uint8_t* c1 = a.sa + (size_t)ex1 * a.st_sa;
+  uint4 ra[8], rb[8];
+  load_act_raw_pair(a.act + (size_t)s0 * a.K, lane, ngroups, ra);
+  load_act_raw_pair(a.act + (size_t)sl1 * a.K, lane, ngroups, rb);
   PairBits P[2] = {};
-  auto load = [&](int i, int r) {
-    const int rr = r <= rlast ? r : rlast;
+  // pair q of the stream into buffer i (pairs past the end re-read the last one)
+  auto load = [&](int i, int q) {
+    const int qq = q < Q ? q : Q - 1;
+    const bool second = qq >= np;
+    const int r = r0 + 2 * (second ? qq - np : qq);
     __builtin_amdgcn_sched_barrier(0);
-    load_pair(P[i], wa, sa, rr, rlast, wrow, srow, po);
+    load_pair(P[i], second ? w1 : w0, second ? c1 : c0, r, rlast, wrow, srow, po);
     __builtin_amdgcn_sched_barrier(0);
   };
-  load(0, r0);
-  prep();
-#pragma unroll 1
-  for (int r = r0; r <= rlast; r += 4) {
+  // pairs q (against xa) and q + 1 (against xb), then their rows
+  auto quad = [&](int q, const float (&xa0)[32], const float (&xa1)[32], const float (&xb0)[32],
+                  const float (&xb1)[32]) __attribute__((always_inline)) {
     float A[4], B[2];
-    load(1, r + 2);
-    A[0] = group_sum(P[0].a0, x0) * e8m0_to_f32(P[0].s0);
-    A[1] = group_sum(P[0].a1, x0) * e8m0_to_f32(P[0].s1);
-    B[0] = group_sum(P[0].b, x1) * e8m0_to_f32(P[0].sb);
-    load(0, r + 4);
-    A[2] = group_sum(P[1].a0, x0) * e8m0_to_f32(P[1].s0);
-    A[3] = group_sum(P[1].a1, x0) * e8m0_to_f32(P[1].s1);
-    B[1] = group_sum(P[1].b, x1) * e8m0_to_f32(P[1].sb);
+    load(1, q + 1);
+    pair_leaves(P[0], xa0, xa1, A[0], A[1], B[0]);
+    load(0, q + 2);
+    pair_leaves(P[1], xb0, xb1, A[2], A[3], B[1]);
     const float v = reduce_pairs(A, B, lane);
-    emit(r + lane, v, 0.0f, lane < 4 && r + lane <= rlast, min(4, rlast - r + 1));
+    // lane L < 4: row L & 1 of pair q + (L >> 1)
+    const int qq = q + ((lane >> 1) & 1);
+    const bool second = qq >= np;
+    const int r = r0 + 2 * (second ? qq - np : qq) + (lane & 1);
+    emit(second ? sl1 : s0, r, v, lane < 4 && qq < Q && r <= rlast);
+  };
+  load(0, 0);
+  float x0[32], x1[32];
+  act_to_f32_pair(ra, lane, ngroups, x0, x1);
+  const bool odd = np & 1;
+  int q = 0;
+#pragma unroll 1
+  for (; q < np - 1; q += 2) quad(q, x0, x1, x0, x1);  // groups within the first slot
+  if (!two) {
+    if (odd) quad(q, x0, x1, x0, x1);  // the last pair alone
+    return;
   }
+  float y0[32], y1[32];
+  act_to_f32_pair(rb, lane, ngroups, y0, y1);
+  if (odd) {  // the group that holds both slots
+    quad(q, x0, x1, y0, y1);
+    q += 2;
+  }
+#pragma unroll 1
+  for (; q < Q; q += 2) quad(q, y0, y1, y0, y1);
 }
 
 // g = W1 x, u = W3 x, h = bf16(silu(g) * u) (or of SiTU-GLU, with each tanh the float nearest
@@ -560,25 +607,39 @@ __global__ __launch_bounds__(kW2Waves * kWave) void decode_w2_combine(DecodeArgs
   const bool paired = ngroups > kWave && ngroups <= kWave + 32;
   const PairLanes po = pair_lanes(lane, ngroups, wrow, srow);
 
-  float x0[32], x1[32];
-  for (int slot = wave; slot < a.topk; slot += kW2Waves) {
-    const int e = __builtin_amdgcn_readlane(my_idx, slot);
-    if (!expert_ok(e, a.E)) continue;
-    uint4 hr[8];
-    float* d = dsh + slot * R - rb0;
-    auto park = [&](int r, float dv, float, bool valid, int) {
-      if (valid) d[r] = dv;
+  if (paired) {
+    // the wave's valid slots two at a time, each two as one stream
+    auto park = [&](int slot, int r, float dv, bool valid) {
+      if (valid) dsh[slot * R + r - rb0] = dv;
     };
-    if (paired) {
-      load_act_raw_pair(a.act + (size_t)slot * a.K, lane, ngroups, hr);
-      stream_pairs(a.wa + (size_t)e * a.st_wa, a.sa + (size_t)e * a.st_sa, rb0, rlast, wrow,
-                   srow, po, x0, x1, lane,
-                   [&]() { act_to_f32_pair(hr, lane, ngroups, x0, x1); }, park);
-    } else {
+    int pend = -1, pend_e = -1;
+    for (int slot = wave; slot < a.topk; slot += kW2Waves) {
+      const int e = __builtin_amdgcn_readlane(my_idx, slot);
+      if (!expert_ok(e, a.E)) continue;
+      if (pend < 0) {
+        pend = slot;
+        pend_e = e;
+        continue;
+      }
+      stream_pairs2(a, pend, pend_e, slot, e, rb0, rlast, wrow, srow, po, lane, ngroups, park);
+      pend = -1;
+    }
+    if (pend >= 0)
+      stream_pairs2(a, pend, pend_e, -1, -1, rb0, rlast, wrow, srow, po, lane, ngroups, park);
+  } else {
+    float x0[32], x1[32];
+    for (int slot = wave; slot < a.topk; slot += kW2Waves) {
+      const int e = __builtin_amdgcn_readlane(my_idx, slot);
+      if (!expert_ok(e, a.E)) continue;
+      uint4 hr[8];
+      float* d = dsh + slot * R - rb0;
       load_act_raw(a.act + (size_t)slot * a.K, lane, ngroups, hr);
       stream_rows<false>(a.wa + (size_t)e * a.st_wa, a.sa + (size_t)e * a.st_sa, nullptr,
                          nullptr, rb0, rlast, wrow, srow, lo, x0, x1, lane,
-                         [&]() { act_to_f32(hr, lane, ngroups, x0, x1); }, park);
+                         [&]() { act_to_f32(hr, lane, ngroups, x0, x1); },
+                         [&](int r, float dv, float, bool valid, int) {
+                           if (valid) d[r] = dv;
+                         });
     }
   }
   __syncthreads();
