@@ -40,7 +40,9 @@ roofline come from HIP events the library records around each of its launches
 
 The default run (decode_t1_e896_router) also measures the 4096-token prefill
 (prefill_t4096_e896: 896 experts, uniform routing, no router) and reports it in the same line
-under "prefill", with its TFLOP/s against the bf16 MFMA peak (--no-prefill skips it), and a
+under "prefill", with its TFLOP/s against the bf16 MFMA peak (--no-prefill skips it) and,
+as context, the TFLOP/s of the same FLOPs as two dense bf16 torch.matmul GEMMs on this GPU
+("dense_bf16_reference"; `--dense-reference` runs only that), and a
 decode batch of 32 tokens through the router with Zipf-skewed expert popularity
 (decode_t32_e896_zipf) under "decode_batch" (--no-batch skips it).
 `cpu_baseline` is the oracle on this host: the median of 3 runs on all of its threads
@@ -851,6 +853,40 @@ def sources_hash(workload=None):
     return h.hexdigest()[:16]
 
 
+def dense_reference(torch, T, H, I, topk, reps=10):
+    """The prefill's FLOPs as two plain dense bf16 GEMMs through torch.matmul (hipBLASLt):
+    [T*topk, H] x [H, 2I] (W1 and W3 side by side) and [T*topk, I] x [I, H] (W2), event-timed
+    on the current stream.  Context for the prefill's TFLOP/s: what the vendor's tuned dense
+    GEMM reaches on this GPU for the same work without grouping by expert or decoding FP4."""
+    M = T * topk
+    g = torch.Generator(device="cuda").manual_seed(0)
+    res = {}
+    total_flops, total_ms = 0.0, 0.0
+    for name, (k, n) in (("w13", (H, 2 * I)), ("w2", (I, H))):
+        a = torch.randn(M, k, dtype=torch.bfloat16, device="cuda", generator=g)
+        b = torch.randn(k, n, dtype=torch.bfloat16, device="cuda", generator=g)
+        for _ in range(3):
+            c = a @ b
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            c = a @ b
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        flops = 2.0 * M * k * n
+        res[name] = {"shape": [M, n, k], "ms": round(ms, 4), "tflops": round(flops / ms / 1e9, 1)}
+        total_flops += flops
+        total_ms += ms
+        del a, b, c
+    torch.cuda.empty_cache()
+    res["tflops"] = round(total_flops / total_ms / 1e9, 1)
+    res["kind"] = "torch.matmul bf16 (hipBLASLt), the prefill's FLOPs as two dense GEMMs"
+    return res
+
+
 def copy_probe():
     import torch
     a = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device="cuda:0")
@@ -1039,6 +1075,8 @@ def main():
                     help="the floating point contract's arithmetic (double sums in the listing's "
                          "order, h in fp32); one token per call")
     ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--dense-reference", action="store_true",
+                    help="time only the prefill's FLOPs as dense bf16 torch.matmul GEMMs")
     ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"))
     ap.add_argument("--stats-from", metavar="KERNEL_STATS_CSV",
                     help="write profiles/kernel_trace_<workload>.md from a rocprofv3 --stats CSV")
@@ -1049,6 +1087,12 @@ def main():
     args = ap.parse_args()
     if args.copy_probe:
         return copy_probe()
+    if args.dense_reference:
+        import torch
+        import k3x_synth as S
+        pw = {w.name: w for w in S.WORKLOADS.values()}[PREFILL_WORKLOAD]
+        print(json.dumps(dense_reference(torch, pw.T, pw.H, pw.I, pw.topk)), flush=True)
+        return
     if args.traffic_from:
         return traffic_from(*args.traffic_from, args.workload)
     if args.stats_from:
@@ -1088,6 +1132,9 @@ def main():
                                                  "config", "roofline", "path", "kernels",
                                                  "cpu_baseline")}
         out["prefill"]["tflops"] = pre["path"]["tflops_wall"]
+        ref = dense_reference(torch, pw.T, pw.H, pw.I, pw.topk)
+        ref["prefill_over_reference"] = round(pre["path"]["tflops_wall"] / ref["tflops"], 4)
+        out["prefill"]["dense_bf16_reference"] = ref
     if args.workload == DEFAULT_WORKLOAD and not args.no_batch and not args.contract:
         # a decode batch of 32 tokens through the router, experts shared Zipf-fashion
         torch.cuda.empty_cache()

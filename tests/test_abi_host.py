@@ -309,6 +309,56 @@ def test_route_moe_host_validation(k3x):
         lib.k3x_expert_pool_destroy(h)
 
 
+def test_residual_route_moe_host_validation(k3x):
+    """k3x_residual_route_moe_forward refuses bad arguments before enqueuing anything: the
+    route_moe checks, NULL outputs, a missing x_next when y_prev is given, misalignment, and
+    x_next or xn overlapping another operand (y may be y_prev)."""
+    lib = k3x.lib()
+    fake = 1 << 40
+    st, h = _create(k3x, _desc(k3x))  # E 8, hidden 256
+    assert st == 0
+    try:
+        r = k3x.k3x_router_desc()
+        r.weight, r.bias, r.n_experts, r.hidden, r.topk, r.renorm, r.routed_scale = \
+            fake, None, 8, 256, 2, 1, 1.0
+        R = ctypes.byref
+        T = 3
+        need = lib.k3x_route_moe_workspace_size(R(r), h, T)
+        xb, yb = T * 256 * 2, T * 256 * 4
+        X, YP, XN, XNX, Y = fake, fake + (1 << 24), fake + (2 << 24), fake + (3 << 24), fake + (4 << 24)
+
+        def fwd(x=X, y_prev=YP, x_next=XNX, xn=XN, y=Y, T=T, ws=fake + (5 << 24), n=need, rr=r):
+            return lib.k3x_residual_route_moe_forward(R(rr), h, x, y_prev, 1e-6, x_next, xn, T,
+                                                      fake, fake, y, ws, n, None)
+
+        E_ARG, E_UNS, E_WS = k3x.K3X_E_INVALID_ARG, k3x.K3X_E_UNSUPPORTED, k3x.K3X_E_WORKSPACE
+        assert fwd(T=-1) == E_ARG
+        assert fwd(n=need - 1) == E_WS
+        assert fwd(xn=None) == E_ARG
+        assert fwd(x=None) == E_ARG
+        assert fwd(y=None) == E_ARG
+        assert fwd(x_next=None) == E_ARG            # y_prev given, nowhere to put x + y_prev
+        assert fwd(x=X + 2) == E_UNS
+        assert fwd(y_prev=YP + 4) == E_UNS
+        assert fwd(x_next=XNX + 8) == E_UNS
+        assert fwd(x_next=X + xb - 16) == E_ARG     # x_next overlaps x
+        assert fwd(x_next=YP + yb - 16) == E_ARG    # x_next overlaps y_prev
+        assert fwd(x_next=XN) == E_ARG              # x_next is xn
+        assert fwd(xn=X + 16) == E_ARG              # xn overlaps x
+        assert fwd(xn=Y + yb - 16) == E_ARG         # xn overlaps y
+        bad = k3x.k3x_router_desc()
+        bad.weight, bad.bias, bad.n_experts, bad.hidden, bad.topk, bad.renorm, bad.routed_scale = \
+            fake, None, 9, 256, 2, 1, 1.0
+        assert fwd(rr=bad) == E_ARG                 # router experts != pool experts
+        if not _gpu_present():
+            # accepted arguments reach the device: without one, a HIP error (y may be y_prev,
+            # and without y_prev neither x_next nor its overlaps matter)
+            assert fwd(y=YP) == k3x.K3X_E_HIP
+            assert fwd(y_prev=None, x_next=X) == k3x.K3X_E_HIP
+    finally:
+        lib.k3x_expert_pool_destroy(h)
+
+
 def test_contract_pool_checks(k3x):
     lib = k3x.lib()
     assert _create(k3x, _desc(k3x, contract=2))[0] == k3x.K3X_E_INVALID_ARG
