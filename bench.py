@@ -842,14 +842,27 @@ def bench_latent(args, torch, S, k3x):
     print(json.dumps(res), flush=True)
 
 
-def sources_hash(workload=None):
-    """Hash of the kernel sources a workload runs (the routed path's, plus the dense kernels
-    for the latent block)."""
+def code_only(text):
+    """C++ source text without its comments and blank space: what the compiler sees, so that
+    editing a comment does not orphan counters taken on the same code."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
+def sources_hash(workload=None, read=None):
+    """Hash of the code of the kernel sources a workload runs (the routed path's, plus the
+    dense kernels for the latent block), comments and spacing left out.  read(name) returns a
+    source's text (default: the file in the tree)."""
     import hashlib
+    if read is None:
+        def read(f):
+            with open(os.path.join(ROOT, "mxfp4_routed_expert_k3x_amd", "csrc", f)) as fh:
+                return fh.read()
     h = hashlib.sha256()
     for f in LATENT_SOURCES if workload in LATENT_WORKLOADS else KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "mxfp4_routed_expert_k3x_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        h.update(code_only(read(f)).encode())
     return h.hexdigest()[:16]
 
 

@@ -30,7 +30,8 @@
 // router path it first selects the experts itself), then W2 with the weighted combine in its
 // epilogue (each workgroup owns a block of output rows of every slot, so the slot-order sum
 // happens in LDS and the per-slot W2 outputs never reach memory; rows of 65..96 groups share
-// the load of their second halves two rows at a time).  Loads run two rows ahead of the
+// the load of their second halves two rows at a time, and a wave's two slots run as one
+// pipeline across the change of slot).  Loads run two rows ahead of the
 // arithmetic (three or more measured slower: the launch streams best with few requests in
 // flight per CU).
 #include <atomic>

@@ -12,6 +12,8 @@
 // For widths that are multiples of 512 (up to 8192) the row is loaded whole and at once (a
 // fixed number of 16-byte chunks per lane) and the block's tokens are staged in LDS while the
 // row is in flight; other widths take a guarded loop that reads the tokens from memory.
+// A single-token variant (route_scores_residual) first forms the token itself: the previous
+// layer's residual update and this layer's RMSNorm, in the order of the standalone kernels.
 //
 // Kernel 2 (route_select): one workgroup per token.  Up to 1024 experts and 16 picks the
 // experts are ranked by sorting networks over (selection key, index) words
