@@ -317,6 +317,11 @@ __device__ __forceinline__ void select_topk(const float* __restrict__ s_t,
 //  3. Wave 0 merges the four waves' lists the same way (every other list read reversed); its
 //     first topk elements are the picks in slot order.  The gates follow from the unbiased
 //     scores as above.
+// Steps 1-3 are the fallback.  First the workgroup narrows the field: the 16th largest of the
+// 64 quad maxima is a lower bound of the 16th largest word (16 quads hold a word at least that
+// large), so every pick is among the words at or above it — about 18 of 896 router scores.
+// If at most 64 words qualify, wave 0 sorts just those (one word per lane, a bitonic network
+// over the lanes of half the wave when at most 32 do); otherwise the networks above run.
 // ---------------------------------------------------------------------------------------
 namespace bitonic {
 
@@ -403,6 +408,50 @@ __device__ __forceinline__ void merge16(uint64_t (&v)[4], int q, int flip) {
   stage<32, 1>(v, q, flip);
 }
 
+// One compare-exchange stage over the lanes of the wave (one word per lane), blocks of K
+// lanes descending when bit K of the lane is clear (the whole wave descends at K = 64).
+template <int K, int J>
+__device__ __forceinline__ uint64_t lane_stage(uint64_t x, int lane) {
+  const bool desc = K >= kWave ? true : (lane & K) == 0;
+  const bool want_hi = ((lane & J) == 0) == desc;
+  const uint64_t o = lane_xor<J>(x);
+  return ((x < o) == want_hi) ? o : x;
+}
+
+// The words of lanes 0..31, largest first by lane (lanes 32..63 likewise among themselves).
+__device__ __forceinline__ uint64_t sort32(uint64_t x, int lane) {
+  x = lane_stage<2, 1>(x, lane);
+  x = lane_stage<4, 2>(x, lane);
+  x = lane_stage<4, 1>(x, lane);
+  x = lane_stage<8, 4>(x, lane);
+  x = lane_stage<8, 2>(x, lane);
+  x = lane_stage<8, 1>(x, lane);
+  x = lane_stage<16, 8>(x, lane);
+  x = lane_stage<16, 4>(x, lane);
+  x = lane_stage<16, 2>(x, lane);
+  x = lane_stage<16, 1>(x, lane);
+  x = lane_stage<32, 16>(x, lane);
+  x = lane_stage<32, 8>(x, lane);
+  x = lane_stage<32, 4>(x, lane);
+  x = lane_stage<32, 2>(x, lane);
+  x = lane_stage<32, 1>(x, lane);
+  return x;
+}
+
+// The wave's 64 words, largest first by lane.
+__device__ __forceinline__ uint64_t sort64(uint64_t x, int lane) {
+  x = sort32(x, lane);
+  x = lane_stage<64, 32>(x, lane);
+  x = lane_stage<64, 16>(x, lane);
+  x = lane_stage<64, 8>(x, lane);
+  x = lane_stage<64, 4>(x, lane);
+  x = lane_stage<64, 2>(x, lane);
+  x = lane_stage<64, 1>(x, lane);
+  return x;
+}
+
+__device__ __forceinline__ uint64_t max64(uint64_t a, uint64_t b) { return a < b ? b : a; }
+
 }  // namespace bitonic
 
 __host__ __device__ inline bool select_bitonic_supported(int32_t E, int32_t topk) {
@@ -418,6 +467,10 @@ __device__ __forceinline__ void select_topk_bitonic(const float* __restrict__ s_
   using namespace bitonic;
   __shared__ float sc_of[4 * kSelThreads];       // unbiased score by expert
   __shared__ uint64_t best[kSelWaves][16];        // each wave's 16 largest words, descending
+  __shared__ uint64_t qmax[kSelThreads / 4];      // the quads' largest words
+  __shared__ uint64_t cand[kSelWaves][kWave];     // each wave's words at or above the bound
+  __shared__ uint32_t ncand[kSelWaves];           // and their number
+  __shared__ uint64_t top16[16];                  // the picks' words in slot order
   __shared__ float ranked[16];
   const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave, q = lane & 3;
   const int quad = lane >> 2;
@@ -432,38 +485,73 @@ __device__ __forceinline__ void select_topk_bitonic(const float* __restrict__ s_
     if (ok[m]) sc_of[e] = sc[m];
     v[m] = ok[m] ? join(~(uint32_t)e, score_key(c[m])) : 0ull;
   }
-  // a quad's list runs in the direction its next partner needs: bit l of the quad index
-  // before the round with partner 2^l quads away
-  sort16(v, q, quad & 1);
-  merge16<1>(v, q, (quad >> 1) & 1);
-  merge16<2>(v, q, (quad >> 2) & 1);
-  merge16<4>(v, q, (quad >> 3) & 1);
-  merge16<8>(v, q, 0);
-  if (lane < 4) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) best[wv][r + 4 * q] = v[r];
-  }
+  // the quad's largest word
+  uint64_t mx = max64(max64(v[0], v[1]), max64(v[2], v[3]));
+  mx = max64(mx, lane_xor<1>(mx));
+  mx = max64(mx, lane_xor<2>(mx));
+  if (q == 0) qmax[wv * 16 + quad] = mx;
   __syncthreads();
-  if (wv != 0) return;
-  // quads 0..3 take the lists of waves 0..3, odd ones reversed (ascending); other quads empty
+  // the bound: the 16th largest quad maximum (every wave sorts the 64 of them itself)
+  const uint64_t sm = sort64(qmax[lane], lane);
+  const uint64_t bound = join((uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)sm, 15),
+                              (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(sm >> 32), 15));
+  // the words at or above it (none of them absent unless the bound is 0): each wave packs
+  // its own into cand[wave] in register-then-lane order
+  uint32_t base = 0;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int i = r + 4 * q;
-    v[r] = quad < kSelWaves ? best[quad][(quad & 1) ? 15 - i : i] : 0ull;
+  for (int m = 0; m < 4; ++m) {
+    const unsigned long long bal = __ballot(v[m] >= bound);
+    const uint32_t off = base + (uint32_t)__builtin_amdgcn_mbcnt_hi(
+                                    (uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+    if (v[m] >= bound && off < (uint32_t)kWave) cand[wv][off] = v[m];
+    base += (uint32_t)__popcll(bal);
   }
-  merge16<1>(v, q, (quad >> 1) & 1);
-  merge16<2>(v, q, 0);
-  // slot i = element i of quad 0: lane i / 4, register i % 4
-  if (lane < 4) {
+  if (lane == 0) ncand[wv] = base;
+  __syncthreads();
+  const uint32_t n0 = ncand[0], n1 = n0 + ncand[1], n2 = n1 + ncand[2], n = n2 + ncand[3];
+  if (n <= (uint32_t)kWave) {
+    if (wv != 0) return;
+    // lane l takes the l-th word of the four lists one after another
+    const uint32_t l = (uint32_t)lane;
+    const int src = (l >= n0) + (l >= n1) + (l >= n2);
+    const uint32_t at = l - (src == 0 ? 0u : src == 1 ? n0 : src == 2 ? n1 : n2);
+    const uint64_t x = l < n ? cand[src][at] : 0ull;
+    const uint64_t t = n <= 32 ? sort32(x, lane) : sort64(x, lane);
+    if (lane < 16) top16[lane] = t;
+  } else {
+    // too many words at the bound (ties, or quads with no expert): the full networks
+    // a quad's list runs in the direction its next partner needs: bit l of the quad index
+    // before the round with partner 2^l quads away
+    sort16(v, q, quad & 1);
+    merge16<1>(v, q, (quad >> 1) & 1);
+    merge16<2>(v, q, (quad >> 2) & 1);
+    merge16<4>(v, q, (quad >> 3) & 1);
+    merge16<8>(v, q, 0);
+    if (lane < 4) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) best[wv][r + 4 * q] = v[r];
+    }
+    __syncthreads();
+    if (wv != 0) return;
+    // quads 0..3 take the lists of waves 0..3, odd ones reversed (ascending); other quads empty
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int i = r + 4 * q;
-      if (i < topk) {
-        const int e = (int)~(uint32_t)v[r];
-        idx_out[i] = e;
-        ranked[i] = sc_of[e];
-      }
+      v[r] = quad < kSelWaves ? best[quad][(quad & 1) ? 15 - i : i] : 0ull;
     }
+    merge16<1>(v, q, (quad >> 1) & 1);
+    merge16<2>(v, q, 0);
+    // slot i = element i of quad 0: lane i / 4, register i % 4
+    if (lane < 4) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) top16[r + 4 * q] = v[r];
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+  if (lane < topk) {
+    const int e = (int)~(uint32_t)top16[lane];
+    idx_out[lane] = e;
+    ranked[lane] = sc_of[e];
   }
   __builtin_amdgcn_wave_barrier();
   // every lane forms the slot-order sum from its own copy of the picks' scores (one LDS read
