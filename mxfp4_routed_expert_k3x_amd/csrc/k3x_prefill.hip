@@ -34,6 +34,8 @@
 // Each K block ends with one wait + barrier: every wave waits for its own copies into the
 // next stage (the copies were issued before the block's weight requests, so the wait leaves
 // those in flight) and for its LDS reads of the current stage, then all four waves meet.
+// Within a block each B fragment is read two fragments before its MFMAs and the scale bytes
+// one block ahead, so no MFMA waits for an LDS read issued just before it.
 //
 // Work is persistent: tile t belongs to die t % 8 (all its row chunks), so the tile's
 // activation rows are fetched into one die's L2 and reused by every chunk; within a die the
@@ -112,6 +114,15 @@ __device__ __forceinline__ uint32_t dword_of(const uint4& v, int s) {
 // where this can differ from the reference, in rare ties, well inside the output tolerance.
 __device__ __forceinline__ float swiglu_fast(float g, float u) {
   return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+}
+
+// Two floats rounded to bf16 (nearest, ties to even) and packed, a in the low half: one
+// gfx950 conversion instruction for the pair.
+__device__ __forceinline__ uint32_t pack_bf16x2_rne(float a, float b) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  const b2 r = __builtin_convertvector(f2{a, b}, b2);
+  return __builtin_bit_cast(uint32_t, r);
 }
 
 template <int N>
@@ -269,18 +280,28 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_prefill(PrefillArgs a, const
       __builtin_amdgcn_sched_barrier(0);
     };
 
-    // MFMAs of one K block: per MFMA step s the four A operands are converted, then for each
-    // column block one B fragment (read one fragment ahead) meets the four A operands.
-    auto compute = [&](int kb, const uint4 (&w)[kRB], const uint8_t* stage) __attribute__((always_inline)) {
-      float scale[kRB];
+    // Scale bytes of K block kb for this lane's four row blocks, and their conversion to the
+    // power-of-two factors.
+    auto read_scales = [&](int kb, uint32_t (&sb)[kRB]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int rb = 0; rb < kRB; ++rb) scale[rb] = e8m0_to_f32(ss[sa[rb] + 4u * (uint32_t)kb]);
+      for (int rb = 0; rb < kRB; ++rb) sb[rb] = ss[sa[rb] + 4u * (uint32_t)kb];
+    };
+    auto to_scales = [&](const uint32_t (&sb)[kRB], float (&sc)[kRB]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb) sc[rb] = e8m0_to_f32(sb[rb]);
+    };
+
+    // MFMAs of one K block: per MFMA step s the four A operands are converted, then for each
+    // column block one B fragment (read two fragments ahead) meets the four A operands.
+    auto compute = [&](const uint4 (&w)[kRB], const float (&scale)[kRB], const uint8_t* stage)
+        __attribute__((always_inline)) {
       auto read_b = [&](int f) __attribute__((always_inline)) {
         return as_bf16x8(*reinterpret_cast<const uint4*>(stage + (f % NBT) * 16 * kXRow + bo[f / NBT]));
       };
       constexpr int kF = 4 * NBT;
-      bf16x8 bq[2];
+      bf16x8 bq[3];
       bq[0] = read_b(0);
+      bq[1] = read_b(1);
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         bf16x8 av[kRB];
@@ -289,26 +310,33 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_prefill(PrefillArgs a, const
 #pragma unroll
         for (int tb = 0; tb < NBT; ++tb) {
           const int f = s * NBT + tb;
-          if (f + 1 < kF) bq[(f + 1) & 1] = read_b(f + 1);
+          if (f + 2 < kF) bq[(f + 2) % 3] = read_b(f + 2);
 #pragma unroll
-          for (int rb = 0; rb < kRB; ++rb) acc[rb][tb] = mfma16x16x32(av[rb], bq[f & 1], acc[rb][tb]);
+          for (int rb = 0; rb < kRB; ++rb) acc[rb][tb] = mfma16x16x32(av[rb], bq[f % 3], acc[rb][tb]);
         }
       }
-      // keep that order: the step's conversions, then per B fragment one LDS read and its
-      // four MFMAs
+      // keep that order: the first two B reads; per MFMA step its conversions, then per B
+      // fragment the read two ahead and its four MFMAs (the groups count exactly these
+      // instructions: the scale bytes are read and converted outside this region)
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);  // conversions
 #pragma unroll
         for (int tb = 0; tb < NBT; ++tb) {
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+          if (s * NBT + tb + 2 < kF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
           __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // MFMAs
         }
       }
     };
     // Step kb: copy activation block kb + 1 into the other stage, request weight block kb + 2,
-    // MFMAs of block kb, then wait for the copy (all but the four weight requests just
-    // issued) and for this wave's LDS reads, and meet at the barrier.
+    // read the scale bytes of block kb + 1, MFMAs of block kb; then wait for the copy (all but
+    // the four weight requests just issued) and for this wave's LDS reads, meet at the
+    // barrier, and convert the scale bytes read for the next step.  The empty asm keeps the
+    // conversion after the barrier: moved up next to the reads, it made every step wait for
+    // them before its first MFMA.
+    uint32_t sbn[kRB];
+    float sc[kRB];
     auto step = [&](int kb, uint8_t* cur, uint8_t* nxt, const uint4 (&wc)[kRB], uint4 (&wn)[kRB])
         __attribute__((always_inline)) {
       __builtin_amdgcn_sched_barrier(0);
@@ -316,8 +344,14 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_prefill(PrefillArgs a, const
       __builtin_amdgcn_sched_barrier(0);
       load_w(min(kb + 2, nk - 1), wn);
       __builtin_amdgcn_sched_barrier(0);
-      compute(kb, wc, cur);
+      read_scales(min(kb + 1, nk - 1), sbn);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(wc, sc, cur);
+      __builtin_amdgcn_sched_barrier(0);
       wait_then_barrier<kRB>();
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb) asm volatile("" : "+v"(sbn[rb]));
+      to_scales(sbn, sc);
     };
     // The K loop: the stage (kb % 2) and the weight set (kb % 3) are fixed in each step of a
     // six-step body; nk is a multiple of 4, so 0, 2 or 4 steps remain after the full groups.
@@ -327,6 +361,8 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_prefill(PrefillArgs a, const
       for (int rb = 0; rb < kRB; ++rb)
 #pragma unroll
         for (int tb = 0; tb < NBT; ++tb) acc[rb][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      read_scales(0, sbn);
+      to_scales(sbn, sc);
       int kb = 0;
       for (; kb + 6 <= nk; kb += 6) {
         step(kb, xs0, xs1, w0, w2);
@@ -365,7 +401,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_prefill(PrefillArgs a, const
                 const bool situ = a.gact == K3X_ACT_SITU;
                 const float h0 = situ ? situ_fast(g0, u0, a.b1, a.b2) : swiglu_fast(g0, u0);
                 const float h1 = situ ? situ_fast(g1, u1, a.b1, a.b2) : swiglu_fast(g1, u1);
-                hv[i / 2] = f32_to_bf16_bits(h0) | (f32_to_bf16_bits(h1) << 16);
+                hv[i / 2] = pack_bf16x2_rne(h0, h1);
               }
               *reinterpret_cast<uint2*>(h + 16 * rb) = make_uint2(hv[0], hv[1]);
             }
