@@ -102,6 +102,10 @@ __device__ __forceinline__ void buf_copy16_lds(__amdgpu_buffer_rsrc_t r, void* l
 // memory clobber, so the compiler moves no memory access across either part.
 template <int N>
 __device__ __forceinline__ void wait_then_barrier() {
+  // the same wait as a builtin first, so that the compiler's own wait tracking knows it and
+  // adds no wait of its own for the LDS copies it retires
+  static_assert(N < 16, "vmcnt");
+  __builtin_amdgcn_s_waitcnt(N | (7 << 4));
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
@@ -233,12 +237,13 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_prefill(PrefillArgs a, const
         buf_copy16_lds(xrs, stage + (16 * j + 4 * wave) * kXRow, xo[j], (uint32_t)(kXRow * kb));
     };
     // weight rows of this wave: W1/W3 mode row blocks 0, 1 of W1 and the same of W3
+    auto load_w1 = [&](int kb, int rb, uint4 (&w)[kRB]) __attribute__((always_inline)) {
+      const uint32_t row = (uint32_t)(kW13 ? r0 + 32 * wave + 16 * (rb % 2) : r0 + 64 * wave + 16 * rb);
+      w[rb] = buf_load16(kW13 && rb >= 2 ? whi : wlo, wl, row * wrow + 64u * (uint32_t)kb);
+    };
     auto load_w = [&](int kb, uint4 (&w)[kRB]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int rb = 0; rb < kRB; ++rb) {
-        const uint32_t row = (uint32_t)(kW13 ? r0 + 32 * wave + 16 * (rb % 2) : r0 + 64 * wave + 16 * rb);
-        w[rb] = buf_load16(kW13 && rb >= 2 ? whi : wlo, wl, row * wrow + 64u * (uint32_t)kb);
-      }
+      for (int rb = 0; rb < kRB; ++rb) load_w1(kb, rb, w);
     };
     // Scale rows of an item: contiguous in each scale tensor (the item's rows are
     // consecutive), copied into ss with the buffer-to-LDS copy; pieces past a region's end
@@ -293,8 +298,8 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_prefill(PrefillArgs a, const
 
     // MFMAs of one K block: per MFMA step s the four A operands are converted, then for each
     // column block one B fragment (read two fragments ahead) meets the four A operands.
-    auto compute = [&](const uint4 (&w)[kRB], const float (&scale)[kRB], const uint8_t* stage)
-        __attribute__((always_inline)) {
+    auto compute = [&](const uint4 (&w)[kRB], const float (&scale)[kRB], const uint8_t* stage,
+                       auto&& request) __attribute__((always_inline)) {
       auto read_b = [&](int f) __attribute__((always_inline)) {
         return as_bf16x8(*reinterpret_cast<const uint4*>(stage + (f % NBT) * 16 * kXRow + bo[f / NBT]));
       };
@@ -313,6 +318,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_prefill(PrefillArgs a, const
           if (f + 2 < kF) bq[(f + 2) % 3] = read_b(f + 2);
 #pragma unroll
           for (int rb = 0; rb < kRB; ++rb) acc[rb][tb] = mfma16x16x32(av[rb], bq[f % 3], acc[rb][tb]);
+          if (tb == 0) request(s);
         }
       }
       // keep that order: the first two B reads; per MFMA step its conversions, then per B
@@ -326,13 +332,16 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_prefill(PrefillArgs a, const
         for (int tb = 0; tb < NBT; ++tb) {
           if (s * NBT + tb + 2 < kF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
           __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // MFMAs
+          if (tb == 0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // weight request
         }
       }
     };
-    // Step kb: copy activation block kb + 1 into the other stage, request weight block kb + 2,
-    // read the scale bytes of block kb + 1, MFMAs of block kb; then wait for the copy (all but
-    // the four weight requests just issued) and for this wave's LDS reads, meet at the
-    // barrier, and convert the scale bytes read for the next step.  The empty asm keeps the
+    // Step kb: copy activation block kb + 1 into the other stage, read the scale bytes of block
+    // kb + 1, MFMAs of block kb with the four requests of weight block kb + 2 spread over them
+    // (one after the first MFMA group of each MFMA step: issued together at the start they
+    // held the wave up behind the copies); then wait for the copy (all but the four weight
+    // requests) and for this wave's LDS reads, meet at the barrier, and convert the scale
+    // bytes read for the next step.  The empty asm keeps the
     // conversion after the barrier: moved up next to the reads, it made every step wait for
     // them before its first MFMA.
     uint32_t sbn[kRB];
@@ -342,11 +351,10 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_prefill(PrefillArgs a, const
       __builtin_amdgcn_sched_barrier(0);
       copy_x(nxt, min(kb + 1, nk - 1));
       __builtin_amdgcn_sched_barrier(0);
-      load_w(min(kb + 2, nk - 1), wn);
-      __builtin_amdgcn_sched_barrier(0);
       read_scales(min(kb + 1, nk - 1), sbn);
       __builtin_amdgcn_sched_barrier(0);
-      compute(wc, sc, cur);
+      const int kw = min(kb + 2, nk - 1);
+      compute(wc, sc, cur, [&](int rb) __attribute__((always_inline)) { load_w1(kw, rb, wn); });
       __builtin_amdgcn_sched_barrier(0);
       wait_then_barrier<kRB>();
 #pragma unroll
@@ -382,31 +390,45 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_prefill(PrefillArgs a, const
       }
     };
 
-    // epilogue: lane holds rows 4q..4q+3 of each row block for column 16 tb + n
-    auto epilogue = [&](int cstart, int cm, int cr0) __attribute__((always_inline)) {
+    // epilogue: lane holds rows 4q..4q+3 of each row block for column 16 tb + n.  W1/W3 mode
+    // picks the activation once per item, so the branch-free body lets the compiler overlap
+    // the evaluations of the item's h values.
+    auto epilogue_h = [&](int cstart, int cm, int cr0, auto situ_c) __attribute__((always_inline)) {
+      constexpr bool situ = decltype(situ_c)::value;
 #pragma unroll
       for (int tb = 0; tb < NBT; ++tb) {
+        uint32_t hv[kRB / 2][2];
+#pragma unroll
+        for (int rb = 0; rb < kRB / 2; ++rb)
+#pragma unroll
+          for (int i = 0; i < 4; i += 2) {
+            const float g0 = acc[rb][tb][i], u0 = acc[rb + kRB / 2][tb][i];
+            const float g1 = acc[rb][tb][i + 1], u1 = acc[rb + kRB / 2][tb][i + 1];
+            const float h0 = situ ? situ_fast(g0, u0, a.b1, a.b2) : swiglu_fast(g0, u0);
+            const float h1 = situ ? situ_fast(g1, u1, a.b1, a.b2) : swiglu_fast(g1, u1);
+            hv[rb][i / 2] = pack_bf16x2_rne(h0, h1);
+          }
         const int col = 16 * tb + n;
         if (col < cm) {
-          const size_t pos = (size_t)(cstart + col);
-          if (kW13) {
-            uint16_t* h = static_cast<uint16_t*>(a.out) + pos * a.rows + cr0 + 32 * wave + 4 * q;
+          uint16_t* h = static_cast<uint16_t*>(a.out) + (size_t)(cstart + col) * a.rows + cr0 + 32 * wave + 4 * q;
 #pragma unroll
-            for (int rb = 0; rb < kRB / 2; ++rb) {
-              uint32_t hv[2];
+          for (int rb = 0; rb < kRB / 2; ++rb)
+            *reinterpret_cast<uint2*>(h + 16 * rb) = make_uint2(hv[rb][0], hv[rb][1]);
+        }
+      }
+    };
+    auto epilogue = [&](int cstart, int cm, int cr0) __attribute__((always_inline)) {
+      if constexpr (kW13) {
+        if (a.gact == K3X_ACT_SITU)
+          epilogue_h(cstart, cm, cr0, std::true_type{});
+        else
+          epilogue_h(cstart, cm, cr0, std::false_type{});
+      } else {
 #pragma unroll
-              for (int i = 0; i < 4; i += 2) {
-                const float g0 = acc[rb][tb][i], u0 = acc[rb + kRB / 2][tb][i];
-                const float g1 = acc[rb][tb][i + 1], u1 = acc[rb + kRB / 2][tb][i + 1];
-                const bool situ = a.gact == K3X_ACT_SITU;
-                const float h0 = situ ? situ_fast(g0, u0, a.b1, a.b2) : swiglu_fast(g0, u0);
-                const float h1 = situ ? situ_fast(g1, u1, a.b1, a.b2) : swiglu_fast(g1, u1);
-                hv[i / 2] = pack_bf16x2_rne(h0, h1);
-              }
-              *reinterpret_cast<uint2*>(h + 16 * rb) = make_uint2(hv[0], hv[1]);
-            }
-          } else {
-            float* d = static_cast<float*>(a.out) + pos * a.rows + cr0 + 64 * wave + 4 * q;
+        for (int tb = 0; tb < NBT; ++tb) {
+          const int col = 16 * tb + n;
+          if (col < cm) {
+            float* d = static_cast<float*>(a.out) + (size_t)(cstart + col) * a.rows + cr0 + 64 * wave + 4 * q;
 #pragma unroll
             for (int rb = 0; rb < kRB; ++rb)
               *reinterpret_cast<float4*>(d + 16 * rb) =
