@@ -212,7 +212,7 @@ hipError_t launch_prefill_gemms(const k3x_pool& p, const uint16_t* x, int32_t T,
 // True when the sorted-tile kernels take the batch: two or more tokens, hidden and inter
 // multiples of 512, K <= 4096 and 32-bit row offsets.
 inline bool use_prefill(int32_t E, int32_t H, int32_t I, int32_t T, int32_t topk) {
-  // Tiles of 96 slots; items of 128 h rows (W1/W3) or 256 d rows (W2); the item's scale rows
+  // Tiles of 96 slots; items of 256 h rows (W1/W3) or 512 d rows (W2); the item's scale rows
   // (K / 32 bytes each, K <= 4096) fit in LDS.  (They also stream the weights of lightly
   // shared experts faster than the 16-slot tiles.)  A single token takes the exact decode
   // path before this is asked.

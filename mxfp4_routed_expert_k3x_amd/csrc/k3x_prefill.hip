@@ -8,12 +8,12 @@
 // with h rounded to bf16 before W2, slot-order combine).
 //
 // Slots are sorted by expert into tiles of at most 96 slots of one expert.  An item is one
-// tile against a chunk of output rows, computed by one workgroup of 4 waves; two workgroups
-// share a CU, each with its own barriers, so while one waits at a barrier the other keeps
-// the matrix cores busy:
-//   - W1/W3 mode: 128 rows of h (each wave 32 rows of W1 and the same 32 rows of W3),
+// tile against a chunk of output rows, computed by one workgroup of 8 waves, one workgroup per
+// CU (two waves per SIMD); the eight waves share each staged activation block, so a CU copies
+// every activation block once per item for twice the weight rows of a 4-wave workgroup:
+//   - W1/W3 mode: 256 rows of h (each wave 32 rows of W1 and the same 32 rows of W3),
 //     epilogue h = bf16(silu(g) * u), or of SiTU-GLU when the pool asks for it;
-//   - W2 mode: 256 rows of d (each wave 64 rows of W2).
+//   - W2 mode: 512 rows of d (each wave 64 rows of W2).
 // h and d are stored by sorted position (row = the slot's index in the sorted order), so W2
 // reads its tile's h rows contiguously and the combine gathers d through the inverse order.
 //
@@ -33,7 +33,7 @@
 //
 // Each K block ends with one wait + barrier: every wave waits for its own copies into the
 // next stage (the copies were issued before the block's weight requests, so the wait leaves
-// those in flight) and for its LDS reads of the current stage, then all four waves meet.
+// those in flight) and for its LDS reads of the current stage, then all eight waves meet.
 // Within a block each B fragment is read two fragments before its MFMAs and the scale bytes
 // one block ahead, so no MFMA waits for an LDS read issued just before it.
 //
@@ -50,7 +50,7 @@ namespace k3x {
 namespace {
 
 constexpr int kTT = 96;                        // slots per tile
-constexpr int kWaves = 4;                      // waves per workgroup; two workgroups per CU
+constexpr int kWaves = 8;                      // waves per workgroup; one workgroup per CU
 constexpr int kThreads = kWave * kWaves;
 constexpr int kRB = 4;                         // 16-row weight blocks per wave
 constexpr int kXRow = 2 * kKBlock;             // bytes of one staged activation row (128 bf16)
@@ -137,10 +137,10 @@ using ic = std::integral_constant<int, N>;
 // header: [0] tile count, [1 + k] end of tile class k in the tile array (the sort writes the
 // tiles class by class; class k needs k + 1 column blocks).
 template <bool kW13>
-__global__ __launch_bounds__(kThreads, 2) void gemm_prefill(PrefillArgs a, const int32_t* __restrict__ header,
+__global__ __launch_bounds__(kThreads, 1) void gemm_prefill(PrefillArgs a, const int32_t* __restrict__ header,
                                                             const int4* __restrict__ tiles,
                                                             const int32_t* __restrict__ perm) {
-  // two activation stages and the item's scale rows: 80 KB, so two workgroups fit a CU
+  // two activation stages (24 KB each) and the item's scale rows (64 KB): 112 KB of the CU's 160
   __shared__ __align__(16) uint8_t xs0[kXStage];
   __shared__ __align__(16) uint8_t xs1[kXStage];
   __shared__ __align__(16) uint8_t ss[kItemWRows * kMaxScaleRow];
@@ -163,9 +163,12 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_prefill(PrefillArgs a, const
   uint32_t bo[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s) bo[s] = (uint32_t)n * kXRow + 16u * (uint32_t)((4 * q + s) ^ n);
-  // the activation rows this lane copies: row 16 j + xr of a stage (j = column block), whose
-  // data piece (lane % 16) ^ xr it brings to position lane % 16
-  const int xr = 4 * wave + lane / 16;
+  // the activation rows this lane copies: row 16 j + xr of a stage (j = a column block of the
+  // wave's copies), whose data piece (lane % 16) ^ xr it brings to position lane % 16
+  const int xr = 4 * (wave % 4) + lane / 16;
+  // the stage's 4 NBT row quads are dealt round-robin: waves 0..3 copy quad wave % 4 of the
+  // even column blocks, waves 4..7 of the odd ones
+  const int wh = __builtin_amdgcn_readfirstlane(wave / 4);
   const uint32_t xpiece = 16u * (uint32_t)((lane % 16) ^ xr);
   // this lane's scale bytes in LDS (group 4 kb + q of row block rb at sa[rb] + 4 kb): W1/W3
   // mode the 128 W1 rows in the first half of ss, the 128 W3 rows in the second; W2 mode the
@@ -196,10 +199,12 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_prefill(PrefillArgs a, const
 
     // ---- item state: expert, first position, slot count, first row ----
     int e, start, m, r0;
-    uint32_t xo[NBT];  // byte offset of this lane's copied activation row of column block j
+    constexpr int kNC = (NBT + 1) / 2;  // copies per wave and stage
+    auto jc = [&](int c) __attribute__((always_inline)) { return 2 * c + wh; };  // their column blocks
+    uint32_t xo[kNC];  // byte offset of this lane's copied activation row of copy c
     __amdgpu_buffer_rsrc_t wlo, whi;
     int ne = 0, nstart = 0, nm = 1, nchunk = 0;
-    int32_t nslot[NBT];
+    int32_t nslot[kNC];
 
     auto fetch_tile = [&](int item, int& te, int& tstart, int& tm, int& tchunk) __attribute__((always_inline)) {
       const int4 tv = tiles[die + kNumXcd * (item / chunks)];
@@ -208,33 +213,34 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_prefill(PrefillArgs a, const
       tm = tv.z;
       tchunk = item % chunks;
     };
-    auto fetch_rows = [&](int tstart, int tm, int32_t (&slot)[NBT]) __attribute__((always_inline)) {
+    auto fetch_rows = [&](int tstart, int tm, int32_t (&slot)[kNC]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int j = 0; j < NBT; ++j) {
+      for (int c = 0; c < kNC; ++c) {
         // rows past the tile repeat its last row
-        const int i = min(16 * j + xr, tm - 1);
-        slot[j] = kW13 ? perm[tstart + i] : tstart + i;
+        const int i = min(16 * min(jc(c), NBT - 1) + xr, tm - 1);
+        slot[c] = kW13 ? perm[tstart + i] : tstart + i;
       }
     };
-    auto enter = [&](int te, int tstart, int tm, int tchunk, const int32_t (&slot)[NBT]) __attribute__((always_inline)) {
+    auto enter = [&](int te, int tstart, int tm, int tchunk, const int32_t (&slot)[kNC]) __attribute__((always_inline)) {
       e = __builtin_amdgcn_readfirstlane(te);
       start = __builtin_amdgcn_readfirstlane(tstart);
       m = __builtin_amdgcn_readfirstlane(tm);
       r0 = __builtin_amdgcn_readfirstlane(tchunk * kRows);
 #pragma unroll
-      for (int j = 0; j < NBT; ++j) {
-        const uint32_t r = kW13 ? (uint32_t)slot[j] / (uint32_t)a.topk : (uint32_t)slot[j];
-        xo[j] = 2u * (r * (uint32_t)a.K) + xpiece;
+      for (int c = 0; c < kNC; ++c) {
+        const uint32_t r = kW13 ? (uint32_t)slot[c] / (uint32_t)a.topk : (uint32_t)slot[c];
+        xo[c] = 2u * (r * (uint32_t)a.K) + xpiece;
       }
       wlo = make_rsrc(a.wa + (size_t)e * a.st_wa, wbytes);
       whi = kW13 ? make_rsrc(a.wb + (size_t)e * a.st_wb, wbytes) : wlo;
     };
 
-    // Activation block kb (this wave's four rows of each column block) into a stage.
+    // Activation block kb (this wave's row quads) into a stage.  With an odd NBT the last copy
+    // of waves 4..7 fills column block NBT, which no MFMA reads (a stage holds six).
     auto copy_x = [&](uint8_t* stage, int kb) __attribute__((always_inline)) {
 #pragma unroll
-      for (int j = 0; j < NBT; ++j)
-        buf_copy16_lds(xrs, stage + (16 * j + 4 * wave) * kXRow, xo[j], (uint32_t)(kXRow * kb));
+      for (int c = 0; c < kNC; ++c)
+        buf_copy16_lds(xrs, stage + (16 * jc(c) + 4 * (wave % 4)) * kXRow, xo[c], (uint32_t)(kXRow * kb));
     };
     // weight rows of this wave: W1/W3 mode row blocks 0, 1 of W1 and the same of W3
     auto load_w1 = [&](int kb, int rb, uint4 (&w)[kRB]) __attribute__((always_inline)) {
@@ -440,7 +446,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_prefill(PrefillArgs a, const
 
     {
       int te, ts, tm, tc;
-      int32_t slot[NBT];
+      int32_t slot[kNC];
       fetch_tile(it, te, ts, tm, tc);
       fetch_rows(ts, tm, slot);
       enter(te, ts, tm, tc, slot);
