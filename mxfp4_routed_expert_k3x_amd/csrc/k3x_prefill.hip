@@ -140,10 +140,19 @@ template <bool kW13>
 __global__ __launch_bounds__(kThreads, 1) void gemm_prefill(PrefillArgs a, const int32_t* __restrict__ header,
                                                             const int4* __restrict__ tiles,
                                                             const int32_t* __restrict__ perm) {
-  // two activation stages (24 KB each) and the item's scale rows (64 KB): 112 KB of the CU's 160
+  // two activation stages (24 KB each) and the item's scale rows (64 KB): 112 KB of the CU's
+  // 160, with the epilogue's slices 122 KB (W1/W3) or 146 KB (W2)
   __shared__ __align__(16) uint8_t xs0[kXStage];
   __shared__ __align__(16) uint8_t xs1[kXStage];
   __shared__ __align__(16) uint8_t ss[kItemWRows * kMaxScaleRow];
+  // The epilogue turns each wave's outputs of one column block around in a slice of its own
+  // (no barrier), so that a store covers whole runs of rows of a position: W1/W3 16
+  // positions x 32 h rows (bf16, rows padded to 40), W2 16 positions x 64 d rows (fp32,
+  // rows padded to 68; 34 KB).  The padding spreads the writes of the 16 positions over the
+  // banks.
+  constexpr int kTrRowH = 40;
+  constexpr int kTrRow = 68;
+  __shared__ __align__(16) float xt[kW13 ? kWaves * 16 * kTrRowH / 2 : kWaves * 16 * kTrRow];
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -414,13 +423,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_prefill(PrefillArgs a, const
             const float h1 = situ ? situ_fast(g1, u1, a.b1, a.b2) : swiglu_fast(g1, u1);
             hv[rb][i / 2] = pack_bf16x2_rne(h0, h1);
           }
-        const int col = 16 * tb + n;
-        if (col < cm) {
-          uint16_t* h = static_cast<uint16_t*>(a.out) + (size_t)(cstart + col) * a.rows + cr0 + 32 * wave + 4 * q;
+        // one 16-byte store per lane: 8 rows of a position, 64 bytes per position
+        uint16_t* tw = reinterpret_cast<uint16_t*>(xt) + wave * 16 * kTrRowH;
 #pragma unroll
-          for (int rb = 0; rb < kRB / 2; ++rb)
-            *reinterpret_cast<uint2*>(h + 16 * rb) = make_uint2(hv[rb][0], hv[rb][1]);
-        }
+        for (int rb = 0; rb < kRB / 2; ++rb)
+          *reinterpret_cast<uint2*>(tw + n * kTrRowH + 16 * rb + 4 * q) = make_uint2(hv[rb][0], hv[rb][1]);
+        const int p = lane / 4;
+        const uint4 v = *reinterpret_cast<const uint4*>(tw + p * kTrRowH + 8 * (lane % 4));
+        const int col = 16 * tb + p;
+        if (col < cm)
+          *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out) + (size_t)(cstart + col) * a.rows + cr0 +
+                                    32 * wave + 8 * (lane % 4)) = v;
       }
     };
     auto epilogue = [&](int cstart, int cm, int cr0) __attribute__((always_inline)) {
@@ -430,15 +443,21 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_prefill(PrefillArgs a, const
         else
           epilogue_h(cstart, cm, cr0, std::false_type{});
       } else {
+        // each store covers 4 positions x 64 rows (256 bytes each)
+        float* tw = xt + wave * 16 * kTrRow;
 #pragma unroll
         for (int tb = 0; tb < NBT; ++tb) {
-          const int col = 16 * tb + n;
-          if (col < cm) {
-            float* d = static_cast<float*>(a.out) + (size_t)(cstart + col) * a.rows + cr0 + 64 * wave + 4 * q;
 #pragma unroll
-            for (int rb = 0; rb < kRB; ++rb)
-              *reinterpret_cast<float4*>(d + 16 * rb) =
-                  make_float4(acc[rb][tb][0], acc[rb][tb][1], acc[rb][tb][2], acc[rb][tb][3]);
+          for (int rb = 0; rb < kRB; ++rb)
+            *reinterpret_cast<f32x4*>(tw + n * kTrRow + 16 * rb + 4 * q) = acc[rb][tb];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int p = 4 * j + lane / 16;
+            const f32x4 v = *reinterpret_cast<const f32x4*>(tw + p * kTrRow + 4 * (lane % 16));
+            const int col = 16 * tb + p;
+            if (col < cm)
+              *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + (size_t)(cstart + col) * a.rows + cr0 +
+                                        64 * wave + 4 * (lane % 16)) = v;
           }
         }
       }
