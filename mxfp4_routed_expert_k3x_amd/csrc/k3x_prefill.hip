@@ -238,14 +238,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_prefill(PrefillArgs a, const
 #pragma unroll
       for (int c = 0; c < kNC; ++c) {
         const uint32_t r = kW13 ? (uint32_t)slot[c] / (uint32_t)a.topk : (uint32_t)slot[c];
-        xo[c] = 2u * (r * (uint32_t)a.K) + xpiece;
+        // a copy into the unused column block NBT (odd NBT, waves 4..7) reads out of range:
+        // the buffer unit then fetches nothing
+        xo[c] = jc(c) < NBT ? 2u * (r * (uint32_t)a.K) + xpiece : 0x80000000u;
       }
       wlo = make_rsrc(a.wa + (size_t)e * a.st_wa, wbytes);
       whi = kW13 ? make_rsrc(a.wb + (size_t)e * a.st_wb, wbytes) : wlo;
     };
 
     // Activation block kb (this wave's row quads) into a stage.  With an odd NBT the last copy
-    // of waves 4..7 fills column block NBT, which no MFMA reads (a stage holds six).
+    // of waves 4..7 targets column block NBT, which no MFMA reads (a stage holds six); its
+    // offset is out of the buffer's range, so it fetches nothing.
     auto copy_x = [&](uint8_t* stage, int kb) __attribute__((always_inline)) {
 #pragma unroll
       for (int c = 0; c < kNC; ++c)
