@@ -49,7 +49,7 @@ extern "C" {
 typedef enum k3x_status {
   K3X_OK = 0,
   K3X_E_INVALID_ARG = -1, /* NULL pointer, negative size, topk out of range, ...          */
-  K3X_E_UNSUPPORTED = -2, /* a shape, group size or alignment this build does not support */
+  K3X_E_UNSUPPORTED = -2, /* a shape, group size or alignment the library does not support */
   K3X_E_WORKSPACE = -3,   /* workspace missing, misaligned or smaller than required        */
   K3X_E_HIP = -4,         /* a HIP launch or runtime error (message in k3x_last_error)    */
   K3X_E_DROPS = -5        /* k3x_fetch_drops: at least one slot named an invalid expert    */
@@ -104,7 +104,7 @@ typedef struct k3x_pool k3x_pool;
  * not finite and positive.  Allocates host memory only; the device
  * tensors are borrowed and must outlive the pool.  Scale bytes are read as given: bytes
  * 2..252 give finite, normal weights for every E2M1 code (6 * 2^125 is the largest); 255
- * zeroes a group; 0, 1, 253 and 254 are outside the range this build promises to reproduce
+ * zeroes a group; 0, 1, 253 and 254 are outside the range the library promises to reproduce
  * exactly (253 and 254 overflow float for the larger codes, 0 and 1 give subnormal weights). */
 k3x_status k3x_expert_pool_create(const k3x_pool_desc *d, k3x_pool **out);
 

@@ -2,7 +2,7 @@
  * k3x oracle -- TEST INFRASTRUCTURE ONLY.
  *
  * A plain, slow, obviously ordered CPU implementation of the routed-expert hot path, used
- * only by the test suite, the smoke check and the bench's CPU-baseline leg to judge the
+ * only by the test suite, the smoke check and the bench's CPU-baseline leg to check the
  * HIP kernels.  The product path never calls it and shares no code, header, table or
  * constant with it.
  *

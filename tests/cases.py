@@ -50,7 +50,7 @@ def assert_y_close_oracle(y, y_ref32, y_ref64_fn, what=""):
     """Verdict against the oracle in its fp32 arithmetic.  The oracle's fp32 sums are one
     rounding of the definition and its fp64 sums another; where the fp32 one already lies
     beyond the tolerance from the fp64 one (a bf16 rounding of a large h that falls the other
-    way, amplified by W2), the result is judged against the fp64 oracle instead, and must
+    way, amplified by W2), the result is checked against the fp64 oracle instead, and must
     then be at least as close to it as the fp32 oracle is, on both measures.  Each such use
     is printed and recorded in FALLBACKS."""
     r32 = y_errors(y, y_ref32)
