@@ -145,15 +145,22 @@ __global__ __launch_bounds__(256) void route_scores_staged(const uint16_t* __res
       __builtin_amdgcn_sched_barrier(0);
     }
   }
+  // each token's sum ends in lane 0; lane k then takes token k's, so the block's sigmoids run
+  // side by side instead of one after another in lane 0
+  double mine = 0.0;
 #pragma unroll
   for (int k = 0; k < NT; ++k) {
     double a = acc[k];
 #pragma unroll
     for (int s = 32; s >= 1; s >>= 1) a = a + __shfl_down(a, s, kWave);
-    if (lane == 0 && k < nt) {
-      const float l = (float)a;
-      scores[(size_t)(t0 + k) * E + e] = (float)(1.0 / (1.0 + exp(-(double)l)));
-    }
+    const uint64_t bits = __builtin_bit_cast(uint64_t, a);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)bits, 0);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(bits >> 32), 0);
+    if (lane == k) mine = __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+  }
+  if (lane < nt) {
+    const float l = (float)mine;
+    scores[(size_t)(t0 + lane) * E + e] = (float)(1.0 / (1.0 + exp(-(double)l)));
   }
 }
 
