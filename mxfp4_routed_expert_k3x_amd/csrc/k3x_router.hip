@@ -7,7 +7,8 @@
 // stays in registers while the wave sums the block's tokens side by side.  Lane L owns the
 // 8-element chunks whose index is L mod 64 and sums their exact bf16*bf16 products in double,
 // in ascending order; the 64 lane partials are then folded p[L] += p[L + s] for s = 32 .. 1
-// with down-shuffles.  The float logit goes through a double sigmoid rounded once to float.
+// with down-shuffles.  The float logit goes through a double sigmoid rounded once to float
+// (for a block of tokens lane k then takes token k's, so the block's sigmoids run side by side).
 // This fixes the summation order completely, so the scores are reproducible bit for bit.
 // For widths that are multiples of 512 (up to 8192) the row is loaded whole and at once (a
 // fixed number of 16-byte chunks per lane) and the block's tokens are staged in LDS while the
