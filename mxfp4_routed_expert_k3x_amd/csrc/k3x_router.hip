@@ -3,8 +3,10 @@
 // for selection only, repeated argmax with ties to the lower expert, gates from the unbiased
 // scores renormalised by their float sum and scaled by routed_scale.
 //
-// Kernel 1 (route_scores): one wave per (expert, block of 4 tokens).  The expert's weight row
-// stays in registers while the wave sums the block's tokens side by side.  Lane L owns the
+// Kernel 1 (route_scores): one wave per (expert, block of 4 tokens); for hidden sizes that are
+// multiples of 512 a block of 4 tokens takes two experts per wave and a single token one.  The
+// weight rows stay in registers while the wave sums the block's tokens side by side, each
+// staged chunk widened once for both experts.  Lane L owns the
 // 8-element chunks whose index is L mod 64 and sums their exact bf16*bf16 products in double,
 // in ascending order; the 64 lane partials are then folded p[L] += p[L + s] for s = 32 .. 1
 // with down-shuffles.  The float logit goes through a double sigmoid rounded once to float
@@ -97,71 +99,90 @@ __global__ __launch_bounds__(256) void route_scores(const uint16_t* __restrict__
   }
 }
 
-// The same scores for H = 512 * NCH: the wave's weight row is requested first (NCH chunks per
-// lane, no guards), the NT-token block is staged in LDS meanwhile, then summed in the order
-// above.  Slots of tokens past T are zero-filled and their sums dropped.
-template <int NCH, int NT>
+// The same scores for H = 512 * NCH: the wave's weight rows (EPW experts) are requested first
+// (NCH chunks per lane and row, no guards), the NT-token block is staged in LDS meanwhile, then
+// summed in the order above; each staged chunk of a token is widened once and used for every
+// one of the wave's experts.  Slots of tokens past T are zero-filled and their sums dropped.
+template <int NCH, int NT, int EPW>
 __global__ __launch_bounds__(256) void route_scores_staged(const uint16_t* __restrict__ x,
                                                            const uint16_t* __restrict__ W,
                                                            int32_t T, int32_t H, int32_t E,
                                                            float* __restrict__ scores) {
   extern __shared__ uint4 xs[];  // [NT][H / 8]
   const int lane = threadIdx.x % kWave;
-  const int e = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  const int e0 = (blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave) * EPW;
   const int t0 = blockIdx.y * NT;
   const int nt = min(NT, T - t0);
   const int cpr = NCH * kWave;
-  uint4 wv[NCH];
-  const uint4* wrow = reinterpret_cast<const uint4*>(W + (size_t)(e < E ? e : E - 1) * H);
+  uint4 wv[EPW][NCH];
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int i = 0; i < NCH; ++i) wv[i] = wrow[lane + kWave * i];
+  for (int u = 0; u < EPW; ++u) {
+    const int e = e0 + u < E ? e0 + u : E - 1;
+    const uint4* wrow = reinterpret_cast<const uint4*>(W + (size_t)e * H);
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) wv[u][i] = wrow[lane + kWave * i];
+  }
   __builtin_amdgcn_sched_barrier(0);
   for (int i = threadIdx.x; i < NT * cpr; i += blockDim.x)
     xs[i] = i < nt * cpr ? reinterpret_cast<const uint4*>(x + (size_t)(t0 + i / cpr) * H)[i % cpr]
                          : make_uint4(0, 0, 0, 0);
   __syncthreads();
-  if (e >= E) return;
-  double acc[NT];
+  if (e0 >= E) return;
+  double acc[EPW][NT];
 #pragma unroll
-  for (int k = 0; k < NT; ++k) acc[k] = 0.0;
+  for (int u = 0; u < EPW; ++u)
+#pragma unroll
+    for (int k = 0; k < NT; ++k) acc[u][k] = 0.0;
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
-    const uint32_t ws[4] = {wv[i].x, wv[i].y, wv[i].z, wv[i].w};
 #pragma unroll
     for (int k = 0; k < NT; ++k) {
       const uint4 xv = xs[k * cpr + lane + kWave * i];
       const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+      double xd[8];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        acc[k] = acc[k] + (double)bf16_bits_to_f32(xw[j] & 0xFFFFu) *
-                              (double)bf16_bits_to_f32(ws[j] & 0xFFFFu);
-        acc[k] = acc[k] + (double)bf16_bits_to_f32(xw[j] >> 16) *
-                              (double)bf16_bits_to_f32(ws[j] >> 16);
+        xd[2 * j] = (double)bf16_bits_to_f32(xw[j] & 0xFFFFu);
+        xd[2 * j + 1] = (double)bf16_bits_to_f32(xw[j] >> 16);
+      }
+#pragma unroll
+      for (int u = 0; u < EPW; ++u) {
+        const uint32_t ws[4] = {wv[u][i].x, wv[u][i].y, wv[u][i].z, wv[u][i].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc[u][k] = acc[u][k] + xd[2 * j] * (double)bf16_bits_to_f32(ws[j] & 0xFFFFu);
+          acc[u][k] = acc[u][k] + xd[2 * j + 1] * (double)bf16_bits_to_f32(ws[j] >> 16);
+        }
       }
     }
     if (NT > 1) {  // one chunk's tokens live at a time
 #pragma unroll
-      for (int k = 0; k < NT; ++k) asm volatile("" : "+v"(acc[k]));
+      for (int u = 0; u < EPW; ++u)
+#pragma unroll
+        for (int k = 0; k < NT; ++k) asm volatile("" : "+v"(acc[u][k]));
       __builtin_amdgcn_sched_barrier(0);
     }
   }
   // each token's sum ends in lane 0; lane k then takes token k's, so the block's sigmoids run
   // side by side instead of one after another in lane 0
-  double mine = 0.0;
 #pragma unroll
-  for (int k = 0; k < NT; ++k) {
-    double a = acc[k];
+  for (int u = 0; u < EPW; ++u) {
+    double mine = 0.0;
 #pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) a = a + __shfl_down(a, s, kWave);
-    const uint64_t bits = __builtin_bit_cast(uint64_t, a);
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)bits, 0);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(bits >> 32), 0);
-    if (lane == k) mine = __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
-  }
-  if (lane < nt) {
-    const float l = (float)mine;
-    scores[(size_t)(t0 + lane) * E + e] = (float)(1.0 / (1.0 + exp(-(double)l)));
+    for (int k = 0; k < NT; ++k) {
+      double a = acc[u][k];
+#pragma unroll
+      for (int s = 32; s >= 1; s >>= 1) a = a + __shfl_down(a, s, kWave);
+      const uint64_t bits = __builtin_bit_cast(uint64_t, a);
+      const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)bits, 0);
+      const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(bits >> 32), 0);
+      if (lane == k) mine = __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+    }
+    if (lane < nt && e0 + u < E) {
+      const float l = (float)mine;
+      scores[(size_t)(t0 + lane) * E + e0 + u] = (float)(1.0 / (1.0 + exp(-(double)l)));
+    }
   }
 }
 
@@ -265,8 +286,8 @@ typedef void (*ScoresKernel)(const uint16_t*, const uint16_t*, int32_t, int32_t,
 
 template <int... N>
 ScoresKernel staged_kernel(int nch, int nt) {
-  constexpr ScoresKernel k1[] = {route_scores_staged<N, 1>...};
-  constexpr ScoresKernel k4[] = {route_scores_staged<N, kRouteTokBlock>...};
+  constexpr ScoresKernel k1[] = {route_scores_staged<N, 1, 1>...};
+  constexpr ScoresKernel k4[] = {route_scores_staged<N, kRouteTokBlock, 2>...};
   return (nt == 1 ? k1 : k4)[nch - 1];
 }
 
@@ -328,7 +349,8 @@ hipError_t launch_route_scores(const k3x_router_desc& r, const uint16_t* x, int3
   hipError_t err;
   if (H % 512 == 0 && H <= 8192) {
     const int nt = T == 1 ? 1 : kRouteTokBlock;
-    dim3 g((E + 3) / 4, (T + nt - 1) / nt);
+    const int epw = nt == 1 ? 1 : 2;  // experts per wave (route_scores_staged's EPW)
+    dim3 g((E + 4 * epw - 1) / (4 * epw), (T + nt - 1) / nt);
     err = launch("route_scores",
                  staged_kernel<1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16>(H / 512, nt),
                  g, dim3(256), (uint32_t)(sizeof(uint16_t) * (size_t)nt * H), s, x, W, T, H, E,
