@@ -206,20 +206,24 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_prefill(PrefillArgs a, const
     constexpr int NBT = decltype(nbc)::value;
     if (it >= hi) return;
 
-    // ---- item state: expert, first position, slot count, first row ----
+    // ---- item state: expert, first position, slot count, first row of the entered item,
+    // and the next item's registers, set up before its first requests go out during the
+    // entered item's last two K steps ----
     int e, start, m, r0;
     constexpr int kNC = (NBT + 1) / 2;  // copies per wave and stage
     auto jc = [&](int c) __attribute__((always_inline)) { return 2 * c + wh; };  // their column blocks
     uint32_t xo[kNC];  // byte offset of this lane's copied activation row of copy c
     __amdgpu_buffer_rsrc_t wlo, whi;
-    int ne = 0, nstart = 0, nm = 1, nchunk = 0;
+    int ne = 0, nstart = 0, nm = 1, nchunk = 0, nr0 = 0;
     int32_t nslot[kNC];
+    uint32_t nxo[kNC];
+    __amdgpu_buffer_rsrc_t nwlo, nwhi;
 
     auto fetch_tile = [&](int item, int& te, int& tstart, int& tm, int& tchunk) __attribute__((always_inline)) {
       const int4 tv = tiles[die + kNumXcd * (item / chunks)];
-      te = tv.x;
-      tstart = tv.y;
-      tm = tv.z;
+      te = __builtin_amdgcn_readfirstlane(tv.x);
+      tstart = __builtin_amdgcn_readfirstlane(tv.y);
+      tm = __builtin_amdgcn_readfirstlane(tv.z);
       tchunk = item % chunks;
     };
     auto fetch_rows = [&](int tstart, int tm, int32_t (&slot)[kNC]) __attribute__((always_inline)) {
@@ -230,48 +234,47 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_prefill(PrefillArgs a, const
         slot[c] = kW13 ? perm[tstart + i] : tstart + i;
       }
     };
-    auto enter = [&](int te, int tstart, int tm, int tchunk, const int32_t (&slot)[kNC]) __attribute__((always_inline)) {
-      e = __builtin_amdgcn_readfirstlane(te);
-      start = __builtin_amdgcn_readfirstlane(tstart);
-      m = __builtin_amdgcn_readfirstlane(tm);
-      r0 = __builtin_amdgcn_readfirstlane(tchunk * kRows);
+    // first row and weight descriptors of an item
+    auto item_rsrc = [&](int te, int tchunk, int& tr0, __amdgpu_buffer_rsrc_t& tlo,
+                         __amdgpu_buffer_rsrc_t& thi) __attribute__((always_inline)) {
+      tr0 = __builtin_amdgcn_readfirstlane(tchunk * kRows);
+      tlo = make_rsrc(a.wa + (size_t)te * a.st_wa, wbytes);
+      thi = kW13 ? make_rsrc(a.wb + (size_t)te * a.st_wb, wbytes) : tlo;
+    };
+    // offsets of this lane's activation copies of an item
+    auto item_xo = [&](const int32_t (&slot)[kNC], uint32_t (&txo)[kNC]) __attribute__((always_inline)) {
 #pragma unroll
       for (int c = 0; c < kNC; ++c) {
         const uint32_t r = kW13 ? (uint32_t)slot[c] / (uint32_t)a.topk : (uint32_t)slot[c];
         // a copy into the unused column block NBT (odd NBT, waves 4..7) reads out of range:
         // the buffer unit then fetches nothing
-        xo[c] = jc(c) < NBT ? 2u * (r * (uint32_t)a.K) + xpiece : 0x80000000u;
+        txo[c] = jc(c) < NBT ? 2u * (r * (uint32_t)a.K) + xpiece : 0x80000000u;
       }
-      wlo = make_rsrc(a.wa + (size_t)e * a.st_wa, wbytes);
-      whi = kW13 ? make_rsrc(a.wb + (size_t)e * a.st_wb, wbytes) : wlo;
     };
 
     // Activation block kb (this wave's row quads) into a stage.  With an odd NBT the last copy
     // of waves 4..7 targets column block NBT, which no MFMA reads (a stage holds six); its
     // offset is out of the buffer's range, so it fetches nothing.
-    auto copy_x = [&](uint8_t* stage, int kb) __attribute__((always_inline)) {
+    auto copy_x = [&](uint8_t* stage, int kb, const uint32_t (&txo)[kNC]) __attribute__((always_inline)) {
 #pragma unroll
       for (int c = 0; c < kNC; ++c)
-        buf_copy16_lds(xrs, stage + (16 * jc(c) + 4 * (wave % 4)) * kXRow, xo[c], (uint32_t)(kXRow * kb));
+        buf_copy16_lds(xrs, stage + (16 * jc(c) + 4 * (wave % 4)) * kXRow, txo[c], (uint32_t)(kXRow * kb));
     };
     // weight rows of this wave: W1/W3 mode row blocks 0, 1 of W1 and the same of W3
-    auto load_w1 = [&](int kb, int rb, uint4 (&w)[kRB]) __attribute__((always_inline)) {
-      const uint32_t row = (uint32_t)(kW13 ? r0 + 32 * wave + 16 * (rb % 2) : r0 + 64 * wave + 16 * rb);
-      w[rb] = buf_load16(kW13 && rb >= 2 ? whi : wlo, wl, row * wrow + 64u * (uint32_t)kb);
-    };
-    auto load_w = [&](int kb, uint4 (&w)[kRB]) __attribute__((always_inline)) {
-#pragma unroll
-      for (int rb = 0; rb < kRB; ++rb) load_w1(kb, rb, w);
+    auto load_w1 = [&](const __amdgpu_buffer_rsrc_t& tlo, const __amdgpu_buffer_rsrc_t& thi, int tr0, int kb,
+                       int rb, uint4 (&w)[kRB]) __attribute__((always_inline)) {
+      const uint32_t row = (uint32_t)(kW13 ? tr0 + 32 * wave + 16 * (rb % 2) : tr0 + 64 * wave + 16 * rb);
+      w[rb] = buf_load16(kW13 && rb >= 2 ? thi : tlo, wl, row * wrow + 64u * (uint32_t)kb);
     };
     // Scale rows of an item: contiguous in each scale tensor (the item's rows are
     // consecutive), copied into ss with the buffer-to-LDS copy; pieces past a region's end
     // repeat its last piece into the unused part of the region (W1/W3 mode: two regions of
     // 16 KB, W2 mode one of 32 KB).
-    auto copy_scales = [&]() __attribute__((always_inline)) {
+    auto copy_scales = [&](int te, int tr0) __attribute__((always_inline)) {
       const int pieces = (int)((kW13 ? kItemWRows / 2 : kItemWRows) * srow / 16);
       constexpr int kPer = (kW13 ? kItemWRows / 2 : kItemWRows) * kMaxScaleRow / 16 / kWave / kWaves;
-      const uint32_t src = (uint32_t)r0 * srow;
-      const __amdgpu_buffer_rsrc_t s1 = make_rsrc(a.sa + (size_t)e * a.st_sa, (uint32_t)a.rows * srow);
+      const uint32_t src = (uint32_t)tr0 * srow;
+      const __amdgpu_buffer_rsrc_t s1 = make_rsrc(a.sa + (size_t)te * a.st_sa, (uint32_t)a.rows * srow);
 #pragma unroll
       for (int j = 0; j < kPer; ++j) {
         const int chunk = j * kWaves + wave;
@@ -279,7 +282,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_prefill(PrefillArgs a, const
         buf_copy16_lds(s1, &ss[chunk * kWave * 16], src + 16u * piece, 0);
       }
       if (kW13) {
-        const __amdgpu_buffer_rsrc_t s3 = make_rsrc(a.sb + (size_t)e * a.st_sb, (uint32_t)a.rows * srow);
+        const __amdgpu_buffer_rsrc_t s3 = make_rsrc(a.sb + (size_t)te * a.st_sb, (uint32_t)a.rows * srow);
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
           const int chunk = j * kWaves + wave;
@@ -289,20 +292,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_prefill(PrefillArgs a, const
       }
     };
 
-    uint4 w0[kRB], w1[kRB], w2[kRB];
+    // four weight sets: block kb lives in set kb % 4, and as K is a multiple of four blocks
+    // every item starts in set 0, so its first two blocks can be requested during the
+    // previous item's last two steps
+    uint4 w0[kRB], w1[kRB], w2[kRB], w3[kRB];
     f32x4 acc[kRB][NBT];
-
-    // the first requests of the entered item: activation block 0, scale rows, weight blocks
-    // 0 and 1; the copies into LDS are the oldest
-    auto start_item = [&]() __attribute__((always_inline)) {
-      copy_x(xs0, 0);
-      copy_scales();
-      __builtin_amdgcn_sched_barrier(0);
-      load_w(0, w0);
-      load_w(1, w1);
-      __builtin_amdgcn_sched_barrier(0);
-    };
-
     // Scale bytes of K block kb for this lane's four row blocks, and their conversion to the
     // power-of-two factors.
     auto read_scales = [&](int kb, uint32_t (&sb)[kRB]) __attribute__((always_inline)) {
@@ -354,35 +348,64 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_prefill(PrefillArgs a, const
         }
       }
     };
-    // Step kb: copy activation block kb + 1 into the other stage, read the scale bytes of block
-    // kb + 1, MFMAs of block kb with the four requests of weight block kb + 2 spread over them
-    // (one after the first MFMA group of each MFMA step: issued together at the start they
-    // held the wave up behind the copies); then wait for the copy (all but the four weight
-    // requests) and for this wave's LDS reads, meet at the barrier, and convert the scale
-    // bytes read for the next step.  The empty asm keeps the
-    // conversion after the barrier: moved up next to the reads, it made every step wait for
-    // them before its first MFMA.
+    // Step kb (kb < nk - 2): copy activation block kb + 1 into the other stage, read the scale
+    // bytes of block kb + 1, MFMAs of block kb with the four requests of weight block kb + 2
+    // spread over them (one after the first MFMA group of each MFMA step: issued together at
+    // the start they held the wave up behind the copies); then wait for the copy (all but the
+    // four weight requests) and for this wave's LDS reads, meet at the barrier, and convert
+    // the scale bytes read for the next step.  The empty asm keeps the conversion after the
+    // barrier: moved up next to the reads, it made every step wait for them before its first
+    // MFMA.
     uint32_t sbn[kRB];
     float sc[kRB];
     auto step = [&](int kb, uint8_t* cur, uint8_t* nxt, const uint4 (&wc)[kRB], uint4 (&wn)[kRB])
         __attribute__((always_inline)) {
       __builtin_amdgcn_sched_barrier(0);
-      copy_x(nxt, min(kb + 1, nk - 1));
+      copy_x(nxt, kb + 1, xo);
       __builtin_amdgcn_sched_barrier(0);
-      read_scales(min(kb + 1, nk - 1), sbn);
+      read_scales(kb + 1, sbn);
       __builtin_amdgcn_sched_barrier(0);
-      const int kw = min(kb + 2, nk - 1);
-      compute(wc, sc, cur, [&](int rb) __attribute__((always_inline)) { load_w1(kw, rb, wn); });
+      compute(wc, sc, cur, [&](int rb) __attribute__((always_inline)) { load_w1(wlo, whi, r0, kb + 2, rb, wn); });
       __builtin_amdgcn_sched_barrier(0);
       wait_then_barrier<kRB>();
 #pragma unroll
       for (int rb = 0; rb < kRB; ++rb) asm volatile("" : "+v"(sbn[rb]));
       to_scales(sbn, sc);
     };
-    // The K loop: the stage (kb % 2) and the weight set (kb % 3) are fixed in each step of a
-    // six-step body; nk is a multiple of 4, so 0, 2 or 4 steps remain after the full groups.
-    // The last steps re-request the last block instead of branching.
-    auto kloop = [&]() __attribute__((always_inline)) {
+    // Step nk - 2: as a step, but the weight requests are the next item's block 0 (set 0).
+    auto step_penultimate = [&](int kb, uint8_t* cur, uint8_t* nxt, const uint4 (&wc)[kRB], uint4 (&wn)[kRB])
+        __attribute__((always_inline)) {
+      __builtin_amdgcn_sched_barrier(0);
+      copy_x(nxt, kb + 1, xo);
+      __builtin_amdgcn_sched_barrier(0);
+      read_scales(kb + 1, sbn);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(wc, sc, cur, [&](int rb) __attribute__((always_inline)) { load_w1(nwlo, nwhi, nr0, 0, rb, wn); });
+      __builtin_amdgcn_sched_barrier(0);
+      wait_then_barrier<kRB>();
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb) asm volatile("" : "+v"(sbn[rb]));
+      to_scales(sbn, sc);
+    };
+    // Step nk - 1: every wave has read the scale rows and stage 0 (barrier of step nk - 2), so
+    // the next item's activation block 0 and scale rows are copied in while this block's
+    // MFMAs run, with its weight block 1 (set 1) requested among them; the wait then covers
+    // everything but those four requests, so the next item can start after the epilogue.
+    auto step_last = [&](uint8_t* cur, uint8_t* nxt, const uint4 (&wc)[kRB], uint4 (&wn)[kRB])
+        __attribute__((always_inline)) {
+      __builtin_amdgcn_sched_barrier(0);
+      copy_x(nxt, 0, nxo);
+      copy_scales(ne, nr0);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(wc, sc, cur, [&](int rb) __attribute__((always_inline)) { load_w1(nwlo, nwhi, nr0, 1, rb, wn); });
+      __builtin_amdgcn_sched_barrier(0);
+      wait_then_barrier<kRB>();
+    };
+    // The K loop: the stage (kb % 2) and the weight set (kb % 4) are fixed in each step of a
+    // four-step body (nk is a multiple of 4); the last body's last two steps request the next
+    // item's first blocks.  The next item's registers are set up before those two steps (the
+    // entered item's own when it is the last: its blocks are then re-read and not used).
+    auto kloop = [&](bool more) __attribute__((always_inline)) {
 #pragma unroll
       for (int rb = 0; rb < kRB; ++rb)
 #pragma unroll
@@ -390,24 +413,30 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_prefill(PrefillArgs a, const
       read_scales(0, sbn);
       to_scales(sbn, sc);
       int kb = 0;
-      for (; kb + 6 <= nk; kb += 6) {
+      for (; kb + 4 < nk; kb += 4) {
         step(kb, xs0, xs1, w0, w2);
-        step(kb + 1, xs1, xs0, w1, w0);
-        step(kb + 2, xs0, xs1, w2, w1);
-        step(kb + 3, xs1, xs0, w0, w2);
-        step(kb + 4, xs0, xs1, w1, w0);
-        step(kb + 5, xs1, xs0, w2, w1);
+        step(kb + 1, xs1, xs0, w1, w3);
+        step(kb + 2, xs0, xs1, w2, w0);
+        step(kb + 3, xs1, xs0, w3, w1);
       }
-      if (kb < nk) {
-        step(kb, xs0, xs1, w0, w2);
-        step(kb + 1, xs1, xs0, w1, w0);
-        if (kb + 2 < nk) {
-          step(kb + 2, xs0, xs1, w2, w1);
-          step(kb + 3, xs1, xs0, w0, w2);
-        }
+      // the next item's rows (W1/W3 mode loads them from the sort's order) two steps ahead of
+      // their use, so that they hold no registers through the rest of the loop
+      if (more) fetch_rows(nstart, nm, nslot);
+      step(kb, xs0, xs1, w0, w2);
+      step(kb + 1, xs1, xs0, w1, w3);
+      if (more) {
+        item_rsrc(ne, nchunk, nr0, nwlo, nwhi);
+        item_xo(nslot, nxo);
+      } else {
+        ne = e;
+        nr0 = r0;
+        nwlo = wlo;
+        nwhi = whi;
+        for (int c = 0; c < kNC; ++c) nxo[c] = xo[c];
       }
+      step_penultimate(kb + 2, xs0, xs1, w2, w0);
+      step_last(xs1, xs0, w3, w1);
     };
-
     // epilogue: lane holds rows 4q..4q+3 of each row block for column 16 tb + n.  W1/W3 mode
     // picks the activation once per item, so the branch-free body lets the compiler overlap
     // the evaluations of the item's h values.
@@ -466,39 +495,45 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_prefill(PrefillArgs a, const
       }
     };
 
+    // the class's first item: its first requests (activation block 0 and the scale rows, the
+    // oldest, then weight blocks 0 and 1), and the wait for the copies
     {
-      int te, ts, tm, tc;
+      int tchunk;
       int32_t slot[kNC];
-      fetch_tile(it, te, ts, tm, tc);
-      fetch_rows(ts, tm, slot);
-      enter(te, ts, tm, tc, slot);
+      fetch_tile(it, e, start, m, tchunk);
+      fetch_rows(start, m, slot);
+      item_rsrc(e, tchunk, r0, wlo, whi);
+      item_xo(slot, xo);
+      copy_x(xs0, 0, xo);
+      copy_scales(e, r0);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb) load_w1(wlo, whi, r0, 0, rb, w0);
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb) load_w1(wlo, whi, r0, 1, rb, w1);
+      __builtin_amdgcn_sched_barrier(0);
+      wait_then_barrier<2 * kRB>();
     }
-    start_item();
     for (;;) {
       const int nit = it + per_die;
       const bool more = nit < hi;
-      if (more) {
-        fetch_tile(nit, ne, nstart, nm, nchunk);
-        fetch_rows(nstart, nm, nslot);
-      }
-      // activation block 0 and the scale rows of this item are in LDS for every wave (the
-      // eight youngest requests, the first weight blocks, may still be in flight)
-      wait_then_barrier<2 * kRB>();
-      kloop();
-      // every wave has finished the item's last block (barrier): the stages and the scale
-      // rows may be refilled; the next item's first requests go out before this item's
-      // epilogue
-      const int cstart = start, cm = m, cr0 = r0;
-      if (more) {
-        enter(ne, nstart, nm, nchunk, nslot);
-        start_item();
-      }
-      epilogue(cstart, cm, cr0);
+      if (more) fetch_tile(nit, ne, nstart, nm, nchunk);
+      // activation block 0 and the scale rows of this item are in LDS for every wave; the
+      // K loop ends with the next item's block 0 and scale rows in LDS and its first weight
+      // blocks requested
+      kloop(more);
+      epilogue(start, m, r0);
       it = nit;
       if (!more) break;
+      e = ne;
+      start = nstart;
+      m = nm;
+      r0 = nr0;
+      for (int c = 0; c < kNC; ++c) xo[c] = nxo[c];
+      wlo = nwlo;
+      whi = nwhi;
     }
   };
-
   run_class(ic<1>{}, local_tiles(header[1]) * chunks);
   run_class(ic<2>{}, local_tiles(header[2]) * chunks);
   run_class(ic<3>{}, local_tiles(header[3]) * chunks);
