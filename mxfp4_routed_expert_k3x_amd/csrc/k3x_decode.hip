@@ -177,6 +177,12 @@ struct LaneOffsets {
   uint32_t wa, wb, sa, sb;  // weight bytes and scale bytes of groups L and 64 + L
 };
 
+// Cache policy of the weight and scale loads: non-temporal.  A token reads each expert row
+// once, its weight bytes in whole cache lines per load instruction, so the stream's lines may
+// leave the caches first.  (The prefill's weight loads must not use it: each of them takes half
+// of every line it touches, and the other half is read one K block later.)
+constexpr int kStreamLoad = 2;
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const uint8_t* p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p), 0, bytes, 0x00020000);
 }
@@ -186,12 +192,12 @@ __device__ __forceinline__ void load_row(RowBits& b, const uint8_t* wexp, const 
                                          const LaneOffsets& o) {
   const __amdgpu_buffer_rsrc_t rw = row_rsrc(wexp + (size_t)r * wrow, wrow);
   const __amdgpu_buffer_rsrc_t rs = row_rsrc(sexp + (size_t)r * srow, srow);
-  const auto v0 = __builtin_amdgcn_raw_buffer_load_b128(rw, o.wa, 0, 0);
-  const auto v1 = __builtin_amdgcn_raw_buffer_load_b128(rw, o.wb, 0, 0);
+  const auto v0 = __builtin_amdgcn_raw_buffer_load_b128(rw, o.wa, 0, kStreamLoad);
+  const auto v1 = __builtin_amdgcn_raw_buffer_load_b128(rw, o.wb, 0, kStreamLoad);
   b.q0 = make_uint4(v0[0], v0[1], v0[2], v0[3]);
   b.q1 = make_uint4(v1[0], v1[1], v1[2], v1[3]);
-  b.s0 = __builtin_amdgcn_raw_buffer_load_b8(rs, o.sa, 0, 0);
-  b.s1 = __builtin_amdgcn_raw_buffer_load_b8(rs, o.sb, 0, 0);
+  b.s0 = __builtin_amdgcn_raw_buffer_load_b8(rs, o.sa, 0, kStreamLoad);
+  b.s1 = __builtin_amdgcn_raw_buffer_load_b8(rs, o.sb, 0, kStreamLoad);
 }
 
 // Reduce-scatter of eight leaves per vector (rows 0..3 of half A, then rows 0..3 of half B)
@@ -318,15 +324,15 @@ __device__ __forceinline__ void load_pair(PairBits& p, const uint8_t* wexp, cons
   const __amdgpu_buffer_rsrc_t s0 = row_rsrc(sexp + (size_t)r * srow, srow);
   const __amdgpu_buffer_rsrc_t s1 = row_rsrc(sexp + (size_t)r1 * srow, srow);
   const __amdgpu_buffer_rsrc_t sb = row_rsrc(sexp + (size_t)r * srow, nrows * srow);
-  const auto v0 = __builtin_amdgcn_raw_buffer_load_b128(w0, o.wa, 0, 0);
-  const auto v1 = __builtin_amdgcn_raw_buffer_load_b128(w1, o.wa, 0, 0);
-  const auto vb = __builtin_amdgcn_raw_buffer_load_b128(wb, o.wb, 0, 0);
+  const auto v0 = __builtin_amdgcn_raw_buffer_load_b128(w0, o.wa, 0, kStreamLoad);
+  const auto v1 = __builtin_amdgcn_raw_buffer_load_b128(w1, o.wa, 0, kStreamLoad);
+  const auto vb = __builtin_amdgcn_raw_buffer_load_b128(wb, o.wb, 0, kStreamLoad);
   p.a0 = make_uint4(v0[0], v0[1], v0[2], v0[3]);
   p.a1 = make_uint4(v1[0], v1[1], v1[2], v1[3]);
   p.b = make_uint4(vb[0], vb[1], vb[2], vb[3]);
-  p.s0 = __builtin_amdgcn_raw_buffer_load_b8(s0, o.sa, 0, 0);
-  p.s1 = __builtin_amdgcn_raw_buffer_load_b8(s1, o.sa, 0, 0);
-  p.sb = __builtin_amdgcn_raw_buffer_load_b8(sb, o.sb, 0, 0);
+  p.s0 = __builtin_amdgcn_raw_buffer_load_b8(s0, o.sa, 0, kStreamLoad);
+  p.s1 = __builtin_amdgcn_raw_buffer_load_b8(s1, o.sa, 0, kStreamLoad);
+  p.sb = __builtin_amdgcn_raw_buffer_load_b8(sb, o.sb, 0, kStreamLoad);
 }
 
 // Activations of the paired layout: x0 = group L, x1 = group 64 + (L & 31) (zero past G).
