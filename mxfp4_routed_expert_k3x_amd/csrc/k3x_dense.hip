@@ -109,6 +109,15 @@ __device__ __forceinline__ void wave_range(int rows, int pair0, int& r0, int& r1
 // row is requested before it, so the row's latency overlaps the staging.  The last row is
 // summed by a second copy of the loop body that requests nothing after it (a wave has only a
 // few rows, and a re-read of its last row would often miss the cache).
+// 16 bytes of a weight row, loaded non-temporal: each row is read once per launch, in whole
+// cache lines per load instruction, so its lines may leave the caches first (the block's
+// activations and the next launch's data stay).
+__device__ __forceinline__ uint4 stream_load16(const uint4* p) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 template <int NCH, int NT, bool kSplit, class Base, class Stage, class Emit>
 __device__ __forceinline__ void stream_dense(int r0, int r1, int na, const uint4* xs, int lane,
                                              Base base, Stage stage, Emit emit) {
@@ -119,7 +128,7 @@ __device__ __forceinline__ void stream_dense(int r0, int r1, int na, const uint4
     pb = pb - kWave * na;
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) b[i] = (i < na ? pa : pb)[lane + kWave * i];
+    for (int i = 0; i < NCH; ++i) b[i] = stream_load16((i < na ? pa : pb) + lane + kWave * i);
     __builtin_amdgcn_sched_barrier(0);
   };
   if (r0 < r1) load(cur, r0);
