@@ -577,7 +577,12 @@ __global__ __launch_bounds__(256) void moe_combine(const float* __restrict__ d,
       const bool ok = j < topk && expert_ok(it[j], E);
       g[jj] = ok ? gt[j] : 0.0f;
       const size_t row = pt ? (size_t)(ok ? pt[j] : 0) : (size_t)t * topk + j;
-      v[jj] = ok ? *reinterpret_cast<const float4*>(d + row * H + r) : make_float4(0.f, 0.f, 0.f, 0.f);
+      if (ok) {  // each d row is read once: non-temporal
+        const f32x4 q = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(d + row * H + r));
+        v[jj] = make_float4(q[0], q[1], q[2], q[3]);
+      } else {
+        v[jj] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
     }
 #pragma unroll
     for (int jj = 0; jj < 16; ++jj) {

@@ -488,8 +488,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_prefill(PrefillArgs a, const
             const f32x4 v = *reinterpret_cast<const f32x4*>(tw + p * kTrRow + 4 * (lane % 16));
             const int col = 16 * tb + p;
             if (col < cm)
-              *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + (size_t)(cstart + col) * a.rows + cr0 +
-                                        64 * wave + 4 * (lane % 16)) = v;
+              // non-temporal: the d rows are read once, by the combine, long after the cache
+              // has turned over
+              __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(static_cast<float*>(a.out) +
+                                                                      (size_t)(cstart + col) * a.rows + cr0 +
+                                                                      64 * wave + 4 * (lane % 16)));
           }
         }
       }
